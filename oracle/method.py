@@ -1,0 +1,157 @@
+"""The method, written out as its plain definition in fp64 (oracle side; test infrastructure).
+
+Source: "Day 0 Support for New LLM Architectures" (Step 1, sparse attention modules): a
+light indexer scores every earlier position for each query, the Top-K positions are kept,
+and exact attention then reads only those rows of the low-rank (latent + RoPE) KV cache;
+Key Optimization 1 orders the chain as relevance scoring, head-weight application, Top-K.
+Key Optimization 2 quantises the indexer's query dynamically; here that is one power-of-two
+scale per (token, head) so that the scaled query fits e4m3 (the reading used throughout).
+The score formula, the shapes and the tie rule (lower position wins) are the build's
+contract; the pages give them only in prose.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import bf16_decode, e4m3_decode, e4m3_round
+
+PAGE = 64
+
+
+# ----------------------------------------------------------------------------- A0
+def a0_scale(amax) -> np.ndarray:
+    """Smallest power of two s with amax <= 448*s (s = 1 when amax = 0).
+
+    Written with the binary exponent: amax = m*2^E with m in [0.5, 1); since 448 = 0.875*2^9,
+    s = 2^(E-9) when m <= 0.875 and 2^(E-8) otherwise."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, E = np.frexp(amax)
+    s = np.where(m <= 0.875, np.ldexp(1.0, E - 9), np.ldexp(1.0, E - 8))
+    return np.where(amax == 0.0, 1.0, s)
+
+
+def a0_quantize(q) -> tuple[np.ndarray, np.ndarray]:
+    """Dynamic e4m3 quantisation of an indexer query [..., H, D]: per (token, head) power-of-
+    two scale s; returns (q_hat, s) with q_hat = RNE_e4m3(q/s)*s, the value the scorer uses."""
+    q = np.asarray(q, dtype=np.float64)
+    s = a0_scale(np.abs(q).max(axis=-1))
+    return e4m3_round(q / s[..., None]) * s[..., None], s
+
+
+# ----------------------------------------------------------------------------- cache rows
+def decode_rows(pool, scale, pt_row, positions, fmt: str) -> np.ndarray:
+    """Logical positions of one request -> fp64 rows, through its page table.
+
+    Physical slot of position s: page_table[s // 64] * 64 + s % 64.  ``fmt`` is 'f32',
+    'bf16' (uint16 bits) or 'e4m3' (uint8 codes times the slot's fp32 scale, exact in fp64)."""
+    positions = np.asarray(positions, dtype=np.int64)
+    D = pool.shape[-1]
+    flat = pool.reshape(-1, D)
+    slot = np.asarray(pt_row, dtype=np.int64)[positions // PAGE] * PAGE + positions % PAGE
+    raw = flat[slot]
+    if fmt == "f32":
+        return raw.astype(np.float64)
+    if fmt == "bf16":
+        return bf16_decode(raw)
+    if fmt == "e4m3":
+        return e4m3_decode(raw) * scale.reshape(-1)[slot].astype(np.float64)[:, None]
+    raise ValueError(fmt)
+
+
+# ----------------------------------------------------------------------------- A1
+def token_scores(q_hat, w, k_hat) -> np.ndarray:
+    """S[s] = sum_h w[h] * max(0, q_hat[h] . k_hat[s]) for every row s of k_hat (fp64)."""
+    dots = np.asarray(k_hat, np.float64) @ np.asarray(q_hat, np.float64).T     # [n, H]
+    return np.maximum(dots, 0.0) @ np.asarray(w, np.float64)
+
+
+# ----------------------------------------------------------------------------- A2
+def topk_token(S, K: int):
+    """Top-K of one query: the k = min(K, n) largest S under (score desc, position asc).
+
+    Returns (idx[K] int32 ascending, -1 padded; the k-th largest score, or None if k = 0).
+    A full stable sort; -0.0 and +0.0 compare equal, so they tie and the position decides."""
+    S = np.asarray(S, dtype=np.float64)
+    n = S.shape[0]
+    k = min(int(K), n)
+    order = np.lexsort((np.arange(n), -S))   # primary: -S ascending; secondary: position
+    sel = np.sort(order[:k])
+    out = np.full(int(K), -1, dtype=np.int32)
+    out[:k] = sel
+    return out, (float(S[order[k - 1]]) if k > 0 else None)
+
+
+# ----------------------------------------------------------------------------- A3/A4
+def sparse_mla_token(q, rows, scale: float, D_v: int):
+    """Exact attention of one token over its selected latent rows (fp64).
+
+    z[h,s] = scale * q[h] . rows[s] (all D_qk dims); p = softmax_s(z); o[h] = sum_s p[h,s] *
+    rows[s, :D_v]; lse[h] = max_s z + ln sum_s exp(z - max).  No rows: o = 0, lse = -inf."""
+    q = np.asarray(q, np.float64)
+    rows = np.asarray(rows, np.float64)
+    H = q.shape[0]
+    if rows.shape[0] == 0:
+        return np.zeros((H, D_v)), np.full(H, -np.inf)
+    z = float(scale) * (q @ rows.T)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ rows[:, :D_v]) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+# ----------------------------------------------------------------------------- driver
+class Oracle:
+    """The oracle over one batch of raw inputs.
+
+    ``inp`` carries the boundary's raw arrays: seq_lens, cu_q, positions, req, page_table,
+    q_idx, w, k_pool, k_scale, q, kv_pool, kv_scale, and ``wl.shape`` (H_I, D_I, K, H, D_qk,
+    D_v, fp32, kv_fp8, softmax_scale).  ``qmode`` is 'fp8' (A0 applied to q_I, as the e4m3
+    scorer does) or 'none' (q_I used as stored)."""
+
+    def __init__(self, inp, qmode: str | None = None):
+        self.inp = inp
+        self.sh = inp.wl.shape
+        self.qmode = qmode or ("none" if self.sh.fp32 else "fp8")
+        self._kcache = (None, None)
+
+    # -- indexer keys of one request, decoded once
+    def k_rows(self, b: int, n: int) -> np.ndarray:
+        cb, rows = self._kcache
+        if cb != b or rows.shape[0] < n:
+            inp = self.inp
+            fmt = "f32" if self.sh.fp32 else "e4m3"
+            L = int(inp.seq_lens[b])
+            rows = decode_rows(inp.k_pool, inp.k_scale, inp.page_table[b], np.arange(L), fmt)
+            self._kcache = (b, rows)
+        return rows[:n]
+
+    def q_hat(self, t: int) -> np.ndarray:
+        qi = self.inp.q_idx[t]
+        qi = qi.astype(np.float64) if self.sh.fp32 else bf16_decode(qi)
+        if self.qmode == "fp8":
+            qi, _ = a0_quantize(qi)
+        return qi
+
+    def scores(self, t: int) -> np.ndarray:
+        """S[t, 0..p_t] (fp64)."""
+        b, p = int(self.inp.req[t]), int(self.inp.positions[t])
+        return token_scores(self.q_hat(t), self.inp.w[t].astype(np.float64),
+                            self.k_rows(b, p + 1))
+
+    def topk(self, t: int, K: int | None = None):
+        S = self.scores(t)
+        idx, kth = topk_token(S, self.sh.K if K is None else K)
+        return idx, S, kth
+
+    def attention(self, t: int, idx):
+        """Attention of token t over the positions in ``idx`` (entries <0 or >=L_b skipped)."""
+        inp, sh = self.inp, self.sh
+        b = int(inp.req[t])
+        L = int(inp.seq_lens[b])
+        idx = np.asarray(idx, dtype=np.int64)
+        idx = idx[(idx >= 0) & (idx < L)]
+        fmt = "f32" if sh.fp32 else ("e4m3" if sh.kv_fp8 else "bf16")
+        rows = decode_rows(inp.kv_pool, inp.kv_scale, inp.page_table[b], idx, fmt)
+        q = inp.q[t].astype(np.float64) if sh.fp32 else bf16_decode(inp.q[t])
+        return sparse_mla_token(q, rows, sh.softmax_scale, sh.D_v)
