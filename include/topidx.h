@@ -1,0 +1,158 @@
+/*
+ * topidx.h - C ABI of libtopidx.so: indexer-driven Top-K sparse attention over a paged
+ * latent (MLA-style) KV cache, for MI355X (gfx950).
+ *
+ * The method: "Day 0 Support for New LLM Architectures", Step 1 (sparse attention modules:
+ * a light indexer scores every earlier position, the Top-K positions are selected, and an
+ * exact sparse-attention kernel reads only those entries of the low-rank KV cache) and Key
+ * Optimization 1 (scoring, head weighting and Top-K fused into one kernel that reads the
+ * paged K cache directly; the chain ends as two kernels: indexer and sparse attention).
+ * "Day-0 Support for Large Model Inference", Core Operator Optimization items 1-2 (index
+ * stays resident on the device; selected rows are gathered, then attention is computed
+ * blockwise with fused normalisation).  "Achieving Day-0 Readiness ... Million-Token
+ * Context", section 2.2 (the cache is split into fixed-size blocks with a block index table).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless the name ends in _host.  The caller owns every
+ *    buffer; the library never allocates device memory, never synchronises the stream and
+ *    keeps no pointer after returning.  All work is enqueued on `stream` (a hipStream_t,
+ *    NULL = the null stream).
+ *  - Arguments are validated on the host before anything is enqueued.  On any status other
+ *    than TIS_OK nothing has been launched and no output has been written, except
+ *    TIS_ERR_HIP (a launch failed part-way; outputs are then unspecified).  The message of
+ *    the last failing call on the calling thread is returned by tis_last_error().
+ *  - Calls are reentrant; calls that share a workspace on overlapping streams race.
+ *  - Layouts are row-major and contiguous.  Caches are paged with 64 tokens per page:
+ *    pool[n_pages][64][D] (+ one fp32 scale per token slot, scale[n_pages][64]).  The
+ *    logical position s of request b lives in slot s % 64 of page page_table[b][s / 64].
+ *  - Request b holds seq_lens[b] positions.  Its query tokens are its LAST
+ *    q_len_b = cu_q[b+1] - cu_q[b] positions (the caller has already appended them to both
+ *    caches); flattened token t of request b sits at position p_t = seq_lens[b] - q_len_b +
+ *    (t - cu_q[b]) and attends causally to positions 0..p_t (n_t = p_t + 1 candidates).
+ *  - Page-table entries read by the library (logical pages below ceil(seq_lens[b]/64)) must
+ *    lie in [0, n_pages); a position whose page is out of range is never read: it scores
+ *    -inf and is skipped by attention.  Scales must be positive and finite; caches hold no
+ *    NaN/Inf codes.
+ */
+#ifndef TOPIDX_H
+#define TOPIDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TIS_ABI_VERSION 1
+#define TIS_PAGE_SIZE 64
+
+typedef enum {
+  TIS_OK = 0,
+  TIS_ERR_INVALID = 1,      /* bad argument (null, size, alignment, workspace too small) */
+  TIS_ERR_UNSUPPORTED = 2,  /* valid but not implemented dtype/shape combination */
+  TIS_ERR_HIP = 3           /* a HIP launch failed; see tis_last_error() */
+} tis_status_t;
+
+typedef enum { TIS_F32 = 0, TIS_BF16 = 1, TIS_E4M3 = 2 /* OCP E4M3FN */ } tis_dtype_t;
+
+/* Indexer query handling: FP8 = quantise each (token, head) row of q_I to e4m3 with the
+ * smallest power-of-two scale s that keeps max|q_I|/s <= 448 (round to nearest even), fold s
+ * into the head weight, and score on FP8 matrix cores; NONE = use q_I as stored (fp32 path). */
+typedef enum { TIS_QMODE_FP8 = 0, TIS_QMODE_NONE = 1 } tis_qmode_t;
+
+/* A ragged, paged batch.  Host copies of seq_lens and cu_q size the launch grids without a
+ * device round trip; they must equal the device copies. */
+typedef struct {
+  int32_t B;                     /* requests, >= 1 */
+  int32_t T;                     /* flattened query tokens = cu_q[B], >= 1 */
+  const int32_t* seq_lens;       /* [B]     positions held by each request (>= its q_len) */
+  const int32_t* cu_q;           /* [B+1]   query-token offsets, cu_q[0] = 0, nondecreasing */
+  const int32_t* seq_lens_host;  /* [B]     host copy */
+  const int32_t* cu_q_host;      /* [B+1]   host copy */
+  const int32_t* page_table;     /* [B][pt_stride] physical page of each logical page */
+  int32_t pt_stride;             /* >= ceil(max seq_len / 64) */
+  int32_t page_size;             /* must be TIS_PAGE_SIZE (64) */
+  int32_t n_pages;               /* pages in each pool (bounds page-table entries) */
+} tis_batch_t;
+
+/* index_score - indexer scores of every causal candidate.
+ *   score[t][s] = sum_h w[t][h] * max(0, q_I[t][h] . k_I[s]) for s in [0, p_t], where
+ *   k_I[s] = k_code[s] * k_scale[s] (e4m3 keys) or the fp32 key.  With TIS_QMODE_FP8 the
+ *   query is first quantised as described at tis_qmode_t.  Accumulation is fp32.
+ * q_idx   [T][H_I][D_I]  q_dt = TIS_BF16 (with k_dt = TIS_E4M3, qmode FP8; H_I = 64,
+ *                        D_I = 128) or TIS_F32 (with k_dt = TIS_F32, qmode NONE;
+ *                        H_I * D_I <= 8192)
+ * w       [T][H_I] fp32 head weights
+ * k_pool  [n_pages][64][D_I]; k_scale [n_pages][64] fp32 (e4m3 keys) or NULL (fp32 keys)
+ * scores  [T][ld_scores] fp32, ld_scores >= max p_t + 1 and a multiple of 4; entries
+ *         s > p_t are not written.
+ * ws      unused by this call (pass NULL, 0).
+ */
+tis_status_t index_score(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
+                         const float* w, const void* k_pool, tis_dtype_t k_dt,
+                         const float* k_scale, int32_t H_I, int32_t D_I, tis_qmode_t qmode,
+                         float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* topk_select - per-token Top-K over the scores of positions 0..p_t.
+ *   Selects the k_t = min(K, p_t + 1) positions that are largest under the total order
+ *   (score descending, position ascending); -0.0 and +0.0 are equal.  Scores must not be NaN.
+ * topk_idx [T][K] int32: the selected positions in ascending order, then -1 up to K.
+ * topk_val [T][K] fp32 or NULL: the score of each emitted position (0 where idx = -1).
+ * ws       workspace of topk_select_workspace_size() bytes (may be 0 / NULL).
+ */
+tis_status_t topk_select(const tis_batch_t* batch, const float* scores, int64_t ld_scores,
+                         int32_t K, int32_t* topk_idx, float* topk_val, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* index_score_topk - index_score followed by topk_select with no score tensor owned by the
+ * caller; identical results to the two calls.  ws: index_score_topk_workspace_size() bytes
+ * (holds the scores that do not stay on chip). */
+tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
+                              const float* w, const void* k_pool, tis_dtype_t k_dt,
+                              const float* k_scale, int32_t H_I, int32_t D_I,
+                              tis_qmode_t qmode, int32_t K, int32_t* topk_idx,
+                              float* topk_val, void* ws, size_t ws_bytes, void* stream);
+
+/* sparse_mla_attn - exact attention of each token over its selected latent rows.
+ *   For token t, head h and each valid entry s of topk_idx[t] (0 <= s < seq_lens[b]; other
+ *   entries, e.g. -1 padding, are skipped; duplicates count as given; causality is not
+ *   checked):  c_s = kv_code[s] * kv_scale[s] (e4m3) or the stored row,
+ *   z_s = softmax_scale * (q[t][h] . c_s[0:D_qk]),  out[t][h] = sum_s softmax(z)_s *
+ *   c_s[0:D_v],  lse[t][h] = ln sum_s exp(z_s)  (natural log).  A token with no valid entry
+ *   gets out = 0 and lse = -inf.  The value vector is the first D_v dims of the same row.
+ * q        [T][H][D_qk]  TIS_BF16 (H = 128, D_qk = 576, D_v = 512, kv TIS_BF16 or TIS_E4M3
+ *                        with kv_scale) or TIS_F32 (kv TIS_F32, kv_scale NULL,
+ *                        D_qk <= 1024, H <= 1024)
+ * kv_pool  [n_pages][64][D_qk]; kv_scale [n_pages][64] fp32 or NULL
+ * topk_idx [T][K] int32 logical positions
+ * out      [T][H][D_v] out_dt = TIS_BF16 or TIS_F32 with bf16 q; TIS_F32 with fp32 inputs.
+ *          (bf16 output rounds to 2^-9 relative; rows of large magnitude need TIS_F32.)
+ * lse      [T][H] fp32 or NULL
+ * ws       workspace of sparse_mla_attn_workspace_size() bytes (split-K partials).
+ */
+tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_t q_dt,
+                             const void* kv_pool, tis_dtype_t kv_dt, const float* kv_scale,
+                             const int32_t* topk_idx, int32_t K, int32_t H, int32_t D_qk,
+                             int32_t D_v, float softmax_scale, void* out, tis_dtype_t out_dt,
+                             float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace sizes in bytes for the calls above, from the host fields of `batch` only. */
+size_t index_score_workspace_size(const tis_batch_t* batch, int32_t H_I, int32_t D_I);
+size_t topk_select_workspace_size(const tis_batch_t* batch, int32_t K);
+size_t index_score_topk_workspace_size(const tis_batch_t* batch, int32_t H_I, int32_t D_I,
+                                       int32_t K);
+size_t sparse_mla_attn_workspace_size(const tis_batch_t* batch, int32_t K, int32_t H,
+                                      int32_t D_qk, int32_t D_v, tis_dtype_t kv_dt);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char* tis_last_error(void);
+
+/* TIS_ABI_VERSION of the loaded library. */
+int32_t tis_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TOPIDX_H */

@@ -1,0 +1,119 @@
+"""The C ABI library on the CPU: it loads, exports every symbol include/topidx.h declares,
+and rejects bad arguments on the host before any launch (no GPU calls are made)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import top_indexed_sparse_amd as tis
+from top_indexed_sparse_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "topidx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    lib = tis.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.tis_abi_version() == 1
+
+
+class FakeBatch:
+    """Host-side view of a batch with dummy (never dereferenced) device pointers."""
+
+    def __init__(self, seq_lens, cu_q, pt_stride=None, page_size=64, n_pages=100):
+        self.sl = np.asarray(seq_lens, np.int32)
+        self.cq = np.asarray(cu_q, np.int32)
+        stride = pt_stride or max(1, -(-int(self.sl.max()) // 64))
+        dummy = 0x100000
+        self.c = L.TisBatch(len(self.sl), int(self.cq[-1]), dummy, dummy, self.sl.ctypes.data,
+                            self.cq.ctypes.data, dummy, stride, page_size, n_pages)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+D = 0x200000  # dummy 16-byte aligned "device" address, never touched on error paths
+
+
+def call_index(b, **kw):
+    a = dict(q=D, qdt=L.TIS_BF16, w=D, k=D, kdt=L.TIS_E4M3, ks=D, H=64, Dd=128,
+             qm=L.TIS_QMODE_FP8, sc=D, ld=1024)
+    a.update(kw)
+    return tis.lib().index_score(b.ref, a["q"], a["qdt"], a["w"], a["k"], a["kdt"], a["ks"],
+                                 a["H"], a["Dd"], a["qm"], a["sc"], a["ld"], None, 0, None)
+
+
+def call_attn(b, **kw):
+    a = dict(q=D, qdt=L.TIS_BF16, kv=D, kvdt=L.TIS_BF16, kvs=None, idx=D, K=64, H=128, Dqk=576,
+             Dv=512, scale=0.1, out=D, odt=L.TIS_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return tis.lib().sparse_mla_attn(b.ref, a["q"], a["qdt"], a["kv"], a["kvdt"], a["kvs"],
+                                     a["idx"], a["K"], a["H"], a["Dqk"], a["Dv"], a["scale"],
+                                     a["out"], a["odt"], None, a["ws"], a["wsb"], None)
+
+
+def last_error():
+    return tis.lib().tis_last_error().decode()
+
+
+def test_batch_validation():
+    lib = tis.lib()
+    assert lib.index_score(None, D, 1, D, D, 2, D, 64, 128, 0, D, 1024, None, 0, None) == 1
+    assert "NULL" in last_error()
+    bad = [
+        FakeBatch([100], [0, 1], page_size=32),              # page size must be 64
+        FakeBatch([100], [1, 2]),                            # cu_q[0] != 0
+        FakeBatch([100, 50], [0, 3, 2]),                     # decreasing cu_q
+        FakeBatch([2], [0, 3]),                              # more queries than positions
+        FakeBatch([1000], [0, 1], pt_stride=2),              # page table too narrow
+    ]
+    for b in bad:
+        assert call_index(b) == L.TIS_ERR_INVALID, last_error()
+
+
+def test_index_argument_validation():
+    b = FakeBatch([1000, 600], [0, 1, 3])
+    assert call_index(b, ld=999) == L.TIS_ERR_INVALID         # ld < max seq len
+    assert call_index(b, ld=1002) == L.TIS_ERR_INVALID        # ld not a multiple of 4
+    assert call_index(b, q=D + 4) == L.TIS_ERR_INVALID        # misaligned
+    assert call_index(b, ks=None) == L.TIS_ERR_INVALID        # e4m3 keys need scales
+    assert call_index(b, H=32) == L.TIS_ERR_UNSUPPORTED
+    assert call_index(b, qdt=L.TIS_F32) == L.TIS_ERR_UNSUPPORTED
+    assert call_index(b, qdt=L.TIS_F32, kdt=L.TIS_F32, qm=L.TIS_QMODE_NONE, ks=None, H=64,
+                      Dd=256) == L.TIS_ERR_UNSUPPORTED   # 64*256 > 8192
+    lib = tis.lib()
+    assert lib.topk_select(b.ref, D, 1024, 0, D, None, None, 0, None) == L.TIS_ERR_INVALID
+    assert lib.topk_select(b.ref, D, 1000, 10, None, None, None, 0, None) == L.TIS_ERR_INVALID
+    need = lib.index_score_topk_workspace_size(b.ref, 64, 128, 16)
+    assert need == 3 * 1000 * 4          # T=3 rows of ld=1000 scores
+    assert lib.index_score_topk(b.ref, D, L.TIS_BF16, D, D, L.TIS_E4M3, D, 64, 128,
+                                L.TIS_QMODE_FP8, 16, D, None, D, need - 1, None) == L.TIS_ERR_INVALID
+    assert "workspace" in last_error()
+
+
+def test_attention_argument_validation():
+    b = FakeBatch([1000], [0, 32])
+    assert call_attn(b, Dv=600) == L.TIS_ERR_INVALID
+    assert call_attn(b, K=0) == L.TIS_ERR_INVALID
+    assert call_attn(b, scale=float("nan")) == L.TIS_ERR_INVALID
+    assert call_attn(b, kvdt=L.TIS_E4M3) == L.TIS_ERR_INVALID      # needs kv_scale
+    assert call_attn(b, kvs=D) == L.TIS_ERR_INVALID                # bf16 takes no scale
+    assert call_attn(b, H=64) == L.TIS_ERR_UNSUPPORTED
+    assert call_attn(b, odt=L.TIS_F32) == L.TIS_ERR_UNSUPPORTED
+    need = tis.lib().sparse_mla_attn_workspace_size(b.ref, 64, 128, 576, 512, L.TIS_BF16)
+    if need:
+        assert call_attn(b, ws=D, wsb=need - 16) == L.TIS_ERR_INVALID
+    # tiny fp32 path needs no workspace
+    assert tis.lib().sparse_mla_attn_workspace_size(b.ref, 64, 8, 80, 64, L.TIS_F32) == 0

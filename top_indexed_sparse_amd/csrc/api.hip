@@ -1,0 +1,311 @@
+// C ABI of libtopidx: host-side validation, workspace sizing and kernel dispatch.
+// Every check runs on the host before anything is enqueued; the library never allocates
+// device memory and never synchronises the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+
+#include "launch.h"
+#include "topidx.h"
+
+#define TIS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+tis_status_t fail(tis_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+tis_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(TIS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Scores that do not stay on chip go to a workspace of at most this many bytes; longer
+// batches are processed in row chunks.
+constexpr size_t kScoreScratchBudget = size_t(1) << 30;
+
+struct HostInfo {
+  int max_n = 0;   // longest causal range of any query token (= max seq_len with q_len > 0)
+  int max_q = 0;   // longest query run of a request
+  bool prefill_like = false;
+};
+
+tis_status_t check_batch(const tis_batch_t* b, HostInfo* hi) {
+  if (!b) return fail(TIS_ERR_INVALID, "batch is NULL");
+  if (b->B < 1 || b->T < 1) return fail(TIS_ERR_INVALID, "batch needs B >= 1 and T >= 1");
+  if (!b->seq_lens || !b->cu_q || !b->seq_lens_host || !b->cu_q_host || !b->page_table)
+    return fail(TIS_ERR_INVALID, "batch has a NULL array");
+  if (b->page_size != TIS_PAGE_SIZE)
+    return fail(TIS_ERR_INVALID, "page_size must be %d (got %d)", TIS_PAGE_SIZE, b->page_size);
+  if (b->pt_stride < 1 || b->n_pages < 1)
+    return fail(TIS_ERR_INVALID, "pt_stride and n_pages must be >= 1");
+  if (b->cu_q_host[0] != 0) return fail(TIS_ERR_INVALID, "cu_q[0] must be 0");
+  if (b->cu_q_host[b->B] != b->T) return fail(TIS_ERR_INVALID, "cu_q[B] must equal T");
+  HostInfo h;
+  for (int r = 0; r < b->B; ++r) {
+    const int q = b->cu_q_host[r + 1] - b->cu_q_host[r];
+    const int L = b->seq_lens_host[r];
+    if (q < 0) return fail(TIS_ERR_INVALID, "cu_q must be nondecreasing (request %d)", r);
+    if (L < q) return fail(TIS_ERR_INVALID, "seq_lens[%d]=%d < its %d query tokens", r, L, q);
+    if ((int64_t)L > (int64_t)b->pt_stride * TIS_PAGE_SIZE)
+      return fail(TIS_ERR_INVALID, "seq_lens[%d]=%d exceeds pt_stride*64", r, L);
+    if (L > (1 << 30)) return fail(TIS_ERR_INVALID, "seq_lens[%d] too large", r);
+    if (q > 0) h.max_n = std::max(h.max_n, L);
+    h.max_q = std::max(h.max_q, q);
+  }
+  h.prefill_like = (int64_t)b->T >= 4 * (int64_t)b->B;
+  if (hi) *hi = h;
+  return TIS_OK;
+}
+
+tis::DevBatch dev_batch(const tis_batch_t* b) {
+  tis::DevBatch d;
+  d.seq_lens = b->seq_lens;
+  d.cu_q = b->cu_q;
+  d.page_table = b->page_table;
+  d.B = b->B;
+  d.T = b->T;
+  d.pt_stride = b->pt_stride;
+  d.n_pages = b->n_pages;
+  return d;
+}
+
+enum class IdxPath { F32, FP8 };
+
+tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* w,
+                              const void* k_pool, tis_dtype_t k_dt, const float* k_scale,
+                              int32_t H_I, int32_t D_I, tis_qmode_t qmode, IdxPath* path) {
+  if (!q_idx || !w || !k_pool) return fail(TIS_ERR_INVALID, "q_idx, w and k_pool must be set");
+  if (!aligned16(q_idx) || !aligned16(k_pool) || !aligned16(w))
+    return fail(TIS_ERR_INVALID, "q_idx, w and k_pool must be 16-byte aligned");
+  if (H_I < 1 || D_I < 1) return fail(TIS_ERR_INVALID, "H_I and D_I must be >= 1");
+  if (q_dt == TIS_F32 && k_dt == TIS_F32 && qmode == TIS_QMODE_NONE) {
+    if (k_scale) return fail(TIS_ERR_INVALID, "fp32 keys take no k_scale");
+    if ((int64_t)H_I * D_I > 8192)
+      return fail(TIS_ERR_UNSUPPORTED, "fp32 indexer supports H_I*D_I <= 8192");
+    *path = IdxPath::F32;
+    return TIS_OK;
+  }
+  if (q_dt == TIS_BF16 && k_dt == TIS_E4M3 && qmode == TIS_QMODE_FP8) {
+    if (!k_scale || !aligned16(k_scale))
+      return fail(TIS_ERR_INVALID, "e4m3 keys need a 16-byte aligned k_scale");
+    if (H_I != 64 || D_I != 128)
+      return fail(TIS_ERR_UNSUPPORTED, "e4m3 indexer supports H_I=64, D_I=128");
+    *path = IdxPath::FP8;
+    return TIS_OK;
+  }
+  return fail(TIS_ERR_UNSUPPORTED, "indexer supports (f32,f32,NONE) and (bf16,e4m3,FP8)");
+}
+
+tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath path, int t0,
+                       int tc, const void* q_idx, const float* w, const void* k_pool,
+                       const float* k_scale, int H_I, int D_I, float* scores, int64_t ld,
+                       hipStream_t st) {
+  const tis::DevBatch d = dev_batch(batch);
+  hipError_t e;
+  if (path == IdxPath::F32)
+    e = tis::launch_index_score_f32(d, t0, tc, hi.max_n, (const float*)q_idx, w,
+                                    (const float*)k_pool, H_I, D_I, scores, ld, st);
+  else
+    e = tis::launch_index_score_fp8(d, t0, tc, hi.max_n, hi.prefill_like,
+                                    (const uint16_t*)q_idx, w, (const uint8_t*)k_pool, k_scale,
+                                    scores, ld, st);
+  return e == hipSuccess ? TIS_OK : hip_fail(e, "index_score launch");
+}
+
+int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
+
+int fused_rows_per_chunk(const tis_batch_t* b, const HostInfo& hi) {
+  const int64_t row_bytes = round4(hi.max_n) * 4;
+  int64_t r = (int64_t)kScoreScratchBudget / std::max<int64_t>(row_bytes, 1);
+  r = std::max<int64_t>(1, std::min<int64_t>(r, b->T));
+  return (int)r;
+}
+
+enum class AttnPath { F32, MFMA };
+
+tis_status_t check_attn_args(const void* q, tis_dtype_t q_dt, const void* kv_pool,
+                             tis_dtype_t kv_dt, const float* kv_scale, const int32_t* topk_idx,
+                             int32_t K, int32_t H, int32_t D_qk, int32_t D_v,
+                             float softmax_scale, const void* out, tis_dtype_t out_dt,
+                             AttnPath* path) {
+  if (!q || !kv_pool || !topk_idx || !out)
+    return fail(TIS_ERR_INVALID, "q, kv_pool, topk_idx and out must be set");
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned16(topk_idx))
+    return fail(TIS_ERR_INVALID, "q, kv_pool, topk_idx and out must be 16-byte aligned");
+  if (K < 1 || H < 1 || D_qk < 1 || D_v < 1) return fail(TIS_ERR_INVALID, "K, H, D must be >= 1");
+  if (D_v > D_qk) return fail(TIS_ERR_INVALID, "D_v (%d) > D_qk (%d)", D_v, D_qk);
+  if (!std::isfinite(softmax_scale)) return fail(TIS_ERR_INVALID, "softmax_scale not finite");
+  if (q_dt == TIS_F32 && kv_dt == TIS_F32 && out_dt == TIS_F32) {
+    if (kv_scale) return fail(TIS_ERR_INVALID, "fp32 cache takes no kv_scale");
+    if (D_qk > 1024 || H > 1024 || (int64_t)(D_qk + 2 * K) * 4 > 64 * 1024)
+      return fail(TIS_ERR_UNSUPPORTED, "fp32 attention supports D_qk<=1024, H<=1024, small K");
+    *path = AttnPath::F32;
+    return TIS_OK;
+  }
+  if (q_dt == TIS_BF16 && (out_dt == TIS_BF16 || out_dt == TIS_F32) &&
+      (kv_dt == TIS_BF16 || kv_dt == TIS_E4M3)) {
+    if (kv_dt == TIS_E4M3 && (!kv_scale || !aligned16(kv_scale)))
+      return fail(TIS_ERR_INVALID, "e4m3 cache needs a 16-byte aligned kv_scale");
+    if (kv_dt == TIS_BF16 && kv_scale) return fail(TIS_ERR_INVALID, "bf16 cache takes no kv_scale");
+    if (H != 128 || D_qk != 576 || D_v != 512)
+      return fail(TIS_ERR_UNSUPPORTED, "bf16 attention supports H=128, D_qk=576, D_v=512");
+    *path = AttnPath::MFMA;
+    return TIS_OK;
+  }
+  return fail(TIS_ERR_UNSUPPORTED, "attention supports all-fp32 or bf16 q/out with bf16|e4m3 cache");
+}
+
+size_t attn_ws_bytes(const tis_batch_t* b, int32_t K, AttnPath path) {
+  if (path == AttnPath::F32) return 0;
+  const int ns = tis::attn_split_count(b->T, K);
+  if (ns == 1) return 0;
+  return (size_t)b->T * ns * 128 * (512 + 4) * sizeof(float);
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+TIS_API int32_t tis_abi_version(void) { return TIS_ABI_VERSION; }
+
+TIS_API const char* tis_last_error(void) { return g_err.c_str(); }
+
+TIS_API size_t index_score_workspace_size(const tis_batch_t* batch, int32_t H_I, int32_t D_I) {
+  (void)batch; (void)H_I; (void)D_I;
+  return 0;
+}
+
+TIS_API size_t topk_select_workspace_size(const tis_batch_t* batch, int32_t K) {
+  (void)batch; (void)K;
+  return 0;
+}
+
+TIS_API size_t index_score_topk_workspace_size(const tis_batch_t* batch, int32_t H_I,
+                                               int32_t D_I, int32_t K) {
+  (void)H_I; (void)D_I; (void)K;
+  HostInfo hi;
+  if (check_batch(batch, &hi) != TIS_OK) return 0;
+  return (size_t)fused_rows_per_chunk(batch, hi) * (size_t)round4(hi.max_n) * sizeof(float);
+}
+
+TIS_API size_t sparse_mla_attn_workspace_size(const tis_batch_t* batch, int32_t K, int32_t H,
+                                              int32_t D_qk, int32_t D_v, tis_dtype_t kv_dt) {
+  if (check_batch(batch, nullptr) != TIS_OK || K < 1) return 0;
+  const bool mfma = (kv_dt == TIS_BF16 || kv_dt == TIS_E4M3) && H == 128 && D_qk == 576 &&
+                    D_v == 512;
+  return attn_ws_bytes(batch, K, mfma ? AttnPath::MFMA : AttnPath::F32);
+}
+
+TIS_API tis_status_t index_score(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
+                                 const float* w, const void* k_pool, tis_dtype_t k_dt,
+                                 const float* k_scale, int32_t H_I, int32_t D_I,
+                                 tis_qmode_t qmode, float* scores, int64_t ld_scores, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  IdxPath path;
+  st = check_index_args(q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I, qmode, &path);
+  if (st != TIS_OK) return st;
+  if (!scores || !aligned16(scores)) return fail(TIS_ERR_INVALID, "scores must be 16-byte aligned");
+  if (ld_scores < hi.max_n || (ld_scores & 3))
+    return fail(TIS_ERR_INVALID, "ld_scores must be >= %d and a multiple of 4", hi.max_n);
+  return run_index(batch, hi, path, 0, batch->T, q_idx, w, k_pool, k_scale, H_I, D_I, scores,
+                   ld_scores, (hipStream_t)stream);
+}
+
+TIS_API tis_status_t topk_select(const tis_batch_t* batch, const float* scores,
+                                 int64_t ld_scores, int32_t K, int32_t* topk_idx,
+                                 float* topk_val, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  if (K < 1) return fail(TIS_ERR_INVALID, "K must be >= 1");
+  if (!scores || !topk_idx) return fail(TIS_ERR_INVALID, "scores and topk_idx must be set");
+  if (!aligned16(scores)) return fail(TIS_ERR_INVALID, "scores must be 16-byte aligned");
+  if (ld_scores < hi.max_n || (ld_scores & 3))
+    return fail(TIS_ERR_INVALID, "ld_scores must be >= %d and a multiple of 4", hi.max_n);
+  hipError_t e = tis::launch_topk(dev_batch(batch), 0, batch->T, scores, ld_scores, K, topk_idx,
+                                  topk_val, (hipStream_t)stream);
+  return e == hipSuccess ? TIS_OK : hip_fail(e, "topk_select launch");
+}
+
+TIS_API tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx,
+                                      tis_dtype_t q_dt, const float* w, const void* k_pool,
+                                      tis_dtype_t k_dt, const float* k_scale, int32_t H_I,
+                                      int32_t D_I, tis_qmode_t qmode, int32_t K,
+                                      int32_t* topk_idx, float* topk_val, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  IdxPath path;
+  st = check_index_args(q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I, qmode, &path);
+  if (st != TIS_OK) return st;
+  if (K < 1) return fail(TIS_ERR_INVALID, "K must be >= 1");
+  if (!topk_idx) return fail(TIS_ERR_INVALID, "topk_idx must be set");
+  const int rows = fused_rows_per_chunk(batch, hi);
+  const int64_t ld = round4(hi.max_n);
+  const size_t need = (size_t)rows * (size_t)ld * sizeof(float);
+  if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
+    return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
+  hipStream_t s = (hipStream_t)stream;
+  float* sc = (float*)ws;
+  const tis::DevBatch d = dev_batch(batch);
+  for (int t0 = 0; t0 < batch->T; t0 += rows) {
+    const int tc = std::min(rows, batch->T - t0);
+    st = run_index(batch, hi, path, t0, tc, q_idx, w, k_pool, k_scale, H_I, D_I, sc, ld, s);
+    if (st != TIS_OK) return st;
+    hipError_t e = tis::launch_topk(d, t0, tc, sc, ld, K, topk_idx, topk_val, s);
+    if (e != hipSuccess) return hip_fail(e, "index_score_topk select launch");
+  }
+  return TIS_OK;
+}
+
+TIS_API tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_t q_dt,
+                                     const void* kv_pool, tis_dtype_t kv_dt,
+                                     const float* kv_scale, const int32_t* topk_idx, int32_t K,
+                                     int32_t H, int32_t D_qk, int32_t D_v, float softmax_scale,
+                                     void* out, tis_dtype_t out_dt, float* lse, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  AttnPath path;
+  st = check_attn_args(q, q_dt, kv_pool, kv_dt, kv_scale, topk_idx, K, H, D_qk, D_v,
+                       softmax_scale, out, out_dt, &path);
+  if (st != TIS_OK) return st;
+  const size_t need = attn_ws_bytes(batch, K, path);
+  if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
+    return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
+  hipStream_t s = (hipStream_t)stream;
+  const tis::DevBatch d = dev_batch(batch);
+  hipError_t e;
+  if (path == AttnPath::F32) {
+    e = tis::launch_mla_attn_f32(d, 0, batch->T, (const float*)q, (const float*)kv_pool, topk_idx,
+                                 K, H, D_qk, D_v, softmax_scale, (float*)out, lse, s);
+  } else {
+    const int ns = tis::attn_split_count(batch->T, K);
+    float* part_o = ns > 1 ? (float*)ws : nullptr;
+    float* part_ml = ns > 1 ? part_o + (size_t)batch->T * ns * 128 * 512 : nullptr;
+    e = tis::launch_mla_attn(d, 0, batch->T, kv_dt == TIS_E4M3, (const uint16_t*)q,
+                             (const uint8_t*)kv_pool, kv_scale, topk_idx, K, softmax_scale, ns,
+                             out, out_dt == TIS_F32, lse, part_o, part_ml, s);
+  }
+  return e == hipSuccess ? TIS_OK : hip_fail(e, "sparse_mla_attn launch");
+}

@@ -1,0 +1,32 @@
+// Host-side launchers of the gfx950 kernels (internal to libtopidx).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace tis {
+
+hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, int max_n,
+                                  const float* q, const float* w, const float* kpool, int H,
+                                  int D, float* scores, int64_t ld, hipStream_t st);
+hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
+                                  bool prefill_like, const uint16_t* q_idx, const float* w,
+                                  const uint8_t* kpool, const float* kscale, float* scores,
+                                  int64_t ld, hipStream_t st);
+hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, const float* scores,
+                       int64_t ld, int K, int32_t* idx, float* val, hipStream_t st);
+hipError_t launch_mla_attn_f32(const DevBatch& bt, int t_begin, int t_count, const float* q,
+                               const float* kv, const int32_t* idx, int K, int H, int Dqk,
+                               int Dv, float scale, float* out, float* lse, hipStream_t st);
+hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp8,
+                           const uint16_t* q, const uint8_t* kv, const float* kvscale,
+                           const int32_t* idx, int K, float softmax_scale, int nsplit,
+                           void* out, bool out_f32, float* lse, float* part_o, float* part_ml,
+                           hipStream_t st);
+int attn_split_count(int t_count, int K);
+int attn_keys_per_split(int K, int nsplit);
+size_t attn_smem_bytes(bool fp8, int kps);
+
+}  // namespace tis
