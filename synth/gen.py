@@ -136,7 +136,7 @@ def make(wl: Workload, mode: str = "continuous", seed: int | None = None,
 
     seq_lens = np.asarray(wl.seq_lens, dtype=np.int32)
     q_lens = np.asarray(wl.q_lens, dtype=np.int32)
-    assert np.all(q_lens >= 1) and np.all(q_lens <= seq_lens)
+    assert np.all(q_lens >= 0) and np.all(q_lens <= seq_lens) and q_lens.sum() >= 1
     cu_q = np.zeros(wl.B + 1, dtype=np.int32)
     cu_q[1:] = np.cumsum(q_lens)
     T = int(cu_q[-1])

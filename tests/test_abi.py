@@ -111,7 +111,7 @@ def test_attention_argument_validation():
     assert call_attn(b, kvdt=L.TIS_E4M3) == L.TIS_ERR_INVALID      # needs kv_scale
     assert call_attn(b, kvs=D) == L.TIS_ERR_INVALID                # bf16 takes no scale
     assert call_attn(b, H=64) == L.TIS_ERR_UNSUPPORTED
-    assert call_attn(b, odt=L.TIS_F32) == L.TIS_ERR_UNSUPPORTED
+    assert call_attn(b, qdt=L.TIS_F32) == L.TIS_ERR_UNSUPPORTED    # fp32 q, bf16 cache
     need = tis.lib().sparse_mla_attn_workspace_size(b.ref, 64, 128, 576, 512, L.TIS_BF16)
     if need:
         assert call_attn(b, ws=D, wsb=need - 16) == L.TIS_ERR_INVALID

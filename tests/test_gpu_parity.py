@@ -103,6 +103,21 @@ def test_ragged_small():
     _common(inp, r, sample_tokens(inp, 80), False)
 
 
+def test_many_requests_with_empty_ones():
+    """150 requests (more than one 64-request window of the token locator), some with no query
+    tokens (cu_q repeats), some with several."""
+    rng = np.random.default_rng(5)
+    B = 150
+    L = rng.integers(40, 700, size=B).tolist()
+    q = [0 if i % 17 == 3 else (5 if i % 23 == 0 else 1) for i in range(B)]
+    q[0] = q[-1] = 0
+    wl = synth.reduced(synth.workload(synth.DECODE32K), L, q)
+    inp = synth.make(wl, "continuous")
+    note(f"case many-requests B={B} T={inp.T}")
+    r = run_path(inp)
+    _common(inp, r, list(range(inp.T)), False)
+
+
 def test_determinism():
     wl = synth.reduced(synth.workload(synth.DECODE32K), [4096, 3000], [1, 1])
     inp = synth.make(wl, "continuous")

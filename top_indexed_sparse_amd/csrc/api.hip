@@ -240,7 +240,7 @@ TIS_API tis_status_t topk_select(const tis_batch_t* batch, const float* scores,
   if (!aligned16(scores)) return fail(TIS_ERR_INVALID, "scores must be 16-byte aligned");
   if (ld_scores < hi.max_n || (ld_scores & 3))
     return fail(TIS_ERR_INVALID, "ld_scores must be >= %d and a multiple of 4", hi.max_n);
-  hipError_t e = tis::launch_topk(dev_batch(batch), 0, batch->T, scores, ld_scores, K, topk_idx,
+  hipError_t e = tis::launch_topk(dev_batch(batch), 0, batch->T, hi.max_n, scores, ld_scores, K, topk_idx,
                                   topk_val, (hipStream_t)stream);
   return e == hipSuccess ? TIS_OK : hip_fail(e, "topk_select launch");
 }
@@ -271,7 +271,7 @@ TIS_API tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_id
     const int tc = std::min(rows, batch->T - t0);
     st = run_index(batch, hi, path, t0, tc, q_idx, w, k_pool, k_scale, H_I, D_I, sc, ld, s);
     if (st != TIS_OK) return st;
-    hipError_t e = tis::launch_topk(d, t0, tc, sc, ld, K, topk_idx, topk_val, s);
+    hipError_t e = tis::launch_topk(d, t0, tc, hi.max_n, sc, ld, K, topk_idx, topk_val, s);
     if (e != hipSuccess) return hip_fail(e, "index_score_topk select launch");
   }
   return TIS_OK;

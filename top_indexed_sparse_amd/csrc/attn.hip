@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256) void mla_attn_f32_kernel(DevBatch bt, int t_be
   int* slots = (int*)(z + K);
   __shared__ float red[64];
   const int t = t_begin + blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int b = find_request(bt, t);
-  const int L = bt.seq_lens[b];
+  const TokLoc loc = locate(bt, t);
+  const int b = loc.b;
+  const int L = loc.L;
   for (int d = tid; d < Dqk; d += blockDim.x) sq[d] = q[((int64_t)t * H + h) * Dqk + d];
   for (int i = tid; i < K; i += blockDim.x) {
     const int s = idx[(int64_t)t * K + i];
@@ -94,12 +95,24 @@ __global__ __launch_bounds__(256) void mla_attn_f32_kernel(DevBatch bt, int t_be
 // ---------------------------------------------------------------- matrix-core kernel
 constexpr int kH = 128, kDqk = 576, kDv = 512, kTile = 32;
 
+// One gather stage holds 32 bf16 rows or 64 e4m3 rows, each followed by a 16-byte pad chunk:
+// 2336 or 2368 chunks of 16 bytes, stored in a 2368-chunk buffer.  Every wave issues ten
+// 16-byte-per-lane global->LDS loads per stage: nine windows of its own (chunks
+// 256i + 64w + lane) and a tenth window [2304, 2368) that all four waves load with identical
+// bytes.  The count per wave is therefore always ten, which lets the waits use immediates.
+// Lanes whose chunk is a pad (or beyond the rows) load row 0 into it; those bytes are never
+// read.
 template <bool FP8>
 struct KvFmt {
   static constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;  // 576 or 1152
-  static constexpr int kChunks = kRowBytes / 16 + 1;        // 16-byte chunks per LDS row (+pad)
-  static constexpr int kRS = kChunks * 16;                  // LDS row stride
-  static constexpr int kTileBytes = kTile * kRS;
+  static constexpr int kCpr = kRowBytes / 16 + 1;           // chunks per LDS row incl. pad
+  static constexpr int kRS = kCpr * 16;                     // LDS row stride
+  static constexpr int kStageRows = FP8 ? 64 : 32;
+  static constexpr int kStageChunks = 2368;
+  static constexpr int kStageBytes = kStageChunks * 16;    // 37888
+  static constexpr int kStages = FP8 ? 3 : 4;               // LDS ring depth
+  static constexpr int kIssue = 10;
+  static_assert(kStageRows * kCpr <= kStageChunks, "stage rows overflow the buffer");
 };
 
 struct AttnSmem {  // offsets into dynamic LDS
@@ -116,14 +129,15 @@ __host__ __device__ constexpr AttnSmem attn_smem(int kps) {
   s.scn = o; o += FP8 ? kps * 4 : 0;
   s.rsc = o; o += FP8 ? kps * 4 : 0;
   o = (o + 15) & ~15;
-  s.tiles = o; o += 2 * KvFmt<FP8>::kTileBytes;
+  s.tiles = o; o += KvFmt<FP8>::kStages * KvFmt<FP8>::kStageBytes;
   s.total = o;
   return s;
 }
 
 // Four consecutive outputs at element offset `off`: fp32, or bf16 (round to nearest even).
-__device__ __forceinline__ void store_out4(void* out, int out_f32, int64_t off, f32x4 v) {
-  if (out_f32) {
+template <bool OUT_F32>
+__device__ __forceinline__ void store_out4(void* out, int64_t off, f32x4 v) {
+  if (OUT_F32) {
     *(f32x4*)((float*)out + off) = v;
   } else {
     const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
@@ -150,11 +164,25 @@ __device__ __forceinline__ void acc_scale(f32x16& acc, float alpha) {
   }
 }
 
-template <bool FP8>
+// s_waitcnt with vmcnt <= n (n < 64), other counters untouched (gfx9 encoding).
+#define TIS_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
+
+__device__ __forceinline__ void wait_stages_after(int later) {
+  // each stage issued after the awaited one contributes 10 outstanding loads per wave
+  switch (later) {
+    case 0: TIS_WAIT_VM(0); break;
+    case 1: TIS_WAIT_VM(10); break;
+    case 2: TIS_WAIT_VM(20); break;
+    default: TIS_WAIT_VM(30); break;
+  }
+}
+
+template <bool FP8, bool OUT_F32>
 __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_count,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
     const float* __restrict__ kvscale, const int32_t* __restrict__ idx, int K, float c2,
-    int nsplit, int kps, void* __restrict__ out, int out_f32, float* __restrict__ lse,
+    int nsplit, int kps, void* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   using F = KvFmt<FP8>;
   extern __shared__ __attribute__((aligned(16))) char sm[];
@@ -169,17 +197,31 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
+  const int g = lane >> 4, gi = lane & 15;
   const int tl = blockIdx.x % t_count, split = blockIdx.x / t_count;
   const int t = t_begin + tl;
-  const int b = find_request(bt, t);
-  const int Lb = bt.seq_lens[b];
+
+  // ---- this wave's 32 query heads as MFMA B fragments (dims 16ks + 8h .. +7); issued first
+  //      so their latency overlaps the index translation
+  bf16x8 qf[kDqk / 16];
+  {
+    const uint16_t* qr = q + ((int64_t)t * kH + wave * 32 + col) * kDqk + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 16; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
+  }
+
+  const TokLoc loc = locate(bt, t);
+  const int b = loc.b;
+  const int Lb = loc.L;
   const int kbeg = split * kps;
   const int nk = min(kps, K - kbeg);
   const int ntiles = (nk + kTile - 1) / kTile;
+  const int nstage = (nk + F::kStageRows - 1) / F::kStageRows;
+  const int nrows = nstage * F::kStageRows;
 
-  // ---- positions -> physical slots (and per-key scale factors)
+  // ---- positions -> physical slots (and per-key scale factors); masked keys read slot 0
   float smax = 0.f;
-  for (int i = tid; i < ntiles * kTile; i += 256) {
+  for (int i = tid; i < nrows; i += 256) {
     int slot = -1;
     if (i < nk) {
       const int s = idx[(int64_t)t * K + kbeg + i];
@@ -200,46 +242,41 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   if (FP8) {
     smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
-    for (int i = tid; i < ntiles * kTile; i += 256) {
+    for (int i = tid; i < nrows; i += 256) {
       const float sc = zs[i];
       scn[i] = sc * inv_smax;
       rsc[i] = sc > 0.f ? smax / sc : 0.f;
       zs[i] = sc * c2;
     }
   }
-  for (int it = tid; it < ntiles; it += 256) {
+  for (int it = tid; it < nrows / kTile; it += 256) {
     uint32_t m = 0u;
     for (int r = 0; r < kTile; ++r) m |= (rows[it * kTile + r] >= 0 ? 1u : 0u) << r;
     masks[it] = m;
   }
   __syncthreads();
 
-  // ---- tile gather: 16-byte chunks straight into LDS (pad chunk per row skipped)
-  auto issue_tile = [&](int it, int buf) {
-    char* tb = tiles + buf * F::kTileBytes;
-    constexpr int nch = kTile * F::kChunks;
-    for (int c = wave * 64; c < nch; c += 256) {
-      const int cc = c + lane;
-      const int r = cc / F::kChunks, cl = cc - r * F::kChunks;
-      if (cc < nch && cl < F::kChunks - 1) {
-        const int slot = rows[it * kTile + r];
-        if (slot >= 0) {
-          __builtin_amdgcn_global_load_lds(kv + (int64_t)slot * F::kRowBytes + cl * 16,
-                                           LDS_PTR(void, tb + c * 16), 16, 0, 0);
-        } else {
-          *(i32x4*)(tb + cc * 16) = i32x4{0, 0, 0, 0};
-        }
-      }
+  // ---- stage gather: ten 1 KB global->LDS loads per wave; slot lookups batched first
+  auto issue_stage = [&](int st) {
+    char* tb = tiles + (st % F::kStages) * F::kStageBytes;
+    int slot[F::kIssue];
+#pragma unroll
+    for (int i = 0; i < F::kIssue; ++i) {
+      const int c = (i < 9 ? 256 * i + 64 * wave : 2304) + lane;
+      const int r = c / F::kCpr;
+      slot[i] = (r < F::kStageRows) ? rows[st * F::kStageRows + r] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < F::kIssue; ++i) {
+      const int w0 = i < 9 ? 256 * i + 64 * wave : 2304;
+      const int c = w0 + lane;
+      const int r = c / F::kCpr;
+      const int cl = c - r * F::kCpr;
+      const bool data = r < F::kStageRows && cl < F::kCpr - 1 && slot[i] >= 0;
+      const int64_t src = data ? (int64_t)slot[i] * F::kRowBytes + cl * 16 : 0;
+      __builtin_amdgcn_global_load_lds(kv + src, LDS_PTR(void, tb + w0 * 16), 16, 0, 0);
     }
   };
-
-  // ---- this wave's 32 query heads as MFMA B fragments (dims 16ks + 8h .. +7)
-  bf16x8 qf[kDqk / 16];
-  {
-    const uint16_t* qr = q + ((int64_t)t * kH + wave * 32 + col) * kDqk + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 16; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
-  }
 
   f32x16 o[kDv / 32];
 #pragma unroll
@@ -249,114 +286,123 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // l_run sums the P values as rounded for the matrix cores (normalises O, which then is an
   // exact convex combination of the rows); le_run sums them unrounded (for lse)
   float m_run = -INFINITY, l_run = 0.f, le_run = 0.f;
-  const int g = lane >> 4, gi = lane & 15;
 
-  if (ntiles > 0) issue_tile(0, 0);
+  constexpr int kTilesPerStage = F::kStageRows / kTile;
+  for (int st = 0; st < min(nstage, F::kStages - 1); ++st) issue_stage(st);
   for (int it = 0; it < ntiles; ++it) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < ntiles) issue_tile(it + 1, (it + 1) & 1);
-    const char* tb = tiles + (it & 1) * F::kTileBytes;
+    const int st = it / kTilesPerStage;
+    if (it % kTilesPerStage == 0) {
+      wait_stages_after(min(F::kStages - 2, nstage - 1 - st));
+      __builtin_amdgcn_s_barrier();
+      if (st + F::kStages - 1 < nstage) issue_stage(st + F::kStages - 1);
+    }
+    const char* sb = tiles + (st % F::kStages) * F::kStageBytes;
+    {
+      const int rb = (it % kTilesPerStage) * kTile;  // first row of this tile in the stage
 
-    // S^T[key][head] over the 576 dims
-    f32x16 s;
+      // S^T[key][head] over the 576 dims
+      f32x16 s;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    const char* arow = tb + col * F::kRS;
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 16; ++ks) {
-      bf16x8 a;
-      if (FP8) {
-        const i32x2 c8 = *(const i32x2*)(arow + 16 * ks + 8 * h);
-        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, false);
-        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, true);
-        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[1], 1.f, false);
-        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[1], 1.f, true);
-        a = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      } else {
-        a = *(const bf16x8*)(arow + 2 * (16 * ks + 8 * h));
-      }
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-    }
-
-    // online softmax, lane = (head col, keys 8(i/4) + 4h + i%4)
-    const uint32_t mask = masks[it];
-    float z[16];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-      float f = c2;
-      if (FP8) f = zs[it * kTile + r];
-      z[i] = ((mask >> r) & 1u) ? s[i] * f : -INFINITY;
-      mt = fmaxf(mt, z[i]);
-    }
-    mt = xor32_max(mt);
-    if (__any(mt > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-#pragma unroll
-      for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], alpha);
-      l_run *= alpha;
-      le_run *= alpha;
-      m_run = m_new;
-    }
-    const bool live = m_run != -INFINITY;
-    float p[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = live ? exp2f(z[i] - m_run) : 0.f;
-      le_run += p[i];
-    }
-
-    if (FP8) {
-      f16x8 pf[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = it * kTile + 8 * (i >> 2) + 4 * h + (i & 3);
-        const _Float16 v = (_Float16)(p[i] * scn[r]);
-        pf[i >> 3][i & 7] = v;
-        l_run = fmaf((float)v, rsc[r], l_run);
-      }
-#pragma unroll
-      for (int mi = 0; mi < kDv / 32; ++mi) {
-        const int v0 = 32 * mi + 16 * (g & 1);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int jj = gi >> 1;
-          const int krow = 16 * ks + 8 * (jj >> 2) + 4 * (g >> 1) + (jj & 3);
-          const i32x2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              LDS_PTR(i32x2, tb + krow * F::kRS + v0 + 8 * (gi & 1)));
-          const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, false);
-          const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, true);
-          const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, false);
-          const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, true);
-          const f16x8 a = f16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-          o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mi], 0, 0, 0);
+      for (int ks = 0; ks < kDqk / 16; ++ks) {
+        bf16x8 a;
+        if (FP8) {
+          const i32x2 c8 = *(const i32x2*)(sb + (rb + col) * F::kRS + 16 * ks + 8 * h);
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, false);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, true);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[1], 1.f, false);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[1], 1.f, true);
+          a = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                      __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3,
+                                      4, 5, 6, 7);
+        } else {
+          a = *(const bf16x8*)(sb + (rb + col) * F::kRS + 2 * (16 * ks + 8 * h));
         }
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
       }
-    } else {
-      bf16x8 pb[2];
+
+      // online softmax, lane = (head col, keys 8(i/4) + 4h + i%4)
+      const uint32_t mask = masks[it];
+      float z[16];
+      float mt = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const __bf16 v = (__bf16)p[i];
-        pb[i >> 3][i & 7] = v;
-        l_run += (float)v;
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        float f = c2;
+        if (FP8) f = zs[it * kTile + r];
+        z[i] = ((mask >> r) & 1u) ? s[i] * f : -INFINITY;
+        mt = fmaxf(mt, z[i]);
       }
+      mt = xor32_max(mt);
+      if (__any(mt > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
 #pragma unroll
-      for (int mi = 0; mi < kDv / 32; ++mi) {
-        const int v0 = 32 * mi + 16 * (g & 1);
+        for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], alpha);
+        l_run *= alpha;
+        le_run *= alpha;
+        m_run = m_new;
+      }
+      const bool live = m_run != -INFINITY;
+      float p[16];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int krow = 16 * ks + 4 * (g >> 1) + (gi >> 2);
-          const char* base = tb + krow * F::kRS + 2 * (v0 + 4 * (gi & 3));
-          // whole-vector moves only: element-wise assembly of this operand from the two
-          // 64-bit halves was mistranslated by the compiler
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base));
-          const bf16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + 8 * F::kRS));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[mi], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        p[i] = live ? exp2f(z[i] - m_run) : 0.f;
+        le_run += p[i];
+      }
+
+      if (FP8) {
+        f16x8 pf[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = it * kTile + 8 * (i >> 2) + 4 * h + (i & 3);
+          const _Float16 v = (_Float16)(p[i] * scn[r]);
+          pf[i >> 3][i & 7] = v;
+          l_run = fmaf((float)v, rsc[r], l_run);
+        }
+#pragma unroll
+        for (int mi = 0; mi < kDv / 32; ++mi) {
+          const int v0 = 32 * mi + 16 * (g & 1);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int jj = gi >> 1;
+            const int krow = rb + 16 * ks + 8 * (jj >> 2) + 4 * (g >> 1) + (jj & 3);
+            const i32x2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                LDS_PTR(i32x2, sb + krow * F::kRS + v0 + 8 * (gi & 1)));
+            const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, false);
+            const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, true);
+            const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, false);
+            const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, true);
+            const f16x8 a = __builtin_shufflevector(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
+                                                    __builtin_shufflevector(a2, a3, 0, 1, 2, 3),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+            o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mi], 0, 0, 0);
+          }
+        }
+      } else {
+        bf16x8 pb[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const __bf16 v = (__bf16)p[i];
+          pb[i >> 3][i & 7] = v;
+          l_run += (float)v;
+        }
+#pragma unroll
+        for (int mi = 0; mi < kDv / 32; ++mi) {
+          const int v0 = 32 * mi + 16 * (g & 1);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int krow = rb + 16 * ks + 4 * (g >> 1) + (gi >> 2);
+            // whole-vector moves only: element-wise assembly of this operand from the two
+            // 64-bit halves was mistranslated by the compiler
+            const char* base = sb + krow * F::kRS + 2 * (v0 + 4 * (gi & 3));
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base));
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + 8 * F::kRS));
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[mi], 0, 0, 0);
+          }
         }
       }
     }
@@ -377,7 +423,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
         const int vd = 32 * mi + 8 * q4 + 4 * h;
         const f32x4 v = {o[mi][4 * q4] * inv, o[mi][4 * q4 + 1] * inv, o[mi][4 * q4 + 2] * inv,
                          o[mi][4 * q4 + 3] * inv};
-        store_out4(out, out_f32, obase + vd, v);
+        store_out4<OUT_F32>(out, obase + vd, v);
       }
     if (lse && h == 0)
       lse[(int64_t)t * kH + head] = le_tot > 0.f ? (m_run + log2f(le_tot)) * kLn2 : -INFINITY;
@@ -400,23 +446,30 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   DevBatch bt, int t_begin, int t_count, const uint16_t* __restrict__ q,                      \
       const uint8_t* __restrict__ kv, const float* __restrict__ kvscale,                      \
       const int32_t* __restrict__ idx, int K, float c2, int nsplit, int kps,                  \
-      void* __restrict__ out, int out_f32, float* __restrict__ lse,                           \
-      float* __restrict__ part_o, float* __restrict__ part_ml
+      void* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,            \
+      float* __restrict__ part_ml
 #define MLA_ATTN_PASS \
-  bt, t_begin, t_count, q, kv, kvscale, idx, K, c2, nsplit, kps, out, out_f32, lse, part_o, part_ml
+  bt, t_begin, t_count, q, kv, kvscale, idx, K, c2, nsplit, kps, out, lse, part_o, part_ml
 
 __global__ __launch_bounds__(256, 1) void mla_attn_bf16_kernel(MLA_ATTN_ARGS) {
-  mla_attn_body<false>(MLA_ATTN_PASS);
+  mla_attn_body<false, false>(MLA_ATTN_PASS);
+}
+__global__ __launch_bounds__(256, 1) void mla_attn_bf16_o32_kernel(MLA_ATTN_ARGS) {
+  mla_attn_body<false, true>(MLA_ATTN_PASS);
 }
 __global__ __launch_bounds__(256, 1) void mla_attn_fp8_kernel(MLA_ATTN_ARGS) {
-  mla_attn_body<true>(MLA_ATTN_PASS);
+  mla_attn_body<true, false>(MLA_ATTN_PASS);
+}
+__global__ __launch_bounds__(256, 1) void mla_attn_fp8_o32_kernel(MLA_ATTN_ARGS) {
+  mla_attn_body<true, true>(MLA_ATTN_PASS);
 }
 
 // Merge split partials (m in log2 units; l = sum of the rounded P, le = unrounded sum):
 // O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j,  lse = M + log2 sum_j 2^(m_j - M) le_j.
+template <bool OUT_F32>
 __global__ __launch_bounds__(128) void mla_combine_kernel(int t_begin, int t_count, int nsplit,
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    void* __restrict__ out, int out_f32, float* __restrict__ lse) {
+    void* __restrict__ out, float* __restrict__ lse) {
   const int tl = blockIdx.x / kH, head = blockIdx.x % kH;
   const int t = t_begin + tl;
   const int tid = threadIdx.x;
@@ -438,7 +491,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int t_begin, int t_cou
     acc += wgt * v;
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  store_out4(out, out_f32, ((int64_t)t * kH + head) * kDv + 4 * tid, acc * inv);
+  store_out4<OUT_F32>(out, ((int64_t)t * kH + head) * kDv + 4 * tid, acc * inv);
   if (lse && tid == 0)
     lse[(int64_t)t * kH + head] = LEsum > 0.f ? (M + log2f(LEsum)) * kLn2 : -INFINITY;
 }
@@ -480,26 +533,22 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
   const int kps = attn_keys_per_split(K, nsplit);
   const float c2 = softmax_scale * kLog2e;
   const size_t shm = attn_smem_bytes(fp8, kps);
-  const void* fn = fp8 ? (const void*)mla_attn_fp8_kernel : (const void*)mla_attn_bf16_kernel;
+  auto* fn = fp8 ? (out_f32 ? mla_attn_fp8_o32_kernel : mla_attn_fp8_kernel)
+                 : (out_f32 ? mla_attn_bf16_o32_kernel : mla_attn_bf16_kernel);
   // above 64 KB the kernel's dynamic LDS limit has to be raised before the launch (a
   // host-side attribute; set on every such launch so it holds on whichever device is current)
   if (shm > 65536) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)shm);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(t_count * nsplit);
-  const int of = out_f32 ? 1 : 0;
-  if (fp8) {
-    hipLaunchKernelGGL(mla_attn_fp8_kernel, grid, dim3(256), shm, st, bt, t_begin, t_count, q,
-                       kv, kvscale, idx, K, c2, nsplit, kps, out, of, lse, part_o, part_ml);
-  } else {
-    hipLaunchKernelGGL(mla_attn_bf16_kernel, grid, dim3(256), shm, st, bt, t_begin, t_count, q,
-                       kv, kvscale, idx, K, c2, nsplit, kps, out, of, lse, part_o, part_ml);
-  }
+  hipLaunchKernelGGL(fn, dim3(t_count * nsplit), dim3(256), shm, st, bt, t_begin, t_count, q, kv,
+                     kvscale, idx, K, c2, nsplit, kps, out, lse, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(t_count * kH), dim3(128), 0, st, t_begin, t_count,
-                     nsplit, part_o, part_ml, out, of, lse);
+  auto* cfn = out_f32 ? mla_combine_kernel<true> : mla_combine_kernel<false>;
+  hipLaunchKernelGGL(cfn, dim3(t_count * kH), dim3(128), 0, st, t_begin, t_count, nsplit, part_o,
+                     part_ml, out, lse);
   return hipGetLastError();
 }
 

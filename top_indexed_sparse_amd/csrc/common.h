@@ -31,19 +31,33 @@ struct DevBatch {
   int32_t B, T, pt_stride, n_pages;
 };
 
-// Request of flattened token t: the largest b with cu_q[b] <= t (empty requests skipped).
-__device__ __forceinline__ int find_request(const DevBatch& bt, int t) {
-  int lo = 0, hi = bt.B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (bt.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
+// Where flattened token t sits: its request b (the largest b with cu_q[b] <= t, so empty
+// requests are skipped), that request's length L = seq_lens[b] and the token's candidate
+// count n = p_t + 1 (positions 0..p_t, p_t = L - (cu_q[b+1] - t)).
+struct TokLoc {
+  int b, L, n;
+};
 
-// Absolute position of token t inside request b: its request's last q_len positions.
-__device__ __forceinline__ int token_position(const DevBatch& bt, int b, int t) {
-  return bt.seq_lens[b] - (bt.cu_q[b + 1] - t);
+// One memory round trip for up to 64 requests (a kernel start waits on this before it can
+// address anything else, so a binary search of dependent loads would stall every wave for
+// several latencies): lane i holds cu_q[i+1] and seq_lens[i] of a 64-request window, and b is
+// the number of i in [1, B-1] with cu_q[i] <= t, which cu_q being nondecreasing makes a prefix
+// count.  Must be called by all 64 lanes of the wave with the same t.
+__device__ __forceinline__ TokLoc locate(const DevBatch& bt, int t) {
+  const int lane = threadIdx.x & 63;
+  for (int base = 0;; base += 64) {
+    const int i = base + lane;
+    const int cq = i + 1 <= bt.B ? bt.cu_q[i + 1] : 0;
+    const int sl = i < bt.B ? bt.seq_lens[i] : 0;
+    const int c = __popcll(__ballot(i + 1 <= bt.B - 1 && cq <= t));
+    if (c < 64) {  // always reached once base + 64 > B - 1
+      TokLoc r;
+      r.b = base + c;
+      r.L = __builtin_amdgcn_readlane(sl, c);
+      r.n = r.L - (__builtin_amdgcn_readlane(cq, c) - t) + 1;
+      return r;
+    }
+  }
 }
 
 // Physical slot (page*64 + offset) of logical position s of request b, or -1 when the page

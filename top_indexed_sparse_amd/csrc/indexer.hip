@@ -27,8 +27,9 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(DevBatch bt, int t_b
     int H, int D, float* __restrict__ scores, int64_t ld) {
   extern __shared__ float sq[];  // [H*D] query, [H] weights
   const int t = t_begin + blockIdx.x;
-  const int b = find_request(bt, t);
-  const int p = token_position(bt, b, t);
+  const TokLoc loc = locate(bt, t);
+  const int b = loc.b;
+  const int p = loc.n - 1;
   const int s = blockIdx.y * blockDim.x + threadIdx.x;
   if ((int)(blockIdx.y * blockDim.x) > p) return;  // whole block beyond the causal range
   for (int i = threadIdx.x; i < H * D; i += blockDim.x) sq[i] = q[(int64_t)t * H * D + i];
@@ -55,24 +56,40 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(DevBatch bt, int t_b
 constexpr int kIH = 64;   // indexer heads
 constexpr int kID = 128;  // indexer head dim
 
-// Quantise this wave's token query to e4m3 in the MFMA A layout and build the per-lane head
-// weights w'[16m + 4g + i] = w * s (s = power-of-two scale of that head).
-__device__ __forceinline__ void a0_prologue(const uint16_t* __restrict__ qrow,
-                                            const float* __restrict__ wrow, int lane,
-                                            i32x8 (&A)[4], float (&wp)[4][4]) {
+// The token's query rows and head weights in the lanes that quantise them: lane (n, g) holds
+// dims [16g, 16g+16) and [64+16g, 64+16g+16) of heads 16m + n, and the weights of heads
+// 16m + 4g + i.  Loading is split from quantising so the loads can be issued early.
+struct QRaw {
+  i32x4 r[4][4];
+  float w[4][4];
+};
+
+__device__ __forceinline__ void a0_load(const uint16_t* __restrict__ qrow,
+                                        const float* __restrict__ wrow, int lane, QRaw& qr) {
   const int n = lane & 15, g = lane >> 4;
-  float inv_s[4], s_q[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const uint16_t* hrow = qrow + (16 * m + n) * kID;
-    i32x4 lo0 = *(const i32x4*)(hrow + 16 * g);
-    i32x4 lo1 = *(const i32x4*)(hrow + 16 * g + 8);
-    i32x4 hi0 = *(const i32x4*)(hrow + 64 + 16 * g);
-    i32x4 hi1 = *(const i32x4*)(hrow + 64 + 16 * g + 8);
-    uint32_t wd[16] = {(uint32_t)lo0[0], (uint32_t)lo0[1], (uint32_t)lo0[2], (uint32_t)lo0[3],
-                       (uint32_t)lo1[0], (uint32_t)lo1[1], (uint32_t)lo1[2], (uint32_t)lo1[3],
-                       (uint32_t)hi0[0], (uint32_t)hi0[1], (uint32_t)hi0[2], (uint32_t)hi0[3],
-                       (uint32_t)hi1[0], (uint32_t)hi1[1], (uint32_t)hi1[2], (uint32_t)hi1[3]};
+    qr.r[m][0] = *(const i32x4*)(hrow + 16 * g);
+    qr.r[m][1] = *(const i32x4*)(hrow + 16 * g + 8);
+    qr.r[m][2] = *(const i32x4*)(hrow + 64 + 16 * g);
+    qr.r[m][3] = *(const i32x4*)(hrow + 64 + 16 * g + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qr.w[m][i] = wrow[16 * m + 4 * g + i];
+  }
+}
+
+// Quantise the query to e4m3 in the MFMA A layout and build the per-lane head weights
+// w'[16m + 4g + i] = w * s (s = power-of-two scale of that head).
+__device__ __forceinline__ void a0_prologue(const QRaw& qr, int lane, i32x8 (&A)[4],
+                                            float (&wp)[4][4]) {
+  const int g = lane >> 4;
+  float inv_s[4], s_q[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    uint32_t wd[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) wd[j] = (uint32_t)qr.r[m][j >> 2][j & 3];
     float v[32];
     float amax = 0.f;
 #pragma unroll
@@ -106,7 +123,7 @@ __device__ __forceinline__ void a0_prologue(const uint16_t* __restrict__ qrow,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float s = __shfl(s_q[m], 4 * g + i);
-      wp[m][i] = wrow[16 * m + 4 * g + i] * s;
+      wp[m][i] = qr.w[m][i] * s;
     }
 }
 
@@ -171,42 +188,61 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(DevBatch bt, int t_b
   }
   if (tl >= t_count) return;
   const int t = t_begin + tl;
-  const int b = find_request(bt, t);
-  const int n = token_position(bt, b, t) + 1;
+  const TokLoc loc = locate(bt, t);
+  const int b = loc.b;
+  const int n = loc.n;
   k1 = min(k1, n);
   if (k0 >= k1) return;
-
-  i32x8 A[4];
-  float wp[4][4];
-  a0_prologue(q_idx + (int64_t)t * kIH * kID, w + (int64_t)t * kIH, lane, A, wp);
 
   const int32_t* pt = bt.page_table + (int64_t)b * bt.pt_stride;
   float* out = scores + (int64_t)tl * ld;
 
-  KTile4 cur, nxt;
-  int page = pt[k0 >> 6];
-  bool ok = page >= 0 && page < bt.n_pages;
-  const uint8_t* pbase = kpool + (int64_t)(ok ? page : 0) * kPage * kID;
-  load_ktile4(pbase, lane, cur);
-  float ks = kscale[(int64_t)(ok ? page : 0) * kPage + lane];
-  for (int base = k0; base < k1; base += 64) {
-    const int nb = base + 64;
-    int npage = 0;
-    bool nok = false;
-    float nks = 0.f;
-    if (nb < k1) {
-      npage = pt[nb >> 6];
-      nok = npage >= 0 && npage < bt.n_pages;
-      const uint8_t* nbase = kpool + (int64_t)(nok ? npage : 0) * kPage * kID;
-      load_ktile4(nbase, lane, nxt);
-      nks = kscale[(int64_t)(nok ? npage : 0) * kPage + lane];
+  // Start-up order matters: everything waits on the page ids, and loads complete in issue
+  // order, so the page ids are requested first, then the query, then the first key groups;
+  // the query is quantised while those groups are in flight.
+  // Page ids of this wave's range, one per lane, fetched once (a scalar page-table load per
+  // group would stall every prefetch on a scalar round trip).
+  const int pg0 = k0 >> 6;
+  const int npg = (k1 - 1) / 64 - pg0 + 1;  // <= 64 pages per wave
+  const int my_page = lane < npg ? pt[pg0 + lane] : 0;
+  QRaw qr;
+  a0_load(q_idx + (int64_t)t * kIH * kID, w + (int64_t)t * kIH, lane, qr);
+
+  // three-slot ring of 64-key groups: while one group is scored the next two are in flight
+  struct Slot {
+    KTile4 kt;
+    float ks;
+    bool ok;
+  };
+  auto fetch = [&](int base, Slot& sl) {
+    if (base < k1) {
+      const int page = __builtin_amdgcn_readlane(my_page, (base >> 6) - pg0);
+      sl.ok = page >= 0 && page < bt.n_pages;
+      const int64_t pg = sl.ok ? page : 0;
+      load_ktile4(kpool + pg * kPage * kID, lane, sl.kt);
+      sl.ks = kscale[pg * kPage + lane];
     }
-    float sc = score_group(A, wp, cur) * ks;
-    if (!ok) sc = -INFINITY;
-    if (base + lane < k1) out[base + lane] = sc;
-    cur = nxt;
-    ok = nok;
-    ks = nks;
+  };
+  Slot s0, s1, s2;
+  fetch(k0, s0);
+  fetch(k0 + 64, s1);
+  i32x8 A[4];
+  float wp[4][4];
+  a0_prologue(qr, lane, A, wp);
+  auto consume = [&](int base, const Slot& sl) {
+    if (base < k1) {
+      float sc = score_group(A, wp, sl.kt) * sl.ks;
+      if (!sl.ok) sc = -INFINITY;
+      if (base + lane < k1) out[base + lane] = sc;
+    }
+  };
+  for (int base = k0; base < k1; base += 192) {
+    fetch(base + 128, s2);
+    consume(base, s0);
+    fetch(base + 192, s0);
+    consume(base + 64, s1);
+    fetch(base + 256, s1);
+    consume(base + 128, s2);
   }
 }
 

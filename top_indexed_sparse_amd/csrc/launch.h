@@ -15,8 +15,9 @@ hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, 
                                   bool prefill_like, const uint16_t* q_idx, const float* w,
                                   const uint8_t* kpool, const float* kscale, float* scores,
                                   int64_t ld, hipStream_t st);
-hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, const float* scores,
-                       int64_t ld, int K, int32_t* idx, float* val, hipStream_t st);
+hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
+                       const float* scores, int64_t ld, int K, int32_t* idx, float* val,
+                       hipStream_t st);
 hipError_t launch_mla_attn_f32(const DevBatch& bt, int t_begin, int t_count, const float* q,
                                const float* kv, const int32_t* idx, int K, int H, int Dqk,
                                int Dv, float scale, float* out, float* lse, hipStream_t st);
