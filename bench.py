@@ -30,32 +30,54 @@ def log(msg):
 
 def algorithmic(inp):
     """Compulsory bytes / flops per step, stage by stage (inputs read once, outputs written
-    once, only the selected rows gathered)."""
+    once, only the selected rows gathered), and per launch of each entry point."""
     import numpy as np
     sh = inp.wl.shape
     n = inp.positions.astype(np.int64) + 1
     k = np.minimum(sh.K, n)
-    kbytes = 1 if not sh.fp32 else 4 * 1
-    kb = (sh.D_I + 4) if not sh.fp32 else 4 * sh.D_I
-    qb = sh.H_I * sh.D_I * (2 if not sh.fp32 else 4) + 4 * sh.H_I
+    kb = (sh.D_I + 4) if not sh.fp32 else 4 * sh.D_I            # key code + scale per position
+    qb = sh.H_I * sh.D_I * (2 if not sh.fp32 else 4) + 4 * sh.H_I  # q_I + w per token
     # each request's keys are read once however many of its tokens query them
     idx_bytes = int(sum(int(L) * kb for L in inp.seq_lens)) + inp.T * qb
     idx_flops = int((2 * sh.H_I * sh.D_I * n).sum())
     topk_bytes = 4 * sh.K * inp.T
     row = sh.D_qk * (1 if sh.kv_fp8 else 2) + (4 if sh.kv_fp8 else 0)
-    attn_bytes = int((k * row).sum()) + inp.T * sh.H * (sh.D_qk * 2 + sh.D_v * 2 + 4)
+    # selected rows + indices + q + O (bf16) + lse
+    attn_bytes = int((k * row).sum()) + inp.T * (4 * sh.K + sh.H * (sh.D_qk * 2 + sh.D_v * 2 + 4))
     attn_flops = int((2 * sh.H * k * (sh.D_qk + sh.D_v)).sum())
-    del kbytes
     return dict(idx_bytes=idx_bytes, idx_flops=idx_flops, topk_bytes=topk_bytes,
                 attn_bytes=attn_bytes, attn_flops=attn_flops,
-                # the unfused scorer also writes one fp32 score per candidate
-                idx_kernel_bytes=idx_bytes + int(4 * n.sum()))
+                # unfused entry points: the scorer also writes one fp32 score per candidate,
+                # the selection reads them back
+                idx_kernel_bytes=idx_bytes + int(4 * n.sum()),
+                topk_kernel_bytes=int(4 * n.sum()) + topk_bytes)
 
 
 def t_roof(a):
     hb = HBM_PEAK_GBS * 1e9
     return (max(a["idx_bytes"] / hb, a["idx_flops"] / FP8_PEAK) + a["topk_bytes"] / hb
             + max(a["attn_bytes"] / hb, a["attn_flops"] / BF16_PEAK))
+
+
+def measured_traffic(entry_point: str):
+    """HBM bytes per launch of an entry point from the committed FETCH_SIZE / WRITE_SIZE counter
+    record (scaled by the copy calibration), or None when any kernel source it covers has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode32k_traffic.json")
+    try:
+        rec = json.load(open(path))["entry_points"][entry_point]
+    except (OSError, KeyError, ValueError):
+        return None
+    pkg = os.path.join(ROOT, "top_indexed_sparse_amd")
+    for rel, digest in rec["sources"].items():
+        try:
+            with open(os.path.join(pkg, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(inp, r_idx, r_out, tokens):
@@ -69,18 +91,20 @@ def cpu_baseline(inp, r_idx, r_out, tokens):
         cores = os.cpu_count()
     orc = Oracle(inp)
     t0 = time.perf_counter()
+    chosen = []
+    for t in tokens:                       # the oracle's own chain, timed
+        idx, S, kth = orc.topk(t)
+        orc.attention(t, idx)
+        chosen.append(idx)
+    dt = time.perf_counter() - t0
     recall_hits = recall_tot = 0
     worst = 0.0
-    for t in tokens:
-        idx, S, kth = orc.topk(t)
-        o, _ = orc.attention(t, idx)
+    for t, idx in zip(tokens, chosen):     # parity of the GPU results (not timed)
         g = r_idx[t]
         recall_hits += len(set(g[g >= 0].tolist()) & set(idx[idx >= 0].tolist()))
         recall_tot += int((idx >= 0).sum())
-        # attention on the GPU's own set for the output comparison
-        og, _ = orc.attention(t, g)
+        og, _ = orc.attention(t, g)        # attention on the GPU's own selected set
         worst = max(worst, float(np.abs(r_out[t] - og).max()))
-    dt = time.perf_counter() - t0
     return dict(value=len(tokens) / dt, unit="queries/s", cores=cores, kind="oracle",
                 sample=f"{len(tokens)} of {inp.T} decode tokens (full per-token chain: e4m3 "
                        f"decode, fp64 scores, full-sort Top-K, fp64 attention)",
@@ -95,6 +119,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (8 times) and exit: the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
@@ -103,6 +130,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": nbytes, "launches": 8}), flush=True)
+        return
 
     import synth
     import top_indexed_sparse_amd as tis
@@ -136,47 +173,60 @@ def main():
         tis.sparse_mla_attn(bt, d.q, d.kv_pool, d.kv_scale, idx[r], sh.softmax_scale, out[r],
                             lse[r], ws=ws_a)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / args.steps
 
-    # dominant kernel: the FP8 scorer, timed alone over the same replicas
-    ld = (bt.max_n + 3) // 4 * 4
-    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    def timed(fn, n):
+        """Average ms per call of fn(i), i = 0..n-1, between HIP events on the stream the
+        library launches on (torch's current stream)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     for i in range(args.warmup):
-        d = reps[i % len(reps)]
-        tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        d = reps[i % len(reps)]
-        tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    idx_ms = e0.elapsed_time(e1) / args.steps
+        step(i)
+    step_ms = timed(step, args.steps)
 
-    # attention kernel alone (its share of the step)
-    e0.record(stream)
-    for i in range(args.steps):
+    # each entry point alone, over the same replicas: the scorer (unfused, writes scores),
+    # the selection over those scores, the attention call
+    ld = (bt.max_n + 3) // 4 * 4
+    scores = [torch.empty((T, ld), dtype=torch.float32, device="cuda") for _ in reps]
+
+    def score(i):
+        d = reps[i % len(reps)]
+        tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores[i % len(reps)])
+
+    def select(i):
+        r = i % len(reps)
+        tis.topk_select(bt, scores[r], K, idx[r])
+
+    def attend(i):
         r = i % len(reps)
         d = reps[r]
         tis.sparse_mla_attn(bt, d.q, d.kv_pool, d.kv_scale, idx[r], sh.softmax_scale, out[r],
                             lse[r], ws=ws_a)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = e0.elapsed_time(e1) / args.steps
 
+    for fn in (score, select, attend):
+        for i in range(max(args.warmup, len(reps))):
+            fn(i)
     a = algorithmic(inp)
+    calls = {
+        "index_score": dict(ms=timed(score, args.steps), bytes=a["idx_kernel_bytes"],
+                            kernels=["idx_score_fp8_kernel"]),
+        "topk_select": dict(ms=timed(select, args.steps), bytes=a["topk_kernel_bytes"],
+                            kernels=["topk_lds_kernel"]),
+        "sparse_mla_attn": dict(ms=timed(attend, args.steps), bytes=a["attn_bytes"],
+                                kernels=["mla_attn_bf16_kernel", "mla_combine_kernel<false>"]),
+    }
+    for c in calls.values():
+        c["gbs"] = c["bytes"] / (c["ms"] * 1e-3) / 1e9
+    dom_name = max(calls, key=lambda k: calls[k]["ms"])
+    dom = calls[dom_name]
     roof_s = t_roof(a)
-    ach = a["idx_kernel_bytes"] / (idx_ms * 1e-3) / 1e9
     res = {
         "metric": "sparse-attn decode queries/s @32K ctx (index+topk+attn)",
         "value": T * 1000.0 / step_ms,
@@ -195,15 +245,15 @@ def main():
                    "topk": K, "heads": sh.H, "qk_dim": sh.D_qk, "v_dim": sh.D_v,
                    "kv_cache": "bf16", "index_keys": "e4m3+fp32 scale/token",
                    "input_replicas": len(reps)},
-        "roofline": {"bound": "hbm", "kernel": "idx_score_fp8_kernel",
-                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                     "launch_us": idx_ms * 1e3, "bytes_per_launch": a["idx_kernel_bytes"]},
+        "roofline": {"bound": "hbm", "entry_point": dom_name, "kernels": dom["kernels"],
+                     "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dom["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(dom_name), "traffic_unit": "bytes/launch",
+                     "launch_us": dom["ms"] * 1e3, "bytes_per_launch": dom["bytes"]},
         "chain_roofline": {"t_roof_us": roof_s * 1e6, "t_step_us": step_ms * 1e3,
                            "frac": roof_s / (step_ms * 1e-3),
-                           "attn_us": attn_ms * 1e3,
-                           "attn_gbs": a["attn_bytes"] / (attn_ms * 1e-3) / 1e9,
-                           "attn_tflops": a["attn_flops"] / (attn_ms * 1e-3) / 1e12},
+                           "attn_tflops": a["attn_flops"] / (calls["sparse_mla_attn"]["ms"] * 1e-3) / 1e12,
+                           "calls": {k: {"us": round(v["ms"] * 1e3, 2), "GB/s": round(v["gbs"], 1)}
+                                     for k, v in calls.items()}},
     }
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
@@ -218,8 +268,9 @@ def main():
             sys.exit(1)
         cb.pop("seconds")
         res["cpu_baseline"] = cb
-    log(f"step {step_ms * 1e3:.1f} us (scorer alone {idx_ms * 1e3:.1f} us, attention alone "
-        f"{attn_ms * 1e3:.1f} us); chain roofline {roof_s * 1e6:.1f} us")
+    log(f"step {step_ms * 1e3:.1f} us; alone: " + ", ".join(
+        f"{k} {v['ms'] * 1e3:.1f} us ({v['gbs']:.0f} GB/s)" for k, v in calls.items())
+        + f"; chain roofline {roof_s * 1e6:.1f} us")
     print(json.dumps(res), flush=True)
 
 

@@ -22,7 +22,8 @@ def make_batch(inp) -> tis.Batch:
     return tis.Batch(inp.seq_lens, inp.cu_q, inp.page_table, inp.n_pages)
 
 
-def run_path(inp, unfused: bool = True, K: int | None = None) -> SimpleNamespace:
+def run_path(inp, unfused: bool = True, K: int | None = None,
+             out_f32: bool = False) -> SimpleNamespace:
     """Fused index_score_topk + sparse_mla_attn (and optionally the unfused chain)."""
     sh = inp.wl.shape
     K = sh.K if K is None else K
@@ -41,8 +42,9 @@ def run_path(inp, unfused: bool = True, K: int | None = None) -> SimpleNamespace
         val2 = torch.empty_like(val)
         tis.topk_select(bt, scores, K, idx2, val2)
     # e4m3 caches hold rows of large magnitude (heavy hitters): their output is kept in fp32,
-    # since bf16 spacing alone exceeds the 2e-2 gate above |O| = 8
-    out_dt = torch.float32 if (sh.fp32 or sh.kv_fp8) else torch.bfloat16
+    # since bf16 spacing alone exceeds the 2e-2 gate above |O| = 8; the same holds for the
+    # 1e-2 gate above |O| = 4, reached when only a few keys are selected (short contexts)
+    out_dt = torch.float32 if (sh.fp32 or sh.kv_fp8 or out_f32) else torch.bfloat16
     out = torch.empty((T, sh.H, sh.D_v), dtype=out_dt, device="cuda")
     lse = torch.empty((T, sh.H), dtype=torch.float32, device="cuda")
     tis.sparse_mla_attn(bt, d.q, d.kv_pool, d.kv_scale, idx, sh.softmax_scale, out, lse)

@@ -114,7 +114,7 @@ def test_many_requests_with_empty_ones():
     wl = synth.reduced(synth.workload(synth.DECODE32K), L, q)
     inp = synth.make(wl, "continuous")
     note(f"case many-requests B={B} T={inp.T}")
-    r = run_path(inp)
+    r = run_path(inp, out_f32=True)  # |O| reaches 4+ over a few hundred keys
     _common(inp, r, list(range(inp.T)), False)
 
 
