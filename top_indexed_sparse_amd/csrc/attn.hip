@@ -29,6 +29,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace tis {
 
@@ -93,46 +94,54 @@ __global__ __launch_bounds__(256) void mla_attn_f32_kernel(DevBatch bt, int t_be
 }
 
 // ---------------------------------------------------------------- matrix-core kernel
-constexpr int kH = 128, kDqk = 576, kDv = 512, kTile = 32;
+constexpr int kH = 128, kDqk = 576, kDv = 512;
+constexpr int kHB = 32;        // heads per workgroup
+constexpr int kWT = 16;        // rows (keys) per wave tile
+constexpr int kSR = 4 * kWT;   // rows per stage: the four waves' tiles
+constexpr int kMaxKps = 2048;  // keys per split (bounds the LDS index table)
 
-// One gather stage holds 32 bf16 rows or 64 e4m3 rows, each followed by a 16-byte pad chunk:
-// 2336 or 2368 chunks of 16 bytes, stored in a 2368-chunk buffer.  Every wave issues ten
-// 16-byte-per-lane global->LDS loads per stage: nine windows of its own (chunks
-// 256i + 64w + lane) and a tenth window [2304, 2368) that all four waves load with identical
-// bytes.  The count per wave is therefore always ten, which lets the waits use immediates.
-// Lanes whose chunk is a pad (or beyond the rows) load row 0 into it; those bytes are never
-// read.
+// Each wave gathers its own 16-row tiles straight into LDS (16-byte global->LDS loads) and
+// is the only reader of them, so the main loop has no workgroup barriers.  A tile has two
+// regions: A holds the value part of each row (its first 512 dims) at a padded row stride,
+// one load instruction per row (every lane a 16-byte chunk of that row, so the source is a
+// per-row scalar base plus the lane offset: no per-lane address arithmetic); B holds the
+// 64 RoPE dims of the 16 rows packed (bf16: two loads, e4m3: one).  The A stride is 4 dwords
+// more than a multiple of 32 banks, and the rows are consumed in the order
+// pi(8h + j) = 8h + 2j (j < 4), 8h + 2(j - 4) + 1 (j >= 4), which makes both the 16-byte
+// key-fragment reads and the transposed value reads free of bank conflicts.  bf16: 1040-byte
+// A rows, 18 loads per tile, two tiles per wave in flight; e4m3: 528-byte A rows, 17 loads,
+// three tiles per wave.
 template <bool FP8>
 struct KvFmt {
-  static constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;  // 576 or 1152
-  static constexpr int kCpr = kRowBytes / 16 + 1;           // chunks per LDS row incl. pad
-  static constexpr int kRS = kCpr * 16;                     // LDS row stride
-  static constexpr int kStageRows = FP8 ? 64 : 32;
-  static constexpr int kStageChunks = 2368;
-  static constexpr int kStageBytes = kStageChunks * 16;    // 37888
-  static constexpr int kStages = FP8 ? 3 : 4;               // LDS ring depth
-  static constexpr int kIssue = 10;
-  static_assert(kStageRows * kCpr <= kStageChunks, "stage rows overflow the buffer");
+  static constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;   // cached row
+  static constexpr int kVBytes = FP8 ? kDv : 2 * kDv;       // value part (region A)
+  static constexpr int kRBytes = kRowBytes - kVBytes;       // RoPE part (region B): 64 / 128
+  static constexpr int kAStride = kVBytes + 16;
+  static constexpr int kABytes = kWT * kAStride;
+  static constexpr int kBBytes = kWT * kRBytes;
+  static constexpr int kWBytes = kABytes + kBBytes;         // one wave tile
+  static constexpr int kBLoads = kBBytes / 1024;            // 64 lanes x 16 bytes each
+  static constexpr int kIssue = kWT + kBLoads;              // loads per wave tile
+  static constexpr int kBufs = FP8 ? 3 : 2;                 // wave tiles in the ring
+  static constexpr int kTiles = kBufs * 4 * kWBytes;        // LDS bytes of all rings
 };
-
-struct AttnSmem {  // offsets into dynamic LDS
-  int rows, masks, zs, scn, rsc, tiles, total;
-};
-template <bool FP8>
-__host__ __device__ constexpr AttnSmem attn_smem(int kps) {
-  AttnSmem s{};
-  int o = 0;
-  s.rows = o; o += kps * 4;
-  s.masks = o; o += ((kps + kTile - 1) / kTile) * 4;
-  o = (o + 15) & ~15;
-  s.zs = o; o += FP8 ? kps * 4 : 0;
-  s.scn = o; o += FP8 ? kps * 4 : 0;
-  s.rsc = o; o += FP8 ? kps * 4 : 0;
-  o = (o + 15) & ~15;
-  s.tiles = o; o += KvFmt<FP8>::kStages * KvFmt<FP8>::kStageBytes;
-  s.total = o;
-  return s;
+__host__ __device__ constexpr int tile_row(int m) {  // pi: consumption order -> tile row
+  return (m & 8) + ((m & 4) ? 2 * (m & 3) + 1 : 2 * (m & 3));
 }
+
+// Dynamic LDS: rings | rows[kMaxKps] | masks[kMaxKps/16] | scl[kMaxKps] (e4m3) | xm[4][3][32].
+// After the main loop the ring area holds the cross-wave exchange of O (4 x 32 x 132 floats).
+constexpr int kXPitch = 132;  // floats per head row of the exchange (128 dims + pad)
+template <bool FP8>
+struct AttnSmem {
+  static constexpr int rows = KvFmt<FP8>::kTiles;
+  static constexpr int masks = rows + kMaxKps * 4;
+  static constexpr int scl = masks + kMaxKps / 16 * 2;
+  static constexpr int xm = scl + (FP8 ? kMaxKps * 4 : 0);
+  static constexpr int total = xm + 4 * 3 * kHB * 4 + 3 * kHB * 4;
+  static_assert(4 * kHB * kXPitch * 4 <= KvFmt<FP8>::kTiles, "exchange does not fit");
+  static_assert(total <= 160 * 1024, "LDS budget");
+};
 
 // Four consecutive outputs at element offset `off`: fp32, or bf16 (round to nearest even).
 template <bool OUT_F32>
@@ -164,20 +173,43 @@ __device__ __forceinline__ void acc_scale(f32x16& acc, float alpha) {
   }
 }
 
-// s_waitcnt with vmcnt <= n (n < 64), other counters untouched (gfx9 encoding).
-#define TIS_WAIT_VM(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
+// s_waitcnt vmcnt(n): the loads into LDS issued before the last n vector-memory operations
+// have landed.  Written as asm with a memory clobber so that no LDS read of the tile can be
+// moved above it.
+#define TIS_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory")
 
-__device__ __forceinline__ void wait_stages_after(int later) {
-  // each stage issued after the awaited one contributes 10 outstanding loads per wave
+// Wait until at most `later` wave tiles (of `issue` loads each) are still in flight.
+template <int kIssue>
+__device__ __forceinline__ void wait_tiles_after(int later) {
   switch (later) {
     case 0: TIS_WAIT_VM(0); break;
-    case 1: TIS_WAIT_VM(10); break;
-    case 2: TIS_WAIT_VM(20); break;
-    default: TIS_WAIT_VM(30); break;
+    case 1: TIS_WAIT_VM(kIssue); break;
+    default: TIS_WAIT_VM(2 * kIssue); break;
   }
 }
 
+// Sum / max over the four 16-lane rows (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float rows4_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xor32_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xor32_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// One workgroup per (token, key split, group of 32 heads); four waves take interleaved
+// 16-key tiles of the split.  Per wave tile:
+//   S^T[16 keys][16 heads] x 2 = K . Q^T on v_mfma_f32_16x16x32_bf16 (K fragments from LDS,
+//     Q^T resident in registers; e4m3 rows are widened exactly per fragment);
+//   online softmax per head (lane-local over 4 keys, then across the four 16-lane rows);
+//   one permlane16 swap moves P^T into the B layout of v_mfma_f32_32x32x16 (keys 8(l/32)+j,
+//     head l%32), and O^T[32 dims][32 heads] += V^T . P^T with V^T read by
+//     ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3, widened to fp16).
+// The running max is raised lazily (only when a tile exceeds it by 2^8).  e4m3: per-row scales
+// enter the fp32 logits and P relative to the split's largest scale; P is fp16 and the
+// normaliser sums the same rounded values.  The four waves' (m, l, O) are merged through LDS;
+// with several splits the workgroup writes fp32 partials for mla_combine_kernel.
 template <bool FP8, bool OUT_F32>
 __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_count,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -185,41 +217,51 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     int nsplit, int kps, void* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   using F = KvFmt<FP8>;
+  using SM = AttnSmem<FP8>;
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  const AttnSmem L = attn_smem<FP8>(kps);
-  int* rows = (int*)(sm + L.rows);
-  uint32_t* masks = (uint32_t*)(sm + L.masks);
-  float* zs = (float*)(sm + L.zs);
-  float* scn = (float*)(sm + L.scn);
-  float* rsc = (float*)(sm + L.rsc);
-  char* tiles = sm + L.tiles;
-  __shared__ float red[8];
+  char* tiles = sm;
+  int* rows = (int*)(sm + SM::rows);
+  uint16_t* masks = (uint16_t*)(sm + SM::masks);
+  float* scl = (float*)(sm + SM::scl);
+  float* xm = (float*)(sm + SM::xm);          // [wave][m, l, le][32 heads]
+  float* xf = xm + 4 * 3 * kHB;               // [M, L, LE][32 heads]
+  __shared__ float red[4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int h = lane >> 5, col = lane & 31;
-  const int g = lane >> 4, gi = lane & 15;
-  const int tl = blockIdx.x % t_count, split = blockIdx.x / t_count;
-  const int t = t_begin + tl;
+  const int c16 = lane & 15, g4 = lane >> 4;  // 16x16 layouts
+  const int c32 = lane & 31, h2 = lane >> 5;  // 32x32 layouts
 
-  // ---- this wave's 32 query heads as MFMA B fragments (dims 16ks + 8h .. +7); issued first
-  //      so their latency overlaps the index translation
-  bf16x8 qf[kDqk / 16];
-  {
-    const uint16_t* qr = q + ((int64_t)t * kH + wave * 32 + col) * kDqk + 8 * h;
+  // workgroup -> (token, split, head group); the workgroups of one token sit on one XCD
+  // (workgroups are dealt to the 8 XCDs round-robin), so its rows are fetched from HBM once
+  // and served to the other head groups from that XCD's L2
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot8 = blockIdx.x >> 3;
+  const int per = nblk >> 3, extra = nblk & 7;
+  const int pidx = xcd * per + min(xcd, extra) + slot8;
+  const int hg = pidx & 3;
+  const int split = (pidx >> 2) % nsplit;
+  const int tl = (pidx >> 2) / nsplit;
+  const int t = t_begin + tl;
+  const int h0 = hg * kHB;
+
+  // ---- Q^T fragments of the 32 heads (B operand of 16x16x32: head c16, dims 32ks + 8g4)
+  bf16x8 qf[2][kDqk / 32];
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 16; ++ks) qf[ks] = *(const bf16x8*)(qr + 16 * ks);
+  for (int ht = 0; ht < 2; ++ht) {
+    const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ht][ks] = *(const bf16x8*)(qr + 32 * ks);
   }
 
   const TokLoc loc = locate(bt, t);
   const int b = loc.b;
   const int Lb = loc.L;
   const int kbeg = split * kps;
-  const int nk = min(kps, K - kbeg);
-  const int ntiles = (nk + kTile - 1) / kTile;
-  const int nstage = (nk + F::kStageRows - 1) / F::kStageRows;
-  const int nrows = nstage * F::kStageRows;
+  const int nk = max(0, min(kps, K - kbeg));
+  const int nstage = (nk + kSR - 1) / kSR;
+  const int nrows = nstage * kSR;
 
-  // ---- positions -> physical slots (and per-key scale factors); masked keys read slot 0
+  // ---- positions -> physical slots (and e4m3 row scales); masked keys read slot 0
   float smax = 0.f;
   for (int i = tid; i < nrows; i += 256) {
     int slot = -1;
@@ -228,9 +270,10 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       if (s >= 0 && s < Lb) slot = (int)slot_of(bt, b, s);
     }
     rows[i] = slot;
-    if (FP8) {
+    if (FP8) {  // scales in consumption order: entry 16*tile + m is row pi(m) of the tile
       const float sc = slot >= 0 ? kvscale[slot] : 0.f;
-      zs[i] = sc;
+      const int r = i & (kWT - 1);
+      scl[(i & ~(kWT - 1)) + ((r & 8) | ((r & 1) << 2) | ((r >> 1) & 3))] = sc;
       smax = fmaxf(smax, sc);
     }
   }
@@ -239,206 +282,323 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     if (lane == 0) red[wave] = smax;
   }
   __syncthreads();
-  if (FP8) {
-    smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
-    for (int i = tid; i < nrows; i += 256) {
-      const float sc = zs[i];
-      scn[i] = sc * inv_smax;
-      rsc[i] = sc > 0.f ? smax / sc : 0.f;
-      zs[i] = sc * c2;
-    }
-  }
-  for (int it = tid; it < nrows / kTile; it += 256) {
+  // per wave tile: bit m = row pi(m) selected (the order in which the keys are consumed)
+  for (int tt = tid; tt < nrows / kWT; tt += 256) {
     uint32_t m = 0u;
-    for (int r = 0; r < kTile; ++r) m |= (rows[it * kTile + r] >= 0 ? 1u : 0u) << r;
-    masks[it] = m;
+    for (int j = 0; j < kWT; ++j) m |= (rows[tt * kWT + tile_row(j)] >= 0 ? 1u : 0u) << j;
+    masks[tt] = (uint16_t)m;
   }
+  if (FP8) smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
   __syncthreads();
 
-  // ---- stage gather: ten 1 KB global->LDS loads per wave; slot lookups batched first
-  auto issue_stage = [&](int st) {
-    char* tb = tiles + (st % F::kStages) * F::kStageBytes;
-    int slot[F::kIssue];
+  // ---- this wave's tile of stage st: rows st*64 + 16*wave .. +15
+  // wave-uniform pieces of the gather addresses live in scalar registers: the row base of
+  // each A-region load is kv + slot * rowbytes (a scalar), the lane adds 16 * lane, and the
+  // LDS destination (M0) is a scalar too
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  auto issue = [&](int st) {
+    char* ta = tiles + ((st % F::kBufs) * 4 + wave_u) * F::kWBytes;
+    char* tbb = ta + F::kABytes;
+    const int* rw = rows + st * kSR + wave_u * kWT;
+    const int my = rw[lane & (kWT - 1)];  // lane r of each 16 holds the slot of row r
+    // region B: lane l of load j takes chunk l % C of row (64 j + l) / C (C = RoPE chunks)
+    constexpr int kRC = F::kRBytes / 16;
+    int bslot[F::kBLoads];
 #pragma unroll
-    for (int i = 0; i < F::kIssue; ++i) {
-      const int c = (i < 9 ? 256 * i + 64 * wave : 2304) + lane;
-      const int r = c / F::kCpr;
-      slot[i] = (r < F::kStageRows) ? rows[st * F::kStageRows + r] : -1;
+    for (int j = 0; j < F::kBLoads; ++j) bslot[j] = rw[(64 * j + lane) / kRC];
+    // region A: one load per row
+#pragma unroll
+    for (int r = 0; r < kWT; ++r) {
+      const uint32_t sr = (uint32_t)max(__builtin_amdgcn_readlane(my, r), 0);
+      // the row base, pinned to scalar registers, selects the scalar-base form of the load
+      const uint64_t base = (uint64_t)(uintptr_t)kv + (uint64_t)sr * F::kRowBytes;
+      const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+      const uint8_t* rowp = (const uint8_t*)(((uint64_t)bhi << 32) | blo);
+      if (FP8) {
+        if (lane < F::kVBytes / 16)
+          __builtin_amdgcn_global_load_lds(rowp + lane16, LDS_PTR(void, ta + r * F::kAStride),
+                                           16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(rowp + lane16, LDS_PTR(void, ta + r * F::kAStride), 16,
+                                         0, 0);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < F::kIssue; ++i) {
-      const int w0 = i < 9 ? 256 * i + 64 * wave : 2304;
-      const int c = w0 + lane;
-      const int r = c / F::kCpr;
-      const int cl = c - r * F::kCpr;
-      const bool data = r < F::kStageRows && cl < F::kCpr - 1 && slot[i] >= 0;
-      const int64_t src = data ? (int64_t)slot[i] * F::kRowBytes + cl * 16 : 0;
-      __builtin_amdgcn_global_load_lds(kv + src, LDS_PTR(void, tb + w0 * 16), 16, 0, 0);
+    for (int j = 0; j < F::kBLoads; ++j) {
+      const int c = (64 * j + lane) % kRC;
+      const uint8_t* src =
+          kv + (uint64_t)(uint32_t)max(bslot[j], 0) * F::kRowBytes + F::kVBytes + 16 * c;
+      __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, tbb + 1024 * j), 16, 0, 0);
     }
   };
 
-  f32x16 o[kDv / 32];
+  f32x16 o[kDv / 32];  // O^T: dims 32mt + 8(i/4) + 4h2 + i%4, head h0 + c32
 #pragma unroll
   for (int mt = 0; mt < kDv / 32; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
-  // l_run sums the P values as rounded for the matrix cores (normalises O, which then is an
-  // exact convex combination of the rows); le_run sums them unrounded (for lse)
-  float m_run = -INFINITY, l_run = 0.f, le_run = 0.f;
+  // per lane two heads, 16ht + c16; l sums P as rounded for the matrix cores (normalises O),
+  // le sums it unrounded (for lse)
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, le_run[2] = {0.f, 0.f};
+  const bool hsel = (lane & 16) != 0;  // the O^T column c32 is head 16*hsel + c16
 
-  constexpr int kTilesPerStage = F::kStageRows / kTile;
-  for (int st = 0; st < min(nstage, F::kStages - 1); ++st) issue_stage(st);
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it / kTilesPerStage;
-    if (it % kTilesPerStage == 0) {
-      wait_stages_after(min(F::kStages - 2, nstage - 1 - st));
-      __builtin_amdgcn_s_barrier();
-      if (st + F::kStages - 1 < nstage) issue_stage(st + F::kStages - 1);
-    }
-    const char* sb = tiles + (st % F::kStages) * F::kStageBytes;
-    {
-      const int rb = (it % kTilesPerStage) * kTile;  // first row of this tile in the stage
+  for (int st = 0; st < min(nstage, F::kBufs - 1); ++st) issue(st);
+  for (int st = 0; st < nstage; ++st) {
+    if (st + F::kBufs - 1 < nstage) issue(st + F::kBufs - 1);
+    wait_tiles_after<F::kIssue>(min(F::kBufs - 1, nstage - 1 - st));
+    const uint32_t mask = masks[st * 4 + wave];
+    const char* sb = tiles + ((st % F::kBufs) * 4 + wave) * F::kWBytes;
+    const int rbase = st * kSR + wave * kWT;
 
-      // S^T[key][head] over the 576 dims
-      f32x16 s;
+    // S^T[key 4g4 + i][head 16ht + c16]
+    f32x4 s[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    for (int ht = 0; ht < 2; ++ht) s[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments are read kPre steps ahead of their use (the latency of an LDS read is
+    // several MFMA steps)
+    constexpr int kPre = 4;
+    using KRaw = typename std::conditional<FP8, i32x2, bf16x8>::type;
+    KRaw kr[kPre];
+    // lane (m = c16, g4): row pi(m), dims 32ks + 8g4 .. +7 (region A below dim 512, B above)
+    const int qr = tile_row(c16);
+    auto kread = [&](int ks) -> KRaw {
+      constexpr int kEB = FP8 ? 1 : 2;  // bytes per element
+      const int d = 32 * ks + 8 * g4;
+      const char* pa = ks < kDv / 32 ? sb + qr * F::kAStride + kEB * d
+                                     : sb + F::kABytes + qr * F::kRBytes + kEB * (d - kDv);
+      return *(const KRaw*)pa;
+    };
 #pragma unroll
-      for (int ks = 0; ks < kDqk / 16; ++ks) {
-        bf16x8 a;
-        if (FP8) {
-          const i32x2 c8 = *(const i32x2*)(sb + (rb + col) * F::kRS + 16 * ks + 8 * h);
-          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, false);
-          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, true);
-          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[1], 1.f, false);
-          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[1], 1.f, true);
-          a = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
-                                      __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3,
-                                      4, 5, 6, 7);
-        } else {
-          a = *(const bf16x8*)(sb + (rb + col) * F::kRS + 2 * (16 * ks + 8 * h));
-        }
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-      }
-
-      // online softmax, lane = (head col, keys 8(i/4) + 4h + i%4)
-      const uint32_t mask = masks[it];
-      float z[16];
-      float mt = -INFINITY;
+    for (int ks = 0; ks < kPre; ++ks) kr[ks] = kread(ks);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-        float f = c2;
-        if (FP8) f = zs[it * kTile + r];
-        z[i] = ((mask >> r) & 1u) ? s[i] * f : -INFINITY;
-        mt = fmaxf(mt, z[i]);
-      }
-      mt = xor32_max(mt);
-      if (__any(mt > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-#pragma unroll
-        for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], alpha);
-        l_run *= alpha;
-        le_run *= alpha;
-        m_run = m_new;
-      }
-      const bool live = m_run != -INFINITY;
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = live ? exp2f(z[i] - m_run) : 0.f;
-        le_run += p[i];
-      }
-
-      if (FP8) {
-        f16x8 pf[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = it * kTile + 8 * (i >> 2) + 4 * h + (i & 3);
-          const _Float16 v = (_Float16)(p[i] * scn[r]);
-          pf[i >> 3][i & 7] = v;
-          l_run = fmaf((float)v, rsc[r], l_run);
-        }
-#pragma unroll
-        for (int mi = 0; mi < kDv / 32; ++mi) {
-          const int v0 = 32 * mi + 16 * (g & 1);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int jj = gi >> 1;
-            const int krow = rb + 16 * ks + 8 * (jj >> 2) + 4 * (g >> 1) + (jj & 3);
-            const i32x2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                LDS_PTR(i32x2, sb + krow * F::kRS + v0 + 8 * (gi & 1)));
-            const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, false);
-            const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, true);
-            const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, false);
-            const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, true);
-            const f16x8 a = __builtin_shufflevector(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
-                                                    __builtin_shufflevector(a2, a3, 0, 1, 2, 3),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
-            o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mi], 0, 0, 0);
-          }
-        }
+    for (int ks = 0; ks < kDqk / 32; ++ks) {
+      const KRaw cur = kr[ks % kPre];
+      if (ks + kPre < kDqk / 32) kr[ks % kPre] = kread(ks + kPre);
+      bf16x8 a;
+      if constexpr (FP8) {
+        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, false);
+        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, true);
+        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, false);
+        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, true);
+        a = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                    __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                    5, 6, 7);
       } else {
-        bf16x8 pb[2];
+        a = cur;
+      }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const __bf16 v = (__bf16)p[i];
-          pb[i >> 3][i & 7] = v;
-          l_run += (float)v;
+      for (int ht = 0; ht < 2; ++ht)
+        s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], s[ht], 0, 0, 0);
+    }
+
+    // ---- online softmax (log2 units)
+    const uint32_t mk = (mask >> (4 * g4)) & 0xFu;
+    f32x4 zsc = {c2, c2, c2, c2};
+    if (FP8) {
+      const f32x4 sc = *(const f32x4*)(scl + rbase + 4 * g4);
+      zsc = sc * c2;
+    }
+    float z[2][4], mt[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      mt[ht] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[ht][i] = ((mk >> i) & 1u) ? s[ht][i] * zsc[i] : -INFINITY;
+        mt[ht] = fmaxf(mt[ht], z[ht][i]);
+      }
+      mt[ht] = rows4_max(mt[ht]);
+    }
+    if (__any(mt[0] > m_run[0] + 8.f || mt[1] > m_run[1] + 8.f)) {
+      float alpha[2];
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const float m_new = fmaxf(m_run[ht], mt[ht]);
+        alpha[ht] = (m_run[ht] == -INFINITY) ? 0.f : exp2f(m_run[ht] - m_new);
+        l_run[ht] *= alpha[ht];
+        le_run[ht] *= alpha[ht];
+        m_run[ht] = m_new;
+      }
+      const float a_sel = hsel ? alpha[1] : alpha[0];
+#pragma unroll
+      for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], a_sel);
+    }
+    float p[2][4];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const bool live = m_run[ht] != -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[ht][i] = live ? __builtin_amdgcn_exp2f(z[ht][i] - m_run[ht]) : 0.f;
+        le_run[ht] += p[ht][i];
+      }
+    }
+
+    // ---- P^T in the 32x32x16 B layout: lane l gets keys 8h2 + j of head c32
+    uint32_t pk[2][2];  // [tile ht][pair]: packed 16-bit P of keys 4g4 + 2*pair + {0,1}
+    if (FP8) {
+      f32x4 rs = {0.f, 0.f, 0.f, 0.f}, sn = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 sc = *(const f32x4*)(scl + rbase + 4 * g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sn[i] = sc[i] * inv_smax;
+        rs[i] = sc[i] > 0.f ? smax / sc[i] : 0.f;
+      }
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const _Float16 v0 = (_Float16)(p[ht][2 * pr] * sn[2 * pr]);
+          const _Float16 v1 = (_Float16)(p[ht][2 * pr + 1] * sn[2 * pr + 1]);
+          l_run[ht] = fmaf((float)v0, rs[2 * pr], l_run[ht]);
+          l_run[ht] = fmaf((float)v1, rs[2 * pr + 1], l_run[ht]);
+          pk[ht][pr] = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
         }
+    } else {
 #pragma unroll
-        for (int mi = 0; mi < kDv / 32; ++mi) {
-          const int v0 = 32 * mi + 16 * (g & 1);
+      for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int krow = rb + 16 * ks + 4 * (g >> 1) + (gi >> 2);
-            // whole-vector moves only: element-wise assembly of this operand from the two
-            // 64-bit halves was mistranslated by the compiler
-            const char* base = sb + krow * F::kRS + 2 * (v0 + 4 * (gi & 3));
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base));
-            const bf16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + 8 * F::kRS));
-            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[mi], 0, 0, 0);
-          }
+        for (int pr = 0; pr < 2; ++pr) {
+          const __bf16 v0 = (__bf16)p[ht][2 * pr];
+          const __bf16 v1 = (__bf16)p[ht][2 * pr + 1];
+          l_run[ht] += (float)v0 + (float)v1;
+          pk[ht][pr] = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
         }
+    }
+    // lanes of the low 16-row of each half keep tile 0 and take tile 0 of the row above;
+    // lanes of the high 16-row take tile 1 of the row below and keep their tile 1
+    i32x4 pb;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      auto r = __builtin_amdgcn_permlane16_swap(pk[0][pr], pk[1][pr], false, false);
+      pb[pr] = (int)r[0];      // keys 8h2 + 2pr + {0,1}
+      pb[2 + pr] = (int)r[1];  // keys 8h2 + 4 + 2pr + {0,1}
+    }
+
+    // ---- O^T[32 dims][32 heads] += V^T[32 dims][16 keys] . P^T
+    const int G = g4;
+#pragma unroll
+    for (int mi = 0; mi < kDv / 32; ++mi) {
+      const int d0 = 32 * mi + 16 * (G & 1);
+      if (FP8) {
+        // lane k of the 16-row group: key j = k / 2 (row pi(8h + j)), bytes d0 + 8 (k % 2)
+        const int kr = 8 * (G >> 1) + 2 * ((c16 >> 1) & 3) + (c16 >> 3);
+        const i32x2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            LDS_PTR(i32x2, sb + kr * F::kAStride + d0 + 8 * (c16 & 1)));
+        const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, false);
+        const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, true);
+        const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, false);
+        const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, true);
+        const f16x8 a = __builtin_shufflevector(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
+                                                __builtin_shufflevector(a2, a3, 0, 1, 2, 3), 0,
+                                                1, 2, 3, 4, 5, 6, 7);
+        o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pb), o[mi],
+                                                       0, 0, 0);
+      } else {
+        // lane k of the 16-row group: keys j = k / 4 (row pi(8h + j) = 8h + 2j) and j + 4
+        // (the next row), dims d0 + 4 (k % 4)
+        const int kr = 8 * (G >> 1) + 2 * (c16 >> 2);
+        // whole-vector moves only: element-wise assembly of this operand from the two
+        // 64-bit halves was mistranslated by the compiler
+        const char* base = sb + kr * F::kAStride + 2 * (d0 + 4 * (c16 & 3));
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base));
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + F::kAStride));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pb),
+                                                        o[mi], 0, 0, 0);
       }
     }
   }
 
-  // ---- epilogue: lane holds head 32w+col, vdims 32mi + 8(i/4) + 4h + i%4
-  const float l_tot = xor32_sum(l_run);
-  const float le_tot = xor32_sum(le_run);
-  const int head = wave * 32 + col;
-  const float oscale = FP8 ? smax : 1.f;
-  if (nsplit == 1) {
-    const float inv = l_tot > 0.f ? oscale / l_tot : 0.f;
-    const int64_t obase = ((int64_t)t * kH + head) * kDv;
+  // ---- merge the four waves: per head M = max m_w, factors 2^(m_w - M)
 #pragma unroll
-    for (int mi = 0; mi < kDv / 32; ++mi)
+  for (int ht = 0; ht < 2; ++ht) {
+    l_run[ht] = rows4_sum(l_run[ht]);
+    le_run[ht] = rows4_sum(le_run[ht]);
+  }
+  if (g4 == 0) {
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      xm[(wave * 3 + 0) * kHB + 16 * ht + c16] = m_run[ht];
+      xm[(wave * 3 + 1) * kHB + 16 * ht + c16] = l_run[ht];
+      xm[(wave * 3 + 2) * kHB + 16 * ht + c16] = le_run[ht];
+    }
+  }
+  __syncthreads();
+  float fme;  // this wave's factor for head c32
+  {
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = xm[(w * 3 + 0) * kHB + c32];
+      M = fmaxf(M, mw[w]);
+    }
+    float Ls = 0.f, LEs = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
+      Ls = fmaf(f, xm[(w * 3 + 1) * kHB + c32], Ls);
+      LEs = fmaf(f, xm[(w * 3 + 2) * kHB + c32], LEs);
+    }
+    fme = mw[wave] == -INFINITY ? 0.f : exp2f(mw[wave] - M);
+    if (FP8) fme *= smax;  // O was accumulated relative to the largest row scale
+    if (wave == 0 && h2 == 0) {
+      xf[0 * kHB + c32] = M;
+      xf[1 * kHB + c32] = Ls;
+      xf[2 * kHB + c32] = LEs;
+      const int head = h0 + c32;
+      if (nsplit == 1) {
+        if (lse) lse[(int64_t)t * kH + head] = LEs > 0.f ? (M + log2f(LEs)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t pr = ((int64_t)tl * nsplit + split) * kH + head;
+        *(f32x4*)(part_ml + pr * 4) = f32x4{M, Ls, LEs, 0.f};
+      }
+    }
+  }
+  // four rounds of 128 dims: every wave stores its scaled O^T, then wave w sums dims
+  // 32w .. 32w+31 of the round over the four waves and writes them out
+  float* xo = (float*)tiles;  // [wave][head][kXPitch]
+  const int sh = lane >> 1;   // summed head
+  const int sd = 16 * (lane & 1);
+#pragma unroll
+  for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], fme);
+#pragma unroll
+  for (int rd = 0; rd < 4; ++rd) {
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int mi = 4 * rd + mm;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int vd = 32 * mi + 8 * q4 + 4 * h;
-        const f32x4 v = {o[mi][4 * q4] * inv, o[mi][4 * q4 + 1] * inv, o[mi][4 * q4 + 2] * inv,
-                         o[mi][4 * q4 + 3] * inv};
-        store_out4<OUT_F32>(out, obase + vd, v);
+        const int d = 32 * mm + 8 * q4 + 4 * h2;
+        const f32x4 v = {o[mi][4 * q4], o[mi][4 * q4 + 1], o[mi][4 * q4 + 2], o[mi][4 * q4 + 3]};
+        *(f32x4*)(xo + (wave * kHB + c32) * kXPitch + d) = v;
       }
-    if (lse && h == 0)
-      lse[(int64_t)t * kH + head] = le_tot > 0.f ? (m_run + log2f(le_tot)) * kLn2 : -INFINITY;
-  } else {
-    const int64_t pr = ((int64_t)tl * nsplit + split) * kH + head;
-    float* po = part_o + pr * kDv;
+    }
+    __syncthreads();
+    const float Ls = xf[1 * kHB + sh];
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
-    for (int mi = 0; mi < kDv / 32; ++mi)
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int d = 32 * wave + sd + 4 * k4;
+      f32x4 acc = *(const f32x4*)(xo + (0 * kHB + sh) * kXPitch + d);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int vd = 32 * mi + 8 * q4 + 4 * h;
-        *(f32x4*)(po + vd) = f32x4{o[mi][4 * q4] * oscale, o[mi][4 * q4 + 1] * oscale,
-                                   o[mi][4 * q4 + 2] * oscale, o[mi][4 * q4 + 3] * oscale};
+      for (int w = 1; w < 4; ++w) acc += *(const f32x4*)(xo + (w * kHB + sh) * kXPitch + d);
+      const int dim = 128 * rd + d;
+      const int head = h0 + sh;
+      if (nsplit == 1) {
+        store_out4<OUT_F32>(out, ((int64_t)t * kH + head) * kDv + dim, acc * inv);
+      } else {
+        const int64_t pr = ((int64_t)tl * nsplit + split) * kH + head;
+        *(f32x4*)(part_o + pr * kDv + dim) = acc;
       }
-    if (h == 0) *(f32x4*)(part_ml + pr * 4) = f32x4{m_run, l_tot, le_tot, 0.f};
+    }
+    __syncthreads();
   }
 }
 
@@ -508,21 +668,23 @@ hipError_t launch_mla_attn_f32(const DevBatch& bt, int t_begin, int t_count, con
 
 int attn_keys_per_split(int K, int nsplit) {
   int kps = (K + nsplit - 1) / nsplit;
-  return (kps + kTile - 1) / kTile * kTile;
+  return (kps + kSR - 1) / kSR * kSR;
 }
 
 int attn_split_count(int t_count, int K) {
-  // enough workgroups to cover the 256 CUs, at least 64 keys per split, <= 2048 keys per
-  // split; recomputed from the rounded split length so that no split is empty
-  int s = (256 + t_count - 1) / t_count;
-  s = std::max(1, std::min(s, (K + 63) / 64));
-  s = std::max(s, (K + 2047) / 2048);
+  // enough workgroups (4 head groups per token and split) to cover the 256 CUs, at least 64
+  // keys per split, at most kMaxKps; recomputed from the rounded split length so that no
+  // split is empty
+  int s = (256 + 4 * t_count - 1) / (4 * t_count);
+  s = std::max(1, std::min(s, (K + kSR - 1) / kSR));
+  s = std::max(s, (K + kMaxKps - 1) / kMaxKps);
   const int kps = attn_keys_per_split(K, s);
   return (K + kps - 1) / kps;
 }
 
 size_t attn_smem_bytes(bool fp8, int kps) {
-  return fp8 ? (size_t)attn_smem<true>(kps).total : (size_t)attn_smem<false>(kps).total;
+  (void)kps;
+  return fp8 ? (size_t)AttnSmem<true>::total : (size_t)AttnSmem<false>::total;
 }
 
 hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp8,
@@ -542,7 +704,7 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
                                        (int)shm);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fn, dim3(t_count * nsplit), dim3(256), shm, st, bt, t_begin, t_count, q, kv,
+  hipLaunchKernelGGL(fn, dim3(t_count * nsplit * 4), dim3(256), shm, st, bt, t_begin, t_count, q, kv,
                      kvscale, idx, K, c2, nsplit, kps, out, lse, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
