@@ -118,6 +118,51 @@ def test_many_requests_with_empty_ones():
     _common(inp, r, list(range(inp.T)), False)
 
 
+def test_attention_workspace_reuse():
+    """One workspace reused by calls of different batch sizes gives the results of fresh
+    workspaces."""
+    import top_indexed_sparse_amd as tis
+    note("case attention workspace reuse")
+    wl = synth.reduced(synth.workload(synth.DECODE32K), [5000, 3000, 4096, 2100], [1, 1, 1, 1])
+    inp = synth.make(wl, "continuous")
+    sh = inp.wl.shape
+    ref = run_path(inp, unfused=False)
+    d, bt = ref.dev, ref.batch
+    idx = torch.tensor(ref.idx, device="cuda")
+    big = tis.sparse_mla_attn_workspace_size(bt, sh.K, sh.H, sh.D_qk, sh.D_v, tis.TIS_BF16)
+    assert big > 0
+    ws = torch.full((big + 4096,), 0x7F, dtype=torch.uint8, device="cuda")
+    for rnd in range(3):
+        out = torch.empty((inp.T, sh.H, sh.D_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((inp.T, sh.H), dtype=torch.float32, device="cuda")
+        tis.sparse_mla_attn(bt, d.q, d.kv_pool, d.kv_scale, idx, sh.softmax_scale, out, lse, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.float().cpu().numpy().astype(np.float64), ref.out), rnd
+        assert np.array_equal(lse.cpu().numpy().astype(np.float64), ref.lse), rnd
+        # a smaller batch through the same workspace
+        bt1 = tis.Batch(inp.seq_lens[:1], inp.cu_q[:2], inp.page_table[:1], inp.n_pages)
+        out1 = torch.empty((1, sh.H, sh.D_v), dtype=torch.bfloat16, device="cuda")
+        tis.sparse_mla_attn(bt1, d.q[:1], d.kv_pool, d.kv_scale, idx[:1].contiguous(),
+                            sh.softmax_scale, out1, None, ws=ws)
+        torch.cuda.synchronize()
+        # (another split count: same values up to rounding)
+        assert np.abs(out1.float().cpu().numpy()[0].astype(np.float64) - ref.out[0]).max() < 1e-2
+
+
+def test_split_merge_for_long_batches():
+    """Many tokens with K above the 2048-key split limit: every token is split and merged."""
+    import dataclasses
+    base = synth.workload(synth.DECODE32K)
+    wl = synth.reduced(base, [6000], [4100], shape=dataclasses.replace(base.shape, K=2560))
+    inp = synth.make(wl, "continuous")
+    note(f"case separate split merge T={inp.T} K={inp.wl.shape.K}")
+    r = run_path(inp, unfused=False, out_f32=True)
+    orc = Oracle(inp)
+    toks = [0, 1, 2047, 2048, 3000, inp.T - 1]
+    check_topk(inp, orc, r.idx, toks, False)
+    check_attention(inp, orc, r, toks)
+
+
 def test_determinism():
     wl = synth.reduced(synth.workload(synth.DECODE32K), [4096, 3000], [1, 1])
     inp = synth.make(wl, "continuous")
