@@ -167,10 +167,10 @@ __device__ __forceinline__ float score_group(const i32x8 (&A)[4], const float (&
   return pair16_sum(k0, k1);
 }
 
-// group_mode == 0: one token per workgroup (blockIdx.x), the four waves split the key chunk
+// group_mode == 0: one token per workgroup (blockIdx.x), its waves split the key chunk
 //                  blockIdx.y.
 // group_mode == 1: four consecutive tokens per workgroup, one per wave, same key chunk.
-__global__ __launch_bounds__(256) void idx_score_fp8_kernel(DevBatch bt, int t_begin,
+__global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
     float* __restrict__ scores, int64_t ld, int group_mode, int chunk) {
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(DevBatch bt, int t_b
     k1 = k0 + chunk;
   } else {
     tl = blockIdx.x;
-    const int part = chunk >> 2;
+    const int part = chunk / (int)(blockDim.x >> 6);
     k0 = blockIdx.y * chunk + wave * part;
     k1 = k0 + part;
   }
@@ -262,10 +262,12 @@ hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, 
                                   const uint8_t* kpool, const float* kscale, float* scores,
                                   int64_t ld, hipStream_t st) {
   const int group = prefill_like ? 1 : 0;
-  const int chunk = prefill_like ? 1024 : 2048;
+  const int chunk = prefill_like ? 1024 : 4096;
   dim3 grid(group ? (t_count + 3) / 4 : t_count, (max_n + chunk - 1) / chunk);
-  hipLaunchKernelGGL(idx_score_fp8_kernel, grid, dim3(256), 0, st, bt, t_begin, t_count, q_idx,
-                     w, kpool, kscale, scores, ld, group, chunk);
+  // decode: one 8-wave workgroup per 4096-key chunk of a token (512 keys per wave); prefill:
+  // four tokens per 4-wave workgroup sharing a 1024-key chunk
+  hipLaunchKernelGGL(idx_score_fp8_kernel, grid, dim3(group ? 256 : 512), 0, st, bt, t_begin,
+                     t_count, q_idx, w, kpool, kscale, scores, ld, group, chunk);
   return hipGetLastError();
 }
 
