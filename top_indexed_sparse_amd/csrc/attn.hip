@@ -244,37 +244,64 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const int t = t_begin + tl;
   const int h0 = hg * kHB;
 
-  // ---- Q^T fragments of the 32 heads (B operand of 16x16x32: head c16, dims 32ks + 8g4)
-  bf16x8 qf[2][kDqk / 32];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ht][ks] = *(const bf16x8*)(qr + 32 * ks);
-  }
-
-  const TokLoc loc = locate(bt, t);
-  const int b = loc.b;
-  const int Lb = loc.L;
   const int kbeg = split * kps;
   const int nk = max(0, min(kps, K - kbeg));
   const int nstage = (nk + kSR - 1) / kSR;
   const int nrows = nstage * kSR;
 
-  // ---- positions -> physical slots (and e4m3 row scales); masked keys read slot 0
+  // ---- positions -> physical slots (and e4m3 row scales); masked keys read slot 0.  Each
+  // thread translates up to kPer rows with its loads batched per step: the positions (they
+  // only need the token) go out together with the token's request lookup, then the pages,
+  // then the scales, so the chain costs three memory latencies however many rows there are.
+  constexpr int kPer = kMaxKps / 256;
+  int pos[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + 256 * j;
+    pos[j] = i < nk ? idx[(int64_t)t * K + kbeg + i] : -1;
+  }
+  const LocLoads lw = locate_issue(bt);
+  const TokLoc loc = locate_finish(bt, t, lw);
+  const int b = loc.b;
+  const int Lb = loc.L;
+  const int32_t* ptb = bt.page_table + (int64_t)b * bt.pt_stride;
+  int slot[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int sp = pos[j];
+    slot[j] = (sp >= 0 && sp < Lb) ? ptb[sp >> 6] : -1;
+  }
+  // Q^T fragments of the 32 heads (B operand of 16x16x32: head c16, dims 32kk + 8g4), issued
+  // after the page lookups: loads complete in issue order, so the slots below wait for the
+  // page entries only, and Q arrives while the slots and the first tiles are in flight
+  bf16x8 qf[2][kDqk / 32];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < kDqk / 32; ++kk) qf[ht][kk] = *(const bf16x8*)(qr + 32 * kk);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int pg = slot[j];
+    slot[j] = (pg >= 0 && pg < bt.n_pages) ? pg * kPage + (pos[j] & (kPage - 1)) : -1;
+  }
   float smax = 0.f;
-  for (int i = tid; i < nrows; i += 256) {
-    int slot = -1;
-    if (i < nk) {
-      const int s = idx[(int64_t)t * K + kbeg + i];
-      if (s >= 0 && s < Lb) slot = (int)slot_of(bt, b, s);
-    }
-    rows[i] = slot;
-    if (FP8) {  // scales in consumption order: entry 16*tile + m is row pi(m) of the tile
-      const float sc = slot >= 0 ? kvscale[slot] : 0.f;
-      const int r = i & (kWT - 1);
-      scl[(i & ~(kWT - 1)) + ((r & 8) | ((r & 1) << 2) | ((r >> 1) & 3))] = sc;
-      smax = fmaxf(smax, sc);
+  float scv[kPer];
+  if (FP8) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) scv[j] = slot[j] >= 0 ? kvscale[slot[j]] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + 256 * j;
+    if (i < nrows) {
+      rows[i] = slot[j];
+      if (FP8) {  // scales in consumption order: entry 16*tile + m is row pi(m) of the tile
+        const int r = i & (kWT - 1);
+        scl[(i & ~(kWT - 1)) + ((r & 8) | ((r & 1) << 2) | ((r >> 1) & 3))] = scv[j];
+        smax = fmaxf(smax, scv[j]);
+      }
     }
   }
   if (FP8) {

@@ -60,6 +60,43 @@ __device__ __forceinline__ TokLoc locate(const DevBatch& bt, int t) {
   }
 }
 
+// The same lookup split in two, so that other loads can be issued between the loads of the
+// first 64-request window and their use.
+struct LocLoads {
+  int cq, sl;
+};
+__device__ __forceinline__ LocLoads locate_issue(const DevBatch& bt) {
+  const int lane = threadIdx.x & 63;
+  LocLoads r;
+  r.cq = lane + 1 <= bt.B ? bt.cu_q[lane + 1] : 0;
+  r.sl = lane < bt.B ? bt.seq_lens[lane] : 0;
+  return r;
+}
+__device__ __forceinline__ TokLoc locate_finish(const DevBatch& bt, int t, LocLoads w0) {
+  const int lane = threadIdx.x & 63;
+  const int c = __popcll(__ballot(lane + 1 <= bt.B - 1 && w0.cq <= t));
+  if (c < 64) {
+    TokLoc r;
+    r.b = c;
+    r.L = __builtin_amdgcn_readlane(w0.sl, c);
+    r.n = r.L - (__builtin_amdgcn_readlane(w0.cq, c) - t) + 1;
+    return r;
+  }
+  for (int base = 64;; base += 64) {  // more than 64 requests: the remaining windows
+    const int i = base + lane;
+    const int cq = i + 1 <= bt.B ? bt.cu_q[i + 1] : 0;
+    const int sl = i < bt.B ? bt.seq_lens[i] : 0;
+    const int cc = __popcll(__ballot(i + 1 <= bt.B - 1 && cq <= t));
+    if (cc < 64) {
+      TokLoc r;
+      r.b = base + cc;
+      r.L = __builtin_amdgcn_readlane(sl, cc);
+      r.n = r.L - (__builtin_amdgcn_readlane(cq, cc) - t) + 1;
+      return r;
+    }
+  }
+}
+
 // Physical slot (page*64 + offset) of logical position s of request b, or -1 when the page
 // table entry is outside [0, n_pages).
 __device__ __forceinline__ int64_t slot_of(const DevBatch& bt, int b, int s) {
