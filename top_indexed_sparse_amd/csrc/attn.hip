@@ -325,41 +325,48 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // LDS destination (M0) is a scalar too
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lane16 = 16u * (uint32_t)lane;
-  auto issue = [&](int st) {
-    char* ta = tiles + ((st % F::kBufs) * 4 + wave_u) * F::kWBytes;
-    char* tbb = ta + F::kABytes;
-    const int* rw = rows + st * kSR + wave_u * kWT;
-    const int my = rw[lane & (kWT - 1)];  // lane r of each 16 holds the slot of row r
-    // region B: lane l of load j takes chunk l % C of row (64 j + l) / C (C = RoPE chunks)
-    constexpr int kRC = F::kRBytes / 16;
+  // the slots of the wave's tile of stage st: lane r of each 16 holds row r (region A), and
+  // bslot[j] the row of region-B chunk l % C of load j (C = RoPE chunks per row)
+  constexpr int kRC = F::kRBytes / 16;
+  struct TileRows {
+    int my;
     int bslot[F::kBLoads];
+  };
+  auto tile_rows = [&](int st) {
+    TileRows tr;
+    const int* rw = rows + st * kSR + wave_u * kWT;
+    tr.my = rw[lane & (kWT - 1)];
 #pragma unroll
-    for (int j = 0; j < F::kBLoads; ++j) bslot[j] = rw[(64 * j + lane) / kRC];
-    // region A: one load per row
-#pragma unroll
-    for (int r = 0; r < kWT; ++r) {
-      const uint32_t sr = (uint32_t)max(__builtin_amdgcn_readlane(my, r), 0);
+    for (int j = 0; j < F::kBLoads; ++j) tr.bslot[j] = rw[(64 * j + lane) / kRC];
+    return tr;
+  };
+  // load j (< kIssue) of the wave's tile of stage st: j < kWT is row j of region A (one
+  // load per row), the rest are the region-B loads
+  auto issue_one = [&](int st, const TileRows& tr, int j) {
+    char* ta = tiles + ((st % F::kBufs) * 4 + wave_u) * F::kWBytes;
+    if (j < kWT) {
+      const uint32_t sr = (uint32_t)max(__builtin_amdgcn_readlane(tr.my, j), 0);
       // the row base, pinned to scalar registers, selects the scalar-base form of the load
       const uint64_t base = (uint64_t)(uintptr_t)kv + (uint64_t)sr * F::kRowBytes;
       const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)base);
       const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
       const uint8_t* rowp = (const uint8_t*)(((uint64_t)bhi << 32) | blo);
-      if (FP8) {
-        if (lane < F::kVBytes / 16)
-          __builtin_amdgcn_global_load_lds(rowp + lane16, LDS_PTR(void, ta + r * F::kAStride),
-                                           16, 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds(rowp + lane16, LDS_PTR(void, ta + r * F::kAStride), 16,
+      if (!FP8 || lane < F::kVBytes / 16)
+        __builtin_amdgcn_global_load_lds(rowp + lane16, LDS_PTR(void, ta + j * F::kAStride), 16,
                                          0, 0);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < F::kBLoads; ++j) {
-      const int c = (64 * j + lane) % kRC;
+    } else {
+      const int jb = j - kWT;
+      const int c = (64 * jb + lane) % kRC;
       const uint8_t* src =
-          kv + (uint64_t)(uint32_t)max(bslot[j], 0) * F::kRowBytes + F::kVBytes + 16 * c;
-      __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, tbb + 1024 * j), 16, 0, 0);
+          kv + (uint64_t)(uint32_t)max(tr.bslot[jb], 0) * F::kRowBytes + F::kVBytes + 16 * c;
+      __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, ta + F::kABytes + 1024 * jb), 16, 0,
+                                       0);
     }
+  };
+  auto issue = [&](int st) {
+    const TileRows tr = tile_rows(st);
+#pragma unroll
+    for (int j = 0; j < F::kIssue; ++j) issue_one(st, tr, j);
   };
 
   f32x16 o[kDv / 32];  // O^T: dims 32mt + 8(i/4) + 4h2 + i%4, head h0 + c32
@@ -372,10 +379,16 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, le_run[2] = {0.f, 0.f};
   const bool hsel = (lane & 16) != 0;  // the O^T column c32 is head 16*hsel + c16
 
+  // tiles of the first kBufs - 1 stages up front; the tile of stage st + kBufs - 1 is issued
+  // during stage st, one load per step of the QK loop, so that the gathers of the four waves
+  // reach the load pipeline spread over the compute instead of in one burst
   for (int st = 0; st < min(nstage, F::kBufs - 1); ++st) issue(st);
   for (int st = 0; st < nstage; ++st) {
-    if (st + F::kBufs - 1 < nstage) issue(st + F::kBufs - 1);
-    wait_tiles_after<F::kIssue>(min(F::kBufs - 1, nstage - 1 - st));
+    wait_tiles_after<F::kIssue>(min(F::kBufs - 2, nstage - 1 - st));
+    const int stn = st + F::kBufs - 1;
+    const bool more = stn < nstage;
+    TileRows trn;
+    if (more) trn = tile_rows(stn);
     const uint32_t mask = masks[st * 4 + wave];
     const char* sb = tiles + ((st % F::kBufs) * 4 + wave) * F::kWBytes;
     const int rbase = st * kSR + wave * kWT;
@@ -419,6 +432,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
         s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], s[ht], 0, 0, 0);
+      if (ks < F::kIssue && more) issue_one(stn, trn, ks);
     }
 
     // ---- online softmax (log2 units)
