@@ -95,22 +95,28 @@ __global__ __launch_bounds__(256) void mla_attn_f32_kernel(DevBatch bt, int t_be
 
 // ---------------------------------------------------------------- matrix-core kernel
 constexpr int kH = 128, kDqk = 576, kDv = 512;
-constexpr int kHB = 32;        // heads per workgroup
-constexpr int kWT = 16;        // rows (keys) per wave tile
-constexpr int kSR = 4 * kWT;   // rows per stage: the four waves' tiles
+constexpr int kHB = 32;        // heads per wave
+constexpr int kHW = 2 * kHB;   // heads per workgroup
+constexpr int kWT = 16;        // rows (keys) per tile
+constexpr int kSR = 2 * kWT;   // rows per stage: the tiles of the two key halves
 constexpr int kMaxKps = 2048;  // keys per split (bounds the LDS index table)
+constexpr float kMFloor = -1e30f;  // running max before the first live key (log2 units)
+// Q^T per wave: 18 fragments of 32 dims per 16 heads; the first kQR stay in registers, the
+// last kQL are kept in LDS (per wave, in the lane order of the operand) and read one step
+// ahead, which leaves the registers for the queue of gathered rows
+constexpr int kNQ = kDqk / 32, kQL = 4, kQR = kNQ - kQL;
 
-// Each wave gathers its own 16-row tiles straight into LDS (16-byte global->LDS loads) and
-// is the only reader of them, so the main loop has no workgroup barriers.  A tile has two
-// regions: A holds the value part of each row (its first 512 dims) at a padded row stride,
+// 16-row tiles are gathered straight into LDS with 16-byte global->LDS loads; the two waves
+// that read a tile (the two head halves of one key half) issue half of its loads each.  A
+// tile has two regions: A holds the value part of each row (its first 512 dims) at a padded row stride,
 // one load instruction per row (every lane a 16-byte chunk of that row, so the source is a
 // per-row scalar base plus the lane offset: no per-lane address arithmetic); B holds the
 // 64 RoPE dims of the 16 rows packed (bf16: two loads, e4m3: one).  The A stride is 4 dwords
 // more than a multiple of 32 banks, and the rows are consumed in the order
 // pi(8h + j) = 8h + 2j (j < 4), 8h + 2(j - 4) + 1 (j >= 4), which makes both the 16-byte
 // key-fragment reads and the transposed value reads free of bank conflicts.  bf16: 1040-byte
-// A rows, 18 loads per tile, two tiles per wave in flight; e4m3: 528-byte A rows, 17 loads,
-// three tiles per wave.
+// A rows, 18 loads per tile, a ring of four stages; e4m3: 528-byte A rows, 17 loads (one of
+// them issued by both waves), a ring of seven stages.
 template <bool FP8>
 struct KvFmt {
   static constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;   // cached row
@@ -121,27 +127,40 @@ struct KvFmt {
   static constexpr int kBBytes = kWT * kRBytes;
   static constexpr int kWBytes = kABytes + kBBytes;         // one wave tile
   static constexpr int kBLoads = kBBytes / 1024;            // 64 lanes x 16 bytes each
-  static constexpr int kIssue = kWT + kBLoads;              // loads per wave tile
-  static constexpr int kBufs = FP8 ? 3 : 2;                 // wave tiles in the ring
-  static constexpr int kTiles = kBufs * 4 * kWBytes;        // LDS bytes of all rings
+  static constexpr int kIssue = kWT + kBLoads;              // loads per tile
+  static constexpr int kIssueW = (kIssue + 1) / 2;          // loads per tile and wave
+  static constexpr int kBufs = 2;                           // stages in the ring
+  static constexpr int kTiles = kBufs * 2 * kWBytes;        // LDS bytes of the ring
 };
 __host__ __device__ constexpr int tile_row(int m) {  // pi: consumption order -> tile row
   return (m & 8) + ((m & 4) ? 2 * (m & 3) + 1 : 2 * (m & 3));
 }
 
-// Dynamic LDS: rings | rows[kMaxKps] | masks[kMaxKps/16] | scl[kMaxKps] (e4m3) | xm[4][3][32].
+// Dynamic LDS: ring (or the exchange) | rows[kMaxKps] | masks[kMaxKps/16] | scl[kMaxKps] (e4m3) | xm[4][3][32].
 // After the main loop the ring area holds the cross-wave exchange of O (4 x 32 x 132 floats).
 constexpr int kXPitch = 132;  // floats per head row of the exchange (128 dims + pad)
 template <bool FP8>
 struct AttnSmem {
-  static constexpr int rows = KvFmt<FP8>::kTiles;
+  static constexpr int kXBytes = 4 * kHB * kXPitch * 4;  // the exchange of O
+  static constexpr int rows = KvFmt<FP8>::kTiles > kXBytes ? KvFmt<FP8>::kTiles : kXBytes;
   static constexpr int masks = rows + kMaxKps * 4;
   static constexpr int scl = masks + kMaxKps / 16 * 2;
   static constexpr int xm = scl + (FP8 ? kMaxKps * 4 : 0);
-  static constexpr int total = xm + 4 * 3 * kHB * 4 + 3 * kHB * 4;
-  static_assert(4 * kHB * kXPitch * 4 <= KvFmt<FP8>::kTiles, "exchange does not fit");
+  static constexpr int qlds = xm + 4 * 3 * kHB * 4 + 2 * 3 * kHB * 4;
+  static constexpr int total = qlds + 4 * 2 * kQL * 1024;
   static_assert(total <= 160 * 1024, "LDS budget");
 };
+
+// Split partials of a bf16 output: the split's normalised O in fp16 scaled by 2^-8, i.e.
+// 11 significant bits for |O| up to 1.6e7 (saturating beyond), half the bytes of fp32 and
+// 8 times finer than bf16 (a bf16 partial adds an error the size of the output rounding).
+constexpr float kPartScale = 1.f / 256.f, kPartUnscale = 256.f;
+__device__ __forceinline__ void store_part16(void* part, int64_t off, f32x4 v) {
+  f16x4 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = (_Float16)fminf(fmaxf(v[i] * kPartScale, -65504.f), 65504.f);
+  *(f16x4*)((uint16_t*)part + off) = h;
+}
 
 // Four consecutive outputs at element offset `off`: fp32, or bf16 (round to nearest even).
 template <bool OUT_F32>
@@ -173,21 +192,6 @@ __device__ __forceinline__ void acc_scale(f32x16& acc, float alpha) {
   }
 }
 
-// s_waitcnt vmcnt(n): the loads into LDS issued before the last n vector-memory operations
-// have landed.  Written as asm with a memory clobber so that no LDS read of the tile can be
-// moved above it.
-#define TIS_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory")
-
-// Wait until at most `later` wave tiles (of `issue` loads each) are still in flight.
-template <int kIssue>
-__device__ __forceinline__ void wait_tiles_after(int later) {
-  switch (later) {
-    case 0: TIS_WAIT_VM(0); break;
-    case 1: TIS_WAIT_VM(kIssue); break;
-    default: TIS_WAIT_VM(2 * kIssue); break;
-  }
-}
-
 // Sum / max over the four 16-lane rows (lanes c, c+16, c+32, c+48).
 __device__ __forceinline__ float rows4_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -198,8 +202,9 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return xor32_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
-// One workgroup per (token, key split, group of 32 heads); four waves take interleaved
-// 16-key tiles of the split.  Per wave tile:
+// One workgroup per (token, key split, group of 64 heads); wave w takes heads 32(w%2) .. +31
+// of the group and the 16-key tiles 2i + w/2 of the split, which it shares with the wave of
+// the other head half.  Per wave tile:
 //   S^T[16 keys][16 heads] x 2 = K . Q^T on v_mfma_f32_16x16x32_bf16 (K fragments from LDS,
 //     Q^T resident in registers; e4m3 rows are widened exactly per fragment);
 //   online softmax per head (lane-local over 4 keys, then across the four 16-lane rows);
@@ -208,8 +213,9 @@ __device__ __forceinline__ float rows4_sum(float x) {
 //     ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3, widened to fp16).
 // The running max is raised lazily (only when a tile exceeds it by 2^8).  e4m3: per-row scales
 // enter the fp32 logits and P relative to the split's largest scale; P is fp16 and the
-// normaliser sums the same rounded values.  The four waves' (m, l, O) are merged through LDS;
-// with several splits the workgroup writes fp32 partials for mla_combine_kernel.
+// normaliser sums the same rounded values.  The two key halves' (m, l, O) of each head are
+// merged through LDS; with several splits the workgroup writes fp32 partials for
+// mla_combine_kernel.
 template <bool FP8, bool OUT_F32>
 __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_count,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -224,12 +230,14 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   uint16_t* masks = (uint16_t*)(sm + SM::masks);
   float* scl = (float*)(sm + SM::scl);
   float* xm = (float*)(sm + SM::xm);          // [wave][m, l, le][32 heads]
-  float* xf = xm + 4 * 3 * kHB;               // [M, L, LE][32 heads]
+  float* xf = xm + 4 * 3 * kHB;               // [head half][M, L, LE][32 heads]
   __shared__ float red[4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;  // 16x16 layouts
   const int c32 = lane & 31, h2 = lane >> 5;  // 32x32 layouts
+  const int hh = wave & 1, kh = wave >> 1;    // head half, key half
+  char* qlds = sm + SM::qlds + wave * (2 * kQL * 1024) + 16 * lane;  // this lane's Q in LDS
 
   // workgroup -> (token, split, head group); the workgroups of one token sit on one XCD
   // (workgroups are dealt to the 8 XCDs round-robin), so its rows are fetched from HBM once
@@ -238,11 +246,11 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const int xcd = blockIdx.x & 7, slot8 = blockIdx.x >> 3;
   const int per = nblk >> 3, extra = nblk & 7;
   const int pidx = xcd * per + min(xcd, extra) + slot8;
-  const int hg = pidx & 3;
-  const int split = (pidx >> 2) % nsplit;
-  const int tl = (pidx >> 2) / nsplit;
+  const int hg = pidx & 1;
+  const int split = (pidx >> 1) % nsplit;
+  const int tl = (pidx >> 1) / nsplit;
   const int t = t_begin + tl;
-  const int h0 = hg * kHB;
+  const int h0 = hg * kHW + hh * kHB;  // this wave's first head
 
   const int kbeg = split * kps;
   const int nk = max(0, min(kps, K - kbeg));
@@ -274,12 +282,16 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // Q^T fragments of the 32 heads (B operand of 16x16x32: head c16, dims 32kk + 8g4), issued
   // after the page lookups: loads complete in issue order, so the slots below wait for the
   // page entries only, and Q arrives while the slots and the first tiles are in flight
-  bf16x8 qf[2][kDqk / 32];
+  bf16x8 qf[2][kQR], qtl[2][kQL];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4;
 #pragma unroll
-    for (int kk = 0; kk < kDqk / 32; ++kk) qf[ht][kk] = *(const bf16x8*)(qr + 32 * kk);
+    for (int kk = 0; kk < kNQ; ++kk) {
+      const bf16x8 v = *(const bf16x8*)(qr + 32 * kk);
+      if (kk < kQR) qf[ht][kk] = v;
+      else qtl[ht][kk - kQR] = v;
+    }
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -319,11 +331,12 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
   __syncthreads();
 
-  // ---- this wave's tile of stage st: rows st*64 + 16*wave .. +15
+  // ---- this wave's tile of stage st: rows st*32 + 16*kh .. +15
   // wave-uniform pieces of the gather addresses live in scalar registers: the row base of
   // each A-region load is kv + slot * rowbytes (a scalar), the lane adds 16 * lane, and the
   // LDS destination (M0) is a scalar too
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int kh_u = __builtin_amdgcn_readfirstlane(kh);
+  const int jlo = __builtin_amdgcn_readfirstlane(hh) ? F::kIssue - F::kIssueW : 0;
   const uint32_t lane16 = 16u * (uint32_t)lane;
   // the slots of the wave's tile of stage st: lane r of each 16 holds row r (region A), and
   // bslot[j] the row of region-B chunk l % C of load j (C = RoPE chunks per row)
@@ -334,39 +347,42 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   };
   auto tile_rows = [&](int st) {
     TileRows tr;
-    const int* rw = rows + st * kSR + wave_u * kWT;
+    const int* rw = rows + st * kSR + kh_u * kWT;
     tr.my = rw[lane & (kWT - 1)];
 #pragma unroll
     for (int j = 0; j < F::kBLoads; ++j) tr.bslot[j] = rw[(64 * j + lane) / kRC];
     return tr;
   };
-  // load j (< kIssue) of the wave's tile of stage st: j < kWT is row j of region A (one
-  // load per row), the rest are the region-B loads
-  auto issue_one = [&](int st, const TileRows& tr, int j) {
-    char* ta = tiles + ((st % F::kBufs) * 4 + wave_u) * F::kWBytes;
+  // load j (< kIssue) of the tile of stage st: j < kWT is row j of region A (one load per
+  // row), the rest are the region-B loads.  Head half 0 issues loads 0 .. kIssueW - 1, head
+  // half 1 the last kIssueW (with 17 loads, load 8 is issued twice: same bytes, same place)
+  // load j of a tile, into registers: j < kWT is row j of region A (lane l: bytes 16l ..
+  // 16l + 15 of the row), the rest are region-B loads; it goes to LDS one stage later
+  auto load_one = [&](const TileRows& tr, int j) -> i32x4 {
     if (j < kWT) {
       const uint32_t sr = (uint32_t)max(__builtin_amdgcn_readlane(tr.my, j), 0);
-      // the row base, pinned to scalar registers, selects the scalar-base form of the load
+      // the row base in scalar registers: the scalar-base form of the load
       const uint64_t base = (uint64_t)(uintptr_t)kv + (uint64_t)sr * F::kRowBytes;
       const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)base);
       const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-      const uint8_t* rowp = (const uint8_t*)(((uint64_t)bhi << 32) | blo);
-      if (!FP8 || lane < F::kVBytes / 16)
-        __builtin_amdgcn_global_load_lds(rowp + lane16, LDS_PTR(void, ta + j * F::kAStride), 16,
-                                         0, 0);
-    } else {
-      const int jb = j - kWT;
-      const int c = (64 * jb + lane) % kRC;
-      const uint8_t* src =
-          kv + (uint64_t)(uint32_t)max(tr.bslot[jb], 0) * F::kRowBytes + F::kVBytes + 16 * c;
-      __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, ta + F::kABytes + 1024 * jb), 16, 0,
-                                       0);
+      const uint64_t rowp = ((uint64_t)bhi << 32) | blo;
+      // (global, not generic: a generic load would also count against the LDS counter)
+      if (!FP8 || lane < F::kVBytes / 16) return *GLOBAL_PTR(const i32x4, rowp + lane16);
+      return i32x4{0, 0, 0, 0};
     }
+    const int jb = j - kWT;  // (a run-time index: select, do not index the array)
+    const int bs = (F::kBLoads == 1 || jb == 0) ? tr.bslot[0] : tr.bslot[F::kBLoads - 1];
+    const int c = (64 * jb + lane) % kRC;
+    return *GLOBAL_PTR(const i32x4, (uintptr_t)kv + (uint64_t)(uint32_t)max(bs, 0) * F::kRowBytes +
+                                        F::kVBytes + 16 * c);
   };
-  auto issue = [&](int st) {
-    const TileRows tr = tile_rows(st);
-#pragma unroll
-    for (int j = 0; j < F::kIssue; ++j) issue_one(st, tr, j);
+  auto write_one = [&](int st, int j, i32x4 v) {
+    char* ta = tiles + ((st % F::kBufs) * 2 + kh) * F::kWBytes;
+    if (j < kWT) {
+      if (!FP8 || lane < F::kVBytes / 16) *(i32x4*)(ta + j * F::kAStride + lane16) = v;
+    } else {
+      *(i32x4*)(ta + F::kABytes + 1024 * (j - kWT) + lane16) = v;
+    }
   };
 
   f32x16 o[kDv / 32];  // O^T: dims 32mt + 8(i/4) + 4h2 + i%4, head h0 + c32
@@ -374,24 +390,44 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   for (int mt = 0; mt < kDv / 32; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
-  // per lane two heads, 16ht + c16; l sums P as rounded for the matrix cores (normalises O),
-  // le sums it unrounded (for lse)
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, le_run[2] = {0.f, 0.f};
+  // per lane two heads, 16ht + c16; le sums P unrounded (for lse, and to normalise O with a
+  // bf16 cache), l sums the fp16 P of an e4m3 cache as rounded for the matrix cores
+  float m_run[2] = {kMFloor, kMFloor}, l_run[2] = {0.f, 0.f}, le_run[2] = {0.f, 0.f};
   const bool hsel = (lane & 16) != 0;  // the O^T column c32 is head 16*hsel + c16
 
-  // tiles of the first kBufs - 1 stages up front; the tile of stage st + kBufs - 1 is issued
-  // during stage st, one load per step of the QK loop, so that the gathers of the four waves
-  // reach the load pipeline spread over the compute instead of in one burst
-  for (int st = 0; st < min(nstage, F::kBufs - 1); ++st) issue(st);
+  // The gathers go through registers: during stage st the loads of the tile of stage st + 2
+  // are issued and the loaded rows of the tile of stage st + 1 are written to LDS, one of each
+  // every other step of the QK loop (a one-stage queue of kIssueW loads per wave).  Each
+  // stage starts with a barrier: the tile of the stage has been written by both of its waves,
+  // and the ring slot written during the stage has been read by both.
+  i32x4 stg[F::kIssueW];
+  if (nstage > 0) {
+    const TileRows tr = tile_rows(0);
+#pragma unroll
+    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr, jlo + j);
+#pragma unroll
+    for (int j = 0; j < F::kIssueW; ++j) write_one(0, jlo + j, stg[j]);
+  }
+  {
+    const TileRows tr = tile_rows(min(1, nstage - 1));
+#pragma unroll
+    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr, jlo + j);
+  }
+  // Q has landed on every path into the loop (otherwise the waits for Q placed inside the loop
+  // would also hold back the queued gathers); its last fragments go to LDS
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+    for (int kk = 0; kk < kQR; ++kk) asm volatile("" ::"v"(qf[ht][kk]));
+#pragma unroll
+    for (int kk = 0; kk < kQL; ++kk) *(bf16x8*)(qlds + (ht * kQL + kk) * 1024) = qtl[ht][kk];
+  }
   for (int st = 0; st < nstage; ++st) {
-    wait_tiles_after<F::kIssue>(min(F::kBufs - 2, nstage - 1 - st));
-    const int stn = st + F::kBufs - 1;
-    const bool more = stn < nstage;
-    TileRows trn;
-    if (more) trn = tile_rows(stn);
-    const uint32_t mask = masks[st * 4 + wave];
-    const char* sb = tiles + ((st % F::kBufs) * 4 + wave) * F::kWBytes;
-    const int rbase = st * kSR + wave * kWT;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const TileRows trn = tile_rows(min(st + 2, nstage - 1));
+    const uint32_t mask = masks[st * 2 + kh];
+    const char* sb = tiles + ((st % F::kBufs) * 2 + kh) * F::kWBytes;
+    const int rbase = st * kSR + kh * kWT;
 
     // S^T[key 4g4 + i][head 16ht + c16]
     f32x4 s[2];
@@ -399,7 +435,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     for (int ht = 0; ht < 2; ++ht) s[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     // K fragments are read kPre steps ahead of their use (the latency of an LDS read is
     // several MFMA steps)
-    constexpr int kPre = 4;
+    constexpr int kPre = 2;
     using KRaw = typename std::conditional<FP8, i32x2, bf16x8>::type;
     KRaw kr[kPre];
     // lane (m = c16, g4): row pi(m), dims 32ks + 8g4 .. +7 (region A below dim 512, B above)
@@ -413,8 +449,14 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     };
 #pragma unroll
     for (int ks = 0; ks < kPre; ++ks) kr[ks] = kread(ks);
+    bf16x8 ql[2][2];  // [step parity][ht]: Q fragments from LDS, read one step ahead
 #pragma unroll
     for (int ks = 0; ks < kDqk / 32; ++ks) {
+      if (ks + 1 >= kQR && ks + 1 < kNQ) {
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          ql[(ks + 1) & 1][ht] = *(const bf16x8*)(qlds + (ht * kQL + ks + 1 - kQR) * 1024);
+      }
       const KRaw cur = kr[ks % kPre];
       if (ks + kPre < kDqk / 32) kr[ks % kPre] = kread(ks + kPre);
       bf16x8 a;
@@ -431,37 +473,58 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       }
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
-        s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], s[ht], 0, 0, 0);
-      if (ks < F::kIssue && more) issue_one(stn, trn, ks);
+        s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, ks < kQR ? qf[ht][ks < kQR ? ks : 0] : ql[ks & 1][ht], s[ht], 0, 0, 0);
+      // (unconditional: near the end of the split they re-load the last tile into the ring
+      // slot that is not read again, and the queue keeps a fixed order for the counters)
+      if ((ks & 1) == 0 && ks / 2 < F::kIssueW) {
+        const int k = ks / 2;
+        write_one(st + 1, jlo + k, stg[k]);
+        stg[k] = load_one(trn, jlo + k);
+      }
     }
 
-    // ---- online softmax (log2 units)
+    // ---- online softmax in log2 units: t = z - m_run with z = s * zsc (zsc = softmax scale *
+    // log2 e, times the row scale for e4m3), p = 2^t.  The running max is raised only when
+    // some t of the tile exceeds 8 (a lane-local test; the exact tile max across the four
+    // 16-lane rows is formed only then), so p <= 2^8.  Masked keys (a split's last tile only)
+    // get s = -inf, hence p = 0; m_run starts at a finite floor so this holds before the first
+    // live key too.  (The mask applies to t, not to s: a masked e4m3 row has scale 0.)
     const uint32_t mk = (mask >> (4 * g4)) & 0xFu;
     f32x4 zsc = {c2, c2, c2, c2};
     if (FP8) {
       const f32x4 sc = *(const f32x4*)(scl + rbase + 4 * g4);
       zsc = sc * c2;
     }
-    float z[2][4], mt[2];
+    float tz[2][4];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      mt[ht] = -INFINITY;
+    for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[ht][i] = ((mk >> i) & 1u) ? s[ht][i] * zsc[i] : -INFINITY;
-        mt[ht] = fmaxf(mt[ht], z[ht][i]);
-      }
-      mt[ht] = rows4_max(mt[ht]);
+      for (int i = 0; i < 4; ++i) tz[ht][i] = fmaf(s[ht][i], zsc[i], -m_run[ht]);
+    if (mask != 0xFFFFu) {  // wave-uniform
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tz[ht][i] = ((mk >> i) & 1u) ? tz[ht][i] : -INFINITY;
     }
-    if (__any(mt[0] > m_run[0] + 8.f || mt[1] > m_run[1] + 8.f)) {
+    const float tmax = fmaxf(fmaxf(fmaxf(tz[0][0], tz[0][1]), fmaxf(tz[0][2], tz[0][3])),
+                             fmaxf(fmaxf(tz[1][0], tz[1][1]), fmaxf(tz[1][2], tz[1][3])));
+    if (__any(tmax > 8.f)) {
       float alpha[2];
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
-        const float m_new = fmaxf(m_run[ht], mt[ht]);
-        alpha[ht] = (m_run[ht] == -INFINITY) ? 0.f : exp2f(m_run[ht] - m_new);
+        float zm = -INFINITY;  // (from z itself: t loses z next to the floor)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((mk >> i) & 1u) zm = fmaxf(zm, s[ht][i] * zsc[i]);
+        const float m_new = fmaxf(m_run[ht], rows4_max(zm));
+        alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
         l_run[ht] *= alpha[ht];
         le_run[ht] *= alpha[ht];
         m_run[ht] = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          tz[ht][i] = ((mk >> i) & 1u) ? fmaf(s[ht][i], zsc[i], -m_new) : -INFINITY;
       }
       const float a_sel = hsel ? alpha[1] : alpha[0];
 #pragma unroll
@@ -469,14 +532,12 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     }
     float p[2][4];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const bool live = m_run[ht] != -INFINITY;
+    for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[ht][i] = live ? __builtin_amdgcn_exp2f(z[ht][i] - m_run[ht]) : 0.f;
+        p[ht][i] = __builtin_amdgcn_exp2f(tz[ht][i]);
         le_run[ht] += p[ht][i];
       }
-    }
 
     // ---- P^T in the 32x32x16 B layout: lane l gets keys 8h2 + j of head c32
     uint32_t pk[2][2];  // [tile ht][pair]: packed 16-bit P of keys 4g4 + 2*pair + {0,1}
@@ -500,16 +561,14 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
                        ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
         }
     } else {
+      // one packed round-to-nearest-even conversion per pair; O is normalised by the sum of
+      // the unrounded P (le), the rounding of each P being far below the output precision
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const __bf16 v0 = (__bf16)p[ht][2 * pr];
-          const __bf16 v1 = (__bf16)p[ht][2 * pr + 1];
-          l_run[ht] += (float)v0 + (float)v1;
-          pk[ht][pr] = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-        }
+        for (int pr = 0; pr < 2; ++pr)
+          pk[ht][pr] = __builtin_bit_cast(
+              uint32_t, __builtin_convertvector(f32x2{p[ht][2 * pr], p[ht][2 * pr + 1]}, bf16x2));
     }
     // lanes of the low 16-row of each half keep tile 0 and take tile 0 of the row above;
     // lanes of the high 16-row take tile 1 of the row below and keep their tile 1
@@ -557,11 +616,12 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     }
   }
 
-  // ---- merge the four waves: per head M = max m_w, factors 2^(m_w - M)
+  // ---- merge the two key halves of each head (waves w and w ^ 2): M = max m, factors
+  // 2^(m - M) (a wave that saw no live key has m at the floor and l = 0)
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    l_run[ht] = rows4_sum(l_run[ht]);
     le_run[ht] = rows4_sum(le_run[ht]);
+    l_run[ht] = FP8 ? rows4_sum(l_run[ht]) : le_run[ht];
   }
   if (g4 == 0) {
 #pragma unroll
@@ -574,25 +634,18 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   __syncthreads();
   float fme;  // this wave's factor for head c32
   {
-    float mw[4], M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      mw[w] = xm[(w * 3 + 0) * kHB + c32];
-      M = fmaxf(M, mw[w]);
-    }
-    float Ls = 0.f, LEs = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);
-      Ls = fmaf(f, xm[(w * 3 + 1) * kHB + c32], Ls);
-      LEs = fmaf(f, xm[(w * 3 + 2) * kHB + c32], LEs);
-    }
-    fme = mw[wave] == -INFINITY ? 0.f : exp2f(mw[wave] - M);
+    const int pw = wave ^ 2;
+    const float m0 = xm[(wave * 3 + 0) * kHB + c32], m1 = xm[(pw * 3 + 0) * kHB + c32];
+    const float M = fmaxf(m0, m1);
+    const float f0 = exp2f(m0 - M), f1 = exp2f(m1 - M);
+    const float Ls = f0 * xm[(wave * 3 + 1) * kHB + c32] + f1 * xm[(pw * 3 + 1) * kHB + c32];
+    const float LEs = f0 * xm[(wave * 3 + 2) * kHB + c32] + f1 * xm[(pw * 3 + 2) * kHB + c32];
+    fme = f0;
     if (FP8) fme *= smax;  // O was accumulated relative to the largest row scale
-    if (wave == 0 && h2 == 0) {
-      xf[0 * kHB + c32] = M;
-      xf[1 * kHB + c32] = Ls;
-      xf[2 * kHB + c32] = LEs;
+    if (kh == 0 && h2 == 0) {
+      xf[(hh * 3 + 0) * kHB + c32] = M;
+      xf[(hh * 3 + 1) * kHB + c32] = Ls;
+      xf[(hh * 3 + 2) * kHB + c32] = LEs;
       const int head = h0 + c32;
       if (nsplit == 1) {
         if (lse) lse[(int64_t)t * kH + head] = LEs > 0.f ? (M + log2f(LEs)) * kLn2 : -INFINITY;
@@ -602,44 +655,50 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       }
     }
   }
-  // four rounds of 128 dims: every wave stores its scaled O^T, then wave w sums dims
-  // 32w .. 32w+31 of the round over the four waves and writes them out
+  // four rounds of 128 dims: every wave stores its scaled O^T, then wave (hh, kh) sums dims
+  // 64kh .. 64kh+63 of the round over the two key halves of head half hh and writes them out
+  // (one straight-line copy of the rounds per kind of output)
   float* xo = (float*)tiles;  // [wave][head][kXPitch]
   const int sh = lane >> 1;   // summed head
-  const int sd = 16 * (lane & 1);
+  const int sd = 64 * kh + 32 * (lane & 1);
 #pragma unroll
   for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], fme);
+  const float Lsh = xf[(hh * 3 + 1) * kHB + sh];
+  const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
+  const int head = h0 + sh;
+  const int64_t orow = ((int64_t)t * kH + head) * kDv;                         // output row
+  const int64_t prow = (((int64_t)tl * nsplit + split) * kH + head) * kDv;    // partial row
+  auto rounds = [&](auto&& emit) {
 #pragma unroll
-  for (int rd = 0; rd < 4; ++rd) {
+    for (int rd = 0; rd < 4; ++rd) {
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const int mi = 4 * rd + mm;
+      for (int mm = 0; mm < 4; ++mm) {
+        const int mi = 4 * rd + mm;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * mm + 8 * q4 + 4 * h2;
-        const f32x4 v = {o[mi][4 * q4], o[mi][4 * q4 + 1], o[mi][4 * q4 + 2], o[mi][4 * q4 + 3]};
-        *(f32x4*)(xo + (wave * kHB + c32) * kXPitch + d) = v;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * mm + 8 * q4 + 4 * h2;
+          const f32x4 v = {o[mi][4 * q4], o[mi][4 * q4 + 1], o[mi][4 * q4 + 2],
+                           o[mi][4 * q4 + 3]};
+          *(f32x4*)(xo + (wave * kHB + c32) * kXPitch + d) = v;
+        }
       }
-    }
-    __syncthreads();
-    const float Ls = xf[1 * kHB + sh];
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+      __syncthreads();
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int d = 32 * wave + sd + 4 * k4;
-      f32x4 acc = *(const f32x4*)(xo + (0 * kHB + sh) * kXPitch + d);
-#pragma unroll
-      for (int w = 1; w < 4; ++w) acc += *(const f32x4*)(xo + (w * kHB + sh) * kXPitch + d);
-      const int dim = 128 * rd + d;
-      const int head = h0 + sh;
-      if (nsplit == 1) {
-        store_out4<OUT_F32>(out, ((int64_t)t * kH + head) * kDv + dim, acc * inv);
-      } else {
-        const int64_t pr = ((int64_t)tl * nsplit + split) * kH + head;
-        *(f32x4*)(part_o + pr * kDv + dim) = acc;
+      for (int k4 = 0; k4 < 8; ++k4) {
+        const int d = sd + 4 * k4;
+        const f32x4 acc = *(const f32x4*)(xo + (hh * kHB + sh) * kXPitch + d) +
+                          *(const f32x4*)(xo + ((hh + 2) * kHB + sh) * kXPitch + d);
+        emit(128 * rd + d, acc);
       }
+      if (rd < 3) __syncthreads();
     }
-    __syncthreads();
+  };
+  if (nsplit == 1) {
+    rounds([&](int dim, f32x4 acc) { store_out4<OUT_F32>(out, orow + dim, acc * inv); });
+  } else if (OUT_F32) {
+    rounds([&](int dim, f32x4 acc) { *(f32x4*)(part_o + prow + dim) = acc; });
+  } else {  // bf16 output: the split's own normalised O as an fp16 partial
+    rounds([&](int dim, f32x4 acc) { store_part16(part_o, prow + dim, acc * inv); });
   }
 }
 
@@ -665,8 +724,45 @@ __global__ __launch_bounds__(256, 1) void mla_attn_fp8_o32_kernel(MLA_ATTN_ARGS)
   mla_attn_body<true, true>(MLA_ATTN_PASS);
 }
 
-// Merge split partials (m in log2 units; l = sum of the rounded P, le = unrounded sum):
+// Merge split partials (m in log2 units; l = the normaliser of O, le = unrounded sum of P):
 // O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j,  lse = M + log2 sum_j 2^(m_j - M) le_j.
+// fp32 output: O_j is the split's unnormalised fp32 sum.  bf16 output: O_j is stored
+// normalised (O_j / l_j) as fp16 (see store_part16), and is weighted by l_j here.
+// One split's partial O for 4 consecutive dims (fp32 unnormalised, or fp16 normalised).
+template <bool OUT_F32>
+__device__ __forceinline__ f32x4 load_part4(const float* part_o, int64_t off) {
+  if (OUT_F32) return *(const f32x4*)(part_o + off);
+  const f16x4 h = *(const f16x4*)((const uint16_t*)part_o + off);
+  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * kPartUnscale;
+}
+
+// Up to N splits: unconditional loads (the split index clamped; the extra copies get weight
+// 0), so that they all go out before the first use.
+template <bool OUT_F32, int N>
+__device__ __forceinline__ void combine_splits(int nsplit, int64_t pr0, int tid,
+                                               const float* __restrict__ part_o,
+                                               const float* __restrict__ part_ml, float& M,
+                                               float& Lsum, float& LEsum, f32x4& acc) {
+  f32x4 ml[N], v[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int64_t pr = pr0 + min(j, nsplit - 1) * kH;
+    ml[j] = *(const f32x4*)(part_ml + pr * 4);
+    v[j] = load_part4<OUT_F32>(part_o, pr * kDv + 4 * tid);
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    if (j < nsplit && ml[j][1] > 0.f) M = fmaxf(M, ml[j][0]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const bool use = j < nsplit && ml[j][1] > 0.f;
+    const float wgt = use ? exp2f(ml[j][0] - M) : 0.f;
+    Lsum = fmaf(wgt, ml[j][1], Lsum);
+    LEsum = fmaf(wgt, ml[j][2], LEsum);
+    acc += (OUT_F32 ? wgt : wgt * ml[j][1]) * v[j];
+  }
+}
+
 template <bool OUT_F32>
 __global__ __launch_bounds__(128) void mla_combine_kernel(int t_begin, int t_count, int nsplit,
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -674,22 +770,29 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int t_begin, int t_cou
   const int tl = blockIdx.x / kH, head = blockIdx.x % kH;
   const int t = t_begin + tl;
   const int tid = threadIdx.x;
-  float M = -INFINITY;
-  for (int j = 0; j < nsplit; ++j) {
-    const int64_t pr = ((int64_t)tl * nsplit + j) * kH + head;
-    if (part_ml[pr * 4 + 1] > 0.f) M = fmaxf(M, part_ml[pr * 4]);
-  }
-  float Lsum = 0.f, LEsum = 0.f;
+  const int64_t pr0 = (int64_t)tl * nsplit * kH + head;  // split j: pr0 + j * kH
+  float M = -INFINITY, Lsum = 0.f, LEsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < nsplit; ++j) {
-    const int64_t pr = ((int64_t)tl * nsplit + j) * kH + head;
-    const f32x4 ml = *(const f32x4*)(part_ml + pr * 4);
-    if (!(ml[1] > 0.f)) continue;
-    const float wgt = exp2f(ml[0] - M);
-    Lsum = fmaf(wgt, ml[1], Lsum);
-    LEsum = fmaf(wgt, ml[2], LEsum);
-    const f32x4 v = *(const f32x4*)(part_o + pr * kDv + 4 * tid);
-    acc += wgt * v;
+  if (nsplit <= 2) {
+    combine_splits<OUT_F32, 2>(nsplit, pr0, tid, part_o, part_ml, M, Lsum, LEsum, acc);
+  } else if (nsplit <= 4) {
+    combine_splits<OUT_F32, 4>(nsplit, pr0, tid, part_o, part_ml, M, Lsum, LEsum, acc);
+  } else if (nsplit <= 8) {
+    combine_splits<OUT_F32, 8>(nsplit, pr0, tid, part_o, part_ml, M, Lsum, LEsum, acc);
+  } else {
+    for (int j = 0; j < nsplit; ++j) {
+      const float* m = part_ml + (pr0 + j * kH) * 4;
+      if (m[1] > 0.f) M = fmaxf(M, m[0]);
+    }
+    for (int j = 0; j < nsplit; ++j) {
+      const f32x4 ml = *(const f32x4*)(part_ml + (pr0 + j * kH) * 4);
+      if (!(ml[1] > 0.f)) continue;
+      const float wgt = exp2f(ml[0] - M);
+      Lsum = fmaf(wgt, ml[1], Lsum);
+      LEsum = fmaf(wgt, ml[2], LEsum);
+      acc += (OUT_F32 ? wgt : wgt * ml[1]) *
+             load_part4<OUT_F32>(part_o, (pr0 + j * kH) * kDv + 4 * tid);
+    }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   store_out4<OUT_F32>(out, ((int64_t)t * kH + head) * kDv + 4 * tid, acc * inv);
@@ -713,10 +816,10 @@ int attn_keys_per_split(int K, int nsplit) {
 }
 
 int attn_split_count(int t_count, int K) {
-  // enough workgroups (4 head groups per token and split) to cover the 256 CUs, at least 64
-  // keys per split, at most kMaxKps; recomputed from the rounded split length so that no
-  // split is empty
-  int s = (256 + 4 * t_count - 1) / (4 * t_count);
+  // enough workgroups (2 head groups per token and split) to cover the 256 CUs, at least one
+  // stage of keys per split, at most kMaxKps; recomputed from the rounded split length so
+  // that no split is empty
+  int s = (256 + 2 * t_count - 1) / (2 * t_count);
   s = std::max(1, std::min(s, (K + kSR - 1) / kSR));
   s = std::max(s, (K + kMaxKps - 1) / kMaxKps);
   const int kps = attn_keys_per_split(K, s);
@@ -745,7 +848,7 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
                                        (int)shm);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fn, dim3(t_count * nsplit * 4), dim3(256), shm, st, bt, t_begin, t_count, q, kv,
+  hipLaunchKernelGGL(fn, dim3(t_count * nsplit * 2), dim3(256), shm, st, bt, t_begin, t_count, q, kv,
                      kvscale, idx, K, c2, nsplit, kps, out, lse, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
