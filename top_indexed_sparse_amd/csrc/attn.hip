@@ -232,6 +232,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   float* xm = (float*)(sm + SM::xm);          // [wave][m, l, le][32 heads]
   float* xf = xm + 4 * 3 * kHB;               // [head half][M, L, LE][32 heads]
   __shared__ float red[4];
+  __shared__ int anyv[4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;  // 16x16 layouts
@@ -320,6 +321,13 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, __shfl_xor(smax, o));
     if (lane == 0) red[wave] = smax;
   }
+  {  // some selected row of the wave's rows (-1 if there is none): one ballot
+    int v = -1;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v = max(v, slot[j]);
+    const uint64_t b = __ballot(v >= 0);
+    if (lane == 0) anyv[wave] = b ? __builtin_amdgcn_readlane(v, __builtin_ctzll(b)) : -1;
+  }
   __syncthreads();
   // per wave tile: bit m = row pi(m) selected (the order in which the keys are consumed)
   for (int tt = tid; tt < nrows / kWT; tt += 256) {
@@ -328,6 +336,11 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     masks[tt] = (uint16_t)m;
   }
   if (FP8) smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // Rows that are not selected are gathered from a selected row of the split (finite data,
+  // whose P is zero: exactly nothing is added).  A split without any selected row skips
+  // the loop, leaving O = 0 and l = 0.
+  const int fill = __builtin_amdgcn_readfirstlane(max(max(anyv[0], anyv[1]), max(anyv[2], anyv[3])));
+  const int nst = fill >= 0 ? nstage : 0;
   const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
   __syncthreads();
 
@@ -360,21 +373,23 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // 16l + 15 of the row), the rest are region-B loads; it goes to LDS one stage later
   auto load_one = [&](const TileRows& tr, int j) -> i32x4 {
     if (j < kWT) {
-      const uint32_t sr = (uint32_t)max(__builtin_amdgcn_readlane(tr.my, j), 0);
+      const int sj = __builtin_amdgcn_readlane(tr.my, j);
+      const uint32_t sr = (uint32_t)(sj >= 0 ? sj : fill);
       // the row base in scalar registers: the scalar-base form of the load
       const uint64_t base = (uint64_t)(uintptr_t)kv + (uint64_t)sr * F::kRowBytes;
       const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)base);
       const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
       const uint64_t rowp = ((uint64_t)bhi << 32) | blo;
-      // (global, not generic: a generic load would also count against the LDS counter)
-      if (!FP8 || lane < F::kVBytes / 16) return *GLOBAL_PTR(const i32x4, rowp + lane16);
-      return i32x4{0, 0, 0, 0};
+      // (global, not generic: a generic load would also count against the LDS counter; all
+      // lanes load, e4m3 lanes 32..63 a copy of lane - 32's chunk, so that no lane-predicated
+      // write of the queue registers makes the counters wait)
+      return *GLOBAL_PTR(const i32x4, rowp + (FP8 ? 16u * (uint32_t)(lane & 31) : lane16));
     }
     const int jb = j - kWT;  // (a run-time index: select, do not index the array)
     const int bs = (F::kBLoads == 1 || jb == 0) ? tr.bslot[0] : tr.bslot[F::kBLoads - 1];
     const int c = (64 * jb + lane) % kRC;
-    return *GLOBAL_PTR(const i32x4, (uintptr_t)kv + (uint64_t)(uint32_t)max(bs, 0) * F::kRowBytes +
-                                        F::kVBytes + 16 * c);
+    return *GLOBAL_PTR(const i32x4, (uintptr_t)kv + (uint64_t)(uint32_t)(bs >= 0 ? bs : fill) *
+                                            F::kRowBytes + F::kVBytes + 16 * c);
   };
   auto write_one = [&](int st, int j, i32x4 v) {
     char* ta = tiles + ((st % F::kBufs) * 2 + kh) * F::kWBytes;
@@ -401,18 +416,17 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // stage starts with a barrier: the tile of the stage has been written by both of its waves,
   // and the ring slot written during the stage has been read by both.
   i32x4 stg[F::kIssueW];
-  if (nstage > 0) {
-    const TileRows tr = tile_rows(0);
+  // (one guarded block from the first gather to the end of the loop: the gathers read `fill`,
+  // and a single path into the loop keeps the counter waits exact)
+  if (nst > 0) {
+    const TileRows tr0 = tile_rows(0);
 #pragma unroll
-    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr, jlo + j);
+    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr0, jlo + j);
 #pragma unroll
     for (int j = 0; j < F::kIssueW; ++j) write_one(0, jlo + j, stg[j]);
-  }
-  {
-    const TileRows tr = tile_rows(min(1, nstage - 1));
+    const TileRows tr1 = tile_rows(min(1, nst - 1));
 #pragma unroll
-    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr, jlo + j);
-  }
+    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr1, jlo + j);
   // Q has landed on every path into the loop (otherwise the waits for Q placed inside the loop
   // would also hold back the queued gathers); its last fragments go to LDS
 #pragma unroll
@@ -422,9 +436,9 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 #pragma unroll
     for (int kk = 0; kk < kQL; ++kk) *(bf16x8*)(qlds + (ht * kQL + kk) * 1024) = qtl[ht][kk];
   }
-  for (int st = 0; st < nstage; ++st) {
+  for (int st = 0; st < nst; ++st) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const TileRows trn = tile_rows(min(st + 2, nstage - 1));
+    const TileRows trn = tile_rows(min(st + 2, nst - 1));
     const uint32_t mask = masks[st * 2 + kh];
     const char* sb = tiles + ((st % F::kBufs) * 2 + kh) * F::kWBytes;
     const int rbase = st * kSR + kh * kWT;
@@ -615,6 +629,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       }
     }
   }
+  }  // nst > 0
 
   // ---- merge the two key halves of each head (waves w and w ^ 2): M = max m, factors
   // 2^(m - M) (a wave that saw no live key has m at the floor and l = 0)
