@@ -48,25 +48,21 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return wave_incl(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
-// Exclusive scan over the 1024 threads; `sh` holds >= 17 words.  Ends with a barrier.
+// Exclusive scan over the 1024 threads with one barrier: the 16 wave totals go to sh[0..15];
+// lane l of every wave reads total l & 15 and scans them on the DPP network.  sh must not be
+// written again before the next barrier after this call (every caller has one in between).
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v);
   if (lane == 63) sh[wid] = inc;
   __syncthreads();
-  if (wid == 0) {
-    const uint32_t x = lane < 16 ? sh[lane] : 0u;
-    const uint32_t xi = wave_incl_scan(x);
-    if (lane < 16) sh[lane] = xi - x;
-    if (lane == 15) sh[16] = xi;
-  }
-  __syncthreads();
-  const uint32_t r = sh[wid] + inc - v;
-  total = sh[16];
-  __syncthreads();
-  return r;
+  const uint32_t w = wave_incl_scan(lane < 16 ? sh[lane] : 0u);
+  total = __builtin_amdgcn_readlane(w, 15);
+  const uint32_t before = wid ? __builtin_amdgcn_readlane(w, wid - 1) : 0u;
+  return before + inc - v;
 }
 
+// Row minimum and maximum over the 1024 threads with one barrier (sh: 32 words, same rule).
 __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   auto fmin_ = [](uint32_t a, uint32_t b) { return min(a, b); };
@@ -75,49 +71,50 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_
   mx = __builtin_amdgcn_readlane(wave_incl(mx, 0u, fmax_), 63);
   if (lane == 0) { sh[wid] = mn; sh[16 + wid] = mx; }
   __syncthreads();
-  if (wid == 0) {
-    uint32_t a = lane < 16 ? sh[lane] : ~0u, c = lane < 16 ? sh[16 + lane] : 0u;
-    a = __builtin_amdgcn_readlane(wave_incl(a, ~0u, fmin_), 63);
-    c = __builtin_amdgcn_readlane(wave_incl(c, 0u, fmax_), 63);
-    if (lane == 0) { sh[32] = a; sh[33] = c; }
-  }
-  __syncthreads();
-  mn = sh[32];
-  mx = sh[33];
-  __syncthreads();
+  mn = __builtin_amdgcn_readlane(wave_incl(lane < 16 ? sh[lane] : ~0u, ~0u, fmin_), 15);
+  mx = __builtin_amdgcn_readlane(wave_incl(lane < 16 ? sh[16 + lane] : 0u, 0u, fmax_), 15);
 }
 
 // LDS of the selection kernel: histogram, scan scratch, picks and the candidate list.
 constexpr int kCandMax = 8192;
+constexpr int kListMax = kCandMax / 2;  // candidate list: keys and positions
 struct SelSmem {
   uint32_t hist[2048];
-  uint32_t sh[40];
+  uint32_t hist2[2048];
+  uint32_t sh[48];    // scan totals (0..15), row min/max (16..47)
   uint32_t pick[4];
   uint32_t candk[kCandMax];
 };
 
 // Radix select of the krem-th largest key among the keys produced by `each` (called with a
 // visitor), over r = key - base with digits of up to 11 bits from bit `hi` down.  Returns the
-// threshold key; krem is left as the number of keys equal to it that are taken.
+// threshold key; krem is left as the number of keys equal to it that are taken.  The two
+// histograms alternate, the next one being cleared while the current one fills: three
+// barriers per digit.
 template <typename Each>
 __device__ __forceinline__ uint32_t radix_select(uint32_t base, int hi, uint32_t& krem,
                                                  SelSmem& S, Each each) {
   const int tid = threadIdx.x;
+  uint32_t* hb[2] = {S.hist, S.hist2};
+  int cur = 0;
   uint32_t prefix = 0u;
+  hb[0][tid] = 0u;
+  hb[0][tid + 1024] = 0u;
+  __syncthreads();
   while (hi > 0) {
     const int lo = max(0, hi - 11);
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
-    S.hist[tid] = 0u;
-    S.hist[tid + 1024] = 0u;
-    __syncthreads();
+    uint32_t* h = hb[cur];
     each([&](uint32_t key) {
       const uint32_t r = key - base;
       const uint32_t top = hi >= 32 ? 0u : (r >> hi);
-      if (top == prefix) atomicAdd(&S.hist[(r >> lo) & dmask], 1u);
+      if (top == prefix) atomicAdd(&h[(r >> lo) & dmask], 1u);
     });
+    hb[cur ^ 1][tid] = 0u;
+    hb[cur ^ 1][tid + 1024] = 0u;
     __syncthreads();
     // bins in descending order: thread i owns bins 2047-2i and 2046-2i
-    const uint32_t ch = S.hist[2047 - 2 * tid], cl = S.hist[2046 - 2 * tid];
+    const uint32_t ch = h[2047 - 2 * tid], cl = h[2046 - 2 * tid];
     uint32_t tot;
     const uint32_t above_h = block_excl_scan(ch + cl, S.sh, tot);
     const uint32_t above_l = above_h + ch;
@@ -133,19 +130,22 @@ __device__ __forceinline__ uint32_t radix_select(uint32_t base, int hi, uint32_t
     prefix = (prefix << (hi - lo)) | S.pick[0];
     krem -= S.pick[1];
     hi = lo;
-    __syncthreads();
+    cur ^= 1;
   }
   return base + prefix;
 }
 
 // One 1024-thread workgroup per row; thread i owns NPT consecutive positions per chunk of
-// 1024*NPT (rows that fit one chunk keep their keys in registers).
+// 1024*NPT (rows that fit one chunk keep their keys in registers, loaded before the token's
+// causal length is known and masked after).
 // Threshold search, rows held in registers: a sample (2 keys per thread, at a fixed stride)
 // is histogrammed over the row's key range; the bin where the sample count from the top
-// reaches 1.25x the expected share of K (plus 16) gives a lower bound T_lo, and the keys
-// >= T_lo (normally ~1.4 K of them) are listed in LDS and radix-selected exactly.  When the
-// list holds fewer than K keys or would overflow (heavy ties, adversarial orders), the exact
-// radix select runs over the whole row instead; both give the same threshold.
+// reaches 1.25x the expected share of K (plus 16) gives a lower bound T_lo.  The keys >= T_lo
+// (normally ~1.4 K of them) are histogrammed again over their own range, which puts the
+// k-th largest key in a bin of a few keys: those are ranked by one wave (or, for larger bins,
+// radix-selected).  When fewer than K keys reach T_lo, or the bin would overflow the list
+// (heavy ties, adversarial orders), the exact radix select runs over the whole row instead;
+// every path gives the same threshold.
 template <int NPT>
 __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_begin,
     const float* __restrict__ scores, int64_t ld, int K, int32_t* __restrict__ out_idx,
@@ -155,8 +155,43 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
   const int tid = threadIdx.x;
   const int tl = blockIdx.x;
   const int t = t_begin + tl;
-  const int n = locate(bt, t).n;
   const float* row = scores + (int64_t)tl * ld;
+  constexpr int CH = 1024 * NPT;
+  uint32_t key[NPT];  // the raw score bits until to_keys, then the order keys
+
+  // scores of chunk c0 at positions < lim (positions past it read nothing)
+  auto load_raw = [&](int c0, int lim) {
+    const int p0 = c0 + tid * NPT;
+#pragma unroll
+    for (int j = 0; j < NPT; j += 4) {
+      const int p = p0 + j;
+      if (p + 3 < lim) {
+        const uint4 f = *(const uint4*)(row + p);
+        key[j] = f.x; key[j + 1] = f.y; key[j + 2] = f.z; key[j + 3] = f.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[j + e] = (p + e < lim) ? __float_as_uint(row[p + e]) : 0u;
+      }
+    }
+  };
+  // Positions past the row hold key 0, which no score maps to (the smallest key, of -inf,
+  // is 0x007fffff): validity is key != 0, and every threshold below is above 0.
+  int n = 0;
+  auto to_keys = [&](int c0) {
+    const int p0 = c0 + tid * NPT;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) key[j] = p0 + j < n ? order_key(__uint_as_float(key[j])) : 0u;
+  };
+  auto load_chunk = [&](int c0) {
+    load_raw(c0, n);
+    to_keys(c0);
+  };
+
+  // the first chunk goes out before the token lookup (up to the row stride, which bounds
+  // every causal length), so the two memory latencies overlap
+  const LocLoads lw = locate_issue(bt);
+  load_raw(0, (int)min<int64_t>(ld, (int64_t)CH));
+  n = locate_finish(bt, t, lw).n;
   int32_t* oi = out_idx + (int64_t)t * K;
   float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
 
@@ -168,27 +203,7 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
     return;
   }
   const int k = K;
-  constexpr int CH = 1024 * NPT;
   const bool cached = n <= CH;
-  uint32_t key[NPT];
-
-  auto load_chunk = [&](int c0) {
-    const int p0 = c0 + tid * NPT;
-#pragma unroll
-    for (int j = 0; j < NPT; j += 4) {
-      const int p = p0 + j;
-      if (p + 3 < n) {
-        float4 f = *(const float4*)(row + p);
-        key[j] = order_key(f.x); key[j + 1] = order_key(f.y);
-        key[j + 2] = order_key(f.z); key[j + 3] = order_key(f.w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) key[j + e] = (p + e < n) ? order_key(row[p + e]) : 0u;
-      }
-    }
-  };
-  // Positions past the row hold key 0, which no score maps to (the smallest key, of -inf,
-  // is 0x007fffff): validity is key != 0, and every threshold below is above 0.
   // visits every valid key of the row (from registers when cached)
   auto each_row = [&](auto&& f) {
     for (int c0 = 0; c0 < n; c0 += CH) {
@@ -199,12 +214,17 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
     }
   };
 
-  if (cached) load_chunk(0);
+  to_keys(0);
+  S.hist[tid] = 0u;
+  S.hist[tid + 1024] = 0u;
+  S.hist2[tid] = 0u;
+  S.hist2[tid + 1024] = 0u;
+  if (tid == 0) S.pick[3] = 0u;
 
-  // ---- key range of the row
+  // ---- key range of the row (its barriers also order the clears above)
   uint32_t kmin = ~0u, kmax = 0u;
   each_row([&](uint32_t kk) { kmin = min(kmin, kk); kmax = max(kmax, kk); });
-  block_minmax(kmin, kmax, S.sh);
+  block_minmax(kmin, kmax, S.sh + 16);
   const uint32_t span = kmax - kmin;
   const int hi = span ? 32 - __clz(span) : 0;
 
@@ -214,9 +234,6 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
   if (cached && hi > 0) {
     // ---- sampled lower bound of the threshold
     const int shift = max(0, hi - 11);
-    S.hist[tid] = 0u;
-    S.hist[tid + 1024] = 0u;
-    __syncthreads();
     if (key[0] != 0u) atomicAdd(&S.hist[(key[0] - kmin) >> shift], 1u);
     if (key[NPT / 2] != 0u) atomicAdd(&S.hist[(key[NPT / 2] - kmin) >> shift], 1u);
     __syncthreads();
@@ -232,29 +249,154 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
       __syncthreads();
     }
     const uint32_t tlo = kmin + (S.pick[2] << shift);
-    // ---- list the keys >= tlo
+    // ---- list the keys >= tlo with their positions, in position order (~1.4 K of them)
     uint32_t c = 0u;
 #pragma unroll
     for (int j = 0; j < NPT; ++j) c += key[j] >= tlo ? 1u : 0u;
     uint32_t C;
     uint32_t o = block_excl_scan(c, S.sh, C);
-    if (C >= (uint32_t)k && C <= (uint32_t)kCandMax) {
+    if (C >= (uint32_t)k && C <= (uint32_t)kListMax) {
+      uint32_t* lk = S.candk;              // keys
+      uint32_t* lp = S.candk + kListMax;   // positions
+      {
+        const uint32_t p0 = (uint32_t)(tid * NPT);
 #pragma unroll
-      for (int j = 0; j < NPT; ++j)
-        if (key[j] >= tlo) S.candk[o++] = key[j];
+        for (int j = 0; j < NPT; ++j)
+          if (key[j] >= tlo) {
+            lk[o] = key[j];
+            lp[o] = p0 + j;
+            ++o;
+          }
+      }
       __syncthreads();
+      // ---- histogram of the list over [tlo, kmax]: the k-th largest lies in one bin
       const uint32_t cspan = kmax - tlo;
-      T = radix_select(tlo, cspan ? 32 - __clz(cspan) : 0, krem, S, [&](auto&& f) {
-        for (uint32_t i = tid; i < C; i += 1024) f(S.candk[i]);
-      });
-      found = true;
+      const int shift2 = max(0, (cspan ? 32 - __clz(cspan) : 0) - 11);
+      for (uint32_t i = tid; i < C; i += 1024) atomicAdd(&S.hist2[(lk[i] - tlo) >> shift2], 1u);
+      __syncthreads();
+      {
+        const uint32_t ch = S.hist2[2047 - 2 * tid], cl = S.hist2[2046 - 2 * tid];
+        uint32_t tot;
+        const uint32_t above_h = block_excl_scan(ch + cl, S.sh, tot);
+        const uint32_t above_l = above_h + ch;
+        if (ch && above_h < (uint32_t)k && (uint32_t)k <= above_h + ch) {
+          S.pick[0] = 2047 - 2 * tid;
+          S.pick[1] = above_h;
+        }
+        if (cl && above_l < (uint32_t)k && (uint32_t)k <= above_l + cl) {
+          S.pick[0] = 2046 - 2 * tid;
+          S.pick[1] = above_l;
+        }
+        __syncthreads();
+      }
+      const uint32_t b2 = S.pick[0];
+      const uint32_t tb = tlo + (b2 << shift2);  // the bin holds keys tb .. tb + 2^shift2 - 1
+      const uint32_t cb = S.hist2[b2];
+      krem = (uint32_t)k - S.pick[1];            // keys of the bin that are taken
+      if (cb == krem) {  // the whole bin: every key >= tb, none equal to the threshold
+        T = tb - 1u;
+        krem = 0u;
+      } else if (cb <= 64u) {
+        // one wave ranks the bin: the key with (# greater) < krem <= (# greater or equal)
+        const uint32_t bhi =
+            (uint32_t)min<uint64_t>((uint64_t)tb + ((1u << shift2) - 1u), 0xffffffffull);
+        uint32_t* bl = S.hist;  // (free since the sample)
+        for (uint32_t i = tid; i < C; i += 1024)
+          if (lk[i] >= tb && lk[i] <= bhi) bl[atomicAdd(&S.pick[3], 1u)] = lk[i];
+        __syncthreads();
+        if (tid < 64) {
+          const uint32_t mine = tid < (int)cb ? bl[tid] : 0u;
+          uint32_t gt = 0u, ge = 0u;
+          for (uint32_t j = 0; j < cb; ++j) {
+            const uint32_t ot = bl[j];
+            gt += ot > mine ? 1u : 0u;
+            ge += ot >= mine ? 1u : 0u;
+          }
+          const uint64_t hit = __ballot(tid < (int)cb && gt < krem && krem <= ge);
+          const int src = (int)__builtin_ctzll(hit);  // (never empty: ranks cover 1..cb)
+          if (tid == 0) {
+            S.pick[0] = __builtin_amdgcn_readlane(mine, src);
+            S.pick[1] = krem - __builtin_amdgcn_readlane(gt, src);
+          }
+        }
+        __syncthreads();
+        T = S.pick[0];
+        krem = S.pick[1];
+      } else {
+        // a larger bin: radix select within it (list keys outside the bin fall outside the
+        // digit prefix and are not counted)
+        T = radix_select(tb, shift2, krem, S, [&](auto&& f) {
+          for (uint32_t i = tid; i < C; i += 1024) f(lk[i]);
+        });
+      }
+      // ---- compaction over the list (position order): an entry is taken if its key is > T,
+      // or == T with fewer than krem earlier entries == T.  Thread i owns entries E*i ..
+      const uint32_t E = (C + 1023u) / 1024u;
+      uint32_t cgt = 0u, ceq = 0u;
+      for (uint32_t e = 0; e < E; ++e) {
+        const uint32_t i = (uint32_t)tid * E + e;
+        if (i < C) {
+          cgt += lk[i] > T ? 1u : 0u;
+          ceq += lk[i] == T ? 1u : 0u;
+        }
+      }
+      uint32_t tot;
+      const uint32_t before = block_excl_scan(cgt | (ceq << 16), S.sh, tot);
+      uint32_t eqb = before >> 16;
+      uint32_t oo = (before & 0xffffu) + min(eqb, krem);
+      for (uint32_t e = 0; e < E; ++e) {
+        const uint32_t i = (uint32_t)tid * E + e;
+        if (i < C) {
+          const uint32_t kk = lk[i];
+          const bool eq = kk == T;
+          if (kk > T || (eq && eqb < krem)) {
+            oi[oo] = (int32_t)lp[i];
+            if (ov) ov[oo] = key_value(kk);
+            ++oo;
+          }
+          eqb += eq ? 1u : 0u;
+        }
+      }
+      return;
     }
   }
-  if (!found) T = radix_select(kmin, hi, krem, S, each_row);
+  if (!found) {
+    krem = (uint32_t)k;
+    T = radix_select(kmin, hi, krem, S, each_row);
+  }
   // T is the threshold key; krem elements equal to T are taken (in position order)
 
   // ---- order-preserving compaction: one scan of the per-thread counts of keys > T (low 16
-  // bits) and == T (high 16 bits; both totals stay below 2^16 per chunk)
+  // bits) and == T (high 16 bits; both totals stay below 2^16 per chunk).  Rows held in
+  // registers stage the k positions and keys in LDS and write them out coalesced.
+  if (cached && k <= kCandMax) {
+    uint32_t cgt = 0u, ceq = 0u;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      cgt += key[j] > T ? 1u : 0u;
+      ceq += key[j] == T ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t before = block_excl_scan(cgt | (ceq << 16), S.sh, tot);
+    uint32_t e = before >> 16;  // ties before this thread
+    uint32_t o = (before & 0xffffu) + min(e, krem);
+    uint32_t sel = 0u;  // bit j: position p0 + j is taken
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const bool eq = key[j] == T;
+      sel |= (key[j] > T || (eq && e < krem)) ? (1u << j) : 0u;
+      e += eq ? 1u : 0u;
+    }
+    const uint32_t p0 = (uint32_t)(tid * NPT);
+    for (; sel; sel &= sel - 1u) S.candk[o++] = p0 + (uint32_t)__builtin_ctz(sel);
+    __syncthreads();
+    for (int i = tid; i < k; i += 1024) {
+      const int32_t p = (int32_t)S.candk[i];
+      oi[i] = p;
+      if (ov) ov[i] = row[p] + 0.f;  // (+ 0: -0.0 comes out as +0.0, as from a key)
+    }
+    return;
+  }
   uint32_t run_gt = 0u, run_eq = 0u;
   for (int c0 = 0; c0 < n; c0 += CH) {
     if (!cached) load_chunk(c0);
