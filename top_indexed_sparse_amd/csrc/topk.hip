@@ -24,8 +24,8 @@ namespace tis {
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0.0 ties with +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = u == 0x80000000u ? 0u : u;  // -0.0 ties with +0.0
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // negative: ~u, else u | sign
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -58,6 +58,23 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   __syncthreads();
   const uint32_t w = wave_incl_scan(lane < 16 ? sh[lane] : 0u);
   total = __builtin_amdgcn_readlane(w, 15);
+  const uint32_t before = wid ? __builtin_amdgcn_readlane(w, wid - 1) : 0u;
+  return before + inc - v;
+}
+
+// The same scan, also returning the maximum of m over the threads (sh: 32 words).
+__device__ __forceinline__ uint32_t block_excl_scan_max(uint32_t v, uint32_t& m, uint32_t* sh,
+                                                        uint32_t& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  auto fmax_ = [](uint32_t a, uint32_t b) { return max(a, b); };
+  const uint32_t inc = wave_incl_scan(v);
+  const uint32_t wm = __builtin_amdgcn_readlane(wave_incl(m, 0u, fmax_), 63);
+  if (lane == 63) sh[wid] = inc;
+  if (lane == 0) sh[16 + wid] = wm;
+  __syncthreads();
+  const uint32_t w = wave_incl_scan(lane < 16 ? sh[lane] : 0u);
+  total = __builtin_amdgcn_readlane(w, 15);
+  m = __builtin_amdgcn_readlane(wave_incl(lane < 16 ? sh[16 + lane] : 0u, 0u, fmax_), 15);
   const uint32_t before = wid ? __builtin_amdgcn_readlane(w, wid - 1) : 0u;
   return before + inc - v;
 }
@@ -179,8 +196,14 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
   int n = 0;
   auto to_keys = [&](int c0) {
     const int p0 = c0 + tid * NPT;
+    if (__all(p0 + NPT <= n)) {  // (the wave is inside the row: no position test)
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) key[j] = p0 + j < n ? order_key(__uint_as_float(key[j])) : 0u;
+      for (int j = 0; j < NPT; ++j) key[j] = order_key(__uint_as_float(key[j]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPT; ++j)
+        key[j] = p0 + j < n ? order_key(__uint_as_float(key[j])) : 0u;
+    }
   };
   auto load_chunk = [&](int c0) {
     load_raw(c0, n);
@@ -221,21 +244,19 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
   S.hist2[tid + 1024] = 0u;
   if (tid == 0) S.pick[3] = 0u;
 
-  // ---- key range of the row (its barriers also order the clears above)
-  uint32_t kmin = ~0u, kmax = 0u;
-  each_row([&](uint32_t kk) { kmin = min(kmin, kk); kmax = max(kmax, kk); });
-  block_minmax(kmin, kmax, S.sh + 16);
-  const uint32_t span = kmax - kmin;
-  const int hi = span ? 32 - __clz(span) : 0;
-
   uint32_t krem = (uint32_t)k;
   uint32_t T = 0u;
-  bool found = false;
-  if (cached && hi > 0) {
-    // ---- sampled lower bound of the threshold
-    const int shift = max(0, hi - 11);
-    if (key[0] != 0u) atomicAdd(&S.hist[(key[0] - kmin) >> shift], 1u);
-    if (key[NPT / 2] != 0u) atomicAdd(&S.hist[(key[NPT / 2] - kmin) >> shift], 1u);
+  if (cached) {
+    // ---- sampled lower bound of the threshold, over the key range of the sample (keys above
+    // it are all candidates anyway); its barrier also orders the clears above
+    uint32_t smin1 = min(key[0] - 1u, key[NPT / 2] - 1u);  // (invalid key 0 -> 0xffffffff)
+    uint32_t smax = max(key[0], key[NPT / 2]);
+    block_minmax(smin1, smax, S.sh + 16);
+    const uint32_t smin = smin1 + 1u;
+    const uint32_t sspan = smax - smin;
+    const int shift = max(0, (sspan ? 32 - __clz(sspan) : 0) - 11);
+    if (key[0] != 0u) atomicAdd(&S.hist[(key[0] - smin) >> shift], 1u);
+    if (key[NPT / 2] != 0u) atomicAdd(&S.hist[(key[NPT / 2] - smin) >> shift], 1u);
     __syncthreads();
     const uint32_t nsamp = (uint32_t)((n + NPT - 1) / NPT + (n + NPT / 2 - 1) / NPT);
     const uint32_t want = min(nsamp, (uint32_t)(((uint64_t)k * nsamp * 5) / (4ull * n)) + 16u);
@@ -248,13 +269,16 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
       if (cl && above_l < want && want <= above_l + cl) S.pick[2] = 2046 - 2 * tid;
       __syncthreads();
     }
-    const uint32_t tlo = kmin + (S.pick[2] << shift);
+    const uint32_t tlo = smin + (S.pick[2] << shift);
     // ---- list the keys >= tlo with their positions, in position order (~1.4 K of them)
-    uint32_t c = 0u;
+    uint32_t c = 0u, kmax = 0u;
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) c += key[j] >= tlo ? 1u : 0u;
+    for (int j = 0; j < NPT; ++j) {
+      c += key[j] >= tlo ? 1u : 0u;
+      kmax = max(kmax, key[j]);
+    }
     uint32_t C;
-    uint32_t o = block_excl_scan(c, S.sh, C);
+    uint32_t o = block_excl_scan_max(c, kmax, S.sh, C);
     if (C >= (uint32_t)k && C <= (uint32_t)kListMax) {
       uint32_t* lk = S.candk;              // keys
       uint32_t* lp = S.candk + kListMax;   // positions
@@ -360,9 +384,14 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
       return;
     }
   }
-  if (!found) {
+  {  // whole-row radix select (streamed rows, or a short list that failed)
+    uint32_t kmin = ~0u, kmax = 0u;
+    each_row([&](uint32_t kk) { kmin = min(kmin, kk); kmax = max(kmax, kk); });
+    __syncthreads();  // (the list path may still be reading sh)
+    block_minmax(kmin, kmax, S.sh + 16);
+    const uint32_t span = kmax - kmin;
     krem = (uint32_t)k;
-    T = radix_select(kmin, hi, krem, S, each_row);
+    T = radix_select(kmin, span ? 32 - __clz(span) : 0, krem, S, each_row);
   }
   // T is the threshold key; krem elements equal to T are taken (in position order)
 
