@@ -64,32 +64,33 @@ struct QRaw {
   float w[4][4];
 };
 
+__device__ __forceinline__ void a0_load_tile(const uint16_t* __restrict__ qrow,
+                                             const float* __restrict__ wrow, int lane, int m,
+                                             i32x4 (&r)[4], float (&wr)[4]) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint16_t* hrow = qrow + (16 * m + n) * kID;
+  r[0] = *(const i32x4*)(hrow + 16 * g);
+  r[1] = *(const i32x4*)(hrow + 16 * g + 8);
+  r[2] = *(const i32x4*)(hrow + 64 + 16 * g);
+  r[3] = *(const i32x4*)(hrow + 64 + 16 * g + 8);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wr[i] = wrow[16 * m + 4 * g + i];
+}
 __device__ __forceinline__ void a0_load(const uint16_t* __restrict__ qrow,
                                         const float* __restrict__ wrow, int lane, QRaw& qr) {
-  const int n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint16_t* hrow = qrow + (16 * m + n) * kID;
-    qr.r[m][0] = *(const i32x4*)(hrow + 16 * g);
-    qr.r[m][1] = *(const i32x4*)(hrow + 16 * g + 8);
-    qr.r[m][2] = *(const i32x4*)(hrow + 64 + 16 * g);
-    qr.r[m][3] = *(const i32x4*)(hrow + 64 + 16 * g + 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qr.w[m][i] = wrow[16 * m + 4 * g + i];
-  }
+  for (int m = 0; m < 4; ++m) a0_load_tile(qrow, wrow, lane, m, qr.r[m], qr.w[m]);
 }
 
-// Quantise the query to e4m3 in the MFMA A layout and build the per-lane head weights
-// w'[16m + 4g + i] = w * s (s = power-of-two scale of that head).
-__device__ __forceinline__ void a0_prologue(const QRaw& qr, int lane, i32x8 (&A)[4],
-                                            float (&wp)[4][4]) {
+// Quantise head tile m of the query (heads 16m .. 16m+15) to e4m3 in the MFMA A layout and
+// build the lane's head weights w'[16m + 4g + i] = w * s (s = power-of-two scale of the head).
+__device__ __forceinline__ void a0_tile(const i32x4 (&r)[4], const float (&wr)[4], int lane,
+                                        i32x8& A, float (&wp)[4]) {
   const int g = lane >> 4;
-  float inv_s[4], s_q[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  {
     uint32_t wd[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) wd[j] = (uint32_t)qr.r[m][j >> 2][j & 3];
+    for (int j = 0; j < 16; ++j) wd[j] = (uint32_t)r[j >> 2][j & 3];
     float v[32];
     float amax = 0.f;
 #pragma unroll
@@ -105,26 +106,28 @@ __device__ __forceinline__ void a0_prologue(const QRaw& qr, int lane, i32x8 (&A)
     float mant = frexpf(amax, &E);
     int e = (mant <= 0.875f) ? E - 9 : E - 8;
     if (amax == 0.f) e = 0;
-    s_q[m] = ldexpf(1.f, e);
-    inv_s[m] = ldexpf(1.f, -e);
+    const float s_q = ldexpf(1.f, e);
+    const float inv_s = ldexpf(1.f, -e);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int word = 0;
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * j] * inv_s[m], v[4 * j + 1] * inv_s[m], word,
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * j] * inv_s, v[4 * j + 1] * inv_s, word,
                                              false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * j + 2] * inv_s[m], v[4 * j + 3] * inv_s[m],
-                                             word, true);
-      A[m][j] = word;
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * j + 2] * inv_s, v[4 * j + 3] * inv_s, word,
+                                             true);
+      A[j] = word;
     }
+    // w'[16m + 4g + i]: the scale of head 16m + r lives in lane r (any g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wp[i] = wr[i] * __shfl(s_q, 4 * g + i);
   }
-  // w'[16m + 4g + i]: the scale of head 16m + r lives in lane r (any g)
+}
+
+// All four head tiles.
+__device__ __forceinline__ void a0_prologue(const QRaw& qr, int lane, i32x8 (&A)[4],
+                                            float (&wp)[4][4]) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = __shfl(s_q[m], 4 * g + i);
-      wp[m][i] = qr.w[m][i] * s;
-    }
+  for (int m = 0; m < 4; ++m) a0_tile(qr.r[m], qr.w[m], lane, A[m], wp[m]);
 }
 
 struct KTile4 {
@@ -186,27 +189,32 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
     k0 = blockIdx.y * chunk + wave * part;
     k1 = k0 + part;
   }
-  if (tl >= t_count) return;
+  if (tl >= t_count) return;  // (decode: the same for every wave of the workgroup)
   const int t = t_begin + tl;
+  // The query goes out first: it needs the token only.  Decode: the eight waves share the
+  // token, so waves 0..3 each quantise one 16-head tile and hand it over through LDS.
+  const uint16_t* qrow = q_idx + (int64_t)t * kIH * kID;
+  const float* wrow = w + (int64_t)t * kIH;
+  QRaw qr;
+  if (group_mode) a0_load(qrow, wrow, lane, qr);
+  else if (wave < 4) a0_load_tile(qrow, wrow, lane, wave, qr.r[0], qr.w[0]);
   const TokLoc loc = locate(bt, t);
   const int b = loc.b;
   const int n = loc.n;
   k1 = min(k1, n);
-  if (k0 >= k1) return;
+  const bool active = k0 < k1;
 
   const int32_t* pt = bt.page_table + (int64_t)b * bt.pt_stride;
   float* out = scores + (int64_t)tl * ld;
 
   // Start-up order matters: everything waits on the page ids, and loads complete in issue
-  // order, so the page ids are requested first, then the query, then the first key groups;
-  // the query is quantised while those groups are in flight.
+  // order, so the page ids are requested before the first key groups; the query is quantised
+  // while those groups are in flight.
   // Page ids of this wave's range, one per lane, fetched once (a scalar page-table load per
   // group would stall every prefetch on a scalar round trip).
   const int pg0 = k0 >> 6;
-  const int npg = (k1 - 1) / 64 - pg0 + 1;  // <= 64 pages per wave
+  const int npg = active ? (k1 - 1) / 64 - pg0 + 1 : 0;  // <= 64 pages per wave
   const int my_page = lane < npg ? pt[pg0 + lane] : 0;
-  QRaw qr;
-  a0_load(q_idx + (int64_t)t * kIH * kID, w + (int64_t)t * kIH, lane, qr);
 
   // three-slot ring of 64-key groups: while one group is scored the next two are in flight
   struct Slot {
@@ -228,7 +236,29 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
   fetch(k0 + 64, s1);
   i32x8 A[4];
   float wp[4][4];
-  a0_prologue(qr, lane, A, wp);
+  if (group_mode) {
+    if (!active) return;
+    a0_prologue(qr, lane, A, wp);
+  } else {
+    __shared__ i32x8 a_sh[4][64];
+    __shared__ f32x4 w_sh[4][64];
+    if (wave < 4) {
+      i32x8 at;
+      float wt[4];
+      a0_tile(qr.r[0], qr.w[0], lane, at, wt);
+      a_sh[wave][lane] = at;
+      w_sh[wave][lane] = f32x4{wt[0], wt[1], wt[2], wt[3]};
+    }
+    __syncthreads();
+    if (!active) return;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      A[m] = a_sh[m][lane];
+      const f32x4 wv = w_sh[m][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wp[m][i] = wv[i];
+    }
+  }
   auto consume = [&](int base, const Slot& sl) {
     if (base < k1) {
       float sc = score_group(A, wp, sl.kt) * sl.ks;
