@@ -111,22 +111,24 @@ constexpr int kNQ = kDqk / 32, kQL = 4, kQR = kNQ - kQL;
 // tile has two regions: A holds the value part of each row (its first 512 dims) at a padded row stride,
 // one load instruction per row (every lane a 16-byte chunk of that row, so the source is a
 // per-row scalar base plus the lane offset: no per-lane address arithmetic); B holds the
-// 64 RoPE dims of the 16 rows packed (bf16: two loads, e4m3: one).  The A stride is 4 dwords
-// more than a multiple of 32 banks, and the rows are consumed in the order
+// 64 RoPE dims of the 16 rows (bf16: two loads, e4m3: one).  The A stride is 8 dwords more
+// than a multiple of the 64 LDS banks and the B stride 4 more than a multiple of 16 (both
+// measured fastest for the reads below), and the rows are consumed in the order
 // pi(8h + j) = 8h + 2j (j < 4), 8h + 2(j - 4) + 1 (j >= 4), which makes both the 16-byte
-// key-fragment reads and the transposed value reads free of bank conflicts.  bf16: 1040-byte
-// A rows, 18 loads per tile, a ring of four stages; e4m3: 528-byte A rows, 17 loads (one of
-// them issued by both waves), a ring of seven stages.
+// key-fragment reads and the transposed value reads nearly free of bank conflicts.  bf16:
+// 1056-byte A rows, 18 loads per tile; e4m3: 544-byte A rows, 17 loads (one of them issued
+// by both waves).
 template <bool FP8>
 struct KvFmt {
   static constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;   // cached row
   static constexpr int kVBytes = FP8 ? kDv : 2 * kDv;       // value part (region A)
   static constexpr int kRBytes = kRowBytes - kVBytes;       // RoPE part (region B): 64 / 128
-  static constexpr int kAStride = kVBytes + 16;
+  static constexpr int kAStride = kVBytes + 32;             // row stride, region A
+  static constexpr int kRStride = kRBytes + 16;             // row stride, region B
   static constexpr int kABytes = kWT * kAStride;
-  static constexpr int kBBytes = kWT * kRBytes;
+  static constexpr int kBBytes = kWT * kRStride;
   static constexpr int kWBytes = kABytes + kBBytes;         // one wave tile
-  static constexpr int kBLoads = kBBytes / 1024;            // 64 lanes x 16 bytes each
+  static constexpr int kBLoads = kWT * kRBytes / 1024;      // 64 lanes x 16 bytes each
   static constexpr int kIssue = kWT + kBLoads;              // loads per tile
   static constexpr int kIssueW = (kIssue + 1) / 2;          // loads per tile and wave
   static constexpr int kBufs = 2;                           // stages in the ring
@@ -396,7 +398,8 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     if (j < kWT) {
       if (!FP8 || lane < F::kVBytes / 16) *(i32x4*)(ta + j * F::kAStride + lane16) = v;
     } else {
-      *(i32x4*)(ta + F::kABytes + 1024 * (j - kWT) + lane16) = v;
+      const int e = 64 * (j - kWT) + lane;  // chunk e % C of row e / C
+      *(i32x4*)(ta + F::kABytes + (e / kRC) * F::kRStride + 16 * (e % kRC)) = v;
     }
   };
 
@@ -458,7 +461,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       constexpr int kEB = FP8 ? 1 : 2;  // bytes per element
       const int d = 32 * ks + 8 * g4;
       const char* pa = ks < kDv / 32 ? sb + qr * F::kAStride + kEB * d
-                                     : sb + F::kABytes + qr * F::kRBytes + kEB * (d - kDv);
+                                     : sb + F::kABytes + qr * F::kRStride + kEB * (d - kDv);
       return *(const KRaw*)pa;
     };
 #pragma unroll
