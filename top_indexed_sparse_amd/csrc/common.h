@@ -23,6 +23,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 namespace tis {
 
 constexpr int kPage = 64;
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no swizzle):
+// accesses at byte offsets at or past the resource's record count are dropped (stores) or
+// read as zero (loads).
+constexpr int kBufDword3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -134,12 +134,35 @@ struct KTile4 {
   i32x4 lo[4], hi[4];
 };
 
-__device__ __forceinline__ void load_ktile4(const uint8_t* __restrict__ page_base, int lane,
-                                            KTile4& kt) {
+// One 8 KB page of keys (64 rows of 128 bytes) in eight non-temporal loads of 1 KB each:
+// load i, lane l gets bytes [1024i + 16l, +16), i.e. row 8i + (l >> 3), bytes 16(l & 7)...
+// (whole rows per instruction stream better than the MFMA layout's 64-byte half rows).
+struct KPage {
+  i32x4 r[8];
+};
+__device__ __forceinline__ void load_kpage(const uint8_t* page_base, int lane, KPage& kp) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    kp.r[i] = __builtin_nontemporal_load((const i32x4*)(page_base + 1024 * i + 16 * lane));
+}
+
+// Rows of the wave's LDS staging buffer are kPitch bytes apart, so that the sixteen rows read
+// by one MFMA-layout load fall on distinct banks.
+constexpr int kPitch = 144;
+constexpr int kStage = 64 * kPitch;  // bytes per wave
+
+// Through the wave's own staging buffer into the MFMA B layout: lane (n = l & 15, g = l >> 4)
+// takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row 16j + n.  (LDS operations of one
+// wave complete in order, so the buffer can be rewritten by the next group without a wait.)
+__device__ __forceinline__ void stage_ktile4(uint8_t* stage, int lane, const KPage& kp,
+                                             KTile4& kt) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *(i32x4*)(stage + (8 * i + (lane >> 3)) * kPitch + 16 * (lane & 7)) = kp.r[i];
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint8_t* row = page_base + (16 * j + n) * kID;
+    const uint8_t* row = stage + (16 * j + n) * kPitch;
     kt.lo[j] = *(const i32x4*)(row + 16 * g);
     kt.hi[j] = *(const i32x4*)(row + 64 + 16 * g);
   }
@@ -170,25 +193,23 @@ __device__ __forceinline__ float score_group(const i32x8 (&A)[4], const float (&
   return pair16_sum(k0, k1);
 }
 
-// group_mode == 0: one token per workgroup (blockIdx.x), its waves split the key chunk
-//                  blockIdx.y.
-// group_mode == 1: four consecutive tokens per workgroup, one per wave, same key chunk.
-__global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_begin,
-    int t_count, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint8_t* __restrict__ kpool, const float* __restrict__ kscale,
-    float* __restrict__ scores, int64_t ld, int group_mode, int chunk) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int tl, k0, k1;
-  if (group_mode) {
-    tl = blockIdx.x * 4 + wave;
-    k0 = blockIdx.y * chunk;
-    k1 = k0 + chunk;
-  } else {
-    tl = blockIdx.x;
-    const int part = chunk / (int)(blockDim.x >> 6);
-    k0 = blockIdx.y * chunk + wave * part;
-    k1 = k0 + part;
-  }
+// GROUP == false (decode): one token per workgroup (blockIdx.x) and key chunk blockIdx.y of
+//   64 pages; the pages are dealt round-robin to the eight waves (wave w scores pages
+//   w, w+8, ... of the chunk), so that at each step the workgroup reads 64 KB of consecutive
+//   pages when the request's pages are consecutive.
+// GROUP == true (prefill): four consecutive tokens per workgroup, one per wave, each over
+//   all pages of the same chunk.
+template <bool GROUP>
+__global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBatch bt,
+    int t_begin, int t_count, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* kpool, const float* kscale,
+    float* __restrict__ scores, int64_t ld, int chunk) {
+  // (the wave index through readfirstlane, so that the ranges derived from it are scalars)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  constexpr int kStep = GROUP ? 1 : 8;  // page stride of a wave within the chunk
+  const int tl = GROUP ? blockIdx.x * 4 + wave : blockIdx.x;
+  const int poff = GROUP ? 0 : wave;    // the wave's first page within the chunk
+  const int k0 = blockIdx.y * chunk;
   if (tl >= t_count) return;  // (decode: the same for every wave of the workgroup)
   const int t = t_begin + tl;
   // The query goes out first: it needs the token only.  Decode: the eight waves share the
@@ -196,48 +217,62 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
   const uint16_t* qrow = q_idx + (int64_t)t * kIH * kID;
   const float* wrow = w + (int64_t)t * kIH;
   QRaw qr;
-  if (group_mode) a0_load(qrow, wrow, lane, qr);
+  if (GROUP) a0_load(qrow, wrow, lane, qr);
   else if (wave < 4) a0_load_tile(qrow, wrow, lane, wave, qr.r[0], qr.w[0]);
   const TokLoc loc = locate(bt, t);
-  const int b = loc.b;
-  const int n = loc.n;
-  k1 = min(k1, n);
-  const bool active = k0 < k1;
+  const int k1 = min(k0 + chunk, loc.n);                 // the chunk's keys in range
+  const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;  // its pages in range (<= 64)
+  const int ng = npg > poff ? (npg - poff + kStep - 1) / kStep : 0;  // this wave's pages
+  const bool active = ng > 0;
+  // A wave with no keys leaves now, unless it quantises a query tile for the others (it
+  // then reads one page of its request and scores nothing).
+  if (!active && (GROUP || wave >= 4)) return;
 
-  const int32_t* pt = bt.page_table + (int64_t)b * bt.pt_stride;
+  const int32_t* pt = bt.page_table + (int64_t)loc.b * bt.pt_stride;
   float* out = scores + (int64_t)tl * ld;
 
   // Start-up order matters: everything waits on the page ids, and loads complete in issue
   // order, so the page ids are requested before the first key groups; the query is quantised
   // while those groups are in flight.
-  // Page ids of this wave's range, one per lane, fetched once (a scalar page-table load per
-  // group would stall every prefetch on a scalar round trip).
-  const int pg0 = k0 >> 6;
-  const int npg = active ? (k1 - 1) / 64 - pg0 + 1 : 0;  // <= 64 pages per wave
-  const int my_page = lane < npg ? pt[pg0 + lane] : 0;
+  // Page ids of the chunk, one per lane, fetched once (a scalar page-table load per group
+  // would stall every prefetch on a scalar round trip).
+  const int pg0 = active ? k0 >> 6 : 0;
+  const int my_page = pt[pg0 + min(lane, max(npg, 1) - 1)];
 
-  // three-slot ring of 64-key groups: while one group is scored the next two are in flight
+  // Four-slot ring of pages: while one is scored the next three are in flight.  Nothing
+  // between the page-id load and the end of the loop branches around a load or a store: a
+  // fetch past the wave's pages re-reads its last one, pages are scored four at a time, and
+  // scores go out through a buffer resource that ends at the chunk's last key in range, so
+  // the hardware drops stores past it.  (Under a branch the compiler waits for every
+  // outstanding load, which would leave one page in flight.)
   struct Slot {
-    KTile4 kt;
+    KPage kp;
     float ks;
     bool ok;
   };
-  auto fetch = [&](int base, Slot& sl) {
-    if (base < k1) {
-      const int page = __builtin_amdgcn_readlane(my_page, (base >> 6) - pg0);
-      sl.ok = page >= 0 && page < bt.n_pages;
-      const int64_t pg = sl.ok ? page : 0;
-      load_ktile4(kpool + pg * kPage * kID, lane, sl.kt);
-      sl.ks = kscale[pg * kPage + lane];
-    }
+  auto fetch = [&](int g, Slot& sl) {
+    const int page = __builtin_amdgcn_readlane(my_page, min(g, max(ng, 1) - 1) * kStep + poff);
+    sl.ok = page >= 0 && page < bt.n_pages;
+    const int64_t pg = sl.ok ? page : 0;
+    load_kpage(kpool + pg * kPage * kID, lane, sl.kp);
+    sl.ks = kscale[pg * kPage + lane];
   };
-  Slot s0, s1, s2;
-  fetch(k0, s0);
-  fetch(k0 + 64, s1);
+  // (kept in this order by the empty asm statements, which the key loads cannot cross as the
+  // key pointers are not marked restrict: the loop's waits count the loads issued after each
+  // slot's, and a scale load moved behind later pages here would make them wait for those
+  // pages too)
+  Slot sl[4];
+  fetch(0, sl[0]);
+  asm volatile("" ::: "memory");
+  fetch(1, sl[1]);
+  asm volatile("" ::: "memory");
+  fetch(2, sl[2]);
+  asm volatile("" ::: "memory");
+  __shared__ __attribute__((aligned(16))) uint8_t stage_sh[(GROUP ? 4 : 8) * kStage];
+  uint8_t* stage = stage_sh + wave * kStage;
   i32x8 A[4];
   float wp[4][4];
-  if (group_mode) {
-    if (!active) return;
+  if (GROUP) {
     a0_prologue(qr, lane, A, wp);
   } else {
     __shared__ i32x8 a_sh[4][64];
@@ -259,20 +294,21 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
       for (int i = 0; i < 4; ++i) wp[m][i] = wv[i];
     }
   }
-  auto consume = [&](int base, const Slot& sl) {
-    if (base < k1) {
-      float sc = score_group(A, wp, sl.kt) * sl.ks;
-      if (!sl.ok) sc = -INFINITY;
-      if (base + lane < k1) out[base + lane] = sc;
+  // stores at byte offset 4*s of the row, kept for s < k1
+  const __amdgpu_buffer_rsrc_t orsrc =
+      __builtin_amdgcn_make_buffer_rsrc(out, 0, k1 * 4, kBufDword3);
+  for (int g = 0; g < ng; g += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      fetch(g + u + 3, sl[(u + 3) & 3]);
+      const Slot& c = sl[u];
+      KTile4 kt;
+      stage_ktile4(stage, lane, c.kp, kt);
+      float sc = score_group(A, wp, kt) * c.ks;
+      if (!c.ok) sc = -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __float_as_uint(sc), orsrc, (k0 + 64 * ((g + u) * kStep + poff) + lane) * 4, 0, 0);
     }
-  };
-  for (int base = k0; base < k1; base += 192) {
-    fetch(base + 128, s2);
-    consume(base, s0);
-    fetch(base + 192, s0);
-    consume(base + 64, s1);
-    fetch(base + 256, s1);
-    consume(base + 128, s2);
   }
 }
 
@@ -296,8 +332,12 @@ hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, 
   dim3 grid(group ? (t_count + 3) / 4 : t_count, (max_n + chunk - 1) / chunk);
   // decode: one 8-wave workgroup per 4096-key chunk of a token (512 keys per wave); prefill:
   // four tokens per 4-wave workgroup sharing a 1024-key chunk
-  hipLaunchKernelGGL(idx_score_fp8_kernel, grid, dim3(group ? 256 : 512), 0, st, bt, t_begin,
-                     t_count, q_idx, w, kpool, kscale, scores, ld, group, chunk);
+  if (group)
+    hipLaunchKernelGGL(idx_score_fp8_kernel<true>, grid, dim3(256), 0, st, bt, t_begin, t_count,
+                       q_idx, w, kpool, kscale, scores, ld, chunk);
+  else
+    hipLaunchKernelGGL(idx_score_fp8_kernel<false>, grid, dim3(512), 0, st, bt, t_begin,
+                       t_count, q_idx, w, kpool, kscale, scores, ld, chunk);
   return hipGetLastError();
 }
 
