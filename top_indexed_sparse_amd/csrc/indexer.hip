@@ -219,55 +219,67 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   QRaw qr;
   if (GROUP) a0_load(qrow, wrow, lane, qr);
   else if (wave < 4) a0_load_tile(qrow, wrow, lane, wave, qr.r[0], qr.w[0]);
+  // Page ids of the chunk, one per lane, fetched once (a scalar page-table load per page
+  // would stall every prefetch on a scalar round trip).  Everything waits on them, so they
+  // are requested together with the token's request lookup, for request min(t, B - 1) (the
+  // request of token t when every request has one token), and again if that was not it.
+  const int pg0 = k0 >> 6;
+  const int pcol = min(pg0 + lane, bt.pt_stride - 1);
+  const int bguess = min(t, bt.B - 1);
+  int my_page = bt.page_table[(int64_t)bguess * bt.pt_stride + pcol];
   const TokLoc loc = locate(bt, t);
   const int k1 = min(k0 + chunk, loc.n);                 // the chunk's keys in range
   const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;  // its pages in range (<= 64)
-  const int ng = npg > poff ? (npg - poff + kStep - 1) / kStep : 0;  // this wave's pages
-  const bool active = ng > 0;
+  const bool active = npg > poff;  // the wave has a page in range
   // A wave with no keys leaves now, unless it quantises a query tile for the others (it
   // then reads one page of its request and scores nothing).
   if (!active && (GROUP || wave >= 4)) return;
-
-  const int32_t* pt = bt.page_table + (int64_t)loc.b * bt.pt_stride;
+  if (loc.b != bguess) my_page = bt.page_table[(int64_t)loc.b * bt.pt_stride + pcol];
   float* out = scores + (int64_t)tl * ld;
-
-  // Start-up order matters: everything waits on the page ids, and loads complete in issue
-  // order, so the page ids are requested before the first key groups; the query is quantised
-  // while those groups are in flight.
-  // Page ids of the chunk, one per lane, fetched once (a scalar page-table load per group
-  // would stall every prefetch on a scalar round trip).
-  const int pg0 = active ? k0 >> 6 : 0;
-  const int my_page = pt[pg0 + min(lane, max(npg, 1) - 1)];
 
   // Four-slot ring of pages: while one is scored the next three are in flight.  Nothing
   // between the page-id load and the end of the loop branches around a load or a store: a
-  // fetch past the wave's pages re-reads its last one, pages are scored four at a time, and
-  // scores go out through a buffer resource that ends at the chunk's last key in range, so
-  // the hardware drops stores past it.  (Under a branch the compiler waits for every
-  // outstanding load, which would leave one page in flight.)
+  // fetch past the chunk's pages re-reads its last one, and scores go out through a buffer
+  // resource that ends at the chunk's last key in range, so the hardware drops stores past
+  // it.  (Under a branch the compiler waits for every outstanding load, which would leave
+  // one page in flight.)  Slots carry their page's index within the chunk.
   struct Slot {
     KPage kp;
     float ks;
     bool ok;
   };
-  auto fetch = [&](int g, Slot& sl) {
-    const int page = __builtin_amdgcn_readlane(my_page, min(g, max(ng, 1) - 1) * kStep + poff);
+  auto fetch = [&](int pidx, Slot& sl) {
+    const int page = __builtin_amdgcn_readlane(my_page, npg > 0 ? min(pidx, npg - 1) : 0);
     sl.ok = page >= 0 && page < bt.n_pages;
     const int64_t pg = sl.ok ? page : 0;
     load_kpage(kpool + pg * kPage * kID, lane, sl.kp);
     sl.ks = kscale[pg * kPage + lane];
+  };
+  // A wave's first three pages are fixed (decode: w, w + 8, w + 16); decode waves then claim
+  // the chunk's remaining pages one at a time from a workgroup counter, so that waves whose
+  // data arrives sooner score more pages.  Either way a wave's pages come in increasing
+  // order, and it stops at the first one past the chunk's pages in range.
+  __shared__ int next_sh;
+  auto claim = [&](int prev) -> int {
+    if (GROUP) return prev + 1;
+    // (every lane adds one, so a claim moves the counter by 64 and lane 0 sees the old value
+    // plus fewer than 64: no branch; an LDS append would do the same, but it addresses LDS
+    // through 16 bits and the counter may sit above 64 KB)
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+               &next_sh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >> 6;
   };
   // (kept in this order by the empty asm statements, which the key loads cannot cross as the
   // key pointers are not marked restrict: the loop's waits count the loads issued after each
   // slot's, and a scale load moved behind later pages here would make them wait for those
   // pages too)
   Slot sl[4];
-  fetch(0, sl[0]);
-  asm volatile("" ::: "memory");
-  fetch(1, sl[1]);
-  asm volatile("" ::: "memory");
-  fetch(2, sl[2]);
-  asm volatile("" ::: "memory");
+  int pi[4];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    pi[k] = poff + k * kStep;
+    fetch(pi[k], sl[k]);
+    asm volatile("" ::: "memory");
+  }
   __shared__ __attribute__((aligned(16))) uint8_t stage_sh[(GROUP ? 4 : 8) * kStage];
   uint8_t* stage = stage_sh + wave * kStage;
   i32x8 A[4];
@@ -284,6 +296,7 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
       a_sh[wave][lane] = at;
       w_sh[wave][lane] = f32x4{wt[0], wt[1], wt[2], wt[3]};
     }
+    if (wave == 0 && lane == 0) next_sh = 3 * kStep * 64;
     __syncthreads();
     if (!active) return;
 #pragma unroll
@@ -297,17 +310,25 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   // stores at byte offset 4*s of the row, kept for s < k1
   const __amdgpu_buffer_rsrc_t orsrc =
       __builtin_amdgcn_make_buffer_rsrc(out, 0, k1 * 4, kBufDword3);
-  for (int g = 0; g < ng; g += 4) {
+  // (pages are taken four at a time with the exit test at the top only: an exit between
+  // them would again make the compiler wait for every outstanding load; a page past the
+  // chunk's is not scored, and its store is dropped)
+  while (pi[0] < npg) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      fetch(g + u + 3, sl[(u + 3) & 3]);
-      const Slot& c = sl[u];
-      KTile4 kt;
-      stage_ktile4(stage, lane, c.kp, kt);
-      float sc = score_group(A, wp, kt) * c.ks;
-      if (!c.ok) sc = -INFINITY;
-      __builtin_amdgcn_raw_buffer_store_b32(
-          __float_as_uint(sc), orsrc, (k0 + 64 * ((g + u) * kStep + poff) + lane) * 4, 0, 0);
+      pi[(u + 3) & 3] = claim(pi[(u + 2) & 3]);
+      fetch(pi[(u + 3) & 3], sl[(u + 3) & 3]);
+      asm volatile("" ::: "memory");  // (the loads go out before this page is scored)
+      float sc = 0.f;
+      if (pi[u] < npg) {
+        const Slot& c = sl[u];
+        KTile4 kt;
+        stage_ktile4(stage, lane, c.kp, kt);
+        sc = score_group(A, wp, kt) * c.ks;
+        if (!c.ok) sc = -INFINITY;
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
+                                            (k0 + 64 * pi[u] + lane) * 4, 0, 0);
     }
   }
 }
