@@ -237,47 +237,48 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   if (loc.b != bguess) my_page = bt.page_table[(int64_t)loc.b * bt.pt_stride + pcol];
   float* out = scores + (int64_t)tl * ld;
 
-  // Four-slot ring of pages: while one is scored the next three are in flight.  Nothing
-  // between the page-id load and the end of the loop branches around a load or a store: a
-  // fetch past the chunk's pages re-reads its last one, and scores go out through a buffer
-  // resource that ends at the chunk's last key in range, so the hardware drops stores past
-  // it.  (Under a branch the compiler waits for every outstanding load, which would leave
-  // one page in flight.)  Slots carry their page's index within the chunk.
+  // Page g of the wave is page poff + g * kStep of the chunk, g < kPages; it is in range while
+  // that is below npg.  A four-slot ring of pages keeps three in flight while one is scored.
+  // Nothing in the page loop branches around a load or a store (under a branch the compiler
+  // waits for every outstanding load, which would leave one page in flight): a fetch past the
+  // wave's last page re-reads that page, a page past it is not scored, and scores go out
+  // through a buffer resource that ends at the chunk's last key in range, so the hardware
+  // drops stores past it.
+  constexpr int kPages = GROUP ? 16 : 8;
+  auto page_id = [&](int g) {
+    return __builtin_amdgcn_readlane(my_page, npg > 0 ? min(poff + g * kStep, npg - 1) : 0);
+  };
   struct Slot {
     KPage kp;
     float ks;
     bool ok;
   };
-  auto fetch = [&](int pidx, Slot& sl) {
-    const int page = __builtin_amdgcn_readlane(my_page, npg > 0 ? min(pidx, npg - 1) : 0);
+  // decode: the key scales of all eight pages go out first (one short stream of small reads,
+  // ahead of the pages, so that waiting for a scale never waits for a page); prefill: each
+  // page's scales go out with the page
+  float ks[GROUP ? 1 : kPages];
+  auto fetch = [&](int g, Slot& sl) {
+    const int page = page_id(g);
     sl.ok = page >= 0 && page < bt.n_pages;
     const int64_t pg = sl.ok ? page : 0;
     load_kpage(kpool + pg * kPage * kID, lane, sl.kp);
-    sl.ks = kscale[pg * kPage + lane];
+    if (GROUP) sl.ks = kscale[pg * kPage + lane];
   };
-  // A wave's first three pages are fixed (decode: w, w + 8, w + 16); decode waves then claim
-  // the chunk's remaining pages one at a time from a workgroup counter, so that waves whose
-  // data arrives sooner score more pages.  Either way a wave's pages come in increasing
-  // order, and it stops at the first one past the chunk's pages in range.
-  __shared__ int next_sh;
-  auto claim = [&](int prev) -> int {
-    if (GROUP) return prev + 1;
-    // (every lane adds one, so a claim moves the counter by 64 and lane 0 sees the old value
-    // plus fewer than 64: no branch; an LDS append would do the same, but it addresses LDS
-    // through 16 bits and the counter may sit above 64 KB)
-    return __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
-               &next_sh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >> 6;
-  };
-  // (kept in this order by the empty asm statements, which the key loads cannot cross as the
-  // key pointers are not marked restrict: the loop's waits count the loads issued after each
-  // slot's, and a scale load moved behind later pages here would make them wait for those
-  // pages too)
-  Slot sl[4];
-  int pi[4];
+  if (!GROUP) {
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    pi[k] = poff + k * kStep;
-    fetch(pi[k], sl[k]);
+    for (int g = 0; g < kPages; ++g) {
+      const int page = page_id(g);
+      ks[GROUP ? 0 : g] = kscale[(int64_t)(page >= 0 && page < bt.n_pages ? page : 0) * kPage + lane];
+    }
+    asm volatile("" ::: "memory");
+  }
+  // (kept in this order by the empty asm statements, which the key loads cannot cross as the
+  // key pointers are not marked restrict: each wait in the loop counts the loads issued after
+  // the page it waits for, and one moved behind later pages would make it wait for those too)
+  Slot sl[4];
+#pragma unroll
+  for (int g = 0; g < 3; ++g) {
+    fetch(g, sl[g]);
     asm volatile("" ::: "memory");
   }
   __shared__ __attribute__((aligned(16))) uint8_t stage_sh[(GROUP ? 4 : 8) * kStage];
@@ -296,7 +297,6 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
       a_sh[wave][lane] = at;
       w_sh[wave][lane] = f32x4{wt[0], wt[1], wt[2], wt[3]};
     }
-    if (wave == 0 && lane == 0) next_sh = 3 * kStep * 64;
     __syncthreads();
     if (!active) return;
 #pragma unroll
@@ -310,25 +310,37 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   // stores at byte offset 4*s of the row, kept for s < k1
   const __amdgpu_buffer_rsrc_t orsrc =
       __builtin_amdgcn_make_buffer_rsrc(out, 0, k1 * 4, kBufDword3);
-  // (pages are taken four at a time with the exit test at the top only: an exit between
-  // them would again make the compiler wait for every outstanding load; a page past the
-  // chunk's is not scored, and its store is dropped)
-  while (pi[0] < npg) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      pi[(u + 3) & 3] = claim(pi[(u + 2) & 3]);
-      fetch(pi[(u + 3) & 3], sl[(u + 3) & 3]);
+  // page g from ring slot u: fetch page g + 3 into the slot freed last (if there is more to
+  // fetch), then score page g
+  auto step = [&](int g, int u, bool more, bool score, float scale) {
+    if (more) {
+      fetch(g + 3, sl[(u + 3) & 3]);
       asm volatile("" ::: "memory");  // (the loads go out before this page is scored)
-      float sc = 0.f;
-      if (pi[u] < npg) {
-        const Slot& c = sl[u];
-        KTile4 kt;
-        stage_ktile4(stage, lane, c.kp, kt);
-        sc = score_group(A, wp, kt) * c.ks;
-        if (!c.ok) sc = -INFINITY;
-      }
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
-                                            (k0 + 64 * pi[u] + lane) * 4, 0, 0);
+    }
+    const Slot& c = sl[u];
+    float sc = 0.f;
+    if (score) {
+      KTile4 kt;
+      stage_ktile4(stage, lane, c.kp, kt);
+      sc = score_group(A, wp, kt) * (GROUP ? c.ks : scale);
+      if (!c.ok) sc = -INFINITY;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
+                                          (k0 + 64 * (poff + g * kStep) + lane) * 4, 0, 0);
+  };
+  if (GROUP) {
+    // sixteen pages four at a time, the exit test only at the top of each four (an exit
+    // between them would again make the compiler wait for every outstanding load)
+    for (int g = 0; g < kPages && g < npg; g += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) step(g + u, u, true, g + u < npg, 0.f);
+    }
+  } else {
+    // eight pages, unrolled in full: straight-line code, whose only exit ends the kernel
+#pragma unroll
+    for (int g = 0; g < kPages; ++g) {
+      if (poff + g * kStep >= npg) return;
+      step(g, g & 3, g + 3 < kPages, true, ks[GROUP ? 0 : g]);  // (g is a constant here)
     }
   }
 }
