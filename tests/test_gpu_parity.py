@@ -208,6 +208,45 @@ def test_out_of_range_pages_are_skipped():
     assert np.abs(out.float().cpu().numpy()[0] - o).max() < 1e-2
 
 
+def test_topk_crafted_rows():
+    """Top-K on crafted score rows: one value everywhere (the short list overflows and the
+    exact whole-row select runs), four distinct values, the largest scores crowded at the
+    end or the start of the row, signed zeros and -inf, mostly exact zeros, and lengths that
+    end inside a block of four.  Every row equals the oracle's Top-K, values included."""
+    import top_indexed_sparse_amd as tis
+    from oracle.method import topk_token
+    rng = np.random.default_rng(20261202)
+    lens = [32768, 32768, 32768, 32768, 20001, 4097, 8190, 32768, 3000]
+    B, K, ld = len(lens), 2048, 32768
+    S = np.zeros((B, ld), np.float32)
+    S[0] = 1.5
+    S[1] = rng.integers(0, 4, ld)
+    S[2] = np.linspace(-1.0, 1.0, ld)
+    S[3] = np.linspace(1.0, -1.0, ld)
+    S[4] = rng.standard_normal(ld)
+    S[4][::7] = -0.0
+    S[4][::11] = 0.0
+    S[4][::13] = -np.inf
+    S[5] = rng.standard_normal(ld)
+    S[6] = rng.exponential(size=ld) * (rng.random(ld) < 0.3)
+    S[7] = rng.standard_normal(ld)
+    S[8] = rng.standard_normal(ld)
+    note("case Top-K on crafted rows")
+    bt = tis.Batch(np.array(lens, np.int32), np.arange(B + 1, dtype=np.int32),
+                   np.zeros((B, 512), np.int32), 1)
+    scores = torch.from_numpy(S).cuda()
+    idx = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+    val = torch.full((B, K), 7.0, dtype=torch.float32, device="cuda")
+    tis.topk_select(bt, scores, K, idx, val)
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    for b in range(B):
+        ref = topk_token(S[b, :lens[b]].astype(np.float64), K)[0]
+        assert np.array_equal(idx[b], ref), b
+        k = int((ref >= 0).sum())
+        assert np.array_equal(val[b, :k], S[b, ref[:k]]), b
+        assert np.all(val[b, k:] == 0.0)
+
+
 def test_decode32k_full_size():
     """The benchmarked workload itself: 32 x 32768, K = 2048, bf16 latent cache."""
     inp = synth.make(synth.workload(synth.DECODE32K), "continuous")
