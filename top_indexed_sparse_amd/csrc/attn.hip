@@ -746,27 +746,34 @@ __global__ __launch_bounds__(256, 1) void mla_attn_fp8_o32_kernel(MLA_ATTN_ARGS)
 // O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j,  lse = M + log2 sum_j 2^(m_j - M) le_j.
 // fp32 output: O_j is the split's unnormalised fp32 sum.  bf16 output: O_j is stored
 // normalised (O_j / l_j) as fp16 (see store_part16), and is weighted by l_j here.
-// One split's partial O for 4 consecutive dims (fp32 unnormalised, or fp16 normalised).
+// One split's partial O for 8 consecutive dims (fp32 unnormalised, or fp16 normalised).
 template <bool OUT_F32>
-__device__ __forceinline__ f32x4 load_part4(const float* part_o, int64_t off) {
-  if (OUT_F32) return *(const f32x4*)(part_o + off);
-  const f16x4 h = *(const f16x4*)((const uint16_t*)part_o + off);
-  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * kPartUnscale;
+__device__ __forceinline__ void load_part8(const float* part_o, int64_t off, f32x4& lo,
+                                           f32x4& hi) {
+  if (OUT_F32) {
+    lo = *(const f32x4*)(part_o + off);
+    hi = *(const f32x4*)(part_o + off + 4);
+  } else {
+    const f16x8 h = *(const f16x8*)((const uint16_t*)part_o + off);
+    lo = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * kPartUnscale;
+    hi = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]} * kPartUnscale;
+  }
 }
 
 // Up to N splits: unconditional loads (the split index clamped; the extra copies get weight
 // 0), so that they all go out before the first use.
 template <bool OUT_F32, int N>
-__device__ __forceinline__ void combine_splits(int nsplit, int64_t pr0, int tid,
+__device__ __forceinline__ void combine_splits(int nsplit, int64_t pr0, int d0,
                                                const float* __restrict__ part_o,
                                                const float* __restrict__ part_ml, float& M,
-                                               float& Lsum, float& LEsum, f32x4& acc) {
-  f32x4 ml[N], v[N];
+                                               float& Lsum, float& LEsum, f32x4& alo,
+                                               f32x4& ahi) {
+  f32x4 ml[N], vlo[N], vhi[N];
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     const int64_t pr = pr0 + min(j, nsplit - 1) * kH;
     ml[j] = *(const f32x4*)(part_ml + pr * 4);
-    v[j] = load_part4<OUT_F32>(part_o, pr * kDv + 4 * tid);
+    load_part8<OUT_F32>(part_o, pr * kDv + d0, vlo[j], vhi[j]);
   }
 #pragma unroll
   for (int j = 0; j < N; ++j)
@@ -777,26 +784,33 @@ __device__ __forceinline__ void combine_splits(int nsplit, int64_t pr0, int tid,
     const float wgt = use ? exp2f(ml[j][0] - M) : 0.f;
     Lsum = fmaf(wgt, ml[j][1], Lsum);
     LEsum = fmaf(wgt, ml[j][2], LEsum);
-    acc += (OUT_F32 ? wgt : wgt * ml[j][1]) * v[j];
+    const float f = OUT_F32 ? wgt : wgt * ml[j][1];
+    alo += f * vlo[j];
+    ahi += f * vhi[j];
   }
 }
 
+// One wave per (token, head), lane l owning dims 8l .. 8l+7 (16-byte partial loads and
+// output stores); four heads per workgroup.
 template <bool OUT_F32>
-__global__ __launch_bounds__(128) void mla_combine_kernel(int t_begin, int t_count, int nsplit,
+__global__ __launch_bounds__(256) void mla_combine_kernel(int t_begin, int t_count, int nsplit,
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     void* __restrict__ out, float* __restrict__ lse) {
-  const int tl = blockIdx.x / kH, head = blockIdx.x % kH;
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, head)
+  const int tl = pair / kH, head = pair % kH;
+  if (tl >= t_count) return;
   const int t = t_begin + tl;
-  const int tid = threadIdx.x;
+  const int d0 = 8 * lane;
   const int64_t pr0 = (int64_t)tl * nsplit * kH + head;  // split j: pr0 + j * kH
   float M = -INFINITY, Lsum = 0.f, LEsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 alo = {0.f, 0.f, 0.f, 0.f}, ahi = {0.f, 0.f, 0.f, 0.f};
   if (nsplit <= 2) {
-    combine_splits<OUT_F32, 2>(nsplit, pr0, tid, part_o, part_ml, M, Lsum, LEsum, acc);
+    combine_splits<OUT_F32, 2>(nsplit, pr0, d0, part_o, part_ml, M, Lsum, LEsum, alo, ahi);
   } else if (nsplit <= 4) {
-    combine_splits<OUT_F32, 4>(nsplit, pr0, tid, part_o, part_ml, M, Lsum, LEsum, acc);
+    combine_splits<OUT_F32, 4>(nsplit, pr0, d0, part_o, part_ml, M, Lsum, LEsum, alo, ahi);
   } else if (nsplit <= 8) {
-    combine_splits<OUT_F32, 8>(nsplit, pr0, tid, part_o, part_ml, M, Lsum, LEsum, acc);
+    combine_splits<OUT_F32, 8>(nsplit, pr0, d0, part_o, part_ml, M, Lsum, LEsum, alo, ahi);
   } else {
     for (int j = 0; j < nsplit; ++j) {
       const float* m = part_ml + (pr0 + j * kH) * 4;
@@ -808,13 +822,18 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int t_begin, int t_cou
       const float wgt = exp2f(ml[0] - M);
       Lsum = fmaf(wgt, ml[1], Lsum);
       LEsum = fmaf(wgt, ml[2], LEsum);
-      acc += (OUT_F32 ? wgt : wgt * ml[1]) *
-             load_part4<OUT_F32>(part_o, (pr0 + j * kH) * kDv + 4 * tid);
+      f32x4 vlo, vhi;
+      load_part8<OUT_F32>(part_o, (pr0 + j * kH) * kDv + d0, vlo, vhi);
+      const float f = OUT_F32 ? wgt : wgt * ml[1];
+      alo += f * vlo;
+      ahi += f * vhi;
     }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  store_out4<OUT_F32>(out, ((int64_t)t * kH + head) * kDv + 4 * tid, acc * inv);
-  if (lse && tid == 0)
+  const int64_t orow = ((int64_t)t * kH + head) * kDv + d0;
+  store_out4<OUT_F32>(out, orow, alo * inv);
+  store_out4<OUT_F32>(out, orow + 4, ahi * inv);
+  if (lse && lane == 0)
     lse[(int64_t)t * kH + head] = LEsum > 0.f ? (M + log2f(LEsum)) * kLn2 : -INFINITY;
 }
 
@@ -871,8 +890,8 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   auto* cfn = out_f32 ? mla_combine_kernel<true> : mla_combine_kernel<false>;
-  hipLaunchKernelGGL(cfn, dim3(t_count * kH), dim3(128), 0, st, t_begin, t_count, nsplit, part_o,
-                     part_ml, out, lse);
+  hipLaunchKernelGGL(cfn, dim3(t_count * kH / 4), dim3(256), 0, st, t_begin, t_count, nsplit,
+                     part_o, part_ml, out, lse);
   return hipGetLastError();
 }
 
