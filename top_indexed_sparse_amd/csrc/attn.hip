@@ -157,24 +157,35 @@ struct AttnSmem {
 // 11 significant bits for |O| up to 1.6e7 (saturating beyond), half the bytes of fp32 and
 // 8 times finer than bf16 (a bf16 partial adds an error the size of the output rounding).
 constexpr float kPartScale = 1.f / 256.f, kPartUnscale = 256.f;
-__device__ __forceinline__ void store_part16(void* part, int64_t off, f32x4 v) {
-  f16x4 h;
+
+// Eight consecutive partials as fp16 (one 16-byte store).
+__device__ __forceinline__ void store_part16x8(void* part, int64_t off, f32x4 lo, f32x4 hi) {
+  f16x8 h;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] = (_Float16)fminf(fmaxf(v[i] * kPartScale, -65504.f), 65504.f);
-  *(f16x4*)((uint16_t*)part + off) = h;
+  for (int i = 0; i < 4; ++i) {
+    h[i] = (_Float16)fminf(fmaxf(lo[i] * kPartScale, -65504.f), 65504.f);
+    h[4 + i] = (_Float16)fminf(fmaxf(hi[i] * kPartScale, -65504.f), 65504.f);
+  }
+  *(f16x8*)((uint16_t*)part + off) = h;
 }
 
-// Four consecutive outputs at element offset `off`: fp32, or bf16 (round to nearest even).
+// Eight consecutive outputs at element offset `off`: fp32 (two 16-byte stores) or bf16
+// (round to nearest even; one 16-byte store).
 template <bool OUT_F32>
-__device__ __forceinline__ void store_out4(void* out, int64_t off, f32x4 v) {
+__device__ __forceinline__ void store_out8(void* out, int64_t off, f32x4 lo, f32x4 hi) {
   if (OUT_F32) {
-    *(f32x4*)((float*)out + off) = v;
+    *(f32x4*)((float*)out + off) = lo;
+    *(f32x4*)((float*)out + off + 4) = hi;
   } else {
-    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
-    *(i32x2*)((uint16_t*)out + off) = i32x2{(int)w0, (int)w1};
+    i32x4 w;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      w[i] = (int)((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo[2 * i]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo[2 * i + 1]) << 16));
+      w[2 + i] = (int)((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi[2 * i]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi[2 * i + 1]) << 16));
+    }
+    *(i32x4*)((uint16_t*)out + off) = w;
   }
 }
 
@@ -674,15 +685,21 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     }
   }
   // four rounds of 128 dims: every wave stores its scaled O^T, then wave (hh, kh) sums dims
-  // 64kh .. 64kh+63 of the round over the two key halves of head half hh and writes them out
-  // (one straight-line copy of the rounds per kind of output)
+  // 64kh .. 64kh+63 of the round over the two key halves of head half hh and writes them out,
+  // lane l taking dims 64kh + 8(l & 7) .. +7 of heads (l >> 3) + 8q, q < 4: eight lanes cover
+  // the 64 dims of a head, so each store instruction writes whole 128-byte lines of fp16 /
+  // bf16 (one straight-line copy of the rounds per kind of output)
   float* xo = (float*)tiles;  // [wave][head][kXPitch]
-  const int sh = lane >> 1;   // summed head
-  const int sd = 64 * kh + 32 * (lane & 1);
+  const int sh = lane >> 3;   // summed head of q = 0
+  const int sd = 64 * kh + 8 * (lane & 7);
 #pragma unroll
   for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], fme);
-  const float Lsh = xf[(hh * 3 + 1) * kHB + sh];
-  const float inv = Lsh > 0.f ? 1.f / Lsh : 0.f;
+  float inv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float L = xf[(hh * 3 + 1) * kHB + sh + 8 * q];
+    inv[q] = L > 0.f ? 1.f / L : 0.f;
+  }
   const int head = h0 + sh;
   const int64_t orow = ((int64_t)t * kH + head) * kDv;                         // output row
   const int64_t prow = (((int64_t)tl * nsplit + split) * kH + head) * kDv;    // partial row
@@ -702,21 +719,30 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       }
       __syncthreads();
 #pragma unroll
-      for (int k4 = 0; k4 < 8; ++k4) {
-        const int d = sd + 4 * k4;
-        const f32x4 acc = *(const f32x4*)(xo + (hh * kHB + sh) * kXPitch + d) +
-                          *(const f32x4*)(xo + ((hh + 2) * kHB + sh) * kXPitch + d);
-        emit(128 * rd + d, acc);
+      for (int q = 0; q < 4; ++q) {
+        const float* a = xo + (hh * kHB + sh + 8 * q) * kXPitch + sd;
+        const float* b = xo + ((hh + 2) * kHB + sh + 8 * q) * kXPitch + sd;
+        const f32x4 lo = *(const f32x4*)a + *(const f32x4*)b;
+        const f32x4 hi = *(const f32x4*)(a + 4) + *(const f32x4*)(b + 4);
+        emit(q, (int64_t)8 * q * kDv + 128 * rd + sd, lo, hi);
       }
       if (rd < 3) __syncthreads();
     }
   };
   if (nsplit == 1) {
-    rounds([&](int dim, f32x4 acc) { store_out4<OUT_F32>(out, orow + dim, acc * inv); });
+    rounds([&](int q, int64_t off, f32x4 lo, f32x4 hi) {
+      store_out8<OUT_F32>(out, orow + off, lo * inv[q], hi * inv[q]);
+    });
   } else if (OUT_F32) {
-    rounds([&](int dim, f32x4 acc) { *(f32x4*)(part_o + prow + dim) = acc; });
+    rounds([&](int q, int64_t off, f32x4 lo, f32x4 hi) {
+      (void)q;
+      *(f32x4*)(part_o + prow + off) = lo;
+      *(f32x4*)(part_o + prow + off + 4) = hi;
+    });
   } else {  // bf16 output: the split's own normalised O as an fp16 partial
-    rounds([&](int dim, f32x4 acc) { store_part16(part_o, prow + dim, acc * inv); });
+    rounds([&](int q, int64_t off, f32x4 lo, f32x4 hi) {
+      store_part16x8(part_o, prow + off, lo * inv[q], hi * inv[q]);
+    });
   }
 }
 
@@ -831,8 +857,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int t_begin, int t_cou
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   const int64_t orow = ((int64_t)t * kH + head) * kDv + d0;
-  store_out4<OUT_F32>(out, orow, alo * inv);
-  store_out4<OUT_F32>(out, orow + 4, ahi * inv);
+  store_out8<OUT_F32>(out, orow, alo * inv, ahi * inv);
   if (lse && lane == 0)
     lse[(int64_t)t * kH + head] = LEsum > 0.f ? (M + log2f(LEsum)) * kLn2 : -INFINITY;
 }
