@@ -72,11 +72,15 @@ __device__ __forceinline__ TokLoc locate(const DevBatch& bt, int t) {
 struct LocLoads {
   int cq, sl;
 };
+// (The loads are unconditional, from clamped indices, with the values masked after: a load
+// under a branch makes the compiler wait for every load issued before the join.)
 __device__ __forceinline__ LocLoads locate_issue(const DevBatch& bt) {
   const int lane = threadIdx.x & 63;
   LocLoads r;
-  r.cq = lane + 1 <= bt.B ? bt.cu_q[lane + 1] : 0;
-  r.sl = lane < bt.B ? bt.seq_lens[lane] : 0;
+  r.cq = bt.cu_q[min(lane + 1, bt.B)];
+  r.sl = bt.seq_lens[min(lane, bt.B - 1)];
+  r.cq = lane + 1 <= bt.B ? r.cq : 0;
+  r.sl = lane < bt.B ? r.sl : 0;
   return r;
 }
 __device__ __forceinline__ TokLoc locate_finish(const DevBatch& bt, int t, LocLoads w0) {

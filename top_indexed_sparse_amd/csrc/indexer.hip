@@ -201,7 +201,7 @@ __device__ __forceinline__ float score_group(const i32x8 (&A)[4], const float (&
 //   all pages of the same chunk.
 template <bool GROUP>
 __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBatch bt,
-    int t_begin, int t_count, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    int t_begin, int t_count, const uint16_t* q_idx, const float* w,
     const uint8_t* kpool, const float* kscale,
     float* __restrict__ scores, int64_t ld, int chunk) {
   // (the wave index through readfirstlane, so that the ranges derived from it are scalars)
@@ -212,22 +212,26 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   const int k0 = blockIdx.y * chunk;
   if (tl >= t_count) return;  // (decode: the same for every wave of the workgroup)
   const int t = t_begin + tl;
-  // The query goes out first: it needs the token only.  Decode: the eight waves share the
-  // token, so waves 0..3 each quantise one 16-head tile and hand it over through LDS.
-  const uint16_t* qrow = q_idx + (int64_t)t * kIH * kID;
-  const float* wrow = w + (int64_t)t * kIH;
-  QRaw qr;
-  if (GROUP) a0_load(qrow, wrow, lane, qr);
-  else if (wave < 4) a0_load_tile(qrow, wrow, lane, wave, qr.r[0], qr.w[0]);
   // Page ids of the chunk, one per lane, fetched once (a scalar page-table load per page
   // would stall every prefetch on a scalar round trip).  Everything waits on them, so they
-  // are requested together with the token's request lookup, for request min(t, B - 1) (the
-  // request of token t when every request has one token), and again if that was not it.
+  // are requested first, together with the token's request lookup, for request min(t, B - 1)
+  // (the request of token t when every request has one token), and again if that was not it.
+  // The query goes out behind them (loads complete in issue order, so the first pages need
+  // not wait for it).  Decode: the eight waves share the token, so waves 0..3 each quantise
+  // one 16-head tile and hand it over through LDS (every wave loads tile wave & 3: a load
+  // under a branch would make the compiler wait for the query before the first pages).
   const int pg0 = k0 >> 6;
   const int pcol = min(pg0 + lane, bt.pt_stride - 1);
   const int bguess = min(t, bt.B - 1);
   int my_page = bt.page_table[(int64_t)bguess * bt.pt_stride + pcol];
-  const TokLoc loc = locate(bt, t);
+  const LocLoads lw = locate_issue(bt);
+  asm volatile("" ::: "memory");  // (the query loads stay behind these)
+  const uint16_t* qrow = q_idx + (int64_t)t * kIH * kID;
+  const float* wrow = w + (int64_t)t * kIH;
+  QRaw qr;
+  if (GROUP) a0_load(qrow, wrow, lane, qr);
+  else a0_load_tile(qrow, wrow, lane, wave & 3, qr.r[0], qr.w[0]);
+  const TokLoc loc = locate_finish(bt, t, lw);
   const int k1 = min(k0 + chunk, loc.n);                 // the chunk's keys in range
   const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;  // its pages in range (<= 64)
   const bool active = npg > poff;  // the wave has a page in range
