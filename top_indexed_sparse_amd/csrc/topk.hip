@@ -209,11 +209,45 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
     load_raw(c0, n);
     to_keys(c0);
   };
+  // The first chunk arrives through LDS: each wave reads its 256*NPT bytes with coalesced
+  // 1 KB loads (16-byte piece P = 64i + lane of the wave's span belongs to thread P / Q of the
+  // wave, Q = NPT/4 pieces per thread), stores them swizzled (piece q of thread u at slot
+  // u*Q + (q ^ ((u >> sw) & (Q-1))), which keeps both the stores and the reads below on 16
+  // distinct 4-bank groups per 16 lanes) and reads its own Q pieces back.  Read directly, each
+  // load instruction would touch 64 lines for 16 bytes of each.  The buffer overlaps S.
+  auto load_first = [&](int lim) {
+    if constexpr (NPT == 4) {
+      load_raw(0, lim);  // (one piece per thread: already coalesced)
+    } else {
+      constexpr int Q = NPT / 4;
+      constexpr int sw = Q == 8 ? 1 : Q == 4 ? 2 : 3;  // log2(16 / Q)
+      const int lane = tid & 63;
+      const int wb = (tid >> 6) * 64 * NPT;  // the wave's first position
+      uint4 v[Q];
+#pragma unroll
+      for (int i = 0; i < Q; ++i) {
+        const int p = wb + 256 * i + 4 * lane;  // (lim and p are multiples of 4)
+        v[i] = *(const uint4*)(row + min(p, lim - 4));
+        if (p >= lim) v[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      char* wbuf = smraw + (tid >> 6) * 64 * NPT * 4;
+#pragma unroll
+      for (int i = 0; i < Q; ++i) {
+        const int u = (64 * i + lane) / Q, q = lane % Q;
+        *(uint4*)(wbuf + 16 * (u * Q + (q ^ ((u >> sw) & (Q - 1))))) = v[i];
+      }
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const uint4 x = *(const uint4*)(wbuf + 16 * (lane * Q + (q ^ ((lane >> sw) & (Q - 1)))));
+        key[4 * q] = x.x; key[4 * q + 1] = x.y; key[4 * q + 2] = x.z; key[4 * q + 3] = x.w;
+      }
+    }
+  };
 
   // the first chunk goes out before the token lookup (up to the row stride, which bounds
   // every causal length), so the two memory latencies overlap
   const LocLoads lw = locate_issue(bt);
-  load_raw(0, (int)min<int64_t>(ld, (int64_t)CH));
+  load_first((int)min<int64_t>(ld, (int64_t)CH));
   n = locate_finish(bt, t, lw).n;
   int32_t* oi = out_idx + (int64_t)t * K;
   float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
@@ -237,6 +271,7 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
     }
   };
 
+  __syncthreads();  // (every wave has read its first chunk back before S is written)
   to_keys(0);
   S.hist[tid] = 0u;
   S.hist[tid + 1024] = 0u;
@@ -469,7 +504,8 @@ hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
   auto* fn = npt == 4 ? topk_select_kernel<4>
              : npt == 8 ? topk_select_kernel<8>
              : npt == 16 ? topk_select_kernel<16> : topk_select_kernel<32>;
-  const size_t shm = sizeof(SelSmem);
+  // dynamic LDS: the selection's, or the first chunk's transposition if larger
+  const size_t shm = std::max(sizeof(SelSmem), (size_t)4096 * (size_t)npt);
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)shm);
   if (e != hipSuccess) return e;
