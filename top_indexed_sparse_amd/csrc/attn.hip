@@ -189,6 +189,13 @@ __device__ __forceinline__ void store_out8(void* out, int64_t off, f32x4 lo, f32
   }
 }
 
+// One accumulator element times alpha, into a VGPR (the accumulator is left as it is).
+__device__ __forceinline__ float acc_read_scaled(float x, float alpha) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1\n\tv_mul_f32 %0, %0, %2" : "=&v"(r) : "a"(x), "v"(alpha));
+  return r;
+}
+
 // Scale an accumulator tile in place, element by element through one VGPR.  Written out so
 // that the tile never leaves the accumulator registers: a plain multiply makes the register
 // allocator move all 256 accumulators of a wave into VGPRs and spill.
@@ -692,14 +699,9 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   float* xo = (float*)tiles;  // [wave][head][kXPitch]
   const int sh = lane >> 3;   // summed head of q = 0
   const int sd = 64 * kh + 8 * (lane & 7);
-#pragma unroll
-  for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], fme);
+  // (the normalisers of the summed heads are read after the first barrier of the rounds:
+  // the merged sums in xf come from the kh = 0 waves)
   float inv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float L = xf[(hh * 3 + 1) * kHB + sh + 8 * q];
-    inv[q] = L > 0.f ? 1.f / L : 0.f;
-  }
   const int head = h0 + sh;
   const int64_t orow = ((int64_t)t * kH + head) * kDv;                         // output row
   const int64_t prow = (((int64_t)tl * nsplit + split) * kH + head) * kDv;    // partial row
@@ -712,12 +714,21 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = 32 * mm + 8 * q4 + 4 * h2;
-          const f32x4 v = {o[mi][4 * q4], o[mi][4 * q4 + 1], o[mi][4 * q4 + 2],
-                           o[mi][4 * q4 + 3]};
+          const f32x4 v = {acc_read_scaled(o[mi][4 * q4], fme),
+                           acc_read_scaled(o[mi][4 * q4 + 1], fme),
+                           acc_read_scaled(o[mi][4 * q4 + 2], fme),
+                           acc_read_scaled(o[mi][4 * q4 + 3], fme)};
           *(f32x4*)(xo + (wave * kHB + c32) * kXPitch + d) = v;
         }
       }
       __syncthreads();
+      if (rd == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float L = xf[(hh * 3 + 1) * kHB + sh + 8 * q];
+          inv[q] = L > 0.f ? 1.f / L : 0.f;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float* a = xo + (hh * kHB + sh + 8 * q) * kXPitch + sd;
