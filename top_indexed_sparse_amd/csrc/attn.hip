@@ -348,13 +348,22 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     const uint64_t b = __ballot(v >= 0);
     if (lane == 0) anyv[wave] = b ? __builtin_amdgcn_readlane(v, __builtin_ctzll(b)) : -1;
   }
-  __syncthreads();
-  // per wave tile: bit m = row pi(m) selected (the order in which the keys are consumed)
-  for (int tt = tid; tt < nrows / kWT; tt += 256) {
-    uint32_t m = 0u;
-    for (int j = 0; j < kWT; ++j) m |= (rows[tt * kWT + tile_row(j)] >= 0 ? 1u : 0u) << j;
-    masks[tt] = (uint16_t)m;
+  // per 16-row tile: bit m = row pi(m) selected (the order in which the keys are consumed),
+  // from one ballot per row step: rows 256j + 64wave + l, four tiles, lane q < 4 writes
+  // tile q's mask (row r of a tile is consumed as m = (r & 8) | (r & 1) << 2 | (r >> 1) & 3)
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint64_t bj = __ballot(slot[j] >= 0);
+    if (lane < 4) {
+      const uint32_t nat = (uint32_t)(bj >> (16 * lane)) & 0xffffu;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        m |= ((nat >> r) & 1u) << ((r & 8) | ((r & 1) << 2) | ((r >> 1) & 3));
+      masks[(256 * j + 64 * wave) / kWT + lane] = (uint16_t)m;
+    }
   }
+  __syncthreads();
   if (FP8) smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   // Rows that are not selected are gathered from a selected row of the split (finite data,
   // whose P is zero: exactly nothing is added).  A split without any selected row skips
@@ -362,7 +371,6 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const int fill = __builtin_amdgcn_readfirstlane(max(max(anyv[0], anyv[1]), max(anyv[2], anyv[3])));
   const int nst = fill >= 0 ? nstage : 0;
   const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
-  __syncthreads();
 
   // ---- this wave's tile of stage st: rows st*32 + 16*kh .. +15
   // wave-uniform pieces of the gather addresses live in scalar registers: the row base of
