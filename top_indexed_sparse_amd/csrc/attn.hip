@@ -102,9 +102,15 @@ constexpr int kSR = 2 * kWT;   // rows per stage: the tiles of the two key halve
 constexpr int kMaxKps = 2048;  // keys per split (bounds the LDS index table)
 constexpr float kMFloor = -1e30f;  // running max before the first live key (log2 units)
 // Q^T per wave: 18 fragments of 32 dims per 16 heads; the first kQR stay in registers, the
-// last kQL are kept in LDS (per wave, in the lane order of the operand) and read one step
-// ahead, which leaves the registers for the queue of gathered rows
+// last kQL are read from LDS one step ahead, which leaves the registers for the queue of
+// gathered rows.  The two waves of a head half (the two key halves) need the same Q: each
+// loads the fragments of one parity from HBM and takes the others from the copy its partner
+// leaves in LDS (one copy per head half, in the lane order of the operand), which halves the
+// Q traffic of the prologue.  So that every register index stays static, the key-half-1
+// wave contracts the dims of each fragment pair in swapped order: its step ks uses fragment
+// ks ^ 1 of both K and Q (the pairs never straddle the value/RoPE boundary).
 constexpr int kNQ = kDqk / 32, kQL = 4, kQR = kNQ - kQL;
+static_assert(kNQ % 2 == 0 && kQR % 2 == 0 && (kDv / 32) % 2 == 0, "fragment pairs");
 
 // 16-row tiles are gathered straight into LDS with 16-byte global->LDS loads; the two waves
 // that read a tile (the two head halves of one key half) issue half of its loads each.  A
@@ -149,7 +155,7 @@ struct AttnSmem {
   static constexpr int scl = masks + kMaxKps / 16 * 2;
   static constexpr int xm = scl + (FP8 ? kMaxKps * 4 : 0);
   static constexpr int qlds = xm + 4 * 3 * kHB * 4 + 2 * 3 * kHB * 4;
-  static constexpr int total = qlds + 4 * 2 * kQL * 1024;
+  static constexpr int total = qlds + 2 * 2 * kNQ * 1024;  // Q: [head half][ht][fragment]
   static_assert(total <= 160 * 1024, "LDS budget");
 };
 
@@ -258,7 +264,11 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const int c16 = lane & 15, g4 = lane >> 4;  // 16x16 layouts
   const int c32 = lane & 31, h2 = lane >> 5;  // 32x32 layouts
   const int hh = wave & 1, kh = wave >> 1;    // head half, key half
-  char* qlds = sm + SM::qlds + wave * (2 * kQL * 1024) + 16 * lane;  // this lane's Q in LDS
+  // this lane's slot in the head half's copy of Q; fragment f of head tile ht at
+  // (ht * kNQ + f) KB.  qxe / qxo address fragment ks ^ kh for even / odd ks.
+  char* const qx = sm + SM::qlds + hh * (2 * kNQ * 1024) + 16 * lane;
+  char* const qxe = qx + 1024 * kh;
+  char* const qxo = qx - 1024 * kh;
 
   // workgroup -> (token, split, head group); the workgroups of one token sit on one XCD
   // (workgroups are dealt to the 8 XCDs round-robin), so its rows are fetched from HBM once
@@ -300,18 +310,20 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     const int sp = pos[j];
     slot[j] = (sp >= 0 && sp < Lb) ? ptb[sp >> 6] : -1;
   }
-  // Q^T fragments of the 32 heads (B operand of 16x16x32: head c16, dims 32kk + 8g4), issued
-  // after the page lookups: loads complete in issue order, so the slots below wait for the
-  // page entries only, and Q arrives while the slots and the first tiles are in flight
-  bf16x8 qf[2][kQR], qtl[2][kQL];
+  // This wave's half of the Q^T fragments of its 32 heads (B operand of 16x16x32: head c16,
+  // dims 32f + 8g4 of fragment f = 2i + kh), issued after the page lookups: loads complete
+  // in issue order, so the slots below wait for the page entries only, and Q arrives while
+  // the slots and the first tiles are in flight.  Register slot ks holds fragment ks ^ kh:
+  // the even slots are loaded here, the odd ones come from the partner's copy.
+  bf16x8 qf[2][kQR], qtl[2][kQL / 2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4;
+    const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4 + 32 * kh;
 #pragma unroll
-    for (int kk = 0; kk < kNQ; ++kk) {
-      const bf16x8 v = *(const bf16x8*)(qr + 32 * kk);
-      if (kk < kQR) qf[ht][kk] = v;
-      else qtl[ht][kk - kQR] = v;
+    for (int i = 0; i < kNQ / 2; ++i) {
+      const bf16x8 v = *(const bf16x8*)(qr + 64 * i);
+      if (2 * i < kQR) qf[ht][2 * i] = v;
+      else qtl[ht][i - kQR / 2] = v;
     }
   }
 #pragma unroll
@@ -457,13 +469,21 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 #pragma unroll
     for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr1, jlo + j);
   // Q has landed on every path into the loop (otherwise the waits for Q placed inside the loop
-  // would also hold back the queued gathers); its last fragments go to LDS
+  // would also hold back the queued gathers): the loaded half goes to the shared copy, and
+  // after a barrier the partner's half of the register fragments comes back from it
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
 #pragma unroll
-    for (int kk = 0; kk < kQR; ++kk) asm volatile("" ::"v"(qf[ht][kk]));
+    for (int i = 0; i < kNQ / 2; ++i)
+      *(bf16x8*)(qxe + (ht * kNQ + 2 * i) * 1024) =
+          2 * i < kQR ? qf[ht][2 * i < kQR ? 2 * i : 0] : qtl[ht][2 * i < kQR ? 0 : i - kQR / 2];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int kk = 0; kk < kQL; ++kk) *(bf16x8*)(qlds + (ht * kQL + kk) * 1024) = qtl[ht][kk];
+  for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+    for (int i = 0; i < kQR / 2; ++i)
+      qf[ht][2 * i + 1] = *(const bf16x8*)(qxo + (ht * kNQ + 2 * i + 1) * 1024);
   }
   for (int st = 0; st < nst; ++st) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -481,11 +501,12 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     constexpr int kPre = 2;
     using KRaw = typename std::conditional<FP8, i32x2, bf16x8>::type;
     KRaw kr[kPre];
-    // lane (m = c16, g4): row pi(m), dims 32ks + 8g4 .. +7 (region A below dim 512, B above)
+    // lane (m = c16, g4): row pi(m), dims 32f + 8g4 .. +7 of fragment f = ks ^ kh (region A
+    // below dim 512, B above)
     const int qr = tile_row(c16);
     auto kread = [&](int ks) -> KRaw {
       constexpr int kEB = FP8 ? 1 : 2;  // bytes per element
-      const int d = 32 * ks + 8 * g4;
+      const int d = 32 * ks + 8 * g4 + ((ks & 1) ? -32 * kh : 32 * kh);
       const char* pa = ks < kDv / 32 ? sb + qr * F::kAStride + kEB * d
                                      : sb + F::kABytes + qr * F::kRStride + kEB * (d - kDv);
       return *(const KRaw*)pa;
@@ -498,7 +519,8 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       if (ks + 1 >= kQR && ks + 1 < kNQ) {
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
-          ql[(ks + 1) & 1][ht] = *(const bf16x8*)(qlds + (ht * kQL + ks + 1 - kQR) * 1024);
+          ql[(ks + 1) & 1][ht] =
+              *(const bf16x8*)(((ks + 1) & 1 ? qxo : qxe) + (ht * kNQ + ks + 1) * 1024);
       }
       const KRaw cur = kr[ks % kPre];
       if (ks + kPre < kDqk / 32) kr[ks % kPre] = kread(ks + kPre);
