@@ -498,7 +498,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     for (int ht = 0; ht < 2; ++ht) s[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     // K fragments are read kPre steps ahead of their use (the latency of an LDS read is
     // several MFMA steps)
-    constexpr int kPre = 2;
+    constexpr int kPre = 3;
     using KRaw = typename std::conditional<FP8, i32x2, bf16x8>::type;
     KRaw kr[kPre];
     // lane (m = c16, g4): row pi(m), dims 32f + 8g4 .. +7 of fragment f = ks ^ kh (region A
