@@ -8,23 +8,26 @@
 // variable lengths).  Every head reads the same latent row: keys are the full 576-wide row
 // (512 latent + 64 RoPE), values are its first 512 dims.
 //
-// Matrix-core kernel (128 heads, bf16 or e4m3 cache), one workgroup per (token, key split):
+// Matrix-core kernel (bf16 or e4m3 cache), one 4-wave workgroup per (token, key split,
+// group of 64 heads); wave (hh, kh) owns 32 heads (half hh of the group) and key half kh
+// of every 32-key stage:
 //   * the split's positions are translated through the page table once into LDS;
-//   * 32-row tiles are gathered straight into LDS with 16-byte global->LDS loads, double
-//     buffered; e4m3 rows stay e4m3 in LDS and are widened per fragment;
-//   * wave w owns heads 32w..32w+31.  S^T = K_tile . Q^T on v_mfma_f32_32x32x16 with Q^T
-//     resident in registers (36 fragments of 16 dims); the accumulator holds, per lane, one
-//     head and 16 keys, so the online softmax is lane-local plus one permlane swap;
-//   * O^T[vdim][head] += V^T . P^T: P is already in the MFMA B layout (the 16 keys of a lane
-//     are reused as the k index, with V^T rows read in the same order), and V^T fragments
-//     come from the row-major tile via ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3);
+//   * 16-row tiles are gathered with 16-byte loads into a one-stage register queue and
+//     written into a two-stage LDS ring, interleaved with the QK matrix ops; e4m3 rows stay
+//     e4m3 in LDS and are widened per fragment;
+//   * S^T = K_tile . Q^T on v_mfma_f32_16x16x32 over 18 fragments of 32 dims, most of Q^T in
+//     registers and the rest in LDS (one copy per head half, loaded half by each of its two
+//     waves);
+//   * O^T[vdim][head] += V^T . P^T on v_mfma_f32_32x32x16: P reaches the B layout with one
+//     permlane16 swap, and V^T fragments come from the row-major tile via
+//     ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3);
 //   * the running max is raised lazily (only when a tile exceeds it by 2^8), so rescaling
 //     the 256 accumulator registers is rare;
 //   * e4m3: per-token scales go into the logits in fp32 and into P relative to the split's
 //     largest scale; P then is fp16 (11-bit significand) so that heavy rows stay accurate,
 //     and the normaliser is accumulated from the same rounded P values;
-//   * with several splits per token, (m, l, unnormalised O) partials are merged by
-//     mla_combine_kernel with log-sum-exp weights.
+//   * the two key halves are merged through LDS; with several splits per token, each split
+//     writes (m, l, O) partials that mla_combine_kernel merges with log-sum-exp weights.
 #include "common.h"
 #include "launch.h"
 
@@ -112,12 +115,13 @@ constexpr float kMFloor = -1e30f;  // running max before the first live key (log
 constexpr int kNQ = kDqk / 32, kQL = 4, kQR = kNQ - kQL;
 static_assert(kNQ % 2 == 0 && kQR % 2 == 0 && (kDv / 32) % 2 == 0, "fragment pairs");
 
-// 16-row tiles are gathered straight into LDS with 16-byte global->LDS loads; the two waves
-// that read a tile (the two head halves of one key half) issue half of its loads each.  A
-// tile has two regions: A holds the value part of each row (its first 512 dims) at a padded row stride,
-// one load instruction per row (every lane a 16-byte chunk of that row, so the source is a
-// per-row scalar base plus the lane offset: no per-lane address arithmetic); B holds the
-// 64 RoPE dims of the 16 rows (bf16: two loads, e4m3: one).  The A stride is 8 dwords more
+// 16-row tiles are gathered with 16-byte loads into registers and written to LDS (a load
+// straight to LDS costs its wave about twice the issue time of a load plus an LDS write); the
+// two waves that read a tile (the two head halves of one key half) issue half of its loads
+// each.  A tile has two regions: A holds the value part of each row (its first 512 dims) at
+// a padded row stride, one load instruction per row (every lane a 16-byte chunk of that row,
+// so the source is a per-row scalar base plus the lane offset: no per-lane address
+// arithmetic); B holds the 64 RoPE dims of the 16 rows (bf16: two loads, e4m3: one).  The A stride is 8 dwords more
 // than a multiple of the 64 LDS banks and the B stride 4 more than a multiple of 16 (both
 // measured fastest for the reads below), and the rows are consumed in the order
 // pi(8h + j) = 8h + 2j (j < 4), 8h + 2(j - 4) + 1 (j >= 4), which makes both the 16-byte
