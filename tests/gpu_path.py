@@ -61,6 +61,59 @@ def run_path(inp, unfused: bool = True, K: int | None = None,
     return r
 
 
+class SampledRows:
+    """Rows of a [T, ...] device tensor copied to the host for a set of tokens only, indexed
+    by token like the full array (``rows[t]`` or ``rows[t, sl]``)."""
+
+    def __init__(self, dev: torch.Tensor, tokens, as_f64: bool = False):
+        self.pos = {int(t): i for i, t in enumerate(tokens)}
+        ix = torch.as_tensor(list(tokens), dtype=torch.long, device=dev.device)
+        rows = dev.index_select(0, ix)
+        self.rows = rows.float().cpu().numpy().astype(np.float64) if as_f64 else rows.cpu().numpy()
+
+    def __getitem__(self, key):
+        if isinstance(key, tuple):
+            return self.rows[(self.pos[int(key[0])],) + key[1:]]
+        return self.rows[self.pos[int(key)]]
+
+
+def run_path_sampled(inp, tokens) -> SimpleNamespace:
+    """The same launches as run_path over the whole batch, for batches whose outputs do not fit
+    the host: fused and unfused Top-K are compared on the device for every token, outputs are
+    checked finite on the device, and only the rows of ``tokens`` come back to the host."""
+    sh = inp.wl.shape
+    K = sh.K
+    d = to_device(inp)
+    bt = make_batch(inp)
+    T = inp.T
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    val = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    tis.index_score_topk(bt, d.q_idx, d.w, d.k_pool, d.k_scale, K, idx, val)
+    ld = (bt.max_n + 3) // 4 * 4
+    scores = torch.full((T, ld), float("nan"), dtype=torch.float32, device="cuda")
+    tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores)
+    idx2 = torch.empty_like(idx)
+    val2 = torch.empty_like(val)
+    tis.topk_select(bt, scores, K, idx2, val2)
+    torch.cuda.synchronize()
+    r = SimpleNamespace()
+    r.fused_equal = bool(torch.equal(idx, idx2)) and bool(torch.equal(val, val2))
+    r.scores = SampledRows(scores, tokens)
+    del scores, idx2, val2
+    out_dt = torch.float32 if (sh.fp32 or sh.kv_fp8) else torch.bfloat16
+    out = torch.empty((T, sh.H, sh.D_v), dtype=out_dt, device="cuda")
+    lse = torch.empty((T, sh.H), dtype=torch.float32, device="cuda")
+    tis.sparse_mla_attn(bt, d.q, d.kv_pool, d.kv_scale, idx, sh.softmax_scale, out, lse)
+    torch.cuda.synchronize()
+    r.out_finite = bool(torch.isfinite(out).all())
+    r.lse_finite = bool(torch.isfinite(lse).all())
+    r.idx = SampledRows(idx, tokens)
+    r.val = SampledRows(val, tokens)
+    r.out = SampledRows(out, tokens, as_f64=True)
+    r.lse = SampledRows(lse, tokens, as_f64=True)
+    return r
+
+
 def check_topk(inp, orc, idx, tokens, exact: bool, K: int | None = None):
     """Top-K gate.  Exact mode: identical ints.  Continuous: recall >= 0.999 overall, every
     index in the symmetric difference within 1e-3 relative of the k-th score, full sets when

@@ -11,7 +11,7 @@ import torch
 import synth
 from oracle import Oracle
 from tests.gpu_path import (check_attention, check_scores, check_topk, note, run_path,
-                            sample_tokens)
+                            run_path_sampled, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -253,3 +253,52 @@ def test_decode32k_full_size():
     note("case decode32k full size")
     r = run_path(inp)
     _common(inp, r, list(range(inp.T)), False)
+
+
+def _full_size(cfg, n_sample):
+    """A workload at its full size: every token through the fused and unfused chains and the
+    attention call; sampled tokens against the oracle."""
+    wl = synth.workload(cfg)
+    note(f"case {wl.name} full size: generating inputs")
+    inp = synth.make(wl, "continuous")
+    tokens = sample_tokens(inp, n_sample)
+    note(f"case {wl.name} full size: T={inp.T} B={inp.B} max L={int(inp.seq_lens.max())}, "
+         f"{len(tokens)} sampled tokens; running")
+    r = run_path_sampled(inp, tokens)
+    note(f"case {wl.name} full size: checking against the oracle")
+    assert r.fused_equal, "fused vs unfused Top-K"
+    assert r.out_finite and r.lse_finite, "non-finite attention output"
+    for t in tokens[:8]:
+        sel = r.idx[t][r.idx[t] >= 0]
+        assert np.array_equal(r.val[t][: sel.size], r.scores[t, sel]), t
+    orc = Oracle(inp)
+    serr = check_scores(inp, orc, r.scores, tokens)
+    rec = check_topk(inp, orc, r.idx, tokens, False)
+    aerr = check_attention(inp, orc, r, tokens)
+    note(f"  {wl.name}: score rel err {serr:.2e}, recall {rec}, attn err {aerr[0]:.2e}, "
+         f"lse err {aerr[1]:.2e}")
+    return inp, r, tokens
+
+
+@pytest.mark.timeout(900)
+def test_decode1m_full_size():
+    """4 x 1,048,576 context, e4m3 caches, planted blocks: every token checked."""
+    inp, r, tokens = _full_size(synth.DECODE1M, 4)
+    assert tokens == list(range(inp.T))
+    for b in range(inp.B):
+        off = inp.info["planted"][b]
+        sel = r.idx[b][r.idx[b] >= 0]
+        assert np.mean((sel >= off) & (sel < off + 4096)) > 0.5
+
+
+@pytest.mark.timeout(900)
+def test_prefill64k_full_size():
+    """One 65,536-token causal prefill, e4m3 latent cache with heavy rows."""
+    _full_size(synth.PREFILL64K, 96)
+
+
+@pytest.mark.timeout(900)
+def test_ragged_full_size():
+    """64 requests of 1K..256K context, 48 decoding and 16 in a 4096-token prefill slice,
+    random page table over a poisoned pool."""
+    _full_size(synth.RAGGED, 96)
