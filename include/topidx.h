@@ -100,7 +100,10 @@ tis_status_t index_score(const tis_batch_t* batch, const void* q_idx, tis_dtype_
  *   (score descending, position ascending); -0.0 and +0.0 are equal.  Scores must not be NaN.
  * topk_idx [T][K] int32: the selected positions in ascending order, then -1 up to K.
  * topk_val [T][K] fp32 or NULL: the score of each emitted position (0 where idx = -1).
- * ws       workspace of topk_select_workspace_size() bytes (may be 0 / NULL).
+ * ws       workspace of topk_select_workspace_size() bytes, 16-byte aligned: nonzero for a
+ *          batch of at most 64 tokens with rows longer than 32768 positions and K <= 4096,
+ *          which are selected by several workgroups per row (otherwise 0 / NULL).  Returns
+ *          TIS_ERR_INVALID when it is too small.
  */
 tis_status_t topk_select(const tis_batch_t* batch, const float* scores, int64_t ld_scores,
                          int32_t K, int32_t* topk_idx, float* topk_val, void* ws,

@@ -97,10 +97,26 @@ def test_index_argument_validation():
     assert lib.topk_select(b.ref, D, 1024, 0, D, None, None, 0, None) == L.TIS_ERR_INVALID
     assert lib.topk_select(b.ref, D, 1000, 10, None, None, None, 0, None) == L.TIS_ERR_INVALID
     need = lib.index_score_topk_workspace_size(b.ref, 64, 128, 16)
-    assert need == 3 * 1000 * 4          # T=3 rows of ld=1000 scores
+    assert need == 12032                 # T=3 rows of ld=1000 scores, rounded up to 256 bytes
     assert lib.index_score_topk(b.ref, D, L.TIS_BF16, D, D, L.TIS_E4M3, D, 64, 128,
                                 L.TIS_QMODE_FP8, 16, D, None, D, need - 1, None) == L.TIS_ERR_INVALID
     assert "workspace" in last_error()
+
+
+def test_long_row_selection_workspace():
+    """Few tokens over rows longer than 32768 positions are selected by several workgroups per
+    row, through a workspace that the size query reports and the call checks."""
+    lib = tis.lib()
+    b = FakeBatch([40000, 1000], [0, 1, 2])
+    need = lib.topk_select_workspace_size(b.ref, 2048)
+    assert need == 2 * (8192 * 8 + 2048 * 4 + 16)
+    assert lib.topk_select_workspace_size(b.ref, 5000) == 0           # K above 4096
+    assert lib.topk_select_workspace_size(FakeBatch([30000], [0, 1]).ref, 2048) == 0
+    assert lib.topk_select(b.ref, D, 40000, 2048, D, None, D, need - 1, None) == L.TIS_ERR_INVALID
+    assert "workspace" in last_error()
+    assert lib.topk_select(b.ref, D, 40000, 2048, D, None, None, need, None) == L.TIS_ERR_INVALID
+    fused = lib.index_score_topk_workspace_size(b.ref, 64, 128, 2048)
+    assert fused == 2 * 40000 * 4 + need  # two score rows (256-byte multiple) + the selection's
 
 
 def test_attention_argument_validation():

@@ -247,6 +247,51 @@ def test_topk_crafted_rows():
         assert np.all(val[b, k:] == 0.0)
 
 
+def test_topk_crafted_long_rows():
+    """Top-K over a few rows longer than 32768 positions (selected by several workgroups per
+    row): unique, tied (the candidate list overflows and the one-workgroup select finishes the
+    row), signed-zero / -inf, sparse and short rows, a 1M-position row, for K = 1, 2048 and 4096
+    (the largest K of that path) and 4100 (the one-workgroup path).  Every row equals the
+    oracle's Top-K, values included."""
+    import top_indexed_sparse_amd as tis
+    from oracle.method import topk_token
+    rng = np.random.default_rng(20261203)
+    lens = [100000, 100000, 70001, 65537, 40000, 50000, 40000, 2000, 1000000]
+    B, ld = len(lens), 1000000
+    S = np.zeros((B, ld), np.float32)
+    S[0] = 1.5
+    S[1] = rng.integers(0, 4, ld)
+    S[2] = np.linspace(-1.0, 1.0, ld)
+    S[3] = np.linspace(1.0, -1.0, ld)
+    S[4] = rng.standard_normal(ld)
+    S[4][::7] = -0.0
+    S[4][::11] = 0.0
+    S[4][::13] = -np.inf
+    S[5] = rng.standard_normal(ld)
+    S[5][lens[5] - 3000:lens[5]] += 4.0
+    S[6] = rng.exponential(size=ld) * (rng.random(ld) < 0.3)
+    S[7] = rng.standard_normal(ld)
+    S[8] = rng.standard_normal(ld)
+    bt = tis.Batch(np.array(lens, np.int32), np.arange(B + 1, dtype=np.int32),
+                   np.zeros((B, -(-ld // 64)), np.int32), 1)
+    scores = torch.from_numpy(S).cuda()
+    refs = {}
+    for K in (1, 2048, 4096, 4100):
+        note(f"case Top-K on crafted long rows, K={K}")
+        idx = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+        val = torch.full((B, K), 7.0, dtype=torch.float32, device="cuda")
+        tis.topk_select(bt, scores, K, idx, val)
+        idx, val = idx.cpu().numpy(), val.cpu().numpy()
+        for b in range(B):
+            if (b, K) not in refs:
+                refs[b, K] = topk_token(S[b, :lens[b]].astype(np.float64), K)[0]
+            ref = refs[b, K]
+            assert np.array_equal(idx[b], ref), (b, K)
+            k = int((ref >= 0).sum())
+            assert np.array_equal(val[b, :k], S[b, ref[:k]]), (b, K)
+            assert np.all(val[b, k:] == 0.0), (b, K)
+
+
 def test_decode32k_full_size():
     """The benchmarked workload itself: 32 x 32768, K = 2048, bf16 latent cache."""
     inp = synth.make(synth.workload(synth.DECODE32K), "continuous")

@@ -156,9 +156,15 @@ def index_score(batch: Batch, q_idx, w, k_pool, k_scale, scores, qmode=None):
     return scores
 
 
-def topk_select(batch: Batch, scores, K: int, topk_idx, topk_val=None):
+def topk_select_workspace_size(batch: Batch, K: int) -> int:
+    return int(lib().topk_select_workspace_size(batch.ref, int(K)))
+
+
+def topk_select(batch: Batch, scores, K: int, topk_idx, topk_val=None, ws=None):
+    need = topk_select_workspace_size(batch, K)
+    ws, nb = _ws(need, ws, scores.device)
     _check(lib().topk_select(batch.ref, _ptr(scores), int(scores.stride(0)), int(K),
-                             _ptr(topk_idx), _ptr(topk_val), None, 0, _stream()))
+                             _ptr(topk_idx), _ptr(topk_val), _ptr(ws), nb, _stream()))
     return topk_idx
 
 

@@ -128,6 +128,11 @@ tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath pat
 
 int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
 
+// the fused call's workspace: the score rows of one chunk, then the selection's workspace
+size_t fused_scores_bytes(int rows, const HostInfo& hi) {
+  return ((size_t)rows * (size_t)round4(hi.max_n) * sizeof(float) + 255) & ~(size_t)255;
+}
+
 int fused_rows_per_chunk(const tis_batch_t* b, const HostInfo& hi) {
   const int64_t row_bytes = round4(hi.max_n) * 4;
   int64_t r = (int64_t)kScoreScratchBudget / std::max<int64_t>(row_bytes, 1);
@@ -189,16 +194,18 @@ TIS_API size_t index_score_workspace_size(const tis_batch_t* batch, int32_t H_I,
 }
 
 TIS_API size_t topk_select_workspace_size(const tis_batch_t* batch, int32_t K) {
-  (void)batch; (void)K;
-  return 0;
+  HostInfo hi;
+  if (check_batch(batch, &hi) != TIS_OK || K < 1) return 0;
+  return tis::topk_ws_bytes(batch->T, hi.max_n, K);
 }
 
 TIS_API size_t index_score_topk_workspace_size(const tis_batch_t* batch, int32_t H_I,
                                                int32_t D_I, int32_t K) {
-  (void)H_I; (void)D_I; (void)K;
+  (void)H_I; (void)D_I;
   HostInfo hi;
-  if (check_batch(batch, &hi) != TIS_OK) return 0;
-  return (size_t)fused_rows_per_chunk(batch, hi) * (size_t)round4(hi.max_n) * sizeof(float);
+  if (check_batch(batch, &hi) != TIS_OK || K < 1) return 0;
+  const int rows = fused_rows_per_chunk(batch, hi);
+  return fused_scores_bytes(rows, hi) + tis::topk_ws_bytes(rows, hi.max_n, K);
 }
 
 TIS_API size_t sparse_mla_attn_workspace_size(const tis_batch_t* batch, int32_t K, int32_t H,
@@ -231,17 +238,19 @@ TIS_API tis_status_t index_score(const tis_batch_t* batch, const void* q_idx, ti
 TIS_API tis_status_t topk_select(const tis_batch_t* batch, const float* scores,
                                  int64_t ld_scores, int32_t K, int32_t* topk_idx,
                                  float* topk_val, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   HostInfo hi;
   tis_status_t st = check_batch(batch, &hi);
   if (st != TIS_OK) return st;
   if (K < 1) return fail(TIS_ERR_INVALID, "K must be >= 1");
   if (!scores || !topk_idx) return fail(TIS_ERR_INVALID, "scores and topk_idx must be set");
+  const size_t need = tis::topk_ws_bytes(batch->T, hi.max_n, K);
+  if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
+    return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
   if (!aligned16(scores)) return fail(TIS_ERR_INVALID, "scores must be 16-byte aligned");
   if (ld_scores < hi.max_n || (ld_scores & 3))
     return fail(TIS_ERR_INVALID, "ld_scores must be >= %d and a multiple of 4", hi.max_n);
-  hipError_t e = tis::launch_topk(dev_batch(batch), 0, batch->T, hi.max_n, scores, ld_scores, K, topk_idx,
-                                  topk_val, (hipStream_t)stream);
+  hipError_t e = tis::launch_topk(dev_batch(batch), 0, batch->T, hi.max_n, scores, ld_scores, K,
+                                  topk_idx, topk_val, ws, (hipStream_t)stream);
   return e == hipSuccess ? TIS_OK : hip_fail(e, "topk_select launch");
 }
 
@@ -261,17 +270,19 @@ TIS_API tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_id
   if (!topk_idx) return fail(TIS_ERR_INVALID, "topk_idx must be set");
   const int rows = fused_rows_per_chunk(batch, hi);
   const int64_t ld = round4(hi.max_n);
-  const size_t need = (size_t)rows * (size_t)ld * sizeof(float);
+  const size_t sbytes = fused_scores_bytes(rows, hi);
+  const size_t need = sbytes + tis::topk_ws_bytes(rows, hi.max_n, K);
   if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
     return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
   hipStream_t s = (hipStream_t)stream;
   float* sc = (float*)ws;
+  void* tws = (char*)ws + sbytes;
   const tis::DevBatch d = dev_batch(batch);
   for (int t0 = 0; t0 < batch->T; t0 += rows) {
     const int tc = std::min(rows, batch->T - t0);
     st = run_index(batch, hi, path, t0, tc, q_idx, w, k_pool, k_scale, H_I, D_I, sc, ld, s);
     if (st != TIS_OK) return st;
-    hipError_t e = tis::launch_topk(d, t0, tc, hi.max_n, sc, ld, K, topk_idx, topk_val, s);
+    hipError_t e = tis::launch_topk(d, t0, tc, hi.max_n, sc, ld, K, topk_idx, topk_val, tws, s);
     if (e != hipSuccess) return hip_fail(e, "index_score_topk select launch");
   }
   return TIS_OK;

@@ -17,7 +17,10 @@ hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, 
                                   int64_t ld, hipStream_t st);
 hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
                        const float* scores, int64_t ld, int K, int32_t* idx, float* val,
-                       hipStream_t st);
+                       void* ws, hipStream_t st);
+// workspace bytes of launch_topk over up to `rows` rows of up to max_n positions (0 when the
+// selection needs none)
+size_t topk_ws_bytes(int rows, int max_n, int K);
 hipError_t launch_mla_attn_f32(const DevBatch& bt, int t_begin, int t_count, const float* q,
                                const float* kv, const int32_t* idx, int K, int H, int Dqk,
                                int Dv, float scale, float* out, float* lse, hipStream_t st);

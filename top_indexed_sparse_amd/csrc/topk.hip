@@ -103,6 +103,11 @@ struct SelSmem {
   uint32_t candk[kCandMax];
 };
 
+// Long-row selection state per row, words [mode, bin, candidates, appended]
+constexpr uint32_t kLongCand = 0u, kLongAll = 1u, kLongOver = 2u;
+constexpr int kLongCap = 8192;     // candidates per row, sorted in LDS
+constexpr int kLongRows = 64;      // at most this many rows per launch take the long-row path
+
 // Radix select of the krem-th largest key among the keys produced by `each` (called with a
 // visitor), over r = key - base with digits of up to 11 bits from bit `hi` down.  Returns the
 // threshold key; krem is left as the number of keys equal to it that are taken.  The two
@@ -165,7 +170,8 @@ __device__ __forceinline__ uint32_t radix_select(uint32_t base, int hi, uint32_t
 // every path gives the same threshold.
 template <int NPT>
 __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int K, int32_t* __restrict__ out_idx,
+    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ only,
+    int32_t* __restrict__ out_idx,
     float* __restrict__ out_val) {
   extern __shared__ __attribute__((aligned(16))) char smraw[];
   SelSmem& S = *(SelSmem*)smraw;
@@ -173,6 +179,8 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
   const int tl = blockIdx.x;
   const int t = t_begin + tl;
   const float* row = scores + (int64_t)tl * ld;
+  // (after the long-row selection: only the rows it left over)
+  if (only && only[4 * tl] != kLongOver) return;
   constexpr int CH = 1024 * NPT;
   uint32_t key[NPT];  // the raw score bits until to_keys, then the order keys
 
@@ -494,9 +502,229 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
   }
 }
 
+
+// ---------------------------------------------------------------- long rows, few of them
+// With few rows of many positions, one workgroup per row leaves most of the chip idle and
+// streams each row through one CU.  Then every row is cut into slices:
+//   0. the row's histogram and state words are cleared;
+//   1. each slice histograms the top 11 bits of its keys in LDS and adds the non-empty bins to
+//      the row's histogram;
+//   2. one workgroup per row finds the bin b holding the k-th largest key: the keys in bins
+//      >= b (at least k of them) are the candidates;
+//   3. each slice appends its candidates (key, position) to the row's list;
+//   4. one workgroup per row sorts the list by (key descending, position ascending) in LDS,
+//      keeps the first k and sorts their positions ascending.
+// Rows with n <= K take every position in step 4.  A row whose list would exceed kLongCap
+// (many equal or nearly equal scores) is marked in step 2 and selected afterwards by the
+// one-workgroup kernel, which skips every other row.  The result is the same selection.
+
+__global__ __launch_bounds__(256) void topk_long_zero_kernel(uint32_t* __restrict__ hist,
+                                                             uint32_t* __restrict__ state) {
+  const int tl = blockIdx.x;
+  for (int i = threadIdx.x; i < 2048; i += 256) hist[(int64_t)tl * 2048 + i] = 0u;
+  if (threadIdx.x < 4) state[4 * tl + threadIdx.x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void topk_long_hist_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int K, int slice,
+    uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[2048];
+  const int tid = threadIdx.x, tl = blockIdx.y;
+  for (int i = tid; i < 2048; i += 256) h[i] = 0u;
+  const int n = locate(bt, t_begin + tl).n;
+  const float* row = scores + (int64_t)tl * ld;
+  const int p0 = blockIdx.x * slice, p1 = min(n, p0 + slice);
+  __syncthreads();
+  if (n > K) {
+    for (int p = p0 + 4 * tid; p < p1; p += 1024) {
+      float v[4];
+      if (p + 3 < p1) {
+        const float4 f = *(const float4*)(row + p);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = p + e < p1 ? row[p + e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p + e < p1) atomicAdd(&h[order_key(v[e]) >> 21], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = hist + (int64_t)tl * 2048;
+  for (int i = tid; i < 2048; i += 256)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+__global__ __launch_bounds__(1024) void topk_long_pick_kernel(DevBatch bt, int t_begin, int K,
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ state) {
+  __shared__ uint32_t sh[48];
+  __shared__ uint32_t pick[2];
+  const int tid = threadIdx.x, tl = blockIdx.x;
+  const int n = locate(bt, t_begin + tl).n;
+  uint32_t* st = state + 4 * tl;
+  if (n <= K) {  // (uniform over the workgroup)
+    if (tid == 0) st[0] = kLongAll;
+    return;
+  }
+  // bins in descending order: thread i owns bins 2047 - 2i and 2046 - 2i
+  const uint32_t* hr = hist + (int64_t)tl * 2048;
+  const uint32_t ch = hr[2047 - 2 * tid], cl = hr[2046 - 2 * tid];
+  uint32_t tot;
+  const uint32_t above_h = block_excl_scan(ch + cl, sh, tot);
+  const uint32_t above_l = above_h + ch;
+  const uint32_t k = (uint32_t)K;
+  if (ch && above_h < k && k <= above_h + ch) {
+    pick[0] = 2047 - 2 * tid;
+    pick[1] = above_h + ch;
+  }
+  if (cl && above_l < k && k <= above_l + cl) {
+    pick[0] = 2046 - 2 * tid;
+    pick[1] = above_l + cl;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    st[0] = pick[1] > (uint32_t)kLongCap ? kLongOver : kLongCand;
+    st[1] = pick[0];
+    st[2] = pick[1];
+  }
+}
+
+__global__ __launch_bounds__(256) void topk_long_gather_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int slice, uint32_t* __restrict__ state,
+    uint64_t* __restrict__ cand) {
+  const int tid = threadIdx.x, lane = tid & 63, tl = blockIdx.y;
+  uint32_t* st = state + 4 * tl;
+  if (st[0] != kLongCand) return;
+  const uint32_t thr = st[1] << 21;  // the candidates: keys in bins >= the picked one
+  const int n = locate(bt, t_begin + tl).n;
+  const float* row = scores + (int64_t)tl * ld;
+  uint64_t* out = cand + (int64_t)tl * kLongCap;
+  const int p0 = blockIdx.x * slice, p1 = min(n, p0 + slice);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int p = p0 + 4 * tid; p < p1; p += 1024) {
+    float v[4];
+    if (p + 3 < p1) {
+      const float4 f = *(const float4*)(row + p);
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = p + e < p1 ? row[p + e] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = order_key(v[e]);
+      const bool take = p + e < p1 && key >= thr;
+      const uint64_t m = __ballot(take);
+      if (m) {  // (uniform over the wave)
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&st[3], (uint32_t)__popcll(m));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const uint32_t o = base + (uint32_t)__popcll(m & below);
+        if (take && o < (uint32_t)kLongCap)
+          out[o] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)(p + e));
+      }
+    }
+  }
+}
+
+// Bitonic sort of v[0..P) (P a power of two) in LDS by 1024 threads; descending when DESC.
+template <bool DESC, typename V>
+__device__ __forceinline__ void lds_bitonic(V* v, int P) {
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < P / 2; i += 1024) {
+        const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool down = ((lo & size) == 0) == DESC;  // this pair's order: larger first
+        const V a = v[lo], b = v[hi];
+        if ((a < b) == down) {
+          v[lo] = b;
+          v[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ state,
+    const uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_val) {
+  extern __shared__ __attribute__((aligned(16))) char smraw[];
+  uint64_t* sk = (uint64_t*)smraw;                    // [kLongCap] candidates
+  uint32_t* sp = (uint32_t*)(smraw + 8 * kLongCap);   // [pow2 >= K] selected positions
+  const int tid = threadIdx.x, tl = blockIdx.x;
+  const int t = t_begin + tl;
+  const uint32_t* st = state + 4 * tl;
+  const uint32_t mode = st[0];
+  if (mode == kLongOver) return;
+  const float* row = scores + (int64_t)tl * ld;
+  int32_t* oi = out_idx + (int64_t)t * K;
+  float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
+  if (mode == kLongAll) {
+    const int n = locate(bt, t).n;
+    for (int i = tid; i < K; i += 1024) {
+      oi[i] = i < n ? i : -1;
+      if (ov) ov[i] = i < n ? row[i] : 0.f;
+    }
+    return;
+  }
+  const int cnt = (int)min(st[3], (uint32_t)kLongCap);  // (= st[2] <= kLongCap)
+  int P = 2;
+  while (P < cnt) P <<= 1;
+  for (int i = tid; i < P; i += 1024) sk[i] = i < cnt ? cand[(int64_t)tl * kLongCap + i] : 0ull;
+  __syncthreads();
+  lds_bitonic<true>(sk, P);  // (key, -position) descending: the first K are the selection
+  int PK = 2;
+  while (PK < K) PK <<= 1;
+  for (int i = tid; i < PK; i += 1024) sp[i] = i < K ? ~(uint32_t)sk[i] : 0xffffffffu;
+  __syncthreads();
+  lds_bitonic<false>(sp, PK);
+  for (int i = tid; i < K; i += 1024) {
+    const uint32_t p = sp[i];
+    oi[i] = (int32_t)p;
+    if (ov) ov[i] = row[p] + 0.f;  // (+ 0: -0.0 comes out as +0.0, as from a key)
+  }
+}
+
+bool topk_long_rows(int max_n, int K) { return max_n > 32768 && K <= kLongCap / 2; }
+constexpr size_t kLongRowBytes = (size_t)kLongCap * 8 + 2048 * 4 + 16;
+
+// workspace of a launch over up to `rows` rows (any smaller launch fits in it too)
+size_t topk_ws_bytes(int rows, int max_n, int K) {
+  return topk_long_rows(max_n, K) ? (size_t)std::min(rows, kLongRows) * kLongRowBytes : 0;
+}
+
 hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
                        const float* scores, int64_t ld, int K, int32_t* idx, float* val,
-                       hipStream_t st) {
+                       void* ws, hipStream_t st) {
+  const uint32_t* only = nullptr;
+  if (t_count <= kLongRows && topk_long_rows(max_n, K)) {
+    // ws: candidates [t_count][kLongCap] | histograms [t_count][2048] | state [t_count][4]
+    uint64_t* cand = (uint64_t*)ws;
+    uint32_t* hist = (uint32_t*)(cand + (size_t)t_count * kLongCap);
+    uint32_t* state = hist + (size_t)t_count * 2048;
+    // slices of a multiple of 1024 positions, about 1024 workgroups in all
+    const int S = std::min((max_n + 8191) / 8192, std::max(1, 1024 / t_count));
+    const int slice = ((max_n + S - 1) / S + 1023) / 1024 * 1024;
+    const int nsl = (max_n + slice - 1) / slice;
+    hipLaunchKernelGGL(topk_long_zero_kernel, dim3(t_count), dim3(256), 0, st, hist, state);
+    hipLaunchKernelGGL(topk_long_hist_kernel, dim3(nsl, t_count), dim3(256), 0, st, bt, t_begin,
+                       scores, ld, K, slice, hist);
+    hipLaunchKernelGGL(topk_long_pick_kernel, dim3(t_count), dim3(1024), 0, st, bt, t_begin, K,
+                       hist, state);
+    hipLaunchKernelGGL(topk_long_gather_kernel, dim3(nsl, t_count), dim3(256), 0, st, bt,
+                       t_begin, scores, ld, slice, state, cand);
+    const size_t fshm = (size_t)kLongCap * 8 + (size_t)kLongCap / 2 * 4;
+    hipError_t e = hipFuncSetAttribute((const void*)topk_long_final_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)fshm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_long_final_kernel, dim3(t_count), dim3(1024), fshm, st, bt, t_begin,
+                       scores, ld, K, state, cand, idx, val);
+    only = state;  // the one-workgroup kernel below finishes the rows marked as overflowing
+  }
   // keys per thread: the smallest power of two (>= 4) that keeps the longest row in registers,
   // up to 32 (32768 positions); longer rows stream through 1024*32-key chunks per pass
   int npt = 4;
@@ -509,8 +737,8 @@ hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(t_count), dim3(1024), shm, st, bt, t_begin, scores, ld, K, idx,
-                     val);
+  hipLaunchKernelGGL(fn, dim3(t_count), dim3(1024), shm, st, bt, t_begin, scores, ld, K, only,
+                     idx, val);
   return hipGetLastError();
 }
 
