@@ -883,21 +883,21 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(int t_begin, int t_cou
   } else if (nsplit <= 8) {
     combine_splits<OUT_F32, 8>(nsplit, pr0, d0, part_o, part_ml, M, Lsum, LEsum, alo, ahi);
   } else {
-    for (int j = 0; j < nsplit; ++j) {
-      const float* m = part_ml + (pr0 + j * kH) * 4;
-      if (m[1] > 0.f) M = fmaxf(M, m[0]);
-    }
-    for (int j = 0; j < nsplit; ++j) {
-      const f32x4 ml = *(const f32x4*)(part_ml + (pr0 + j * kH) * 4);
-      if (!(ml[1] > 0.f)) continue;
-      const float wgt = exp2f(ml[0] - M);
-      Lsum = fmaf(wgt, ml[1], Lsum);
-      LEsum = fmaf(wgt, ml[2], LEsum);
-      f32x4 vlo, vhi;
-      load_part8<OUT_F32>(part_o, (pr0 + j * kH) * kDv + d0, vlo, vhi);
-      const float f = OUT_F32 ? wgt : wgt * ml[1];
-      alo += f * vlo;
-      ahi += f * vhi;
+    // eight splits at a time (their loads all in flight), each group merged into the running
+    // sums with the factors 2^(M - M') and 2^(Mc - M') of the new maximum M'
+    for (int j0 = 0; j0 < nsplit; j0 += 8) {
+      float Mc = -INFINITY, Lc = 0.f, LEc = 0.f;
+      f32x4 clo = {0.f, 0.f, 0.f, 0.f}, chi = {0.f, 0.f, 0.f, 0.f};
+      combine_splits<OUT_F32, 8>(min(8, nsplit - j0), pr0 + (int64_t)j0 * kH, d0, part_o,
+                                 part_ml, Mc, Lc, LEc, clo, chi);
+      const float Mn = fmaxf(M, Mc);
+      const float fa = M > -INFINITY ? exp2f(M - Mn) : 0.f;
+      const float fc = Mc > -INFINITY ? exp2f(Mc - Mn) : 0.f;
+      Lsum = Lsum * fa + Lc * fc;
+      LEsum = LEsum * fa + LEc * fc;
+      alo = alo * fa + clo * fc;
+      ahi = ahi * fa + chi * fc;
+      M = Mn;
     }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;

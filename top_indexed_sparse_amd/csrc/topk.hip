@@ -103,10 +103,11 @@ struct SelSmem {
   uint32_t candk[kCandMax];
 };
 
-// Long-row selection state per row, words [mode, bin, candidates, appended]
+// Long-row selection state per row, words [mode, bin, candidates, keys above the bin]
 constexpr uint32_t kLongCand = 0u, kLongAll = 1u, kLongOver = 2u;
-constexpr int kLongCap = 8192;     // candidates per row, sorted in LDS
-constexpr int kLongRows = 64;      // at most this many rows per launch take the long-row path
+constexpr int kLongCap = 8192;      // candidates per row (8 per thread of the last step)
+constexpr int kLongRows = 64;       // at most this many rows per launch take the long-row path
+constexpr int kLongSlices = 1024;   // slices per row at most
 
 // Radix select of the krem-th largest key among the keys produced by `each` (called with a
 // visitor), over r = key - base with digits of up to 11 bits from bit `hi` down.  Returns the
@@ -511,9 +512,11 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
 //      the row's histogram;
 //   2. one workgroup per row finds the bin b holding the k-th largest key: the keys in bins
 //      >= b (at least k of them) are the candidates;
-//   3. each slice appends its candidates (key, position) to the row's list;
-//   4. one workgroup per row sorts the list by (key descending, position ascending) in LDS,
-//      keeps the first k and sorts their positions ascending.
+//   3. each slice counts its candidates, then writes them (key, position) to the row's list
+//      at the offset of the slices before it, so the list is in position order;
+//   4. one workgroup per row holds the list in registers, radix-selects the threshold key T
+//      among the keys of the picked bin (the keys above it are all taken) and keeps the keys
+//      > T and the first ones == T, in list (= position) order.
 // Rows with n <= K take every position in step 4.  A row whose list would exceed kLongCap
 // (many equal or nearly equal scores) is marked in step 2 and selected afterwards by the
 // one-workgroup kernel, which skips every other row.  The result is the same selection.
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(256) void topk_long_hist_kernel(DevBatch bt, int t_
 __global__ __launch_bounds__(1024) void topk_long_pick_kernel(DevBatch bt, int t_begin, int K,
     const uint32_t* __restrict__ hist, uint32_t* __restrict__ state) {
   __shared__ uint32_t sh[48];
-  __shared__ uint32_t pick[2];
+  __shared__ uint32_t pick[3];
   const int tid = threadIdx.x, tl = blockIdx.x;
   const int n = locate(bt, t_begin + tl).n;
   uint32_t* st = state + 4 * tl;
@@ -577,74 +580,95 @@ __global__ __launch_bounds__(1024) void topk_long_pick_kernel(DevBatch bt, int t
   if (ch && above_h < k && k <= above_h + ch) {
     pick[0] = 2047 - 2 * tid;
     pick[1] = above_h + ch;
+    pick[2] = above_h;
   }
   if (cl && above_l < k && k <= above_l + cl) {
     pick[0] = 2046 - 2 * tid;
     pick[1] = above_l + cl;
+    pick[2] = above_l;
   }
   __syncthreads();
   if (tid == 0) {
     st[0] = pick[1] > (uint32_t)kLongCap ? kLongOver : kLongCand;
     st[1] = pick[0];
     st[2] = pick[1];
+    st[3] = pick[2];
   }
 }
 
-__global__ __launch_bounds__(256) void topk_long_gather_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int slice, uint32_t* __restrict__ state,
-    uint64_t* __restrict__ cand) {
-  const int tid = threadIdx.x, lane = tid & 63, tl = blockIdx.y;
-  uint32_t* st = state + 4 * tl;
+// keys of positions p .. p + 3 of a slice ending at p1 (key 0 past it)
+__device__ __forceinline__ void long_keys4(const float* row, int p, int p1, uint32_t key[4]) {
+  float v[4];
+  if (p + 3 < p1) {
+    const float4 f = *(const float4*)(row + p);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p + e < p1 ? row[p + e] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) key[e] = p + e < p1 ? order_key(v[e]) : 0u;
+}
+
+__global__ __launch_bounds__(256) void topk_long_count_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int slice, const uint32_t* __restrict__ state,
+    uint32_t* __restrict__ counts) {
+  __shared__ uint32_t c_sh;
+  const int tid = threadIdx.x, tl = blockIdx.y;
+  const uint32_t* st = state + 4 * tl;
   if (st[0] != kLongCand) return;
   const uint32_t thr = st[1] << 21;  // the candidates: keys in bins >= the picked one
   const int n = locate(bt, t_begin + tl).n;
   const float* row = scores + (int64_t)tl * ld;
-  uint64_t* out = cand + (int64_t)tl * kLongCap;
   const int p0 = blockIdx.x * slice, p1 = min(n, p0 + slice);
-  const uint64_t below = (1ull << lane) - 1ull;
+  if (tid == 0) c_sh = 0u;
+  __syncthreads();
+  uint32_t c = 0u;
   for (int p = p0 + 4 * tid; p < p1; p += 1024) {
-    float v[4];
-    if (p + 3 < p1) {
-      const float4 f = *(const float4*)(row + p);
-      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    } else {
+    uint32_t key[4];
+    long_keys4(row, p, p1, key);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = p + e < p1 ? row[p + e] : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = order_key(v[e]);
-      const bool take = p + e < p1 && key >= thr;
-      const uint64_t m = __ballot(take);
-      if (m) {  // (uniform over the wave)
-        uint32_t base = 0u;
-        if (lane == 0) base = atomicAdd(&st[3], (uint32_t)__popcll(m));
-        base = __builtin_amdgcn_readfirstlane(base);
-        const uint32_t o = base + (uint32_t)__popcll(m & below);
-        if (take && o < (uint32_t)kLongCap)
-          out[o] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)(p + e));
-      }
-    }
+    for (int e = 0; e < 4; ++e) c += key[e] >= thr && key[e] != 0u ? 1u : 0u;
   }
+  if (c) atomicAdd(&c_sh, c);
+  __syncthreads();
+  if (tid == 0) counts[(int64_t)tl * kLongSlices + blockIdx.x] = c_sh;
 }
 
-// Bitonic sort of v[0..P) (P a power of two) in LDS by 1024 threads; descending when DESC.
-template <bool DESC, typename V>
-__device__ __forceinline__ void lds_bitonic(V* v, int P) {
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < P / 2; i += 1024) {
-        const int lo = ((i & ~(stride - 1)) << 1) | (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool down = ((lo & size) == 0) == DESC;  // this pair's order: larger first
-        const V a = v[lo], b = v[hi];
-        if ((a < b) == down) {
-          v[lo] = b;
-          v[hi] = a;
-        }
+__global__ __launch_bounds__(1024) void topk_long_write_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int slice, const uint32_t* __restrict__ state,
+    const uint32_t* __restrict__ counts, uint64_t* __restrict__ cand) {
+  __shared__ uint32_t sh[48];
+  const int tid = threadIdx.x, tl = blockIdx.y, s = blockIdx.x;
+  const uint32_t* st = state + 4 * tl;
+  if (st[0] != kLongCand) return;  // (uniform over the workgroup)
+  const uint32_t thr = st[1] << 21;
+  const int n = locate(bt, t_begin + tl).n;
+  const float* row = scores + (int64_t)tl * ld;
+  uint64_t* out = cand + (int64_t)tl * kLongCap;
+  const int p0 = s * slice, p1 = min(n, p0 + slice);
+  // this slice's offset: the candidates of the slices before it (s < 1024 threads)
+  uint32_t base;
+  block_excl_scan(tid < s ? counts[(int64_t)tl * kLongSlices + tid] : 0u, sh, base);
+  const int iters = p1 > p0 ? (p1 - p0 + 4095) / 4096 : 0;
+  for (int it = 0; it < iters; ++it) {
+    const int p = p0 + 4096 * it + 4 * tid;
+    uint32_t key[4];
+    long_keys4(row, p, p1, key);
+    uint32_t c = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += key[e] >= thr && key[e] != 0u ? 1u : 0u;
+    __syncthreads();  // (sh of the previous scan has been read)
+    uint32_t tot;
+    uint32_t o = base + block_excl_scan(c, sh, tot);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (key[e] >= thr && key[e] != 0u) {
+        if (o < (uint32_t)kLongCap) out[o] = ((uint64_t)key[e] << 32) | (uint32_t)(p + e);
+        ++o;
       }
-      __syncthreads();
     }
+    base += tot;
   }
 }
 
@@ -653,8 +677,7 @@ __global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int 
     const uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx,
     float* __restrict__ out_val) {
   extern __shared__ __attribute__((aligned(16))) char smraw[];
-  uint64_t* sk = (uint64_t*)smraw;                    // [kLongCap] candidates
-  uint32_t* sp = (uint32_t*)(smraw + 8 * kLongCap);   // [pow2 >= K] selected positions
+  SelSmem& S = *(SelSmem*)smraw;
   const int tid = threadIdx.x, tl = blockIdx.x;
   const int t = t_begin + tl;
   const uint32_t* st = state + 4 * tl;
@@ -671,26 +694,51 @@ __global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int 
     }
     return;
   }
-  const int cnt = (int)min(st[3], (uint32_t)kLongCap);  // (= st[2] <= kLongCap)
-  int P = 2;
-  while (P < cnt) P <<= 1;
-  for (int i = tid; i < P; i += 1024) sk[i] = i < cnt ? cand[(int64_t)tl * kLongCap + i] : 0ull;
+  // the list, 8 consecutive entries per thread (position order); key 0 past its end
+  const uint32_t cnt = min(st[2], (uint32_t)kLongCap);
+  uint32_t key[8], pos[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t i = 8u * tid + j;
+    const uint64_t c = i < cnt ? cand[(int64_t)tl * kLongCap + i] : 0ull;
+    key[j] = (uint32_t)(c >> 32);
+    pos[j] = (uint32_t)c;
+  }
+  // the keys above the picked bin are all taken; the rest come from within it
+  uint32_t krem = (uint32_t)K - st[3];
+  const uint32_t T = radix_select(st[1] << 21, 21, krem, S, [&](auto&& f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (key[j] != 0u) f(key[j]);
+  });
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    gt += key[j] > T ? 1u : 0u;
+    eq += key[j] == T ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t er = block_excl_scan(eq, S.sh, tot);  // ties before this thread's
+  const uint32_t teq = er < krem ? min(eq, krem - er) : 0u;
   __syncthreads();
-  lds_bitonic<true>(sk, P);  // (key, -position) descending: the first K are the selection
-  int PK = 2;
-  while (PK < K) PK <<= 1;
-  for (int i = tid; i < PK; i += 1024) sp[i] = i < K ? ~(uint32_t)sk[i] : 0xffffffffu;
-  __syncthreads();
-  lds_bitonic<false>(sp, PK);
-  for (int i = tid; i < K; i += 1024) {
-    const uint32_t p = sp[i];
-    oi[i] = (int32_t)p;
-    if (ov) ov[i] = row[p] + 0.f;  // (+ 0: -0.0 comes out as +0.0, as from a key)
+  uint32_t o = block_excl_scan(gt + teq, S.sh, tot);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bool sel = key[j] > T;
+    if (key[j] == T) {
+      sel = er < krem;
+      ++er;
+    }
+    if (sel && o < (uint32_t)K) {  // (exactly K are selected; the bound keeps it in the row)
+      oi[o] = (int32_t)pos[j];
+      if (ov) ov[o] = row[pos[j]] + 0.f;  // (+ 0: -0.0 comes out as +0.0, as from a key)
+      ++o;
+    }
   }
 }
 
 bool topk_long_rows(int max_n, int K) { return max_n > 32768 && K <= kLongCap / 2; }
-constexpr size_t kLongRowBytes = (size_t)kLongCap * 8 + 2048 * 4 + 16;
+constexpr size_t kLongRowBytes = (size_t)kLongCap * 8 + 2048 * 4 + kLongSlices * 4 + 16;
 
 // workspace of a launch over up to `rows` rows (any smaller launch fits in it too)
 size_t topk_ws_bytes(int rows, int max_n, int K) {
@@ -702,22 +750,27 @@ hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
                        void* ws, hipStream_t st) {
   const uint32_t* only = nullptr;
   if (t_count <= kLongRows && topk_long_rows(max_n, K)) {
-    // ws: candidates [t_count][kLongCap] | histograms [t_count][2048] | state [t_count][4]
+    // ws: candidates [t_count][kLongCap] | histograms [t_count][2048] |
+    //     slice counts [t_count][kLongSlices] | state [t_count][4]
     uint64_t* cand = (uint64_t*)ws;
     uint32_t* hist = (uint32_t*)(cand + (size_t)t_count * kLongCap);
-    uint32_t* state = hist + (size_t)t_count * 2048;
-    // slices of a multiple of 1024 positions, about 1024 workgroups in all
-    const int S = std::min((max_n + 8191) / 8192, std::max(1, 1024 / t_count));
-    const int slice = ((max_n + S - 1) / S + 1023) / 1024 * 1024;
+    uint32_t* counts = hist + (size_t)t_count * 2048;
+    uint32_t* state = counts + (size_t)t_count * kLongSlices;
+    // slices of a multiple of 4096 positions, about 1024 workgroups in all (at most
+    // kLongSlices per row)
+    const int S = std::min((max_n + 8191) / 8192, std::max(1, kLongSlices / t_count));
+    const int slice = ((max_n + S - 1) / S + 4095) / 4096 * 4096;
     const int nsl = (max_n + slice - 1) / slice;
     hipLaunchKernelGGL(topk_long_zero_kernel, dim3(t_count), dim3(256), 0, st, hist, state);
     hipLaunchKernelGGL(topk_long_hist_kernel, dim3(nsl, t_count), dim3(256), 0, st, bt, t_begin,
                        scores, ld, K, slice, hist);
     hipLaunchKernelGGL(topk_long_pick_kernel, dim3(t_count), dim3(1024), 0, st, bt, t_begin, K,
                        hist, state);
-    hipLaunchKernelGGL(topk_long_gather_kernel, dim3(nsl, t_count), dim3(256), 0, st, bt,
-                       t_begin, scores, ld, slice, state, cand);
-    const size_t fshm = (size_t)kLongCap * 8 + (size_t)kLongCap / 2 * 4;
+    hipLaunchKernelGGL(topk_long_count_kernel, dim3(nsl, t_count), dim3(256), 0, st, bt,
+                       t_begin, scores, ld, slice, state, counts);
+    hipLaunchKernelGGL(topk_long_write_kernel, dim3(nsl, t_count), dim3(1024), 0, st, bt,
+                       t_begin, scores, ld, slice, state, counts, cand);
+    const size_t fshm = sizeof(SelSmem);
     hipError_t e = hipFuncSetAttribute((const void*)topk_long_final_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)fshm);
     if (e != hipSuccess) return e;
