@@ -6,6 +6,10 @@ One step = index_score_topk + sparse_mla_attn over one batch of the decode32k wo
 128 heads over a bf16 576-wide latent cache).  Inputs sit in HBM before timing; the timed
 steps rotate over several independent replicas of every input so that the 256 MB last-level
 cache cannot serve a step from the previous one.  Prints one JSON line.
+
+--workload tiny|prefill64k|decode1m|ragged measures another workload the same way (one
+input replica: their inputs dwarf the last-level cache) and prints its own line, without the
+oracle baseline; the default line is decode32k.
 """
 from __future__ import annotations
 
@@ -119,6 +123,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="decode32k",
+                    choices=["tiny", "decode32k", "prefill64k", "decode1m", "ragged"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (8 times) and exit: the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -146,8 +152,12 @@ def main():
     from synth.device import to_device
 
     torch.cuda.set_device(0)
-    wl = synth.workload(synth.DECODE32K)
+    main_line = args.workload == "decode32k"
+    wl = synth.workload(synth.NAMES.index(args.workload))
     sh = wl.shape
+    if not main_line:
+        args.replicas = 1
+        args.no_cpu_baseline = True
     t0 = time.perf_counter()
     inp = synth.make(wl, "continuous")
     log(f"generated {wl.name} in {time.perf_counter() - t0:.1f}s")
@@ -158,12 +168,13 @@ def main():
     bt = tis.Batch(inp.seq_lens, inp.cu_q, inp.page_table, inp.n_pages)
     T, K = inp.T, sh.K
     idx = [torch.empty((T, K), dtype=torch.int32, device="cuda") for _ in reps]
-    out = [torch.empty((T, sh.H, sh.D_v), dtype=torch.bfloat16, device="cuda") for _ in reps]
+    out_dt, out_code = (torch.float32, tis.TIS_F32) if sh.fp32 else (torch.bfloat16, tis.TIS_BF16)
+    out = [torch.empty((T, sh.H, sh.D_v), dtype=out_dt, device="cuda") for _ in reps]
     lse = [torch.empty((T, sh.H), dtype=torch.float32, device="cuda") for _ in reps]
     ws_i = torch.empty(tis.index_score_topk_workspace_size(bt, sh.H_I, sh.D_I, K),
                        dtype=torch.uint8, device="cuda")
-    ws_a = torch.empty(max(1, tis.sparse_mla_attn_workspace_size(bt, K, sh.H, sh.D_qk, sh.D_v,
-                                                                 tis.TIS_BF16)),
+    ws_a_bytes = tis.sparse_mla_attn_workspace_size(bt, K, sh.H, sh.D_qk, sh.D_v, out_code)
+    ws_a = torch.empty(max(1, ws_a_bytes),
                        dtype=torch.uint8, device="cuda")
 
     def step(i):
@@ -214,23 +225,45 @@ def main():
         for i in range(max(args.warmup, len(reps))):
             fn(i)
     a = algorithmic(inp)
+    kv = "f32" if sh.fp32 else ("fp8" if sh.kv_fp8 else "bf16")
     calls = {
         "index_score": dict(ms=timed(score, args.steps), bytes=a["idx_kernel_bytes"],
-                            kernels=["idx_score_fp8_kernel"]),
+                            flops=a["idx_flops"], peak=FP8_PEAK,
+                            kernels=["idx_score_f32_kernel" if sh.fp32 else "idx_score_fp8_kernel"]),
         "topk_select": dict(ms=timed(select, args.steps), bytes=a["topk_kernel_bytes"],
-                            kernels=["topk_lds_kernel"]),
+                            flops=0, peak=FP8_PEAK, kernels=["topk_select_kernel"]),
         "sparse_mla_attn": dict(ms=timed(attend, args.steps), bytes=a["attn_bytes"],
-                                kernels=["mla_attn_bf16_kernel", "mla_combine_kernel<false>"]),
+                                flops=a["attn_flops"], peak=BF16_PEAK,
+                                kernels=[f"mla_attn_{kv}_kernel"] + (
+                                    ["mla_combine_kernel"] if ws_a_bytes > 0 and not sh.fp32
+                                    else [])),
     }
     for c in calls.values():
         c["gbs"] = c["bytes"] / (c["ms"] * 1e-3) / 1e9
+        c["tflops"] = c["flops"] / (c["ms"] * 1e-3) / 1e12
+        # the roofline that binds: matrix throughput above the ridge point, HBM below it
+        c["mfma"] = c["flops"] / c["bytes"] > c["peak"] / (HBM_PEAK_GBS * 1e9)
     dom_name = max(calls, key=lambda k: calls[k]["ms"])
     dom = calls[dom_name]
     roof_s = t_roof(a)
+    decode = all(int(x) <= 1 for x in inp.q_lens)
+    if dom["mfma"]:
+        roofline = {"bound": "mfma", "entry_point": dom_name, "kernels": dom["kernels"],
+                    "achieved": dom["tflops"], "peak": dom["peak"] / 1e12, "unit": "TFLOP/s",
+                    "frac": dom["tflops"] * 1e12 / dom["peak"], "traffic": None,
+                    "launch_us": dom["ms"] * 1e3, "flops_per_launch": dom["flops"]}
+    else:
+        roofline = {"bound": "hbm", "entry_point": dom_name, "kernels": dom["kernels"],
+                    "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": dom["gbs"] / HBM_PEAK_GBS,
+                    "traffic": measured_traffic(dom_name) if main_line else None,
+                    "traffic_unit": "bytes/launch", "launch_us": dom["ms"] * 1e3,
+                    "bytes_per_launch": dom["bytes"]}
     res = {
-        "metric": "sparse-attn decode queries/s @32K ctx (index+topk+attn)",
+        "metric": ("sparse-attn decode queries/s @32K ctx (index+topk+attn)" if main_line else
+                   f"{wl.name} {'queries' if decode else 'tokens'}/s (index+topk+attn)"),
         "value": T * 1000.0 / step_ms,
-        "unit": "queries/s",
+        "unit": "queries/s" if decode else "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -238,21 +271,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8 indexer / bf16 attention, fp32 accumulate",
+        "dtype": ("fp32" if sh.fp32 else
+                  f"fp8 indexer / bf16 attention over a {kv} cache, fp32 accumulate"),
         "data": "synthetic",
-        "config": {"workload": "decode32k", "batch": T, "context": int(inp.seq_lens[0]),
-                   "new_tokens_per_request": 1, "indexer_heads": sh.H_I, "indexer_dim": sh.D_I,
-                   "topk": K, "heads": sh.H, "qk_dim": sh.D_qk, "v_dim": sh.D_v,
-                   "kv_cache": "bf16", "index_keys": "e4m3+fp32 scale/token",
-                   "input_replicas": len(reps)},
-        "roofline": {"bound": "hbm", "entry_point": dom_name, "kernels": dom["kernels"],
-                     "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dom["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(dom_name), "traffic_unit": "bytes/launch",
-                     "launch_us": dom["ms"] * 1e3, "bytes_per_launch": dom["bytes"]},
+        "config": ({"workload": "decode32k", "batch": T, "context": int(inp.seq_lens[0]),
+                    "new_tokens_per_request": 1, "indexer_heads": sh.H_I, "indexer_dim": sh.D_I,
+                    "topk": K, "heads": sh.H, "qk_dim": sh.D_qk, "v_dim": sh.D_v,
+                    "kv_cache": "bf16", "index_keys": "e4m3+fp32 scale/token",
+                    "input_replicas": len(reps)} if main_line else
+                   {"workload": wl.name, "requests": inp.B, "query_tokens": T,
+                    "max_context": int(inp.seq_lens.max()),
+                    "cached_tokens": int(inp.seq_lens.sum()), "indexer_heads": sh.H_I,
+                    "indexer_dim": sh.D_I, "topk": K, "heads": sh.H, "qk_dim": sh.D_qk,
+                    "v_dim": sh.D_v, "kv_cache": kv, "input_replicas": len(reps)}),
+        "roofline": roofline,
         "chain_roofline": {"t_roof_us": roof_s * 1e6, "t_step_us": step_ms * 1e3,
                            "frac": roof_s / (step_ms * 1e-3),
                            "attn_tflops": a["attn_flops"] / (calls["sparse_mla_attn"]["ms"] * 1e-3) / 1e12,
-                           "calls": {k: {"us": round(v["ms"] * 1e3, 2), "GB/s": round(v["gbs"], 1)}
+                           "calls": {k: {"us": round(v["ms"] * 1e3, 2), "GB/s": round(v["gbs"], 1),
+                                         "TFLOP/s": round(v["tflops"], 1)}
                                      for k, v in calls.items()}},
     }
     if not args.no_cpu_baseline:
