@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import synth
+from synth.device import to_device
 from oracle import Oracle
 from tests.gpu_path import (check_attention, check_scores, check_topk, note, run_path,
                             run_path_sampled, sample_tokens)
@@ -290,6 +291,59 @@ def test_topk_crafted_long_rows():
             k = int((ref >= 0).sum())
             assert np.array_equal(val[b, :k], S[b, ref[:k]]), (b, K)
             assert np.all(val[b, k:] == 0.0), (b, K)
+
+
+@pytest.mark.parametrize("lens", [[40000, 5000], [8000, 3000, 12000]])
+def test_graph_capture_replays(lens):
+    """The fused selection and the attention call captured in a HIP graph: every replay, with
+    eager calls and synchronisations in between, equals the eager result bit for bit (the path
+    allocates nothing and clears memory with kernels, not memsets).  [40000, 5000] takes the
+    several-workgroups-per-row selection."""
+    import top_indexed_sparse_amd as tis
+    wl = synth.reduced(synth.workload(synth.DECODE32K), lens, [1] * len(lens))
+    inp = synth.make(wl, "continuous")
+    note(f"case graph capture, lens {lens}")
+    sh, K, T = wl.shape, wl.shape.K, inp.T
+    d = to_device(inp)
+    bt = tis.Batch(inp.seq_lens, inp.cu_q, inp.page_table, inp.n_pages)
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    val = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, sh.H, sh.D_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, sh.H), dtype=torch.float32, device="cuda")
+    ws_i = torch.empty(max(1, tis.index_score_topk_workspace_size(bt, sh.H_I, sh.D_I, K)),
+                       dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(1, tis.sparse_mla_attn_workspace_size(bt, K, sh.H, sh.D_qk, sh.D_v,
+                                                                 tis.TIS_BF16)),
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        tis.index_score_topk(bt, d.q_idx, d.w, d.k_pool, d.k_scale, K, idx, val, ws=ws_i)
+        tis.sparse_mla_attn(bt, d.q, d.kv_pool, d.kv_scale, idx, sh.softmax_scale, out, lse,
+                            ws=ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (idx, val, out, lse)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        idx.fill_(-5)
+        val.zero_()
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip((idx, val, out, lse), ref):
+            assert torch.equal(x, y), f"replay {rep} differs"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
 
 
 def test_decode32k_full_size():
