@@ -923,11 +923,12 @@ int attn_keys_per_split(int K, int nsplit) {
 }
 
 int attn_split_count(int t_count, int K) {
-  // enough workgroups (2 head groups per token and split) to cover the 256 CUs, at least one
-  // stage of keys per split, at most kMaxKps; recomputed from the rounded split length so
-  // that no split is empty
+  // enough workgroups (2 head groups per token and split) to cover the 256 CUs, at least four
+  // stages of keys per split (a workgroup's prologue and epilogue cost about as much as four
+  // stages: shorter splits only add partials), at most kMaxKps; recomputed from the rounded
+  // split length so that no split is empty
   int s = (256 + 2 * t_count - 1) / (2 * t_count);
-  s = std::max(1, std::min(s, (K + kSR - 1) / kSR));
+  s = std::max(1, std::min(s, (K + 4 * kSR - 1) / (4 * kSR)));
   s = std::max(s, (K + kMaxKps - 1) / kMaxKps);
   const int kps = attn_keys_per_split(K, s);
   return (K + kps - 1) / kps;
