@@ -110,8 +110,9 @@ tis_status_t topk_select(const tis_batch_t* batch, const float* scores, int64_t 
                          size_t ws_bytes, void* stream);
 
 /* index_score_topk - index_score followed by topk_select with no score tensor owned by the
- * caller; identical results to the two calls.  ws: index_score_topk_workspace_size() bytes
- * (holds the scores that do not stay on chip). */
+ * caller; identical results to the two calls.  ws: index_score_topk_workspace_size() bytes,
+ * 16-byte aligned (the score rows of one chunk of tokens, then the selection's workspace as for
+ * topk_select over that chunk). */
 tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
                               const float* w, const void* k_pool, tis_dtype_t k_dt,
                               const float* k_scale, int32_t H_I, int32_t D_I,
