@@ -346,20 +346,22 @@ def test_graph_capture_replays(lens):
         torch.cuda.synchronize()
 
 
-def test_decode32k_full_size():
-    """The benchmarked workload itself: 32 x 32768, K = 2048, bf16 latent cache."""
-    inp = synth.make(synth.workload(synth.DECODE32K), "continuous")
-    note("case decode32k full size")
+@pytest.mark.parametrize("mode", ["continuous", "exact"])
+def test_decode32k_full_size(mode):
+    """The benchmarked workload itself: 32 x 32768, K = 2048, bf16 latent cache (exact mode:
+    integer scores, Top-K bit-exact)."""
+    inp = synth.make(synth.workload(synth.DECODE32K), mode)
+    note(f"case decode32k full size, {mode}")
     r = run_path(inp)
-    _common(inp, r, list(range(inp.T)), False)
+    _common(inp, r, list(range(inp.T)), mode == "exact")
 
 
-def _full_size(cfg, n_sample):
+def _full_size(cfg, n_sample, mode="continuous"):
     """A workload at its full size: every token through the fused and unfused chains and the
-    attention call; sampled tokens against the oracle."""
+    attention call; sampled tokens against the oracle (Top-K bit-exact in exact mode)."""
     wl = synth.workload(cfg)
-    note(f"case {wl.name} full size: generating inputs")
-    inp = synth.make(wl, "continuous")
+    note(f"case {wl.name} full size, {mode}: generating inputs")
+    inp = synth.make(wl, mode)
     tokens = sample_tokens(inp, n_sample)
     note(f"case {wl.name} full size: T={inp.T} B={inp.B} max L={int(inp.seq_lens.max())}, "
          f"{len(tokens)} sampled tokens; running")
@@ -372,18 +374,22 @@ def _full_size(cfg, n_sample):
         assert np.array_equal(r.val[t][: sel.size], r.scores[t, sel]), t
     orc = Oracle(inp)
     serr = check_scores(inp, orc, r.scores, tokens)
-    rec = check_topk(inp, orc, r.idx, tokens, False)
+    rec = check_topk(inp, orc, r.idx, tokens, mode == "exact")
     aerr = check_attention(inp, orc, r, tokens)
-    note(f"  {wl.name}: score rel err {serr:.2e}, recall {rec}, attn err {aerr[0]:.2e}, "
+    note(f"  {wl.name}/{mode}: score rel err {serr:.2e}, recall {rec}, attn err {aerr[0]:.2e}, "
          f"lse err {aerr[1]:.2e}")
     return inp, r, tokens
 
 
 @pytest.mark.timeout(900)
-def test_decode1m_full_size():
-    """4 x 1,048,576 context, e4m3 caches, planted blocks: every token checked."""
-    inp, r, tokens = _full_size(synth.DECODE1M, 4)
+@pytest.mark.parametrize("mode", ["continuous", "exact"])
+def test_decode1m_full_size(mode):
+    """4 x 1,048,576 context, e4m3 caches, planted blocks (continuous mode): every token
+    checked.  Exact mode: integer scores with heavy ties, selected bit-exact."""
+    inp, r, tokens = _full_size(synth.DECODE1M, 4, mode)
     assert tokens == list(range(inp.T))
+    if mode == "exact":
+        return
     for b in range(inp.B):
         off = inp.info["planted"][b]
         sel = r.idx[b][r.idx[b] >= 0]
