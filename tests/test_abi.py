@@ -78,9 +78,17 @@ def test_batch_validation():
         FakeBatch([100, 50], [0, 3, 2]),                     # decreasing cu_q
         FakeBatch([2], [0, 3]),                              # more queries than positions
         FakeBatch([1000], [0, 1], pt_stride=2),              # page table too narrow
+        FakeBatch([(1 << 28) + 1], [0, 1]),                  # longer than 2^28 positions
+        FakeBatch([1000], [0, 1], n_pages=(1 << 24) + 1),    # more than 2^24 pages
     ]
     for b in bad:
         assert call_index(b) == L.TIS_ERR_INVALID, last_error()
+    # the largest sizes themselves pass the batch check (seen through a size query, which
+    # launches nothing: 0 would mean a rejected batch)
+    big = FakeBatch([1 << 28], [0, 1], n_pages=1 << 24)
+    assert lib.topk_select_workspace_size(big.ref, 2048) > 0
+    for b in bad[-2:]:
+        assert lib.topk_select_workspace_size(b.ref, 2048) == 0
 
 
 def test_index_argument_validation():

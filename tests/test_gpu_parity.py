@@ -11,13 +11,16 @@ import torch
 import synth
 from synth.device import to_device
 from oracle import Oracle
-from tests.gpu_path import (check_attention, check_scores, check_topk, note, run_path,
+from tests.gpu_path import (attend, check_attention, check_scores, check_topk, note, run_path,
                             run_path_sampled, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
 
-def _common(inp, r, tokens, exact):
+def _common(inp, r, tokens, exact, also_bf16=False):
+    """Fused == unfused, emitted values, scores, Top-K and attention gates.  also_bf16: the
+    attention call is run again with a bf16 output (the benchmarked form for e4m3 caches)
+    and gated as well."""
     orc = Oracle(inp)
     # fused and unfused chains agree exactly
     assert np.array_equal(r.idx, r.idx2), "fused vs unfused Top-K"
@@ -31,6 +34,11 @@ def _common(inp, r, tokens, exact):
     aerr = check_attention(inp, orc, r, tokens)
     note(f"  {inp.wl.name}/{inp.mode}: score rel err {serr:.2e}, recall {rec}, "
          f"attn err {aerr[0]:.2e}, lse err {aerr[1]:.2e}")
+    if also_bf16 and not r.out_bf16:
+        rb = attend(inp, r, "bf16")
+        berr = check_attention(inp, orc, rb, tokens)
+        note(f"  {inp.wl.name}/{inp.mode}: bf16 output: attn err {berr[0]:.2e}, "
+             f"lse err {berr[1]:.2e}")
     return serr
 
 
@@ -76,15 +84,15 @@ def test_prefill_shapes_small(mode):
     note(f"case prefill-small mode={mode} T={inp.T}")
     r = run_path(inp)
     toks = sample_tokens(inp, 120)
-    _common(inp, r, toks, mode == "exact")
+    _common(inp, r, toks, mode == "exact", also_bf16=True)
 
 
 def test_decode1m_shapes_small():
     wl = synth.reduced(synth.workload(synth.DECODE1M), [70000, 40000], [1, 1])
     inp = synth.make(wl, "continuous")
-    note("case decode1m-small")
+    note("case decode1m-small (16 key splits per token)")
     r = run_path(inp)
-    _common(inp, r, list(range(inp.T)), False)
+    _common(inp, r, list(range(inp.T)), False, also_bf16=True)
     # the planted block dominates the selection
     for b in range(inp.B):
         off = inp.info["planted"][b]
@@ -94,14 +102,29 @@ def test_decode1m_shapes_small():
         assert frac > 0.5
 
 
-def test_ragged_small():
+@pytest.mark.parametrize("mode", ["continuous", "exact"])
+def test_ragged_small(mode):
     L = [1024, 3000, 700, 5000, 64, 2100]
     q = [1, 300, 1, 1, 64, 1]
     wl = synth.reduced(synth.workload(synth.RAGGED), L, q)
-    inp = synth.make(wl, "continuous")
-    note(f"case ragged-small T={inp.T}")
+    inp = synth.make(wl, mode)
+    note(f"case ragged-small mode={mode} T={inp.T}")
     r = run_path(inp)
-    _common(inp, r, sample_tokens(inp, 80), False)
+    _common(inp, r, sample_tokens(inp, 80), mode == "exact", also_bf16=True)
+
+
+@pytest.mark.parametrize("mode", ["continuous", "exact"])
+def test_decode_shapes_e4m3_cache(mode):
+    """decode32k shapes over an e4m3 latent cache: 32 tokens, so each token's keys are split
+    in four and merged (fp16 partials for a bf16 output, fp32 partials for an fp32 one)."""
+    import dataclasses
+    base = synth.workload(synth.DECODE32K)
+    L = [4096, 3000, 2500, 5000] * 8
+    wl = synth.reduced(base, L, [1] * 32, shape=dataclasses.replace(base.shape, kv_fp8=True))
+    inp = synth.make(wl, mode)
+    note(f"case decode-shapes e4m3 cache mode={mode} T={inp.T}")
+    r = run_path(inp)
+    _common(inp, r, list(range(inp.T)), mode == "exact", also_bf16=True)
 
 
 def test_many_requests_with_empty_ones():
@@ -358,26 +381,32 @@ def test_decode32k_full_size(mode):
 
 def _full_size(cfg, n_sample, mode="continuous"):
     """A workload at its full size: every token through the fused and unfused chains and the
-    attention call; sampled tokens against the oracle (Top-K bit-exact in exact mode)."""
-    wl = synth.workload(cfg)
+    attention call (e4m3 caches: with a bf16 output, the benchmarked form, and with an fp32
+    one); sampled tokens against the oracle (Top-K bit-exact in exact mode)."""
+    wl = synth.workload(cfg, mode)
     note(f"case {wl.name} full size, {mode}: generating inputs")
     inp = synth.make(wl, mode)
     tokens = sample_tokens(inp, n_sample)
     note(f"case {wl.name} full size: T={inp.T} B={inp.B} max L={int(inp.seq_lens.max())}, "
          f"{len(tokens)} sampled tokens; running")
-    r = run_path_sampled(inp, tokens)
+    outs = ["bf16", "f32"] if wl.shape.kv_fp8 else ["bf16"]
+    r = run_path_sampled(inp, tokens, outs)
     note(f"case {wl.name} full size: checking against the oracle")
     assert r.fused_equal, "fused vs unfused Top-K"
-    assert r.out_finite and r.lse_finite, "non-finite attention output"
+    for name, a in r.att.items():
+        assert a.out_finite and a.lse_finite, f"non-finite attention output ({name})"
     for t in tokens[:8]:
         sel = r.idx[t][r.idx[t] >= 0]
         assert np.array_equal(r.val[t][: sel.size], r.scores[t, sel]), t
     orc = Oracle(inp)
     serr = check_scores(inp, orc, r.scores, tokens)
     rec = check_topk(inp, orc, r.idx, tokens, mode == "exact")
-    aerr = check_attention(inp, orc, r, tokens)
-    note(f"  {wl.name}/{mode}: score rel err {serr:.2e}, recall {rec}, attn err {aerr[0]:.2e}, "
-         f"lse err {aerr[1]:.2e}")
+    for name, a in r.att.items():
+        aerr = check_attention(inp, orc, a, tokens)
+        note(f"  {wl.name}/{mode}: score rel err {serr:.2e}, recall {rec}, {name} output: "
+             f"attn err {aerr[0]:.2e}, lse err {aerr[1]:.2e}")
+    if mode == "exact":
+        assert serr == 0.0, "exact-mode scores must be exact"
     return inp, r, tokens
 
 
@@ -397,13 +426,41 @@ def test_decode1m_full_size(mode):
 
 
 @pytest.mark.timeout(900)
-def test_prefill64k_full_size():
-    """One 65,536-token causal prefill, e4m3 latent cache with heavy rows."""
-    _full_size(synth.PREFILL64K, 96)
+@pytest.mark.parametrize("mode", ["continuous", "exact"])
+def test_prefill64k_full_size(mode):
+    """One 65,536-token causal prefill, e4m3 latent cache with heavy rows (exact mode:
+    integer scores, Top-K bit-exact on the sampled tokens)."""
+    _full_size(synth.PREFILL64K, 96, mode)
 
 
 @pytest.mark.timeout(900)
-def test_ragged_full_size():
+@pytest.mark.parametrize("mode", ["continuous", "exact"])
+def test_ragged_full_size(mode):
     """64 requests of 1K..256K context, 48 decoding and 16 in a 4096-token prefill slice,
-    random page table over a poisoned pool."""
-    _full_size(synth.RAGGED, 96)
+    random page table over a poisoned pool (exact mode: Top-K bit-exact)."""
+    _full_size(synth.RAGGED, 96, mode)
+
+
+def test_tiny_query_heads():
+    """Query heads whose largest |q_I| is below 2^-119 get a power-of-two scale below 2^-127
+    (no reciprocal overflow: finite scores that match the oracle).  Token 0 has one such head,
+    token 1 has all 64; their values stay in bf16's normal range."""
+    from synth.gen import to_bf16_bits
+    wl = synth.reduced(synth.workload(synth.DECODE32K), [3000, 2500, 4096], [1, 1, 1])
+    inp = synth.make(wl, "continuous")
+    qf = (inp.q_idx.astype(np.uint32) << 16).view(np.float32).copy()
+    mag = np.float32(0.5) + np.abs(qf)                   # |q| >= 0.5 before scaling
+    tiny = np.sign(qf) * mag * np.float32(2.0 ** -123)
+    qf[0, 5] = tiny[0, 5]
+    qf[1] = tiny[1]
+    assert np.all(np.abs(qf[0, 5]) >= 2.0 ** -126) and np.all(np.abs(qf[1]) >= 2.0 ** -126)
+    inp.q_idx = to_bf16_bits(qf)
+    note("case tiny query heads")
+    r = run_path(inp)
+    assert np.all(np.isfinite(r.scores[0, :3000])) and np.all(np.isfinite(r.scores[1, :2500]))
+    orc = Oracle(inp)
+    serr = check_scores(inp, orc, r.scores, [0, 1, 2])
+    check_topk(inp, orc, r.idx, [0, 1, 2], False)
+    assert np.array_equal(r.idx, r.idx2)
+    note(f"  tiny query heads: score rel err {serr:.2e}")
+    assert serr < 1e-3

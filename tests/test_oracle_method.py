@@ -5,6 +5,7 @@ subtraction) fails at least one of them; ``test_pins_catch_planted_mistakes`` ch
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -53,6 +54,33 @@ def test_a0_quantize_bounds_and_exact_ints():
     qi = rng.integers(-3, 4, (20, 4, 32)).astype(np.float64)
     qh, s = a0_quantize(qi)
     assert np.array_equal(qh, qi)
+
+
+# ----------------------------------------------------------------------------- cache rows
+def _e4m3_page_case():
+    """The hand-worked e4m3 pages of tests/golden/e4m3_rows_handworked.json as raw arrays."""
+    g = json.load(open(os.path.join(GOLD, "e4m3_rows_handworked.json")))
+    P, page, D = g["n_pages"], g["page_size"], g["dim"]
+    pool = np.full((P, page, D), g["fill"]["code"], dtype=np.uint8)
+    scale = np.full((P, page), g["fill"]["scale"], dtype=np.float32)
+    for e in g["slots"]:
+        pool.reshape(-1, D)[e["slot"]] = e["codes"]
+        if "scale_bits" in e:
+            sc = np.array([int(e["scale_bits"], 16)], np.uint32).view(np.float32)[0]
+        else:
+            sc = np.float32(e["scale"])
+        scale.reshape(-1)[e["slot"]] = sc
+    exp = np.array([[float(Fraction(v)) for v in row] for row in g["expected_exact"]])
+    assert np.array_equal(exp, np.array(g["expected"]))
+    return pool, scale, np.array(g["page_table"]), np.array(g["positions"]), exp
+
+
+def test_e4m3_rows_handworked():
+    """decode_rows on e4m3 pages: code times the slot's own scale (non-unit, non-dyadic),
+    through a page table that is not the identity."""
+    pool, scale, pt, pos, exp = _e4m3_page_case()
+    got = decode_rows(pool, scale, pt, pos, "e4m3")
+    assert np.array_equal(got, exp)
 
 
 # ----------------------------------------------------------------------------- scores / topk
@@ -250,3 +278,17 @@ def test_pins_catch_planted_mistakes():
     for f in (no_scale, v_from_tail):
         o, _ = f(q2, rows, 0.4, 4)
         assert not np.allclose(o, o_ref)
+    # e4m3 rows: the scale dropped, applied twice, taken from the position instead of the
+    # slot, or the page table ignored
+    from oracle.codecs import e4m3_decode
+    pool, scale, pt, pos, exp = _e4m3_page_case()
+    flat, sflat = pool.reshape(-1, pool.shape[-1]), scale.reshape(-1).astype(np.float64)
+    slot = pt[pos // 64] * 64 + pos % 64
+    wrong_rows = [
+        e4m3_decode(flat[slot]),
+        e4m3_decode(flat[slot]) * (sflat[slot] ** 2)[:, None],
+        e4m3_decode(flat[slot]) * sflat[pos][:, None],
+        e4m3_decode(flat[pos]) * sflat[pos][:, None],
+    ]
+    for rows_bad in wrong_rows:
+        assert not np.array_equal(rows_bad, exp)

@@ -33,6 +33,12 @@ tis_status_t hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Size limits that keep every position, slot and byte offset the kernels form in 32-bit
+// arithmetic in range: a score row of kMaxSeqLen fp32 values spans 2^30 bytes, and a slot
+// (page * 64 + offset) stays below 2^30.
+constexpr int kMaxSeqLen = 1 << 28;
+constexpr int kMaxPages = 1 << 24;
+
 // Scores that do not stay on chip go to a workspace of at most this many bytes; longer
 // batches are processed in row chunks.
 constexpr size_t kScoreScratchBudget = size_t(1) << 30;
@@ -52,6 +58,8 @@ tis_status_t check_batch(const tis_batch_t* b, HostInfo* hi) {
     return fail(TIS_ERR_INVALID, "page_size must be %d (got %d)", TIS_PAGE_SIZE, b->page_size);
   if (b->pt_stride < 1 || b->n_pages < 1)
     return fail(TIS_ERR_INVALID, "pt_stride and n_pages must be >= 1");
+  if (b->n_pages > kMaxPages)
+    return fail(TIS_ERR_INVALID, "n_pages must be <= %d (got %d)", kMaxPages, b->n_pages);
   if (b->cu_q_host[0] != 0) return fail(TIS_ERR_INVALID, "cu_q[0] must be 0");
   if (b->cu_q_host[b->B] != b->T) return fail(TIS_ERR_INVALID, "cu_q[B] must equal T");
   HostInfo h;
@@ -62,7 +70,8 @@ tis_status_t check_batch(const tis_batch_t* b, HostInfo* hi) {
     if (L < q) return fail(TIS_ERR_INVALID, "seq_lens[%d]=%d < its %d query tokens", r, L, q);
     if ((int64_t)L > (int64_t)b->pt_stride * TIS_PAGE_SIZE)
       return fail(TIS_ERR_INVALID, "seq_lens[%d]=%d exceeds pt_stride*64", r, L);
-    if (L > (1 << 30)) return fail(TIS_ERR_INVALID, "seq_lens[%d] too large", r);
+    if (L > kMaxSeqLen)
+      return fail(TIS_ERR_INVALID, "seq_lens[%d]=%d exceeds %d", r, L, kMaxSeqLen);
     if (q > 0) h.max_n = std::max(h.max_n, L);
     h.max_q = std::max(h.max_q, q);
   }

@@ -106,20 +106,21 @@ __device__ __forceinline__ void a0_tile(const i32x4 (&r)[4], const float (&wr)[4
     float mant = frexpf(amax, &E);
     int e = (mant <= 0.875f) ? E - 9 : E - 8;
     if (amax == 0.f) e = 0;
-    const float s_q = ldexpf(1.f, e);
-    const float inv_s = ldexpf(1.f, -e);
+    // q / 2^e by exponent adjustment (exact: the quotient is at most 448); a reciprocal scale
+    // would overflow to inf for heads with max |q| below about 2^-118
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int word = 0;
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * j] * inv_s, v[4 * j + 1] * inv_s, word,
-                                             false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * j + 2] * inv_s, v[4 * j + 3] * inv_s, word,
-                                             true);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * j], -e), ldexpf(v[4 * j + 1], -e),
+                                             word, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * j + 2], -e), ldexpf(v[4 * j + 3], -e),
+                                             word, true);
       A[j] = word;
     }
-    // w'[16m + 4g + i]: the scale of head 16m + r lives in lane r (any g)
+    // w'[16m + 4g + i] = w * 2^e: the exponent of head 16m + r lives in lane r (any g); for
+    // such tiny heads w' is subnormal (gradual underflow, never inf or NaN)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wp[i] = wr[i] * __shfl(s_q, 4 * g + i);
+    for (int i = 0; i < 4; ++i) wp[i] = ldexpf(wr[i], __shfl(e, 4 * g + i));
   }
 }
 
