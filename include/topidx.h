@@ -119,6 +119,21 @@ tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx, tis_d
                               tis_qmode_t qmode, int32_t K, int32_t* topk_idx,
                               float* topk_val, void* ws, size_t ws_bytes, void* stream);
 
+/* index_score_topk_noalloc - index_score_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * same arguments and results as index_score_topk without ws/ws_bytes: the workspace is a
+ * 64 MiB scratch array that the library holds on each device until the process ends (its
+ * address is looked up on the first call on a device; no call allocates or frees anything).
+ * The score rows of one chunk of tokens must fit it: a batch whose longest causal range exceeds
+ * about 15.5M positions returns TIS_ERR_INVALID before anything is enqueued.  Every call on a
+ * device shares that device's scratch, so calls that overlap on one device (on other streams
+ * or threads) race; calls ordered on one stream do not. */
+tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const void* q_idx,
+                                      tis_dtype_t q_dt, const float* w, const void* k_pool,
+                                      tis_dtype_t k_dt, const float* k_scale, int32_t H_I,
+                                      int32_t D_I, tis_qmode_t qmode, int32_t K,
+                                      int32_t* topk_idx, float* topk_val, void* stream);
+
 /* sparse_mla_attn - exact attention of each token over its selected latent rows.
  *   For token t, head h and each valid entry s of topk_idx[t] (0 <= s < seq_lens[b]; other
  *   entries, e.g. -1 padding, are skipped; duplicates count as given; causality is not

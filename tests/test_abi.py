@@ -141,3 +141,16 @@ def test_attention_argument_validation():
         assert call_attn(b, ws=D, wsb=need - 16) == L.TIS_ERR_INVALID
     # tiny fp32 path needs no workspace
     assert tis.lib().sparse_mla_attn_workspace_size(b.ref, 64, 8, 80, 64, L.TIS_F32) == 0
+
+
+def test_noalloc_rejects_rows_beyond_its_scratch():
+    """index_score_topk_noalloc holds a 64 MiB scratch per device: a batch whose score row
+    does not fit is rejected on the host, before the scratch is looked up or anything runs."""
+    lib = tis.lib()
+    b = FakeBatch([20_000_000], [0, 1])
+    st = lib.index_score_topk_noalloc(b.ref, D, L.TIS_BF16, D, D, L.TIS_E4M3, D, 64, 128,
+                                      L.TIS_QMODE_FP8, 2048, D, None, None)
+    assert st == L.TIS_ERR_INVALID and "scratch" in last_error()
+    # argument errors come first, as for index_score_topk
+    assert lib.index_score_topk_noalloc(b.ref, D, L.TIS_BF16, D, D, L.TIS_E4M3, D, 64, 128,
+                                        L.TIS_QMODE_FP8, 0, D, None, None) == L.TIS_ERR_INVALID

@@ -17,7 +17,8 @@ TIS_F32, TIS_BF16, TIS_E4M3 = 0, 1, 2
 TIS_QMODE_FP8, TIS_QMODE_NONE = 0, 1
 PAGE_SIZE = 64
 
-EXPORTS = ("index_score", "topk_select", "index_score_topk", "sparse_mla_attn",
+EXPORTS = ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
+           "sparse_mla_attn",
            "index_score_workspace_size", "topk_select_workspace_size",
            "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size",
            "tis_last_error", "tis_abi_version")
@@ -62,9 +63,12 @@ def lib():
     L.topk_select.argtypes = [_BP, _P, _I64, _I32, _P, _P, _P, _SZ, _P]
     L.index_score_topk.argtypes = [_BP, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P,
                                    _P, _P, _SZ, _P]
+    L.index_score_topk_noalloc.argtypes = [_BP, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32,
+                                           _I32, _P, _P, _P]
     L.sparse_mla_attn.argtypes = [_BP, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F,
                                   _P, _I32, _P, _P, _SZ, _P]
-    for f in ("index_score", "topk_select", "index_score_topk", "sparse_mla_attn"):
+    for f in ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
+              "sparse_mla_attn"):
         getattr(L, f).restype = _I32
     L.index_score_workspace_size.argtypes = [_BP, _I32, _I32]
     L.topk_select_workspace_size.argtypes = [_BP, _I32]
@@ -182,6 +186,19 @@ def index_score_topk(batch: Batch, q_idx, w, k_pool, k_scale, K: int, topk_idx, 
     _check(lib().index_score_topk(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_pool),
                                   _dtype(k_pool), _ptr(k_scale), H_I, D_I, qmode, int(K),
                                   _ptr(topk_idx), _ptr(topk_val), _ptr(ws), nb, _stream()))
+    return topk_idx
+
+
+def index_score_topk_noalloc(batch: Batch, q_idx, w, k_pool, k_scale, K: int, topk_idx,
+                             topk_val=None, qmode=None):
+    """index_score_topk with the library's own per-device scratch (allocates nothing)."""
+    H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    if qmode is None:
+        qmode = TIS_QMODE_NONE if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
+    _check(lib().index_score_topk_noalloc(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w),
+                                          _ptr(k_pool), _dtype(k_pool), _ptr(k_scale), H_I, D_I,
+                                          qmode, int(K), _ptr(topk_idx), _ptr(topk_val),
+                                          _stream()))
     return topk_idx
 
 

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -142,11 +143,12 @@ size_t fused_scores_bytes(int rows, const HostInfo& hi) {
   return ((size_t)rows * (size_t)round4(hi.max_n) * sizeof(float) + 255) & ~(size_t)255;
 }
 
-int fused_rows_per_chunk(const tis_batch_t* b, const HostInfo& hi) {
+// score rows per chunk under a byte budget for the score rows (0 if one row does not fit)
+int fused_rows_per_chunk(const tis_batch_t* b, const HostInfo& hi,
+                         size_t budget = kScoreScratchBudget) {
   const int64_t row_bytes = round4(hi.max_n) * 4;
-  int64_t r = (int64_t)kScoreScratchBudget / std::max<int64_t>(row_bytes, 1);
-  r = std::max<int64_t>(1, std::min<int64_t>(r, b->T));
-  return (int)r;
+  int64_t r = (int64_t)budget / std::max<int64_t>(row_bytes, 1);
+  return (int)std::min<int64_t>(r, b->T);
 }
 
 enum class AttnPath { F32, MFMA };
@@ -213,7 +215,7 @@ TIS_API size_t index_score_topk_workspace_size(const tis_batch_t* batch, int32_t
   (void)H_I; (void)D_I;
   HostInfo hi;
   if (check_batch(batch, &hi) != TIS_OK || K < 1) return 0;
-  const int rows = fused_rows_per_chunk(batch, hi);
+  const int rows = std::max(1, fused_rows_per_chunk(batch, hi));
   return fused_scores_bytes(rows, hi) + tis::topk_ws_bytes(rows, hi.max_n, K);
 }
 
@@ -263,6 +265,75 @@ TIS_API tis_status_t topk_select(const tis_batch_t* batch, const float* scores,
   return e == hipSuccess ? TIS_OK : hip_fail(e, "topk_select launch");
 }
 
+namespace {
+
+// The fused chain over `rows`-token chunks with its workspace at ws (score rows, then the
+// selection's workspace); the arguments have been checked.
+tis_status_t fused_run(const tis_batch_t* batch, const HostInfo& hi, IdxPath path,
+                       const void* q_idx, const float* w, const void* k_pool,
+                       const float* k_scale, int32_t H_I, int32_t D_I, int32_t K,
+                       int32_t* topk_idx, float* topk_val, int rows, void* ws, hipStream_t s) {
+  const int64_t ld = round4(hi.max_n);
+  const size_t sbytes = fused_scores_bytes(rows, hi);
+  float* sc = (float*)ws;
+  void* tws = (char*)ws + sbytes;
+  const tis::DevBatch d = dev_batch(batch);
+  for (int t0 = 0; t0 < batch->T; t0 += rows) {
+    const int tc = std::min(rows, batch->T - t0);
+    tis_status_t st =
+        run_index(batch, hi, path, t0, tc, q_idx, w, k_pool, k_scale, H_I, D_I, sc, ld, s);
+    if (st != TIS_OK) return st;
+    hipError_t e = tis::launch_topk(d, t0, tc, hi.max_n, sc, ld, K, topk_idx, topk_val, tws, s);
+    if (e != hipSuccess) return hip_fail(e, "index_score_topk select launch");
+  }
+  return TIS_OK;
+}
+
+tis_status_t fused_checks(const tis_batch_t* batch, HostInfo* hi, const void* q_idx,
+                          tis_dtype_t q_dt, const float* w, const void* k_pool,
+                          tis_dtype_t k_dt, const float* k_scale, int32_t H_I, int32_t D_I,
+                          tis_qmode_t qmode, int32_t K, const int32_t* topk_idx,
+                          IdxPath* path) {
+  tis_status_t st = check_batch(batch, hi);
+  if (st != TIS_OK) return st;
+  st = check_index_args(q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I, qmode, path);
+  if (st != TIS_OK) return st;
+  if (K < 1) return fail(TIS_ERR_INVALID, "K must be >= 1");
+  if (!topk_idx) return fail(TIS_ERR_INVALID, "topk_idx must be set");
+  return TIS_OK;
+}
+
+// ---- the allocation-free variant's scratch: one array per device, held until the process
+// ends.  Host code never passes the array's name to a kernel (in host code it only stands in
+// for the symbol): its device address is looked up once per device and used instead.
+constexpr size_t kNoAllocScratch = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device (or null)
+
+tis_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TIS_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(TIS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TIS_OK;
+}
+
+}  // namespace
+
 TIS_API tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx,
                                       tis_dtype_t q_dt, const float* w, const void* k_pool,
                                       tis_dtype_t k_dt, const float* k_scale, int32_t H_I,
@@ -270,31 +341,46 @@ TIS_API tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_id
                                       int32_t* topk_idx, float* topk_val, void* ws,
                                       size_t ws_bytes, void* stream) {
   HostInfo hi;
-  tis_status_t st = check_batch(batch, &hi);
-  if (st != TIS_OK) return st;
   IdxPath path;
-  st = check_index_args(q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I, qmode, &path);
+  tis_status_t st = fused_checks(batch, &hi, q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I,
+                                 qmode, K, topk_idx, &path);
   if (st != TIS_OK) return st;
-  if (K < 1) return fail(TIS_ERR_INVALID, "K must be >= 1");
-  if (!topk_idx) return fail(TIS_ERR_INVALID, "topk_idx must be set");
-  const int rows = fused_rows_per_chunk(batch, hi);
-  const int64_t ld = round4(hi.max_n);
-  const size_t sbytes = fused_scores_bytes(rows, hi);
-  const size_t need = sbytes + tis::topk_ws_bytes(rows, hi.max_n, K);
+  const int rows = std::max(1, fused_rows_per_chunk(batch, hi));
+  const size_t need = fused_scores_bytes(rows, hi) + tis::topk_ws_bytes(rows, hi.max_n, K);
   if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
     return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
-  hipStream_t s = (hipStream_t)stream;
-  float* sc = (float*)ws;
-  void* tws = (char*)ws + sbytes;
-  const tis::DevBatch d = dev_batch(batch);
-  for (int t0 = 0; t0 < batch->T; t0 += rows) {
-    const int tc = std::min(rows, batch->T - t0);
-    st = run_index(batch, hi, path, t0, tc, q_idx, w, k_pool, k_scale, H_I, D_I, sc, ld, s);
-    if (st != TIS_OK) return st;
-    hipError_t e = tis::launch_topk(d, t0, tc, hi.max_n, sc, ld, K, topk_idx, topk_val, tws, s);
-    if (e != hipSuccess) return hip_fail(e, "index_score_topk select launch");
-  }
-  return TIS_OK;
+  return fused_run(batch, hi, path, q_idx, w, k_pool, k_scale, H_I, D_I, K, topk_idx, topk_val,
+                   rows, ws, (hipStream_t)stream);
+}
+
+TIS_API tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const void* q_idx,
+                                              tis_dtype_t q_dt, const float* w,
+                                              const void* k_pool, tis_dtype_t k_dt,
+                                              const float* k_scale, int32_t H_I, int32_t D_I,
+                                              tis_qmode_t qmode, int32_t K, int32_t* topk_idx,
+                                              float* topk_val, void* stream) {
+  HostInfo hi;
+  IdxPath path;
+  tis_status_t st = fused_checks(batch, &hi, q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I,
+                                 qmode, K, topk_idx, &path);
+  if (st != TIS_OK) return st;
+  // the selection's workspace is bounded by its 64-row limit; the rest holds score rows
+  const size_t sel = tis::topk_ws_bytes(64, hi.max_n, K);
+  const int rows = fused_rows_per_chunk(batch, hi, kNoAllocScratch - sel - 256);
+  if (rows < 1)
+    return fail(TIS_ERR_INVALID,
+                "index_score_topk_noalloc: a score row of %d positions does not fit its %zu-byte "
+                "scratch (at most %zu positions)", hi.max_n, kNoAllocScratch,
+                (kNoAllocScratch - sel - 256) / 4);
+  const size_t need = fused_scores_bytes(rows, hi) + tis::topk_ws_bytes(rows, hi.max_n, K);
+  if (need > kNoAllocScratch)
+    return fail(TIS_ERR_INVALID, "index_score_topk_noalloc: needs %zu bytes of scratch, has %zu",
+                need, kNoAllocScratch);
+  void* ptr = nullptr;
+  st = scratch_address(&ptr);
+  if (st != TIS_OK) return st;
+  return fused_run(batch, hi, path, q_idx, w, k_pool, k_scale, H_I, D_I, K, topk_idx, topk_val,
+                   rows, ptr, (hipStream_t)stream);
 }
 
 TIS_API tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_t q_dt,
