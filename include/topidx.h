@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define TIS_ABI_VERSION 1
+#define TIS_ABI_VERSION 2
 #define TIS_PAGE_SIZE 64
 
 typedef enum {
@@ -56,13 +56,22 @@ typedef enum {
 
 typedef enum { TIS_F32 = 0, TIS_BF16 = 1, TIS_E4M3 = 2 /* OCP E4M3FN */ } tis_dtype_t;
 
-/* Indexer query handling: FP8 = quantise each (token, head) row of q_I to e4m3 with the
- * smallest power-of-two scale s that keeps max|q_I|/s <= 448 (round to nearest even), fold s
- * into the head weight, and score on FP8 matrix cores; NONE = use q_I as stored (fp32 path). */
-typedef enum { TIS_QMODE_FP8 = 0, TIS_QMODE_NONE = 1 } tis_qmode_t;
+/* Indexer query handling ("Day 0 Support for New LLM Architectures", Key Optimization 1: a
+ * BF16 and a quantised implementation are kept side by side; Key Optimization 2: the indexer
+ * query is quantised dynamically to FP8):
+ *   TIS_QMODE_FP8  - quantise each (token, head) row of q_I to e4m3 with the smallest
+ *                    power-of-two scale s that keeps max|q_I|/s <= 448 (round to nearest
+ *                    even), fold s into the head weight, and score on FP8 matrix cores;
+ *   TIS_QMODE_BF16 - use q_I as stored: bf16 queries are multiplied on bf16 matrix cores with
+ *                    the e4m3 keys widened to bf16 (exactly: every e4m3 value is a bf16
+ *                    value); fp32 queries with fp32 keys use the fp32 kernel. */
+typedef enum { TIS_QMODE_FP8 = 0, TIS_QMODE_BF16 = 1 } tis_qmode_t;
 
-/* A ragged, paged batch.  Host copies of seq_lens and cu_q size the launch grids without a
- * device round trip; they must equal the device copies. */
+/* A ragged, paged batch ("Achieving Day-0 Readiness ... Million-Token Context", section 2.2:
+ * the cache is cut into fixed-size blocks located through a block index table; "Day-0
+ * Support for Large Model Inference", Core Operator Optimization item 2: requests of
+ * different lengths share one launch).  Host copies of seq_lens and cu_q size the launch
+ * grids without a device round trip; they must equal the device copies. */
 typedef struct {
   int32_t B;                     /* requests, >= 1 */
   int32_t T;                     /* flattened query tokens = cu_q[B], >= 1 */
@@ -76,12 +85,14 @@ typedef struct {
   int32_t n_pages;               /* pages in each pool (bounds page-table entries) */
 } tis_batch_t;
 
-/* index_score - indexer scores of every causal candidate.
+/* index_score - indexer scores of every causal candidate ("Day 0 Support for New LLM
+ * Architectures", Step 1: the light indexer scores each earlier position; Key Optimization 1:
+ * relevance scores and head weights computed reading the paged K cache directly).
  *   score[t][s] = sum_h w[t][h] * max(0, q_I[t][h] . k_I[s]) for s in [0, p_t], where
  *   k_I[s] = k_code[s] * k_scale[s] (e4m3 keys) or the fp32 key.  With TIS_QMODE_FP8 the
  *   query is first quantised as described at tis_qmode_t.  Accumulation is fp32.
- * q_idx   [T][H_I][D_I]  q_dt = TIS_BF16 (with k_dt = TIS_E4M3, qmode FP8; H_I = 64,
- *                        D_I = 128) or TIS_F32 (with k_dt = TIS_F32, qmode NONE;
+ * q_idx   [T][H_I][D_I]  q_dt = TIS_BF16 (with k_dt = TIS_E4M3, qmode FP8 or BF16;
+ *                        H_I = 64, D_I = 128) or TIS_F32 (with k_dt = TIS_F32, qmode BF16;
  *                        H_I * D_I <= 8192)
  * w       [T][H_I] fp32 head weights
  * k_pool  [n_pages][64][D_I]; k_scale [n_pages][64] fp32 (e4m3 keys) or NULL (fp32 keys)
@@ -95,7 +106,10 @@ tis_status_t index_score(const tis_batch_t* batch, const void* q_idx, tis_dtype_
                          float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
                          void* stream);
 
-/* topk_select - per-token Top-K over the scores of positions 0..p_t.
+/* topk_select - per-token Top-K over the scores of positions 0..p_t ("Day 0 Support for New
+ * LLM Architectures", Step 1 and Key Optimization 1: the Top-K positions of the relevance
+ * scores are kept; "Achieving Day-0 Readiness ... Million-Token Context", section 2.1:
+ * selection is an operator of its own on the device, the index never leaving it).
  *   Selects the k_t = min(K, p_t + 1) positions that are largest under the total order
  *   (score descending, position ascending); -0.0 and +0.0 are equal.  Scores must not be NaN.
  * topk_idx [T][K] int32: the selected positions in ascending order, then -1 up to K.
@@ -110,7 +124,8 @@ tis_status_t topk_select(const tis_batch_t* batch, const float* scores, int64_t 
                          size_t ws_bytes, void* stream);
 
 /* index_score_topk - index_score followed by topk_select with no score tensor owned by the
- * caller; identical results to the two calls.  ws: index_score_topk_workspace_size() bytes,
+ * caller; identical results to the two calls ("Day 0 Support for New LLM Architectures", Key
+ * Optimization 1: scoring, head weighting and Top-K fused into one kernel chain).  ws: index_score_topk_workspace_size() bytes,
  * 16-byte aligned (the score rows of one chunk of tokens, then the selection's workspace as for
  * topk_select over that chunk). */
 tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
@@ -134,7 +149,11 @@ tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const void* q_id
                                       int32_t D_I, tis_qmode_t qmode, int32_t K,
                                       int32_t* topk_idx, float* topk_val, void* stream);
 
-/* sparse_mla_attn - exact attention of each token over its selected latent rows.
+/* sparse_mla_attn - exact attention of each token over its selected latent rows ("Day 0
+ * Support for New LLM Architectures", Step 1: the sparse-attention kernel reads only the
+ * selected entries of the low-rank KV cache and computes exact attention over them; "Day-0
+ * Support for Large Model Inference", Core Operator Optimization item 2: the scattered rows
+ * are gathered and attention is computed blockwise with the normalisation fused in).
  *   For token t, head h and each valid entry s of topk_idx[t] (0 <= s < seq_lens[b]; other
  *   entries, e.g. -1 padding, are skipped; duplicates count as given; causality is not
  *   checked):  c_s = kv_code[s] * kv_scale[s] (e4m3) or the stored row,
@@ -157,7 +176,11 @@ tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_
                              int32_t D_v, float softmax_scale, void* out, tis_dtype_t out_dt,
                              float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace sizes in bytes for the calls above, from the host fields of `batch` only. */
+/* Workspace sizes in bytes for the calls above, from the host fields of `batch` only (the
+ * caller owns every buffer).  index_score needs none and returns 0.  topk_select: nonzero only
+ * for the several-workgroups-per-row selection (see topk_select).  index_score_topk: one chunk
+ * of score rows plus that selection's workspace.  sparse_mla_attn: the split partials, nonzero
+ * when a token's keys are split across workgroups. */
 size_t index_score_workspace_size(const tis_batch_t* batch, int32_t H_I, int32_t D_I);
 size_t topk_select_workspace_size(const tis_batch_t* batch, int32_t K);
 size_t index_score_topk_workspace_size(const tis_batch_t* batch, int32_t H_I, int32_t D_I,

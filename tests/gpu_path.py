@@ -33,8 +33,9 @@ def _out_dtype(sh, out):
 
 
 def run_path(inp, unfused: bool = True, K: int | None = None, out: str | None = None,
-             out_f32: bool = False) -> SimpleNamespace:
-    """Fused index_score_topk + sparse_mla_attn (and optionally the unfused chain)."""
+             out_f32: bool = False, qmode: int | None = None) -> SimpleNamespace:
+    """Fused index_score_topk + sparse_mla_attn (and optionally the unfused chain); qmode is
+    the indexer's query mode (default: FP8 for bf16 queries, as stored for fp32 ones)."""
     sh = inp.wl.shape
     K = sh.K if K is None else K
     d = to_device(inp)
@@ -43,11 +44,11 @@ def run_path(inp, unfused: bool = True, K: int | None = None, out: str | None = 
     r = SimpleNamespace()
     idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
     val = torch.empty((T, K), dtype=torch.float32, device="cuda")
-    tis.index_score_topk(bt, d.q_idx, d.w, d.k_pool, d.k_scale, K, idx, val)
+    tis.index_score_topk(bt, d.q_idx, d.w, d.k_pool, d.k_scale, K, idx, val, qmode=qmode)
     if unfused:
         ld = (bt.max_n + 3) // 4 * 4
         scores = torch.full((T, ld), float("nan"), dtype=torch.float32, device="cuda")
-        tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores)
+        tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores, qmode=qmode)
         idx2 = torch.empty_like(idx)
         val2 = torch.empty_like(val)
         tis.topk_select(bt, scores, K, idx2, val2)

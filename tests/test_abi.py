@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     lib = tis.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tis_abi_version() == 1
+    assert lib.tis_abi_version() == 2
 
 
 class FakeBatch:
@@ -99,7 +99,7 @@ def test_index_argument_validation():
     assert call_index(b, ks=None) == L.TIS_ERR_INVALID        # e4m3 keys need scales
     assert call_index(b, H=32) == L.TIS_ERR_UNSUPPORTED
     assert call_index(b, qdt=L.TIS_F32) == L.TIS_ERR_UNSUPPORTED
-    assert call_index(b, qdt=L.TIS_F32, kdt=L.TIS_F32, qm=L.TIS_QMODE_NONE, ks=None, H=64,
+    assert call_index(b, qdt=L.TIS_F32, kdt=L.TIS_F32, qm=L.TIS_QMODE_BF16, ks=None, H=64,
                       Dd=256) == L.TIS_ERR_UNSUPPORTED   # 64*256 > 8192
     lib = tis.lib()
     assert lib.topk_select(b.ref, D, 1024, 0, D, None, None, 0, None) == L.TIS_ERR_INVALID
@@ -154,3 +154,18 @@ def test_noalloc_rejects_rows_beyond_its_scratch():
     # argument errors come first, as for index_score_topk
     assert lib.index_score_topk_noalloc(b.ref, D, L.TIS_BF16, D, D, L.TIS_E4M3, D, 64, 128,
                                         L.TIS_QMODE_FP8, 0, D, None, None) == L.TIS_ERR_INVALID
+
+
+def test_query_modes():
+    """The two indexer query modes of the header: FP8 (dynamic e4m3 query) = 0 and BF16 (the
+    query as stored) = 1; combinations outside the supported ones are refused on the host."""
+    src = open(os.path.join(ROOT, "include", "topidx.h")).read()
+    assert re.search(r"TIS_QMODE_FP8\s*=\s*0", src) and re.search(r"TIS_QMODE_BF16\s*=\s*1", src)
+    assert (L.TIS_QMODE_FP8, L.TIS_QMODE_BF16) == (0, 1)
+    b = FakeBatch([1000, 600], [0, 1, 3])
+    # fp32 queries and keys: only "as stored"
+    assert call_index(b, qdt=L.TIS_F32, kdt=L.TIS_F32, qm=L.TIS_QMODE_FP8, ks=None, H=4,
+                      Dd=32) == L.TIS_ERR_UNSUPPORTED
+    assert call_index(b, qm=7) == L.TIS_ERR_UNSUPPORTED
+    assert call_index(b, qm=L.TIS_QMODE_BF16, H=32) == L.TIS_ERR_UNSUPPORTED
+    assert call_index(b, qm=L.TIS_QMODE_BF16, ks=None) == L.TIS_ERR_INVALID

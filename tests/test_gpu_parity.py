@@ -17,11 +17,11 @@ from tests.gpu_path import (attend, check_attention, check_scores, check_topk, n
 pytestmark = pytest.mark.gpu
 
 
-def _common(inp, r, tokens, exact, also_bf16=False):
+def _common(inp, r, tokens, exact, also_bf16=False, qmode=None):
     """Fused == unfused, emitted values, scores, Top-K and attention gates.  also_bf16: the
     attention call is run again with a bf16 output (the benchmarked form for e4m3 caches)
-    and gated as well."""
-    orc = Oracle(inp)
+    and gated as well.  qmode: the oracle's query mode ('fp8' or 'none')."""
+    orc = Oracle(inp, qmode=qmode)
     # fused and unfused chains agree exactly
     assert np.array_equal(r.idx, r.idx2), "fused vs unfused Top-K"
     assert np.array_equal(r.val, r.val2), "fused vs unfused Top-K values"
@@ -464,3 +464,26 @@ def test_tiny_query_heads():
     assert np.array_equal(r.idx, r.idx2)
     note(f"  tiny query heads: score rel err {serr:.2e}")
     assert serr < 1e-3
+
+
+@pytest.mark.parametrize("mode", ["continuous", "exact"])
+@pytest.mark.parametrize("shape", ["decode", "prefill"])
+def test_bf16_query_mode(shape, mode):
+    """TIS_QMODE_BF16: q_I as stored on bf16 matrix cores over the exactly widened e4m3 keys,
+    against the oracle with no query quantisation (exact mode: scores and Top-K bit-exact);
+    decode shapes (8-wave workgroups, one token each) and prefill shapes (four tokens per
+    workgroup)."""
+    import top_indexed_sparse_amd as tis
+    if shape == "decode":
+        wl = synth.reduced(synth.workload(synth.DECODE32K), [4096, 1500, 5000, 2049], [1, 1, 2, 1])
+    else:
+        wl = synth.reduced(synth.workload(synth.PREFILL64K), [2600], [2600])
+    inp = synth.make(wl, mode)
+    note(f"case bf16 query mode, {shape} shapes, mode={mode} T={inp.T}")
+    r = run_path(inp, qmode=tis.TIS_QMODE_BF16)
+    toks = list(range(inp.T)) if inp.T <= 64 else sample_tokens(inp, 100)
+    serr = _common(inp, r, toks, mode == "exact", qmode="none")
+    if mode == "exact":
+        assert serr == 0.0
+    else:
+        assert serr < 1e-4

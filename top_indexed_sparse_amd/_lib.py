@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libtopidx.so")
 
 TIS_OK, TIS_ERR_INVALID, TIS_ERR_UNSUPPORTED, TIS_ERR_HIP = 0, 1, 2, 3
 TIS_F32, TIS_BF16, TIS_E4M3 = 0, 1, 2
-TIS_QMODE_FP8, TIS_QMODE_NONE = 0, 1
+TIS_QMODE_FP8, TIS_QMODE_BF16 = 0, 1
 PAGE_SIZE = 64
 
 EXPORTS = ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
@@ -77,7 +77,7 @@ def lib():
     for f in ("index_score_workspace_size", "topk_select_workspace_size",
               "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size"):
         getattr(L, f).restype = _SZ
-    if L.tis_abi_version() != 1:
+    if L.tis_abi_version() != 2:
         raise RuntimeError("libtopidx ABI version mismatch")
     _lib = L
     return L
@@ -153,7 +153,7 @@ def index_score(batch: Batch, q_idx, w, k_pool, k_scale, scores, qmode=None):
     """scores[t, s] for s <= p_t (see index_score in topidx.h)."""
     H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
     if qmode is None:
-        qmode = TIS_QMODE_NONE if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
+        qmode = TIS_QMODE_BF16 if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
     _check(lib().index_score(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_pool),
                              _dtype(k_pool), _ptr(k_scale), H_I, D_I, qmode, _ptr(scores),
                              int(scores.stride(0)), None, 0, _stream()))
@@ -180,7 +180,7 @@ def index_score_topk(batch: Batch, q_idx, w, k_pool, k_scale, K: int, topk_idx, 
                      ws=None, qmode=None):
     H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
     if qmode is None:
-        qmode = TIS_QMODE_NONE if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
+        qmode = TIS_QMODE_BF16 if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
     need = index_score_topk_workspace_size(batch, H_I, D_I, K)
     ws, nb = _ws(need, ws, q_idx.device)
     _check(lib().index_score_topk(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_pool),
@@ -194,7 +194,7 @@ def index_score_topk_noalloc(batch: Batch, q_idx, w, k_pool, k_scale, K: int, to
     """index_score_topk with the library's own per-device scratch (allocates nothing)."""
     H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
     if qmode is None:
-        qmode = TIS_QMODE_NONE if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
+        qmode = TIS_QMODE_BF16 if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
     _check(lib().index_score_topk_noalloc(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w),
                                           _ptr(k_pool), _dtype(k_pool), _ptr(k_scale), H_I, D_I,
                                           qmode, int(K), _ptr(topk_idx), _ptr(topk_val),

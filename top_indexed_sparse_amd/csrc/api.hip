@@ -93,7 +93,7 @@ tis::DevBatch dev_batch(const tis_batch_t* b) {
   return d;
 }
 
-enum class IdxPath { F32, FP8 };
+enum class IdxPath { F32, FP8, BF16 };  // fp32 kernel; matrix-core scorer, e4m3 / bf16 query
 
 tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* w,
                               const void* k_pool, tis_dtype_t k_dt, const float* k_scale,
@@ -102,22 +102,24 @@ tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* 
   if (!aligned16(q_idx) || !aligned16(k_pool) || !aligned16(w))
     return fail(TIS_ERR_INVALID, "q_idx, w and k_pool must be 16-byte aligned");
   if (H_I < 1 || D_I < 1) return fail(TIS_ERR_INVALID, "H_I and D_I must be >= 1");
-  if (q_dt == TIS_F32 && k_dt == TIS_F32 && qmode == TIS_QMODE_NONE) {
+  if (q_dt == TIS_F32 && k_dt == TIS_F32 && qmode == TIS_QMODE_BF16) {
     if (k_scale) return fail(TIS_ERR_INVALID, "fp32 keys take no k_scale");
     if ((int64_t)H_I * D_I > 8192)
       return fail(TIS_ERR_UNSUPPORTED, "fp32 indexer supports H_I*D_I <= 8192");
     *path = IdxPath::F32;
     return TIS_OK;
   }
-  if (q_dt == TIS_BF16 && k_dt == TIS_E4M3 && qmode == TIS_QMODE_FP8) {
+  if (q_dt == TIS_BF16 && k_dt == TIS_E4M3 &&
+      (qmode == TIS_QMODE_FP8 || qmode == TIS_QMODE_BF16)) {
     if (!k_scale || !aligned16(k_scale))
       return fail(TIS_ERR_INVALID, "e4m3 keys need a 16-byte aligned k_scale");
     if (H_I != 64 || D_I != 128)
       return fail(TIS_ERR_UNSUPPORTED, "e4m3 indexer supports H_I=64, D_I=128");
-    *path = IdxPath::FP8;
+    *path = qmode == TIS_QMODE_FP8 ? IdxPath::FP8 : IdxPath::BF16;
     return TIS_OK;
   }
-  return fail(TIS_ERR_UNSUPPORTED, "indexer supports (f32,f32,NONE) and (bf16,e4m3,FP8)");
+  return fail(TIS_ERR_UNSUPPORTED,
+              "indexer supports (f32, f32, BF16) and (bf16, e4m3, FP8 or BF16) for (q, k, qmode)");
 }
 
 tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath path, int t0,
@@ -131,8 +133,8 @@ tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath pat
                                     (const float*)k_pool, H_I, D_I, scores, ld, st);
   else
     e = tis::launch_index_score_fp8(d, t0, tc, hi.max_n, hi.prefill_like,
-                                    (const uint16_t*)q_idx, w, (const uint8_t*)k_pool, k_scale,
-                                    scores, ld, st);
+                                    path == IdxPath::BF16, (const uint16_t*)q_idx, w,
+                                    (const uint8_t*)k_pool, k_scale, scores, ld, st);
   return e == hipSuccess ? TIS_OK : hip_fail(e, "index_score launch");
 }
 

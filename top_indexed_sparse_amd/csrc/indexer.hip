@@ -16,6 +16,13 @@
 //   The accumulator of tile m holds heads 16m + 4g + i (i < 4) of key (l & 15): ReLU and
 //   head weights are applied in-lane, and two permlane swaps finish the head sum while
 //   transposing four 16-key tiles so that lane l ends with the score of key base + l.
+//
+// bf16 query mode (the quantisation-free implementation kept beside the quantised one, as in
+// Key Optimization 1): the same kernel with q_I used as stored on v_mfma_f32_16x16x32_bf16.
+// The 32 query dims a lane holds are already the four 8-dim k-steps of that instruction's A
+// layout (dims 16g.., 16g+8.., 64+16g.., 64+16g+8..), and each staged 16-byte run of key
+// bytes widens exactly (every e4m3 value is a bf16 value) into two B operands of the same
+// dims; the weights are used as given.
 #include "common.h"
 #include "launch.h"
 
@@ -169,22 +176,63 @@ __device__ __forceinline__ void stage_ktile4(uint8_t* stage, int lane, const KPa
   }
 }
 
+// The query's A operands for the four 16-head tiles: e4m3 (one 16x16x128 step per tile) or
+// bf16 as stored (four 16x16x32 steps per tile, each the i32x4 of 8 dims the lane loaded).
+template <bool BQ>
+struct QOps {
+  i32x8 a[4];
+};
+template <>
+struct QOps<true> {
+  i32x4 a[4][4];
+};
+
+// 8 e4m3 codes (two dwords) widened to bf16, exactly (scale 1)
+__device__ __forceinline__ bf16x8 widen8_bf16(int lo, int hi) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
+                                 6, 7);
+}
+
 // Scores of the 64 keys of one page-aligned group; lane l returns key base + l (unscaled).
-__device__ __forceinline__ float score_group(const i32x8 (&A)[4], const float (&wp)[4][4],
+template <bool BQ>
+__device__ __forceinline__ float score_group(const QOps<BQ>& A, const float (&wp)[4][4],
                                              const KTile4& kt) {
   float v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    i32x8 B;
-    B[0] = kt.lo[j][0]; B[1] = kt.lo[j][1]; B[2] = kt.lo[j][2]; B[3] = kt.lo[j][3];
-    B[4] = kt.hi[j][0]; B[5] = kt.hi[j][1]; B[6] = kt.hi[j][2]; B[7] = kt.hi[j][3];
     float acc = 0.f;
+    if constexpr (BQ) {
+      bf16x8 B[4];
+      B[0] = widen8_bf16(kt.lo[j][0], kt.lo[j][1]);
+      B[1] = widen8_bf16(kt.lo[j][2], kt.lo[j][3]);
+      B[2] = widen8_bf16(kt.hi[j][0], kt.hi[j][1]);
+      B[3] = widen8_bf16(kt.hi[j][2], kt.hi[j][3]);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[m], B, c, 0, 0, 0, 0, 0, 0);
+      for (int m = 0; m < 4; ++m) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], fmaxf(c[i], 0.f), acc);
+        for (int st = 0; st < 4; ++st)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A.a[m][st]),
+                                                      B[st], c, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], fmaxf(c[i], 0.f), acc);
+      }
+    } else {
+      i32x8 B;
+      B[0] = kt.lo[j][0]; B[1] = kt.lo[j][1]; B[2] = kt.lo[j][2]; B[3] = kt.lo[j][3];
+      B[4] = kt.hi[j][0]; B[5] = kt.hi[j][1]; B[6] = kt.hi[j][2]; B[7] = kt.hi[j][3];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], fmaxf(c[i], 0.f), acc);
+      }
     }
     v[j] = acc;
   }
@@ -200,7 +248,7 @@ __device__ __forceinline__ float score_group(const i32x8 (&A)[4], const float (&
 //   pages when the request's pages are consecutive.
 // GROUP == true (prefill): four consecutive tokens per workgroup, one per wave, each over
 //   all pages of the same chunk.
-template <bool GROUP>
+template <bool GROUP, bool BQ>
 __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBatch bt,
     int t_begin, int t_count, const uint16_t* q_idx, const float* w,
     const uint8_t* kpool, const float* kscale,
@@ -288,25 +336,51 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   }
   __shared__ __attribute__((aligned(16))) uint8_t stage_sh[(GROUP ? 4 : 8) * kStage];
   uint8_t* stage = stage_sh + wave * kStage;
-  i32x8 A[4];
+  QOps<BQ> A;
   float wp[4][4];
   if (GROUP) {
-    a0_prologue(qr, lane, A, wp);
+    if constexpr (BQ) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          A.a[m][i] = qr.r[m][i];
+          wp[m][i] = qr.w[m][i];
+        }
+    } else {
+      a0_prologue(qr, lane, A.a, wp);
+    }
   } else {
-    __shared__ i32x8 a_sh[4][64];
+    // (e4m3: one 32-byte operand per lane and tile; bf16: the 64 loaded bytes as they are)
+    __shared__ i32x4 a_sh[4][BQ ? 4 : 2][64];
     __shared__ f32x4 w_sh[4][64];
     if (wave < 4) {
-      i32x8 at;
       float wt[4];
-      a0_tile(qr.r[0], qr.w[0], lane, at, wt);
-      a_sh[wave][lane] = at;
+      if constexpr (BQ) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a_sh[wave][i][lane] = qr.r[0][i];
+          wt[i] = qr.w[0][i];
+        }
+      } else {
+        i32x8 at;
+        a0_tile(qr.r[0], qr.w[0], lane, at, wt);
+        a_sh[wave][0][lane] = i32x4{at[0], at[1], at[2], at[3]};
+        a_sh[wave][1][lane] = i32x4{at[4], at[5], at[6], at[7]};
+      }
       w_sh[wave][lane] = f32x4{wt[0], wt[1], wt[2], wt[3]};
     }
     __syncthreads();
     if (!active) return;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      A[m] = a_sh[m][lane];
+      if constexpr (BQ) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A.a[m][i] = a_sh[m][i][lane];
+      } else {
+        const i32x4 lo = a_sh[m][0][lane], hi = a_sh[m][1][lane];
+        A.a[m] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
       const f32x4 wv = w_sh[m][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) wp[m][i] = wv[i];
@@ -327,7 +401,7 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
     if (score) {
       KTile4 kt;
       stage_ktile4(stage, lane, c.kp, kt);
-      sc = score_group(A, wp, kt) * (GROUP ? c.ks : scale);
+      sc = score_group<BQ>(A, wp, kt) * (GROUP ? c.ks : scale);
       if (!c.ok) sc = -INFINITY;
     }
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
@@ -362,20 +436,20 @@ hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, 
 }
 
 hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, const uint16_t* q_idx, const float* w,
-                                  const uint8_t* kpool, const float* kscale, float* scores,
-                                  int64_t ld, hipStream_t st) {
+                                  bool prefill_like, bool bf16_query, const uint16_t* q_idx,
+                                  const float* w, const uint8_t* kpool, const float* kscale,
+                                  float* scores, int64_t ld, hipStream_t st) {
   const int group = prefill_like ? 1 : 0;
   const int chunk = prefill_like ? 1024 : 4096;
   dim3 grid(group ? (t_count + 3) / 4 : t_count, (max_n + chunk - 1) / chunk);
   // decode: one 8-wave workgroup per 4096-key chunk of a token (512 keys per wave); prefill:
   // four tokens per 4-wave workgroup sharing a 1024-key chunk
-  if (group)
-    hipLaunchKernelGGL(idx_score_fp8_kernel<true>, grid, dim3(256), 0, st, bt, t_begin, t_count,
-                       q_idx, w, kpool, kscale, scores, ld, chunk);
-  else
-    hipLaunchKernelGGL(idx_score_fp8_kernel<false>, grid, dim3(512), 0, st, bt, t_begin,
-                       t_count, q_idx, w, kpool, kscale, scores, ld, chunk);
+  auto* fn = group ? (bf16_query ? idx_score_fp8_kernel<true, true>
+                                 : idx_score_fp8_kernel<true, false>)
+                   : (bf16_query ? idx_score_fp8_kernel<false, true>
+                                 : idx_score_fp8_kernel<false, false>);
+  hipLaunchKernelGGL(fn, grid, dim3(group ? 256 : 512), 0, st, bt, t_begin, t_count, q_idx, w,
+                     kpool, kscale, scores, ld, chunk);
   return hipGetLastError();
 }
 

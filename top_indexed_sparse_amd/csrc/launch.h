@@ -12,9 +12,9 @@ hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, 
                                   const float* q, const float* w, const float* kpool, int H,
                                   int D, float* scores, int64_t ld, hipStream_t st);
 hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, const uint16_t* q_idx, const float* w,
-                                  const uint8_t* kpool, const float* kscale, float* scores,
-                                  int64_t ld, hipStream_t st);
+                                  bool prefill_like, bool bf16_query, const uint16_t* q_idx,
+                                  const float* w, const uint8_t* kpool, const float* kscale,
+                                  float* scores, int64_t ld, hipStream_t st);
 hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
                        const float* scores, int64_t ld, int K, int32_t* idx, float* val,
                        void* ws, hipStream_t st);
