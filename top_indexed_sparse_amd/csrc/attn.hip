@@ -9,30 +9,35 @@
 // (512 latent + 64 RoPE), values are its first 512 dims.
 //
 // Matrix-core kernel (bf16 or e4m3 cache), one 4-wave workgroup per (token, key split,
-// group of 64 heads); wave (hh, kh) owns 32 heads (half hh of the group) and key half kh
-// of every 32-key stage:
+// group of 64 heads); wave (hh, dv) owns 32 heads (half hh of the group) and value dims
+// 256dv .. 256dv + 255 over every key of the split:
 //   * the split's positions are translated through the page table once into LDS;
-//   * 16-row tiles are gathered with 16-byte loads into a one-stage register queue and
-//     written into a two-stage LDS ring, interleaved with the QK matrix ops; e4m3 rows stay
-//     e4m3 in LDS and are widened per fragment;
-//   * S^T = K_tile . Q^T on v_mfma_f32_16x16x32 over 18 fragments of 32 dims, most of Q^T in
-//     registers and the rest in LDS (one copy per head half, loaded half by each of its two
-//     waves);
+//   * 32-row stages are gathered with 16-byte loads (each wave a fixed eight rows) into a
+//     one-stage register queue and written into a three-stage LDS ring; e4m3 rows stay e4m3
+//     in LDS and are widened per fragment;
+//   * each wave multiplies its half of the 576 contracted dims, S^T = K . Q^T on
+//     v_mfma_f32_16x16x32 (all of its Q^T in registers), and the two waves of a head half
+//     add their partial logits through LDS;
 //   * O^T[vdim][head] += V^T . P^T on v_mfma_f32_32x32x16: P reaches the B layout with one
 //     permlane16 swap, and V^T fragments come from the row-major tile via
 //     ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3);
-//   * the running max is raised lazily (only when a tile exceeds it by 2^8), so rescaling
-//     the 256 accumulator registers is rare;
+//   * the stages are software pipelined (QK^T of stage st beside the softmax of stage
+//     st - 1, then PV of st - 1 beside the ring writes and gathers), with the order of
+//     matrix and vector work pinned by scheduling fences;
+//   * the running max is raised lazily (only when a stage exceeds it by 2^8), so rescaling
+//     the accumulators is rare;
 //   * e4m3: per-token scales go into the logits in fp32 and into P relative to the split's
 //     largest scale; P then is fp16 (11-bit significand) so that heavy rows stay accurate,
 //     and the normaliser is accumulated from the same rounded P values;
-//   * the two key halves are merged through LDS; with several splits per token, each split
-//     writes (m, l, O) partials that mla_combine_kernel merges with log-sum-exp weights.
+//   * each wave writes its own O (through LDS, in whole lines); with several splits per
+//     token, the (m, l, O) partials are merged by mla_combine_kernel with log-sum-exp
+//     weights.
 #include "common.h"
 #include "launch.h"
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 namespace tis {
 
@@ -104,17 +109,6 @@ constexpr int kWT = 16;        // rows (keys) per tile
 constexpr int kSR = 2 * kWT;   // rows per stage: the tiles of the two key halves
 constexpr int kMaxKps = 2048;  // keys per split (bounds the LDS index table)
 constexpr float kMFloor = -1e30f;  // running max before the first live key (log2 units)
-// Q^T per wave: 18 fragments of 32 dims per 16 heads; the first kQR stay in registers, the
-// last kQL are read from LDS one step ahead, which leaves the registers for the queue of
-// gathered rows.  The two waves of a head half (the two key halves) need the same Q: each
-// loads the fragments of one parity from HBM and takes the others from the copy its partner
-// leaves in LDS (one copy per head half, in the lane order of the operand), which halves the
-// Q traffic of the prologue.  So that every register index stays static, the key-half-1
-// wave contracts the dims of each fragment pair in swapped order: its step ks uses fragment
-// ks ^ 1 of both K and Q (the pairs never straddle the value/RoPE boundary).
-constexpr int kNQ = kDqk / 32, kQL = 4, kQR = kNQ - kQL;
-static_assert(kNQ % 2 == 0 && kQR % 2 == 0 && (kDv / 32) % 2 == 0, "fragment pairs");
-
 // 16-row tiles are gathered with 16-byte loads into registers and written to LDS (a load
 // straight to LDS costs its wave about twice the issue time of a load plus an LDS write); the
 // two waves that read a tile (the two head halves of one key half) issue half of its loads
@@ -148,19 +142,29 @@ __host__ __device__ constexpr int tile_row(int m) {  // pi: consumption order ->
   return (m & 8) + ((m & 4) ? 2 * (m & 3) + 1 : 2 * (m & 3));
 }
 
-// Dynamic LDS: ring (or the exchange) | rows[kMaxKps] | masks[kMaxKps/16] | scl[kMaxKps] (e4m3) | xm[4][3][32].
-// After the main loop the ring area holds the cross-wave exchange of O (4 x 32 x 132 floats).
-constexpr int kXPitch = 132;  // floats per head row of the exchange (128 dims + pad)
+// Q^T per wave: 9 fragments of 32 dims (8 of value dims, 1 of RoPE dims) per 16 heads, the
+// wave's half of the contracted dims, all in registers.
+constexpr int kNQ2 = 9;
+constexpr int kDvW = kDv / 2;  // value dims per wave
+constexpr int kRing = 3;       // stages in the LDS ring
+// LDS reads in flight per wave: one wave per SIMD keeps the LDS busy only with many reads
+// outstanding (K fragments read this many steps ahead, V^T this many dim tiles ahead)
+constexpr int kKPre = 6, kVPre = 3;
+constexpr int kOStage = kDvW + 4;  // floats per head row when O is staged for the stores
+
+// Dynamic LDS: ring of three stages (two tiles each) | rows[kMaxKps] | masks[kMaxKps/16] |
+// scl[kMaxKps] (e4m3) | partial logits [2][4 waves][4 tiles][64 lanes] f32x4 | red/anyv.
 template <bool FP8>
 struct AttnSmem {
-  static constexpr int kXBytes = 4 * kHB * kXPitch * 4;  // the exchange of O
-  static constexpr int rows = KvFmt<FP8>::kTiles > kXBytes ? KvFmt<FP8>::kTiles : kXBytes;
+  static constexpr int rows = kRing * 2 * KvFmt<FP8>::kWBytes;
   static constexpr int masks = rows + kMaxKps * 4;
   static constexpr int scl = masks + kMaxKps / 16 * 2;
-  static constexpr int xm = scl + (FP8 ? kMaxKps * 4 : 0);
-  static constexpr int qlds = xm + 4 * 3 * kHB * 4 + 2 * 3 * kHB * 4;
-  static constexpr int total = qlds + 2 * 2 * kNQ * 1024;  // Q: [head half][ht][fragment]
-  static_assert(total <= 160 * 1024, "LDS budget");
+  static constexpr int xs = scl + (FP8 ? kMaxKps * 4 : 0);
+  static constexpr int red = xs + 2 * 4 * 4096;
+  // after the loop the whole area holds the waves' O, staged for whole-line stores
+  static constexpr int ostage = 4 * kHB * kOStage * 4;
+  static constexpr int total = red + 64 > ostage ? red + 64 : ostage;
+  static_assert(xs % 16 == 0 && total <= 160 * 1024, "LDS budget");
 };
 
 // Split partials of a bf16 output: the split's normalised O in fp16 scaled by 2^-8, i.e.
@@ -232,20 +236,28 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return xor32_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
-// One workgroup per (token, key split, group of 64 heads); wave w takes heads 32(w%2) .. +31
-// of the group and the 16-key tiles 2i + w/2 of the split, which it shares with the wave of
-// the other head half.  Per wave tile:
-//   S^T[16 keys][16 heads] x 2 = K . Q^T on v_mfma_f32_16x16x32_bf16 (K fragments from LDS,
-//     Q^T resident in registers; e4m3 rows are widened exactly per fragment);
-//   online softmax per head (lane-local over 4 keys, then across the four 16-lane rows);
-//   one permlane16 swap moves P^T into the B layout of v_mfma_f32_32x32x16 (keys 8(l/32)+j,
-//     head l%32), and O^T[32 dims][32 heads] += V^T . P^T with V^T read by
-//     ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3, widened to fp16).
-// The running max is raised lazily (only when a tile exceeds it by 2^8).  e4m3: per-row scales
-// enter the fp32 logits and P relative to the split's largest scale; P is fp16 and the
-// normaliser sums the same rounded values.  The two key halves' (m, l, O) of each head are
-// merged through LDS; with several splits the workgroup writes fp32 partials for
-// mla_combine_kernel.
+// One workgroup per (token, key split, group of 64 heads).  Wave w = (hh, dv) = (w & 1, w >> 1)
+// owns heads 32hh .. 32hh + 31 of the group and value dims 256dv .. 256dv + 255, over every key
+// of the split; its QK^T covers one half of the 576 contracted dims (value dims 256dv.. and RoPE
+// dims 512 + 32dv..), and the two waves of a head half (w and w ^ 2) add their partial logits
+// through LDS.  Per 32-key stage (two 16-row tiles) and wave:
+//   S^T[16 keys][16 heads] x 2 x 2 = K . Q^T on v_mfma_f32_16x16x32_bf16 over 9 fragments of 32
+//     dims (K fragments from LDS, all of the wave's Q^T resident in registers; e4m3 rows are
+//     widened exactly per fragment);
+//   the partial logits go to LDS; after the next barrier each wave adds its partner's and runs
+//   the online softmax per head (lane-local over 8 keys, then across the four 16-lane rows);
+//   one permlane16 swap per tile moves P^T into the B layout of v_mfma_f32_32x32x16, and
+//   O^T[32 dims][32 heads] += V^T . P^T for the wave's 8 dim tiles, V^T read by
+//   ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3, widened to fp16).
+// The stages are software pipelined.  In the iteration of stage st a wave computes its partial
+// QK^T of stage st while it finishes the softmax of stage st - 1 (whose logits its partner
+// completed before the barrier), then runs PV of stage st - 1 while it writes the gathered rows
+// of stage st + 1 into the LDS ring (three stages) and issues the gathers of stage st + 3 (two
+// stages of rows in flight in registers).  The running max is raised lazily (only when a tile
+// exceeds it by 2^8), by recomputing the stage's softmax.  e4m3: per-row scales enter the fp32
+// logits and P relative to the split's largest scale; P is fp16 and the normaliser sums the same
+// rounded values.  Each wave writes its own heads' dims of O (or, with several splits, the
+// partials that mla_combine_kernel merges), transposed through LDS into whole lines.
 template <bool FP8, bool OUT_F32>
 __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_count,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -255,28 +267,23 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   using F = KvFmt<FP8>;
   using SM = AttnSmem<FP8>;
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  char* tiles = sm;
+  char* ring = sm;
   int* rows = (int*)(sm + SM::rows);
   uint16_t* masks = (uint16_t*)(sm + SM::masks);
   float* scl = (float*)(sm + SM::scl);
-  float* xm = (float*)(sm + SM::xm);          // [wave][m, l, le][32 heads]
-  float* xf = xm + 4 * 3 * kHB;               // [head half][M, L, LE][32 heads]
-  __shared__ float red[4];
-  __shared__ int anyv[4];
+  char* xs = sm + SM::xs;  // partial logits [2 buffers][4 waves][4 tiles][64 lanes] f32x4
+  float* red = (float*)(sm + SM::red);
+  int* anyv = (int*)(red + 4);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;  // 16x16 layouts
   const int c32 = lane & 31, h2 = lane >> 5;  // 32x32 layouts
-  const int hh = wave & 1, kh = wave >> 1;    // head half, key half
-  // this lane's slot in the head half's copy of Q; fragment f of head tile ht at
-  // (ht * kNQ + f) KB.  qxe / qxo address fragment ks ^ kh for even / odd ks.
-  char* const qx = sm + SM::qlds + hh * (2 * kNQ * 1024) + 16 * lane;
-  char* const qxe = qx + 1024 * kh;
-  char* const qxo = qx - 1024 * kh;
+  const int hh = wave & 1, dv = wave >> 1;    // head half, value-dim half
+  const int partner = wave ^ 2;
 
   // workgroup -> (token, split, head group); the workgroups of one token sit on one XCD
   // (workgroups are dealt to the 8 XCDs round-robin), so its rows are fetched from HBM once
-  // and served to the other head groups from that XCD's L2
+  // and served to the other head group from that XCD's L2
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7, slot8 = blockIdx.x >> 3;
   const int per = nblk >> 3, extra = nblk & 7;
@@ -314,21 +321,17 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     const int sp = pos[j];
     slot[j] = (sp >= 0 && sp < Lb) ? ptb[sp >> 6] : -1;
   }
-  // This wave's half of the Q^T fragments of its 32 heads (B operand of 16x16x32: head c16,
-  // dims 32f + 8g4 of fragment f = 2i + kh), issued after the page lookups: loads complete
-  // in issue order, so the slots below wait for the page entries only, and Q arrives while
-  // the slots and the first tiles are in flight.  Register slot ks holds fragment ks ^ kh:
-  // the even slots are loaded here, the odd ones come from the partner's copy.
-  bf16x8 qf[2][kQR], qtl[2][kQL / 2];
+  // The wave's Q^T fragments (B operand of 16x16x32: head 16ht + c16, dims 8g4.. of fragment
+  // ks = value dims 256dv + 32ks (ks < 8) or RoPE dims 512 + 32dv (ks = 8)), issued after the
+  // page lookups: loads complete in issue order, so the slots below wait for the page entries
+  // only, and Q arrives while the slots and the first tiles are in flight.
+  bf16x8 qf[2][kNQ2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4 + 32 * kh;
+    const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4;
 #pragma unroll
-    for (int i = 0; i < kNQ / 2; ++i) {
-      const bf16x8 v = *(const bf16x8*)(qr + 64 * i);
-      if (2 * i < kQR) qf[ht][2 * i] = v;
-      else qtl[ht][i - kQR / 2] = v;
-    }
+    for (int ks = 0; ks < kNQ2; ++ks)
+      qf[ht][ks] = *(const bf16x8*)(qr + (ks < kNQ2 - 1 ? 256 * dv + 32 * ks : kDv + 32 * dv));
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -361,8 +364,8 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     int v = -1;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) v = max(v, slot[j]);
-    const uint64_t b = __ballot(v >= 0);
-    if (lane == 0) anyv[wave] = b ? __builtin_amdgcn_readlane(v, __builtin_ctzll(b)) : -1;
+    const uint64_t bb = __ballot(v >= 0);
+    if (lane == 0) anyv[wave] = bb ? __builtin_amdgcn_readlane(v, __builtin_ctzll(bb)) : -1;
   }
   // per 16-row tile: bit m = row pi(m) selected (the order in which the keys are consumed),
   // from one ballot per row step: rows 256j + 64wave + l, four tiles, lane q < 4 writes
@@ -388,231 +391,209 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const int nst = fill >= 0 ? nstage : 0;
   const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
 
-  // ---- this wave's tile of stage st: rows st*32 + 16*kh .. +15
-  // wave-uniform pieces of the gather addresses live in scalar registers: the row base of
-  // each A-region load is kv + slot * rowbytes (a scalar), the lane adds 16 * lane, and the
-  // LDS destination (M0) is a scalar too
-  const int kh_u = __builtin_amdgcn_readfirstlane(kh);
-  const int jlo = __builtin_amdgcn_readfirstlane(hh) ? F::kIssue - F::kIssueW : 0;
-  const uint32_t lane16 = 16u * (uint32_t)lane;
-  // the slots of the wave's tile of stage st: lane r of each 16 holds row r (region A), and
-  // bslot[j] the row of region-B chunk l % C of load j (C = RoPE chunks per row)
-  constexpr int kRC = F::kRBytes / 16;
-  struct TileRows {
-    int my;
-    int bslot[F::kBLoads];
+  // ---- gathers: wave w loads rows 8w .. 8w + 7 of each stage, i.e. rows 8(w & 1) .. of tile
+  // w >> 1.  bf16: one load per row for its 1 KB value part (lane l: bytes 16l ..; the row
+  // base is a scalar), one load for the eight rows' RoPE parts (lane l: row l >> 3, chunk
+  // l & 7).  e4m3: one load per two rows' 512-byte value parts (lane l: row 2k + (l >> 5),
+  // bytes 16(l & 31)), one load for the eight rows' RoPE parts (lane l: row (l >> 2) & 7, chunk
+  // l & 3; lanes 32.. repeat lanes 0..31: same bytes to the same place).
+  constexpr int kNL = FP8 ? 5 : 9;  // loads per wave and stage
+  struct Gath {
+    int s[kNL];  // slot read by load k (per lane)
   };
-  auto tile_rows = [&](int st) {
-    TileRows tr;
-    const int* rw = rows + st * kSR + kh_u * kWT;
-    tr.my = rw[lane & (kWT - 1)];
+  auto gath_rows = [&](int st) {
+    Gath g;
+    const int* rr = rows + st * kSR + 8 * wave;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int j = 0; j < F::kBLoads; ++j) tr.bslot[j] = rw[(64 * j + lane) / kRC];
-    return tr;
-  };
-  // load j (< kIssue) of the tile of stage st: j < kWT is row j of region A (one load per
-  // row), the rest are the region-B loads.  Head half 0 issues loads 0 .. kIssueW - 1, head
-  // half 1 the last kIssueW (with 17 loads, load 8 is issued twice: same bytes, same place)
-  // load j of a tile, into registers: j < kWT is row j of region A (lane l: bytes 16l ..
-  // 16l + 15 of the row), the rest are region-B loads; it goes to LDS one stage later
-  auto load_one = [&](const TileRows& tr, int j) -> i32x4 {
-    if (j < kWT) {
-      const int sj = __builtin_amdgcn_readlane(tr.my, j);
-      const uint32_t sr = (uint32_t)(sj >= 0 ? sj : fill);
-      // the row base in scalar registers: the scalar-base form of the load
-      const uint64_t base = (uint64_t)(uintptr_t)kv + (uint64_t)sr * F::kRowBytes;
-      const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-      const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-      const uint64_t rowp = ((uint64_t)bhi << 32) | blo;
-      // (global, not generic: a generic load would also count against the LDS counter; all
-      // lanes load, e4m3 lanes 32..63 a copy of lane - 32's chunk, so that no lane-predicated
-      // write of the queue registers makes the counters wait)
-      return *GLOBAL_PTR(const i32x4, rowp + (FP8 ? 16u * (uint32_t)(lane & 31) : lane16));
-    }
-    const int jb = j - kWT;  // (a run-time index: select, do not index the array)
-    const int bs = (F::kBLoads == 1 || jb == 0) ? tr.bslot[0] : tr.bslot[F::kBLoads - 1];
-    const int c = (64 * jb + lane) % kRC;
-    return *GLOBAL_PTR(const i32x4, (uintptr_t)kv + (uint64_t)(uint32_t)(bs >= 0 ? bs : fill) *
-                                            F::kRowBytes + F::kVBytes + 16 * c);
-  };
-  auto write_one = [&](int st, int j, i32x4 v) {
-    char* ta = tiles + ((st % F::kBufs) * 2 + kh) * F::kWBytes;
-    if (j < kWT) {
-      if (!FP8 || lane < F::kVBytes / 16) *(i32x4*)(ta + j * F::kAStride + lane16) = v;
+      for (int k = 0; k < 4; ++k) g.s[k] = rr[2 * k + (lane >> 5)];
+      g.s[4] = rr[(lane >> 2) & 7];
     } else {
-      const int e = 64 * (j - kWT) + lane;  // chunk e % C of row e / C
-      *(i32x4*)(ta + F::kABytes + (e / kRC) * F::kRStride + 16 * (e % kRC)) = v;
-    }
-  };
-
-  f32x16 o[kDv / 32];  // O^T: dims 32mt + 8(i/4) + 4h2 + i%4, head h0 + c32
+      const int mine = rr[lane & 7];
 #pragma unroll
-  for (int mt = 0; mt < kDv / 32; ++mt)
+      for (int k = 0; k < 8; ++k) g.s[k] = __builtin_amdgcn_readlane(mine, k);
+      g.s[8] = rr[lane >> 3];
+    }
+#pragma unroll
+    for (int k = 0; k < kNL; ++k) g.s[k] = g.s[k] >= 0 ? g.s[k] : fill;
+    return g;
+  };
+  auto gload = [&](const Gath& g, int k) -> i32x4 {
+    if (FP8) {
+      const uint64_t rb = (uint64_t)(uintptr_t)kv + (uint64_t)(uint32_t)g.s[k] * F::kRowBytes;
+      return *GLOBAL_PTR(const i32x4, rb + (k < 4 ? 16u * (uint32_t)(lane & 31)
+                                                  : F::kVBytes + 16u * (uint32_t)(lane & 3)));
+    }
+    if (k < 8) {  // the row base in scalar registers: the scalar-base form of the load
+      const uint64_t rb = (uint64_t)(uintptr_t)kv + (uint64_t)(uint32_t)g.s[k] * F::kRowBytes;
+      const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)rb);
+      const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(rb >> 32));
+      return *GLOBAL_PTR(const i32x4, (((uint64_t)bhi << 32) | blo) + 16u * (uint32_t)lane);
+    }
+    const uint64_t rb = (uint64_t)(uintptr_t)kv + (uint64_t)(uint32_t)g.s[k] * F::kRowBytes;
+    return *GLOBAL_PTR(const i32x4, rb + F::kVBytes + 16u * (uint32_t)(lane & 7));
+  };
+  // LDS byte offset of load k's 16 bytes within a ring slot (the wave's tile and rows)
+  const int wtile = (wave >> 1) * F::kWBytes;
+  const int rw0 = 8 * (wave & 1);
+  auto gofs = [&](int k) -> int {
+    if (FP8) {
+      if (k < 4) return wtile + (rw0 + 2 * k + (lane >> 5)) * F::kAStride + 16 * (lane & 31);
+      return wtile + F::kABytes + (rw0 + ((lane >> 2) & 7)) * F::kRStride + 16 * (lane & 3);
+    }
+    if (k < 8) return wtile + (rw0 + k) * F::kAStride + 16 * lane;
+    return wtile + F::kABytes + (rw0 + (lane >> 3)) * F::kRStride + 16 * (lane & 7);
+  };
+  constexpr int kSlot = 2 * F::kWBytes;
+
+  // ---- register state
+  f32x16 o[kDvW / 32];  // O^T: dims 256dv + 32mt + 8(i/4) + 4h2 + i%4, head h0 + c32
+#pragma unroll
+  for (int mt = 0; mt < kDvW / 32; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
   // per lane two heads, 16ht + c16; le sums P unrounded (for lse, and to normalise O with a
   // bf16 cache), l sums the fp16 P of an e4m3 cache as rounded for the matrix cores
   float m_run[2] = {kMFloor, kMFloor}, l_run[2] = {0.f, 0.f}, le_run[2] = {0.f, 0.f};
   const bool hsel = (lane & 16) != 0;  // the O^T column c32 is head 16*hsel + c16
+  i32x4 qq[kNL];                       // the gathered rows of the next stage to write
+  f32x4 sp[2][2];                      // partial logits of the stage being multiplied
+  f32x4 prev[2][2];                    // partial logits of the stage in softmax
+  const int qrow = tile_row(c16);
+  using KRaw = typename std::conditional<FP8, i32x2, bf16x8>::type;
+  constexpr int kEB = FP8 ? 1 : 2;     // bytes per cached element
 
-  // The gathers go through registers: during stage st the loads of the tile of stage st + 2
-  // are issued and the loaded rows of the tile of stage st + 1 are written to LDS, one of each
-  // every other step of the QK loop (a one-stage queue of kIssueW loads per wave).  Each
-  // stage starts with a barrier: the tile of the stage has been written by both of its waves,
-  // and the ring slot written during the stage has been read by both.
-  i32x4 stg[F::kIssueW];
-  // (one guarded block from the first gather to the end of the loop: the gathers read `fill`,
-  // and a single path into the loop keeps the counter waits exact)
-  if (nst > 0) {
-    const TileRows tr0 = tile_rows(0);
+  // K fragment f = 2ks + kt of the stage at ring offset so: lane (m = c16, g4): row pi(m),
+  // dims 8g4 .. + 7 of the wave's fragment ks
+  auto kread = [&](int so, int f) -> KRaw {
+    const int ks = f >> 1, kt = f & 1;
+    const char* tb = ring + so + kt * F::kWBytes;
+    const char* pa = ks < kNQ2 - 1
+                         ? tb + qrow * F::kAStride + kEB * (256 * dv + 32 * ks + 8 * g4)
+                         : tb + F::kABytes + qrow * F::kRStride + kEB * (32 * dv + 8 * g4);
+    return *(const KRaw*)pa;
+  };
+  auto widen = [&](KRaw cur) -> bf16x8 {
+    if constexpr (FP8) {
+      const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, false);
+      const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, true);
+      const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, false);
+      const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, true);
+      return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                     __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                     5, 6, 7);
+    } else {
+      return cur;
+    }
+  };
+  // partial QK^T of the stage at ring offset so into sp
+  auto qk = [&](int so) {
 #pragma unroll
-    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr0, jlo + j);
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int j = 0; j < F::kIssueW; ++j) write_one(0, jlo + j, stg[j]);
-    const TileRows tr1 = tile_rows(min(1, nst - 1));
-#pragma unroll
-    for (int j = 0; j < F::kIssueW; ++j) stg[j] = load_one(tr1, jlo + j);
-  // Q has landed on every path into the loop (otherwise the waits for Q placed inside the loop
-  // would also hold back the queued gathers): the loaded half goes to the shared copy, and
-  // after a barrier the partner's half of the register fragments comes back from it
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-#pragma unroll
-    for (int i = 0; i < kNQ / 2; ++i)
-      *(bf16x8*)(qxe + (ht * kNQ + 2 * i) * 1024) =
-          2 * i < kQR ? qf[ht][2 * i < kQR ? 2 * i : 0] : qtl[ht][2 * i < kQR ? 0 : i - kQR / 2];
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-#pragma unroll
-    for (int i = 0; i < kQR / 2; ++i)
-      qf[ht][2 * i + 1] = *(const bf16x8*)(qxo + (ht * kNQ + 2 * i + 1) * 1024);
-  }
-  for (int st = 0; st < nst; ++st) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const TileRows trn = tile_rows(min(st + 2, nst - 1));
-    const uint32_t mask = masks[st * 2 + kh];
-    const char* sb = tiles + ((st % F::kBufs) * 2 + kh) * F::kWBytes;
-    const int rbase = st * kSR + kh * kWT;
-
-    // S^T[key 4g4 + i][head 16ht + c16]
-    f32x4 s[2];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) s[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // K fragments are read kPre steps ahead of their use (the latency of an LDS read is
-    // several MFMA steps)
-    constexpr int kPre = 3;
-    using KRaw = typename std::conditional<FP8, i32x2, bf16x8>::type;
+      for (int ht = 0; ht < 2; ++ht) sp[kt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kPre = 3;  // fragments read ahead of their use
+    constexpr int kNF = 2 * kNQ2;
     KRaw kr[kPre];
-    // lane (m = c16, g4): row pi(m), dims 32f + 8g4 .. +7 of fragment f = ks ^ kh (region A
-    // below dim 512, B above)
-    const int qr = tile_row(c16);
-    auto kread = [&](int ks) -> KRaw {
-      constexpr int kEB = FP8 ? 1 : 2;  // bytes per element
-      const int d = 32 * ks + 8 * g4 + ((ks & 1) ? -32 * kh : 32 * kh);
-      const char* pa = ks < kDv / 32 ? sb + qr * F::kAStride + kEB * d
-                                     : sb + F::kABytes + qr * F::kRStride + kEB * (d - kDv);
-      return *(const KRaw*)pa;
-    };
 #pragma unroll
-    for (int ks = 0; ks < kPre; ++ks) kr[ks] = kread(ks);
-    bf16x8 ql[2][2];  // [step parity][ht]: Q fragments from LDS, read one step ahead
+    for (int f = 0; f < kPre; ++f) kr[f] = kread(so, f);
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) {
-      if (ks + 1 >= kQR && ks + 1 < kNQ) {
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
-          ql[(ks + 1) & 1][ht] =
-              *(const bf16x8*)(((ks + 1) & 1 ? qxo : qxe) + (ht * kNQ + ks + 1) * 1024);
-      }
-      const KRaw cur = kr[ks % kPre];
-      if (ks + kPre < kDqk / 32) kr[ks % kPre] = kread(ks + kPre);
-      bf16x8 a;
-      if constexpr (FP8) {
-        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, false);
-        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, true);
-        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, false);
-        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, true);
-        a = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
-                                    __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
-                                    5, 6, 7);
-      } else {
-        a = cur;
-      }
+    for (int f = 0; f < kNF; ++f) {
+      const KRaw cur = kr[f % kPre];
+      if (f + kPre < kNF) kr[f % kPre] = kread(so, f + kPre);
+      const bf16x8 a = widen(cur);
+      const int ks = f >> 1, kt = f & 1;
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
-        s[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a, ks < kQR ? qf[ht][ks < kQR ? ks : 0] : ql[ks & 1][ht], s[ht], 0, 0, 0);
-      // (unconditional: near the end of the split they re-load the last tile into the ring
-      // slot that is not read again, and the queue keeps a fixed order for the counters)
-      if ((ks & 1) == 0 && ks / 2 < F::kIssueW) {
-        const int k = ks / 2;
-        write_one(st + 1, jlo + k, stg[k]);
-        stg[k] = load_one(trn, jlo + k);
-      }
+        sp[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], sp[kt][ht], 0, 0, 0);
     }
+  };
 
-    // ---- online softmax in log2 units: t = z - m_run with z = s * zsc (zsc = softmax scale *
-    // log2 e, times the row scale for e4m3), p = 2^t.  The running max is raised only when
-    // some t of the tile exceeds 8 (a lane-local test; the exact tile max across the four
-    // 16-lane rows is formed only then), so p <= 2^8.  Masked keys (a split's last tile only)
-    // get s = -inf, hence p = 0; m_run starts at a finite floor so this holds before the first
-    // live key too.  (The mask applies to t, not to s: a masked e4m3 row has scale 0.)
-    const uint32_t mk = (mask >> (4 * g4)) & 0xFu;
-    f32x4 zsc = {c2, c2, c2, c2};
-    if (FP8) {
-      const f32x4 sc = *(const f32x4*)(scl + rbase + 4 * g4);
-      zsc = sc * c2;
+  // ---- softmax of stage st: logits s = own partial (prev) + the partner's (LDS buffer xo);
+  // t = z - m_run with z = s * zsc (zsc = softmax scale * log2 e, times the row scale for e4m3),
+  // p = 2^t.  Masked keys get t = -inf, hence p = 0; m_run starts at a finite floor so this
+  // holds before the first live key too.  Returns whether the running max must be raised
+  // (some t of the stage above 8: a lane-local test, uniform through __any).
+  float pv[2][2][4];
+  uint32_t mk[2];
+  f32x4 zsc[2];
+  // logits of stage st: own partial (prev) + the partner's (LDS buffer xo)
+  auto logits = [&](int xo, f32x4 (&sf)[2][2]) {
+    const char* xb = xs + xo + partner * 4096 + 16 * lane;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        sf[kt][ht] = prev[kt][ht] + *(const f32x4*)(xb + (2 * kt + ht) * 1024);
+  };
+  auto soft1 = [&](int st, int xo) {
+    f32x4 sf[2][2];
+    logits(xo, sf);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      mk[kt] = ((uint32_t)masks[st * 2 + kt] >> (4 * g4)) & 0xFu;
+      zsc[kt] = f32x4{c2, c2, c2, c2};
+      if (FP8) zsc[kt] = *(const f32x4*)(scl + st * kSR + kt * kWT + 4 * g4) * c2;
     }
-    float tz[2][4];
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tz[ht][i] = fmaf(s[ht][i], zsc[i], -m_run[ht]);
-    if (mask != 0xFFFFu) {  // wave-uniform
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tz[ht][i] = ((mk >> i) & 1u) ? tz[ht][i] : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const float v = fmaf(sf[kt][ht][i], zsc[kt][i], -m_run[ht]);
+          const float tzv = ((mk[kt] >> i) & 1u) ? v : -INFINITY;
+          tmax = fmaxf(tmax, tzv);
+          pv[kt][ht][i] = __builtin_amdgcn_exp2f(tzv);
+        }
+    return tmax > 8.f;
+  };
+  // raise the running max of each head to the stage's, rescale l, le and O, recompute p
+  auto raise = [&](int xo) {
+    f32x4 s_full[2][2];
+    logits(xo, s_full);
+    float alpha[2];
+    const float m_old[2] = {m_run[0], m_run[1]};
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      float zm = -INFINITY;  // (from z itself: t loses z next to the floor)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((mk[kt] >> i) & 1u) zm = fmaxf(zm, s_full[kt][ht][i] * zsc[kt][i]);
+      const float m_new = fmaxf(m_run[ht], rows4_max(zm));
+      alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
+      l_run[ht] *= alpha[ht];
+      le_run[ht] *= alpha[ht];
+      m_run[ht] = m_new;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pv[kt][ht][i] = ((mk[kt] >> i) & 1u)
+                              ? __builtin_amdgcn_exp2f(fmaf(s_full[kt][ht][i], zsc[kt][i], -m_new))
+                              : 0.f;
     }
-    const float tmax = fmaxf(fmaxf(fmaxf(tz[0][0], tz[0][1]), fmaxf(tz[0][2], tz[0][3])),
-                             fmaxf(fmaxf(tz[1][0], tz[1][1]), fmaxf(tz[1][2], tz[1][3])));
-    if (__any(tmax > 8.f)) {
-      float alpha[2];
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        float zm = -INFINITY;  // (from z itself: t loses z next to the floor)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if ((mk >> i) & 1u) zm = fmaxf(zm, s[ht][i] * zsc[i]);
-        const float m_new = fmaxf(m_run[ht], rows4_max(zm));
-        alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
-        l_run[ht] *= alpha[ht];
-        le_run[ht] *= alpha[ht];
-        m_run[ht] = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          tz[ht][i] = ((mk >> i) & 1u) ? fmaf(s[ht][i], zsc[i], -m_new) : -INFINITY;
-      }
+    // O is rescaled only once some head has seen a live key before: on the first live stage
+    // (every running max still at the floor) O is zero and the factor is 0
+    if (__any(m_old[0] > kMFloor || m_old[1] > kMFloor)) {
       const float a_sel = hsel ? alpha[1] : alpha[0];
 #pragma unroll
-      for (int mi = 0; mi < kDv / 32; ++mi) acc_scale(o[mi], a_sel);
+      for (int mi = 0; mi < kDvW / 32; ++mi) acc_scale(o[mi], a_sel);
     }
-    float p[2][4];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[ht][i] = __builtin_amdgcn_exp2f(tz[ht][i]);
-        le_run[ht] += p[ht][i];
-      }
-
-    // ---- P^T in the 32x32x16 B layout: lane l gets keys 8h2 + j of head c32
-    uint32_t pk[2][2];  // [tile ht][pair]: packed 16-bit P of keys 4g4 + 2*pair + {0,1}
+  };
+  // normaliser terms of the stage (added to le / l by commit) and P^T in the 32x32x16 B
+  // layout per tile: lane l gets keys 8h2 + j of head c32
+  i32x4 pb[2];
+  float le_add[2], l_add[2];
+  // P^T of tile kt (and, e4m3, its normaliser terms as rounded for the matrix cores)
+  auto pack_tile = [&](int kt) {
+    uint32_t pk[2][2];  // [ht][pair]: packed 16-bit P of keys 4g4 + 2*pair + {0,1}
     if (FP8) {
-      f32x4 rs = {0.f, 0.f, 0.f, 0.f}, sn = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 sc = *(const f32x4*)(scl + rbase + 4 * g4);
+      const f32x4 sc = zsc[kt] * (1.f / c2);
+      f32x4 rs, sn;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sn[i] = sc[i] * inv_smax;
@@ -622,10 +603,10 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
-          const _Float16 v0 = (_Float16)(p[ht][2 * pr] * sn[2 * pr]);
-          const _Float16 v1 = (_Float16)(p[ht][2 * pr + 1] * sn[2 * pr + 1]);
-          l_run[ht] = fmaf((float)v0, rs[2 * pr], l_run[ht]);
-          l_run[ht] = fmaf((float)v1, rs[2 * pr + 1], l_run[ht]);
+          const _Float16 v0 = (_Float16)(pv[kt][ht][2 * pr] * sn[2 * pr]);
+          const _Float16 v1 = (_Float16)(pv[kt][ht][2 * pr + 1] * sn[2 * pr + 1]);
+          l_add[ht] = fmaf((float)v0, rs[2 * pr], l_add[ht]);
+          l_add[ht] = fmaf((float)v1, rs[2 * pr + 1], l_add[ht]);
           pk[ht][pr] = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
         }
@@ -637,157 +618,313 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr)
           pk[ht][pr] = __builtin_bit_cast(
-              uint32_t, __builtin_convertvector(f32x2{p[ht][2 * pr], p[ht][2 * pr + 1]}, bf16x2));
+              uint32_t,
+              __builtin_convertvector(f32x2{pv[kt][ht][2 * pr], pv[kt][ht][2 * pr + 1]}, bf16x2));
     }
     // lanes of the low 16-row of each half keep tile 0 and take tile 0 of the row above;
     // lanes of the high 16-row take tile 1 of the row below and keep their tile 1
-    i32x4 pb;
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       auto r = __builtin_amdgcn_permlane16_swap(pk[0][pr], pk[1][pr], false, false);
-      pb[pr] = (int)r[0];      // keys 8h2 + 2pr + {0,1}
-      pb[2 + pr] = (int)r[1];  // keys 8h2 + 4 + 2pr + {0,1}
+      pb[kt][pr] = (int)r[0];      // keys 8h2 + 2pr + {0,1}
+      pb[kt][2 + pr] = (int)r[1];  // keys 8h2 + 4 + 2pr + {0,1}
     }
-
-    // ---- O^T[32 dims][32 heads] += V^T[32 dims][16 keys] . P^T
-    const int G = g4;
+  };
+  auto soft2 = [&]() {
 #pragma unroll
-    for (int mi = 0; mi < kDv / 32; ++mi) {
-      const int d0 = 32 * mi + 16 * (G & 1);
-      if (FP8) {
-        // lane k of the 16-row group: key j = k / 2 (row pi(8h + j)), bytes d0 + 8 (k % 2)
-        const int kr = 8 * (G >> 1) + 2 * ((c16 >> 1) & 3) + (c16 >> 3);
-        const i32x2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            LDS_PTR(i32x2, sb + kr * F::kAStride + d0 + 8 * (c16 & 1)));
-        const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, false);
-        const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, true);
-        const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, false);
-        const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, true);
-        const f16x8 a = __builtin_shufflevector(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
-                                                __builtin_shufflevector(a2, a3, 0, 1, 2, 3), 0,
-                                                1, 2, 3, 4, 5, 6, 7);
-        o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pb), o[mi],
-                                                       0, 0, 0);
-      } else {
-        // lane k of the 16-row group: keys j = k / 4 (row pi(8h + j) = 8h + 2j) and j + 4
-        // (the next row), dims d0 + 4 (k % 4)
-        const int kr = 8 * (G >> 1) + 2 * (c16 >> 2);
-        // whole-vector moves only: element-wise assembly of this operand from the two
-        // 64-bit halves was mistranslated by the compiler
-        const char* base = sb + kr * F::kAStride + 2 * (d0 + 4 * (c16 & 3));
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base));
-        const bf16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + F::kAStride));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pb),
-                                                        o[mi], 0, 0, 0);
-      }
+    for (int ht = 0; ht < 2; ++ht) {
+      le_add[ht] = l_add[ht] = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) le_add[ht] += pv[kt][ht][i];
     }
-  }
-  }  // nst > 0
+    pack_tile(0);
+    pack_tile(1);
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      le_run[ht] += le_add[ht];
+      l_run[ht] += l_add[ht];
+    }
+  };
+  // ---- region 1 of an iteration: the partial QK^T of the stage at ring offset so (36 matrix
+  // ops, two per fragment step) with the softmax of stage sst cut into slices between them,
+  // so that the vector work runs while the matrix cores are busy.  The order is pinned with
+  // scheduling fences (left alone, the scheduler issues the matrix ops back to back and the
+  // softmax after them).  Returns whether the running max must be raised.
+  auto qk_soft = [&](int so, int sst, int xo) -> bool {
+    // the partner's logits, masks and row scales of stage sst go out first
+    const char* xb = xs + xo + partner * 4096 + 16 * lane;
+    f32x4 px[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) px[kt][ht] = *(const f32x4*)(xb + (2 * kt + ht) * 1024);
+    const uint32_t mraw = *(const uint32_t*)(masks + sst * 2);  // both tiles' masks
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      zsc[kt] = f32x4{c2, c2, c2, c2};
+      if (FP8) zsc[kt] = *(const f32x4*)(scl + sst * kSR + kt * kWT + 4 * g4) * c2;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) sp[kt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kNF = 2 * kNQ2;
+    KRaw kr[kKPre];
+#pragma unroll
+    for (int f = 0; f < kKPre; ++f) kr[f] = kread(so, f);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) le_add[ht] = l_add[ht] = 0.f;
+    // softmax slice after fragment step j: for j = 2 .. 17 the logit, exponential and sum of
+    // value v = j - 2 (tile v >> 3, head tile (v >> 2) & 1, key i = v & 3); at j = 10 the P^T
+    // operand of tile 0 (tile 1's follows the last step)
+    auto slice = [&](int j) {
+      if (j >= 2) {
+        const int v = j - 2, kt = v >> 3, ht = (v >> 2) & 1, i = v & 3;
+        if ((v & 7) == 0) mk[kt] = (mraw >> (16 * kt + 4 * g4)) & 0xFu;
+        const float sf = prev[kt][ht][i] + px[kt][ht][i];
+        const float z = fmaf(sf, zsc[kt][i], -m_run[ht]);
+        const float tzv = ((mk[kt] >> i) & 1u) ? z : -INFINITY;
+        tmax = fmaxf(tmax, tzv);
+        pv[kt][ht][i] = __builtin_amdgcn_exp2f(tzv);
+        le_add[ht] += pv[kt][ht][i];
+      }
+      if (j == 10) pack_tile(0);
+    };
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      const KRaw cur = kr[f % kKPre];
+      if (f + kKPre < kNF) kr[f % kKPre] = kread(so, f + kKPre);
+      const bf16x8 a = widen(cur);
+      const int ks = f >> 1, kt = f & 1;
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        sp[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], sp[kt][ht], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      slice(f);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pack_tile(1);
+    return tmax > 8.f;
+  };
 
-  // ---- merge the two key halves of each head (waves w and w ^ 2): M = max m, factors
-  // 2^(m - M) (a wave that saw no live key has m at the floor and l = 0)
+  // ---- O^T[32 dims][32 heads] += V^T[32 dims][16 keys] . P^T over the wave's 8 dim tiles of
+  // the stage at ring offset so; `side(mi)` runs after the products of dim tile mi are issued
+  using VOp = typename std::conditional<FP8, f16x8, bf16x8>::type;
+  auto vread = [&](int so, int mi, int kt) -> VOp {
+    const int G = g4;
+    const int d0 = 256 * dv + 32 * mi + 16 * (G & 1);
+    const char* sb = ring + so + kt * F::kWBytes;
+    if constexpr (FP8) {
+      // lane k of the 16-row group: key j = k / 2 (row pi(8h + j)), bytes d0 + 8 (k % 2)
+      const int kr = 8 * (G >> 1) + 2 * ((c16 >> 1) & 3) + (c16 >> 3);
+      const i32x2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          LDS_PTR(i32x2, sb + kr * F::kAStride + d0 + 8 * (c16 & 1)));
+      const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, false);
+      const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, true);
+      const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, false);
+      const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, true);
+      return __builtin_shufflevector(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
+                                     __builtin_shufflevector(a2, a3, 0, 1, 2, 3), 0, 1, 2, 3,
+                                     4, 5, 6, 7);
+    } else {
+      // lane k of the 16-row group: keys j = k / 4 (row pi(8h + j) = 8h + 2j) and j + 4
+      // (the next row), dims d0 + 4 (k % 4).  Whole-vector moves only: element-wise assembly
+      // of this operand from the two 64-bit halves was mistranslated by the compiler.
+      const int kr = 8 * (G >> 1) + 2 * (c16 >> 2);
+      const char* base = sb + kr * F::kAStride + 2 * (d0 + 4 * (c16 & 3));
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base));
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + F::kAStride));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto vmma = [&](int mi, VOp a, int kt) {
+    if constexpr (FP8)
+      o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pb[kt]), o[mi],
+                                                     0, 0, 0);
+    else
+      o[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pb[kt]),
+                                                      o[mi], 0, 0, 0);
+  };
+  // ---- O^T[32 dims][32 heads] += V^T[32 dims][16 keys] . P^T over the wave's 8 dim tiles of
+  // the stage at ring offset so, V^T read one dim tile ahead; side_a(mi) / side_b(mi) run
+  // between the two products of dim tile mi (the order pinned as in region 1)
+  auto pv_mul = [&](int so, auto&& side_a, auto&& side_b) {
+    constexpr int kNM = kDvW / 32;
+    VOp vq[kVPre][2];  // V^T of dim tiles mi .. mi + kVPre - 1 in flight
+#pragma unroll
+    for (int m = 0; m < kVPre; ++m) {
+      vq[m][0] = vread(so, m, 0);
+      vq[m][1] = vread(so, m, 1);
+    }
+#pragma unroll
+    for (int mi = 0; mi < kNM; ++mi) {
+      const VOp c0 = vq[mi % kVPre][0], c1 = vq[mi % kVPre][1];
+      if (mi + kVPre < kNM) {
+        vq[mi % kVPre][0] = vread(so, mi + kVPre, 0);
+        vq[mi % kVPre][1] = vread(so, mi + kVPre, 1);
+      }
+      vmma(mi, c0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      side_a(mi);
+      __builtin_amdgcn_sched_barrier(0);
+      vmma(mi, c1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      side_b(mi);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto write_xs = [&](int xo) {
+    char* xb = xs + xo + wave * 4096 + 16 * lane;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) *(f32x4*)(xb + (2 * kt + ht) * 1024) = sp[kt][ht];
+  };
+  auto copy_prev = [&]() {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) prev[kt][ht] = sp[kt][ht];
+  };
+  // One iteration for stage st >= 1.  Ring slots rotate as (so_pv, so_qk, so_wr) = slots of
+  // stages st - 1, st, st + 1; the logits buffers alternate with the parity of the stage.
+  int so_pv = 0, so_qk = kSlot, so_wr = 2 * kSlot;
+  auto iteration = [&](int st) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const Gath g2 = gath_rows(min(st + 2, nst - 1));
+    const int xo_prev = ((st - 1) & 1) * 4 * 4096, xo_cur = (st & 1) * 4 * 4096;
+    // region 1: softmax of stage st - 1 (speculating that the running max holds) interleaved
+    // with the partial QK^T of stage st
+    const bool up = qk_soft(so_qk, st - 1, xo_prev);
+    if (__any(up)) {  // (rare: the running max is raised and the stage's softmax redone)
+      raise(xo_prev);
+      soft2();
+    }
+    // region 2: PV of stage st - 1, with the rows of stage st + 1 written from the queue, the
+    // gathers of stage st + 2 issued into it, and this stage's partial logits to LDS
+    commit();
+    write_xs(xo_cur);
+    copy_prev();
+    pv_mul(
+        so_pv,
+        [&](int mi) {  // the queued rows of stage st + 1 into their ring slot
+          if (mi < kNL) *(i32x4*)(ring + so_wr + gofs(mi)) = qq[mi < kNL ? mi : 0];
+          if (mi == kDvW / 32 - 1 && kNL > kDvW / 32)  // (bf16: the ninth load)
+            *(i32x4*)(ring + so_wr + gofs(kNL - 1)) = qq[kNL - 1];
+        },
+        [&](int mi) {  // the gathers of stage st + 2 into the queue
+          if (mi < kNL) qq[mi < kNL ? mi : 0] = gload(g2, mi < kNL ? mi : 0);
+          if (mi == kDvW / 32 - 1 && kNL > kDvW / 32) qq[kNL - 1] = gload(g2, kNL - 1);
+        });
+    const int t0 = so_pv;
+    so_pv = so_qk;
+    so_qk = so_wr;
+    so_wr = t0;
+  };
+
+  if (nst > 0) {
+    // prologue: stage 0 straight into slot 0, stage 1 into the queue; after the barrier,
+    // stage 1 into slot 1, stage 2 into the queue, and QK^T of stage 0
+    {
+      // (both stages' gathers go out before the first is waited for)
+      const Gath g0 = gath_rows(0);
+      const Gath g1 = gath_rows(min(1, nst - 1));
+      i32x4 q0[kNL];
+#pragma unroll
+      for (int k = 0; k < kNL; ++k) q0[k] = gload(g0, k);
+#pragma unroll
+      for (int k = 0; k < kNL; ++k) qq[k] = gload(g1, k);
+#pragma unroll
+      for (int k = 0; k < kNL; ++k) *(i32x4*)(ring + gofs(k)) = q0[k];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+#pragma unroll
+      for (int k = 0; k < kNL; ++k) *(i32x4*)(ring + kSlot + gofs(k)) = qq[k];
+      const Gath g2 = gath_rows(min(2, nst - 1));
+#pragma unroll
+      for (int k = 0; k < kNL; ++k) qq[k] = gload(g2, k);
+      qk(0);
+      write_xs(0);
+      copy_prev();
+    }
+    // slots: stage 0 in slot 0 (PV next), stage 1 in slot 1 (QK next), stage 2 goes to slot 2
+    for (int st = 1; st < nst; ++st) iteration(st);
+    // softmax and PV of the last stage
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int xo_last = ((nst - 1) & 1) * 4 * 4096;
+    const bool up = soft1(nst - 1, xo_last);
+    if (__any(up)) raise(xo_last);
+    soft2();
+    commit();
+    pv_mul(so_pv, [](int) {}, [](int) {});
+  }
+
+  // ---- per head: normaliser and lse over the four 16-lane rows; lane l holds head c32's
+  // (the two waves of a head half computed the same values)
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     le_run[ht] = rows4_sum(le_run[ht]);
     l_run[ht] = FP8 ? rows4_sum(l_run[ht]) : le_run[ht];
   }
-  if (g4 == 0) {
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      xm[(wave * 3 + 0) * kHB + 16 * ht + c16] = m_run[ht];
-      xm[(wave * 3 + 1) * kHB + 16 * ht + c16] = l_run[ht];
-      xm[(wave * 3 + 2) * kHB + 16 * ht + c16] = le_run[ht];
+  const float M = hsel ? m_run[1] : m_run[0];
+  const float Ls = hsel ? l_run[1] : l_run[0];
+  const float LEs = hsel ? le_run[1] : le_run[0];
+  const int head = h0 + c32;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  // O was accumulated relative to the largest row scale (e4m3)
+  const float fo = FP8 ? smax : 1.f;
+  if (dv == 0 && h2 == 0) {
+    if (nsplit == 1) {
+      if (lse) lse[(int64_t)t * kH + head] = LEs > 0.f ? (M + log2f(LEs)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t pr = ((int64_t)tl * nsplit + split) * kH + head;
+      *(f32x4*)(part_ml + pr * 4) = f32x4{M, Ls, LEs, 0.f};
     }
   }
-  __syncthreads();
-  float fme;  // this wave's factor for head c32
-  {
-    const int pw = wave ^ 2;
-    const float m0 = xm[(wave * 3 + 0) * kHB + c32], m1 = xm[(pw * 3 + 0) * kHB + c32];
-    const float M = fmaxf(m0, m1);
-    const float f0 = exp2f(m0 - M), f1 = exp2f(m1 - M);
-    const float Ls = f0 * xm[(wave * 3 + 1) * kHB + c32] + f1 * xm[(pw * 3 + 1) * kHB + c32];
-    const float LEs = f0 * xm[(wave * 3 + 2) * kHB + c32] + f1 * xm[(pw * 3 + 2) * kHB + c32];
-    fme = f0;
-    if (FP8) fme *= smax;  // O was accumulated relative to the largest row scale
-    if (kh == 0 && h2 == 0) {
-      xf[(hh * 3 + 0) * kHB + c32] = M;
-      xf[(hh * 3 + 1) * kHB + c32] = Ls;
-      xf[(hh * 3 + 2) * kHB + c32] = LEs;
-      const int head = h0 + c32;
-      if (nsplit == 1) {
-        if (lse) lse[(int64_t)t * kH + head] = LEs > 0.f ? (M + log2f(LEs)) * kLn2 : -INFINITY;
-      } else {
-        const int64_t pr = ((int64_t)tl * nsplit + split) * kH + head;
-        *(f32x4*)(part_ml + pr * 4) = f32x4{M, Ls, LEs, 0.f};
-      }
+  // ---- the wave's O (its 32 heads x 256 dims) through LDS into whole lines: each lane stores
+  // its four dims of head c32 (scaled) into a per-wave [32 heads][256 dims] fp32 staging area
+  // over the ring, then each store instruction writes 16 bytes per lane of two heads' rows
+  __syncthreads();  // (every wave is done with the ring)
+  float* xw = (float*)(sm + wave * (kHB * kOStage * 4));
+  const float f = (nsplit > 1 && OUT_F32) ? fo : fo * inv;  // fp32 partials stay unnormalised
+#pragma unroll
+  for (int mi = 0; mi < kDvW / 32; ++mi)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 v = {acc_read_scaled(o[mi][4 * q4], f), acc_read_scaled(o[mi][4 * q4 + 1], f),
+                       acc_read_scaled(o[mi][4 * q4 + 2], f),
+                       acc_read_scaled(o[mi][4 * q4 + 3], f)};
+      *(f32x4*)(xw + c32 * kOStage + 32 * mi + 8 * q4 + 4 * h2) = v;
     }
-  }
-  // four rounds of 128 dims: every wave stores its scaled O^T, then wave (hh, kh) sums dims
-  // 64kh .. 64kh+63 of the round over the two key halves of head half hh and writes them out,
-  // lane l taking dims 64kh + 8(l & 7) .. +7 of heads (l >> 3) + 8q, q < 4: eight lanes cover
-  // the 64 dims of a head, so each store instruction writes whole 128-byte lines of fp16 /
-  // bf16 (one straight-line copy of the rounds per kind of output)
-  float* xo = (float*)tiles;  // [wave][head][kXPitch]
-  const int sh = lane >> 3;   // summed head of q = 0
-  const int sd = 64 * kh + 8 * (lane & 7);
-  // (the normalisers of the summed heads are read after the first barrier of the rounds:
-  // the merged sums in xf come from the kh = 0 waves)
-  float inv[4];
-  const int head = h0 + sh;
-  const int64_t orow = ((int64_t)t * kH + head) * kDv;                         // output row
-  const int64_t prow = (((int64_t)tl * nsplit + split) * kH + head) * kDv;    // partial row
-  auto rounds = [&](auto&& emit) {
-#pragma unroll
-    for (int rd = 0; rd < 4; ++rd) {
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const int mi = 4 * rd + mm;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = 32 * mm + 8 * q4 + 4 * h2;
-          const f32x4 v = {acc_read_scaled(o[mi][4 * q4], fme),
-                           acc_read_scaled(o[mi][4 * q4 + 1], fme),
-                           acc_read_scaled(o[mi][4 * q4 + 2], fme),
-                           acc_read_scaled(o[mi][4 * q4 + 3], fme)};
-          *(f32x4*)(xo + (wave * kHB + c32) * kXPitch + d) = v;
-        }
-      }
-      __syncthreads();
-      if (rd == 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float L = xf[(hh * 3 + 1) * kHB + sh + 8 * q];
-          inv[q] = L > 0.f ? 1.f / L : 0.f;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float* a = xo + (hh * kHB + sh + 8 * q) * kXPitch + sd;
-        const float* b = xo + ((hh + 2) * kHB + sh + 8 * q) * kXPitch + sd;
-        const f32x4 lo = *(const f32x4*)a + *(const f32x4*)b;
-        const f32x4 hi = *(const f32x4*)(a + 4) + *(const f32x4*)(b + 4);
-        emit(q, (int64_t)8 * q * kDv + 128 * rd + sd, lo, hi);
-      }
-      if (rd < 3) __syncthreads();
+  // (the wave reads back only what it wrote: LDS operations of a wave complete in order)
+  const int64_t obase = ((int64_t)t * kH + h0) * kDv + 256 * dv;
+  const int64_t pbase = (((int64_t)tl * nsplit + split) * kH + h0) * kDv + 256 * dv;
+  if (OUT_F32) {
+    // 64 lanes x 16 bytes = one head's 256 dims per store
+#pragma unroll 4
+    for (int hr = 0; hr < kHB; ++hr) {
+      const f32x4 v = *(const f32x4*)(xw + hr * kOStage + 4 * lane);
+      if (nsplit == 1) *(f32x4*)((float*)out + obase + (int64_t)hr * kDv + 4 * lane) = v;
+      else *(f32x4*)(part_o + pbase + (int64_t)hr * kDv + 4 * lane) = v;
     }
-  };
-  if (nsplit == 1) {
-    rounds([&](int q, int64_t off, f32x4 lo, f32x4 hi) {
-      store_out8<OUT_F32>(out, orow + off, lo * inv[q], hi * inv[q]);
-    });
-  } else if (OUT_F32) {
-    rounds([&](int q, int64_t off, f32x4 lo, f32x4 hi) {
-      (void)q;
-      *(f32x4*)(part_o + prow + off) = lo;
-      *(f32x4*)(part_o + prow + off + 4) = hi;
-    });
-  } else {  // bf16 output: the split's own normalised O as an fp16 partial
-    rounds([&](int q, int64_t off, f32x4 lo, f32x4 hi) {
-      store_part16x8(part_o, prow + off, lo * inv[q], hi * inv[q]);
-    });
+  } else {
+    // 32 lanes x 8 dims (16 bytes of bf16 / fp16) per head, two heads per store
+#pragma unroll 4
+    for (int hr = 0; hr < kHB; hr += 2) {
+      const int hx = hr + (lane >> 5);
+      const float* src = xw + hx * kOStage + 8 * (lane & 31);
+      const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
+      const int64_t off = (int64_t)hx * kDv + 8 * (lane & 31);
+      if (nsplit == 1) store_out8<false>(out, obase + off, lo, hi);
+      else store_part16x8(part_o, pbase + off, lo, hi);
+    }
   }
 }
 
