@@ -316,6 +316,45 @@ def test_topk_crafted_long_rows():
             assert np.all(val[b, k:] == 0.0), (b, K)
 
 
+def test_fused_call_crafted_scores():
+    """index_score_topk on crafted score rows made by the scorer itself: every key page holds
+    the same codes, so a token's score at position s is the key scale of s times one per-token
+    constant, and the scales shape the rows: one value everywhere (the short list overflows and
+    the exact whole-row select runs), eight values (ties at the threshold), rising and falling
+    ramps, mostly exact zeros, a row no longer than K, a 65536-position row (several
+    workgroups per row) and one that ends one position into a 4096-position block.  Fused ==
+    unfused bit for bit, every row equals the oracle's Top-K of the scores the scorer wrote,
+    and those scores pass the score gate."""
+    from oracle.method import topk_token
+    lens = [32768, 32768, 32768, 32768, 20001, 1500, 65536, 4097]
+    wl = synth.reduced(synth.workload(synth.DECODE32K), lens, [1] * len(lens))
+    inp = synth.make(wl, "continuous")
+    rng = np.random.default_rng(20261204)
+    inp.k_pool = np.ascontiguousarray(
+        np.broadcast_to(inp.k_pool[inp.page_table[0, 0]], inp.k_pool.shape))
+    ks = inp.k_scale.copy()
+    for b, n in enumerate(lens):
+        pos = np.arange(n)
+        v = {0: np.full(n, 0.75), 1: rng.integers(1, 9, n) / 8.0,
+             2: np.linspace(0.5, 2.0, n), 3: np.linspace(2.0, 0.5, n),
+             4: rng.exponential(size=n) * (rng.random(n) < 0.05)}.get(b)
+        if v is None:
+            v = rng.exponential(size=n) + 0.01
+        ks[inp.page_table[b, pos // 64], pos % 64] = v.astype(np.float32)
+    inp.k_scale = ks
+    note(f"case fused call on crafted score rows T={inp.T}")
+    r = run_path(inp)
+    assert np.array_equal(r.idx, r.idx2), "fused vs unfused Top-K"
+    assert np.array_equal(r.val, r.val2), "fused vs unfused Top-K values"
+    K = inp.wl.shape.K
+    for t, n in enumerate(lens):
+        ref = topk_token(r.scores[t, :n].astype(np.float64), K)[0]
+        assert np.array_equal(r.idx[t], ref), t
+        k = int((ref >= 0).sum())
+        assert np.array_equal(r.val[t, :k], r.scores[t, ref[:k]]), t
+    check_scores(inp, Oracle(inp), r.scores, [0, 1, 4, 5, 7])
+
+
 @pytest.mark.parametrize("lens", [[40000, 5000], [8000, 3000, 12000]])
 def test_graph_capture_replays(lens):
     """The fused selection and the attention call captured in a HIP graph: every replay, with

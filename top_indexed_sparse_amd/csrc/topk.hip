@@ -549,8 +549,10 @@ __global__ __launch_bounds__(256) void topk_long_hist_kernel(DevBatch bt, int t_
         for (int e = 0; e < 4; ++e) v[e] = p + e < p1 ? row[p + e] : 0.f;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (p + e < p1) atomicAdd(&h[order_key(v[e]) >> 21], 1u);
+      for (int e = 0; e < 4; ++e) {  // (key 0 is never listed: it is not counted either)
+        const uint32_t k = order_key(v[e]);
+        if (p + e < p1 && k != 0u) atomicAdd(&h[k >> 21], 1u);
+      }
     }
   }
   __syncthreads();
@@ -573,6 +575,11 @@ __global__ __launch_bounds__(1024) void topk_long_pick_kernel(DevBatch bt, int t
   // bins in descending order: thread i owns bins 2047 - 2i and 2046 - 2i
   const uint32_t* hr = hist + (int64_t)tl * 2048;
   const uint32_t ch = hr[2047 - 2 * tid], cl = hr[2046 - 2 * tid];
+  if (tid == 0) {  // (no bin reaches K only when keys 0 were left out: overflow, as for ties)
+    pick[0] = 0u;
+    pick[1] = ~0u;
+    pick[2] = 0u;
+  }
   uint32_t tot;
   const uint32_t above_h = block_excl_scan(ch + cl, sh, tot);
   const uint32_t above_l = above_h + ch;
@@ -681,6 +688,11 @@ __global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int 
   const int tid = threadIdx.x, tl = blockIdx.x;
   const int t = t_begin + tl;
   const uint32_t* st = state + 4 * tl;
+  // the list, 8 consecutive entries per thread (position order), requested with the state
+  // (entries past the list's end are not used)
+  uint64_t cv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cv[j] = cand[(int64_t)tl * kLongCap + 8 * tid + j];
   const uint32_t mode = st[0];
   if (mode == kLongOver) return;
   const float* row = scores + (int64_t)tl * ld;
@@ -694,13 +706,12 @@ __global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int 
     }
     return;
   }
-  // the list, 8 consecutive entries per thread (position order); key 0 past its end
+  // key 0 past the list's end
   const uint32_t cnt = min(st[2], (uint32_t)kLongCap);
   uint32_t key[8], pos[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint32_t i = 8u * tid + j;
-    const uint64_t c = i < cnt ? cand[(int64_t)tl * kLongCap + i] : 0ull;
+    const uint64_t c = 8u * tid + j < cnt ? cv[j] : 0ull;
     key[j] = (uint32_t)(c >> 32);
     pos[j] = (uint32_t)c;
   }
@@ -731,7 +742,7 @@ __global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int 
     }
     if (sel && o < (uint32_t)K) {  // (exactly K are selected; the bound keeps it in the row)
       oi[o] = (int32_t)pos[j];
-      if (ov) ov[o] = row[pos[j]] + 0.f;  // (+ 0: -0.0 comes out as +0.0, as from a key)
+      if (ov) ov[o] = key_value(key[j]);  // (the score; -0.0 comes out as +0.0)
       ++o;
     }
   }
