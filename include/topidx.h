@@ -29,6 +29,7 @@
  *    q_len_b = cu_q[b+1] - cu_q[b] positions (the caller has already appended them to both
  *    caches); flattened token t of request b sits at position p_t = seq_lens[b] - q_len_b +
  *    (t - cu_q[b]) and attends causally to positions 0..p_t (n_t = p_t + 1 candidates).
+ *    cache_append writes those rows.
  *  - Page-table entries read by the library (logical pages below ceil(seq_lens[b]/64)) must
  *    lie in [0, n_pages); a position whose page is out of range is never read: it scores
  *    -inf and is skipped by attention.  Scales must be positive and finite; caches hold no
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define TIS_ABI_VERSION 2
+#define TIS_ABI_VERSION 3
 #define TIS_PAGE_SIZE 64
 
 typedef enum {
@@ -175,6 +176,31 @@ tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_
                              const int32_t* topk_idx, int32_t K, int32_t H, int32_t D_qk,
                              int32_t D_v, float softmax_scale, void* out, tis_dtype_t out_dt,
                              float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* cache_append - write the rows of the batch's query tokens into their slots of one paged
+ * cache, the step before the path ("Day-0 Support for Large Model Inference", Core Operator
+ * Optimization item 1: the index stays on the device and is updated incrementally; "Day 0
+ * Support for New LLM Architectures", Key Optimization 2: an FP8 cache whose scale factors
+ * are computed online, here one fp32 scale per token over the whole row).
+ *   Row t of `rows` goes to position p_t of its request (see the conventions above), i.e.
+ *   slot page_table[b][p_t / 64] * 64 + p_t % 64, and is stored as
+ *     TIS_E4M3: pool_scale[slot] = amax / 448 rounded to fp32 (amax = the largest |x| of the
+ *               row; a scale of 0 is replaced by 1), and each code is the e4m3 round-to-
+ *               nearest-even of the fp32 quotient x / pool_scale[slot], clamped to +-448
+ *               (the sign of zero is kept);
+ *     TIS_BF16: x rounded to bf16, to nearest even (pool_scale unused, must be NULL).
+ *   A token whose page-table entry lies outside [0, n_pages) is not written.  Rows must be
+ *   finite.  Call it once per cache (indexer keys: D = D_I; latent rows: D = D_qk).
+ * rows        [T][D] TIS_F32 or TIS_BF16, 16-byte aligned
+ * D           a multiple of 16, 16 <= D <= 2048
+ * pool        [n_pages][64][D] of pool_dt (TIS_E4M3 or TIS_BF16), 16-byte aligned
+ * pool_scale  [n_pages][64] fp32 (TIS_E4M3) or NULL (TIS_BF16)
+ * Other slots of pool and pool_scale are left as they are.  Tokens of one call must not
+ * share a slot (two writes of one slot race).
+ */
+tis_status_t cache_append(const tis_batch_t* batch, const void* rows, tis_dtype_t rows_dt,
+                          int32_t D, void* pool, tis_dtype_t pool_dt, float* pool_scale,
+                          void* stream);
 
 /* Workspace sizes in bytes for the calls above, from the host fields of `batch` only (the
  * caller owns every buffer).  index_score needs none and returns 0.  topk_select: nonzero only

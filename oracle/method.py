@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import bf16_decode, e4m3_decode, e4m3_round
+from .codecs import bf16_decode, bf16_round, e4m3_decode, e4m3_encode, e4m3_round
 
 PAGE = 64
 
@@ -56,6 +56,59 @@ def decode_rows(pool, scale, pt_row, positions, fmt: str) -> np.ndarray:
     if fmt == "e4m3":
         return e4m3_decode(raw) * scale.reshape(-1)[slot].astype(np.float64)[:, None]
     raise ValueError(fmt)
+
+
+# ----------------------------------------------------------------------------- N1
+def quantize_row_e4m3(x) -> tuple[np.ndarray, np.float32]:
+    """One cached row's per-token e4m3 quantisation, for the FP8 cache of "Day 0 Support for
+    New LLM Architectures", Key Optimization 2 (FP8 cache whose scale factors are computed
+    online; here one fp32 scale per token over the whole row).
+
+    scale = amax/448 rounded to fp32, so that the largest magnitude maps to the largest finite
+    e4m3 value (448); a scale of 0 (an all-zero row, or amax/448 below the fp32 range) is
+    replaced by 1.  Each element's code is the e4m3 round-to-nearest-even of the fp32 quotient
+    x/scale, clamped to +-448 first.  Both quotients are formed in fp64 from fp32 operands and
+    rounded once to fp32, which equals the correctly rounded fp32 division (53 >= 2*24 + 2
+    bits).  x: fp32 values (one row).  Returns (uint8 codes, fp32 scale)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    scale = float(np.float32(amax / 448.0))
+    if scale == 0.0:
+        scale = 1.0
+    y = (x / scale).astype(np.float32).astype(np.float64)
+    return e4m3_encode(np.clip(y, -448.0, 448.0)), np.float32(scale)
+
+
+def cache_append(pool, scale, pt_row, positions, rows, fmt: str):
+    """Append new rows of one request to a paged cache ("Day-0 Support for Large Model
+    Inference", Core Operator Optimization 1: the selection index is kept on the device and
+    updated incrementally; "Achieving Day-0 Readiness ... Million-Token Context", section 2.2:
+    fixed-size blocks located through a block index table).
+
+    Row i goes to logical position positions[i], i.e. physical slot
+    page_table[p // 64] * 64 + p % 64, and is stored in the cache's format: 'e4m3' codes with
+    the slot's fp32 scale (quantize_row_e4m3), or 'bf16' (round to nearest even, scale
+    untouched).  A position whose page-table entry lies outside the pool is not written.
+    Returns updated copies (pool, scale); the arguments are not modified."""
+    pool = np.array(pool, copy=True)
+    scale = None if scale is None else np.array(scale, copy=True)
+    D = pool.shape[-1]
+    flat = pool.reshape(-1, D)
+    sflat = None if scale is None else scale.reshape(-1)
+    n_slots = flat.shape[0]
+    rows = np.asarray(rows, dtype=np.float32)
+    for i, p in enumerate(np.asarray(positions, dtype=np.int64)):
+        page = int(np.asarray(pt_row)[p // PAGE])
+        slot = page * PAGE + int(p % PAGE)
+        if page < 0 or slot >= n_slots:
+            continue
+        if fmt == "e4m3":
+            flat[slot], sflat[slot] = quantize_row_e4m3(rows[i])
+        elif fmt == "bf16":
+            flat[slot] = bf16_round(rows[i])
+        else:
+            raise ValueError(fmt)
+    return pool, scale
 
 
 # ----------------------------------------------------------------------------- A1

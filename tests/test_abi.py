@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     lib = tis.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tis_abi_version() == 2
+    assert lib.tis_abi_version() == 3
 
 
 class FakeBatch:
@@ -169,3 +169,23 @@ def test_query_modes():
     assert call_index(b, qm=7) == L.TIS_ERR_UNSUPPORTED
     assert call_index(b, qm=L.TIS_QMODE_BF16, H=32) == L.TIS_ERR_UNSUPPORTED
     assert call_index(b, qm=L.TIS_QMODE_BF16, ks=None) == L.TIS_ERR_INVALID
+
+
+def test_cache_append_argument_validation():
+    """cache_append: rows and pool set and aligned, D a multiple of 16 in [16, 2048], fp32 or
+    bf16 rows, an e4m3 cache with (a bf16 cache without) its scale array."""
+    lib = tis.lib()
+    b = FakeBatch([1000, 600], [0, 1, 3])
+
+    def call(rows=D, rdt=L.TIS_F32, Dd=576, pool=D, pdt=L.TIS_E4M3, ps=D):
+        return lib.cache_append(b.ref, rows, rdt, Dd, pool, pdt, ps, None)
+
+    assert call(rows=None) == L.TIS_ERR_INVALID
+    assert call(pool=D + 8) == L.TIS_ERR_INVALID
+    assert call(Dd=100) == L.TIS_ERR_INVALID
+    assert call(Dd=4096) == L.TIS_ERR_INVALID
+    assert call(ps=None) == L.TIS_ERR_INVALID
+    assert call(pdt=L.TIS_BF16) == L.TIS_ERR_INVALID          # bf16 cache takes no scale
+    assert call(rdt=L.TIS_E4M3) == L.TIS_ERR_UNSUPPORTED
+    assert call(pdt=L.TIS_F32, ps=None) == L.TIS_ERR_UNSUPPORTED
+    assert lib.cache_append(None, D, 0, 576, D, 2, D, None) == L.TIS_ERR_INVALID

@@ -1,15 +1,16 @@
 """MI355X-native indexer-driven Top-K sparse attention (libtopidx, gfx950).
 
 The Python surface mirrors the C ABI in include/topidx.h one to one: index_score,
-topk_select, index_score_topk and sparse_mla_attn, plus workspace-size queries.  All
+topk_select, index_score_topk (and its allocation-free variant), sparse_mla_attn and
+cache_append, plus workspace-size queries.  All
 computation happens in the HIP kernels of libtopidx.so."""
-from ._lib import (Batch, TisError, index_score, index_score_topk, index_score_topk_noalloc,
+from ._lib import (Batch, TisError, cache_append, index_score, index_score_topk, index_score_topk_noalloc,
                    index_score_topk_workspace_size,
                    lib, sparse_mla_attn, sparse_mla_attn_workspace_size, topk_select,
                    topk_select_workspace_size,
                    TIS_F32, TIS_BF16, TIS_E4M3, TIS_QMODE_FP8, TIS_QMODE_BF16, LIB_PATH, EXPORTS)
 
-__all__ = ["Batch", "TisError", "index_score", "index_score_topk", "index_score_topk_noalloc",
+__all__ = ["Batch", "TisError", "cache_append", "index_score", "index_score_topk", "index_score_topk_noalloc",
            "index_score_topk_workspace_size", "lib", "sparse_mla_attn",
            "sparse_mla_attn_workspace_size", "topk_select", "topk_select_workspace_size", "TIS_F32", "TIS_BF16", "TIS_E4M3",
            "TIS_QMODE_FP8", "TIS_QMODE_BF16", "LIB_PATH", "EXPORTS"]

@@ -18,7 +18,7 @@ TIS_QMODE_FP8, TIS_QMODE_BF16 = 0, 1
 PAGE_SIZE = 64
 
 EXPORTS = ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
-           "sparse_mla_attn",
+           "sparse_mla_attn", "cache_append",
            "index_score_workspace_size", "topk_select_workspace_size",
            "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size",
            "tis_last_error", "tis_abi_version")
@@ -67,8 +67,9 @@ def lib():
                                            _I32, _P, _P, _P]
     L.sparse_mla_attn.argtypes = [_BP, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F,
                                   _P, _I32, _P, _P, _SZ, _P]
+    L.cache_append.argtypes = [_BP, _P, _I32, _I32, _P, _I32, _P, _P]
     for f in ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
-              "sparse_mla_attn"):
+              "sparse_mla_attn", "cache_append"):
         getattr(L, f).restype = _I32
     L.index_score_workspace_size.argtypes = [_BP, _I32, _I32]
     L.topk_select_workspace_size.argtypes = [_BP, _I32]
@@ -77,7 +78,7 @@ def lib():
     for f in ("index_score_workspace_size", "topk_select_workspace_size",
               "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size"):
         getattr(L, f).restype = _SZ
-    if L.tis_abi_version() != 2:
+    if L.tis_abi_version() != 3:
         raise RuntimeError("libtopidx ABI version mismatch")
     _lib = L
     return L
@@ -220,3 +221,13 @@ def sparse_mla_attn(batch: Batch, q, kv_pool, kv_scale, topk_idx, softmax_scale:
                                  float(softmax_scale), _ptr(out), _dtype(out), _ptr(lse),
                                  _ptr(ws), nb, _stream()))
     return out
+
+
+def cache_append(batch: Batch, rows, pool, pool_scale=None):
+    """Write rows [T][D] (fp32 or bf16) of the batch's query tokens into their slots of a paged
+    cache pool [n_pages][64][D] (uint8 e4m3 codes with pool_scale [n_pages][64] fp32, or bf16
+    with pool_scale None)."""
+    D = int(rows.shape[-1])
+    _check(lib().cache_append(batch.ref, _ptr(rows), _dtype(rows), D, _ptr(pool), _dtype(pool),
+                              _ptr(pool_scale), _stream()))
+    return pool

@@ -385,6 +385,31 @@ TIS_API tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const vo
                    rows, ptr, (hipStream_t)stream);
 }
 
+TIS_API tis_status_t cache_append(const tis_batch_t* batch, const void* rows,
+                                  tis_dtype_t rows_dt, int32_t D, void* pool, tis_dtype_t pool_dt,
+                                  float* pool_scale, void* stream) {
+  tis_status_t st = check_batch(batch, nullptr);
+  if (st != TIS_OK) return st;
+  if (!rows || !pool) return fail(TIS_ERR_INVALID, "rows and pool must be set");
+  if (!aligned16(rows) || !aligned16(pool))
+    return fail(TIS_ERR_INVALID, "rows and pool must be 16-byte aligned");
+  if (D < 16 || D > 2048 || D % 16)
+    return fail(TIS_ERR_INVALID, "D must be a multiple of 16 in [16, 2048] (got %d)", D);
+  if (rows_dt != TIS_F32 && rows_dt != TIS_BF16)
+    return fail(TIS_ERR_UNSUPPORTED, "cache_append takes fp32 or bf16 rows");
+  if (pool_dt == TIS_E4M3) {
+    if (!pool_scale || ((uintptr_t)pool_scale & 3))
+      return fail(TIS_ERR_INVALID, "an e4m3 cache needs a 4-byte aligned pool_scale");
+  } else if (pool_dt == TIS_BF16) {
+    if (pool_scale) return fail(TIS_ERR_INVALID, "a bf16 cache takes no pool_scale");
+  } else {
+    return fail(TIS_ERR_UNSUPPORTED, "cache_append writes e4m3 or bf16 caches");
+  }
+  hipError_t e = tis::launch_cache_append(dev_batch(batch), rows, rows_dt == TIS_BF16, D, pool,
+                                          pool_dt == TIS_E4M3, pool_scale, (hipStream_t)stream);
+  return e == hipSuccess ? TIS_OK : hip_fail(e, "cache_append launch");
+}
+
 TIS_API tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_t q_dt,
                                      const void* kv_pool, tis_dtype_t kv_dt,
                                      const float* kv_scale, const int32_t* topk_idx, int32_t K,

@@ -32,5 +32,7 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
 int attn_split_count(int t_count, int K);
 int attn_keys_per_split(int K, int nsplit);
 size_t attn_smem_bytes(bool fp8, int kps);
+hipError_t launch_cache_append(const DevBatch& bt, const void* rows, bool rows_bf16, int D,
+                               void* pool, bool pool_e4m3, float* pool_scale, hipStream_t st);
 
 }  // namespace tis
