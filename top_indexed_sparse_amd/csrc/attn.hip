@@ -13,14 +13,16 @@
 // 256dv .. 256dv + 255 over every key of the split:
 //   * the split's positions are translated through the page table once into LDS;
 //   * 32-row stages are gathered with 16-byte loads (each wave a fixed eight rows) into a
-//     one-stage register queue and written into a three-stage LDS ring; e4m3 rows stay e4m3
-//     in LDS and are widened per fragment;
+//     one-stage register queue and written into a three-stage LDS ring; the value part of an
+//     e4m3 row is widened exactly to fp16 as it is written (once per workgroup), its RoPE part
+//     stays e4m3 and is widened per fragment; the matrix cores then run on fp16 (Q rounded to
+//     fp16 once), and on bf16 for a bf16 cache;
 //   * each wave multiplies its half of the 576 contracted dims, S^T = K . Q^T on
 //     v_mfma_f32_16x16x32 (all of its Q^T in registers), and the two waves of a head half
 //     add their partial logits through LDS;
 //   * O^T[vdim][head] += V^T . P^T on v_mfma_f32_32x32x16: P reaches the B layout with one
 //     permlane16 swap, and V^T fragments come from the row-major tile via
-//     ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3);
+//     ds_read_b64_tr_b16 (bf16 / fp16);
 //   * the stages are software pipelined (QK^T of stage st beside the softmax of stage
 //     st - 1, then PV of st - 1 beside the ring writes and gathers), with the order of
 //     matrix and vector work pinned by scheduling fences;
@@ -119,24 +121,21 @@ constexpr float kMFloor = -1e30f;  // running max before the first live key (log
 // than a multiple of the 64 LDS banks and the B stride 4 more than a multiple of 16 (both
 // measured fastest for the reads below), and the rows are consumed in the order
 // pi(8h + j) = 8h + 2j (j < 4), 8h + 2(j - 4) + 1 (j >= 4), which makes both the 16-byte
-// key-fragment reads and the transposed value reads nearly free of bank conflicts.  bf16:
-// 1056-byte A rows, 18 loads per tile; e4m3: 544-byte A rows, 17 loads (one of them issued
-// by both waves).
+// key-fragment reads and the transposed value reads nearly free of bank conflicts.  Region A
+// holds 16-bit values in both cases (an e4m3 row's value part is widened exactly to fp16 as it
+// is written, once per workgroup, instead of at every fragment read); region B holds the RoPE
+// dims as cached (bf16, or e4m3, widened per fragment: one fragment of nine), which keeps the
+// e4m3 kernel's LDS, with its row-scale table, within the 160 KB.
 template <bool FP8>
 struct KvFmt {
-  static constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;   // cached row
-  static constexpr int kVBytes = FP8 ? kDv : 2 * kDv;       // value part (region A)
-  static constexpr int kRBytes = kRowBytes - kVBytes;       // RoPE part (region B): 64 / 128
-  static constexpr int kAStride = kVBytes + 32;             // row stride, region A
-  static constexpr int kRStride = kRBytes + 16;             // row stride, region B
+  static constexpr int kRowBytes = FP8 ? kDqk : 2 * kDqk;   // cached row (global memory)
+  static constexpr int kVBytes = FP8 ? kDv : 2 * kDv;       // its value part
+  static constexpr int kRBytes = kRowBytes - kVBytes;       // its RoPE part: 64 / 128
+  static constexpr int kAStride = 2 * kDv + 32;             // row stride, region A (16-bit)
+  static constexpr int kRStride = kRBytes + 16;             // row stride, region B (as cached)
   static constexpr int kABytes = kWT * kAStride;
   static constexpr int kBBytes = kWT * kRStride;
   static constexpr int kWBytes = kABytes + kBBytes;         // one wave tile
-  static constexpr int kBLoads = kWT * kRBytes / 1024;      // 64 lanes x 16 bytes each
-  static constexpr int kIssue = kWT + kBLoads;              // loads per tile
-  static constexpr int kIssueW = (kIssue + 1) / 2;          // loads per tile and wave
-  static constexpr int kBufs = 2;                           // stages in the ring
-  static constexpr int kTiles = kBufs * 2 * kWBytes;        // LDS bytes of the ring
 };
 __host__ __device__ constexpr int tile_row(int m) {  // pi: consumption order -> tile row
   return (m & 8) + ((m & 4) ? 2 * (m & 3) + 1 : 2 * (m & 3));
@@ -241,14 +240,14 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // of the split; its QK^T covers one half of the 576 contracted dims (value dims 256dv.. and RoPE
 // dims 512 + 32dv..), and the two waves of a head half (w and w ^ 2) add their partial logits
 // through LDS.  Per 32-key stage (two 16-row tiles) and wave:
-//   S^T[16 keys][16 heads] x 2 x 2 = K . Q^T on v_mfma_f32_16x16x32_bf16 over 9 fragments of 32
+//   S^T[16 keys][16 heads] x 2 x 2 = K . Q^T on v_mfma_f32_16x16x32_bf16 (fp16 for e4m3) over 9 fragments of 32
 //     dims (K fragments from LDS, all of the wave's Q^T resident in registers; e4m3 rows are
-//     widened exactly per fragment);
+//     widened exactly: value dims to fp16 as the row is written, RoPE dims per fragment);
 //   the partial logits go to LDS; after the next barrier each wave adds its partner's and runs
 //   the online softmax per head (lane-local over 8 keys, then across the four 16-lane rows);
 //   one permlane16 swap per tile moves P^T into the B layout of v_mfma_f32_32x32x16, and
 //   O^T[32 dims][32 heads] += V^T . P^T for the wave's 8 dim tiles, V^T read by
-//   ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (e4m3, widened to fp16).
+//   ds_read_b64_tr_b16 (bf16 / fp16).
 // The stages are software pipelined.  In the iteration of stage st a wave computes its partial
 // QK^T of stage st while it finishes the softmax of stage st - 1 (whose logits its partner
 // completed before the barrier), then runs PV of stage st - 1 while it writes the gathered rows
@@ -325,14 +324,18 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // ks = value dims 256dv + 32ks (ks < 8) or RoPE dims 512 + 32dv (ks = 8)), issued after the
   // page lookups: loads complete in issue order, so the slots below wait for the page entries
   // only, and Q arrives while the slots and the first tiles are in flight.
-  bf16x8 qf[2][kNQ2];
+  // (e4m3 cache: the matrix cores run on fp16, and Q is rounded to fp16 once, before the first
+  // stage; bf16 -> fp16 is exact for |q| in [2^-14, 65504])
+  using QOp = typename std::conditional<FP8, f16x8, bf16x8>::type;
+  bf16x8 qb[2][kNQ2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const uint16_t* qr = q + ((int64_t)t * kH + h0 + 16 * ht + c16) * kDqk + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < kNQ2; ++ks)
-      qf[ht][ks] = *(const bf16x8*)(qr + (ks < kNQ2 - 1 ? 256 * dv + 32 * ks : kDv + 32 * dv));
+      qb[ht][ks] = *(const bf16x8*)(qr + (ks < kNQ2 - 1 ? 256 * dv + 32 * ks : kDv + 32 * dv));
   }
+  QOp qf[2][kNQ2];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int pg = slot[j];
@@ -437,14 +440,35 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const int wtile = (wave >> 1) * F::kWBytes;
   const int rw0 = 8 * (wave & 1);
   auto gofs = [&](int k) -> int {
-    if (FP8) {
-      if (k < 4) return wtile + (rw0 + 2 * k + (lane >> 5)) * F::kAStride + 16 * (lane & 31);
+    if (FP8) {  // (value loads: the 32 bytes their 16 codes widen to)
+      if (k < 4) return wtile + (rw0 + 2 * k + (lane >> 5)) * F::kAStride + 32 * (lane & 31);
       return wtile + F::kABytes + (rw0 + ((lane >> 2) & 7)) * F::kRStride + 16 * (lane & 3);
     }
     if (k < 8) return wtile + (rw0 + k) * F::kAStride + 16 * lane;
     return wtile + F::kABytes + (rw0 + (lane >> 3)) * F::kRStride + 16 * (lane & 7);
   };
   constexpr int kSlot = 2 * F::kWBytes;
+  // load k's data into its place in the ring slot at offset so (e4m3 value loads: the 16
+  // codes widened exactly to fp16, two 16-byte writes)
+  auto put = [&](int so, int k, const i32x4& v) {
+    char* dst = ring + so + gofs(k);
+    if constexpr (FP8) {
+      if (k < 4) {
+        i32x4 h[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i], 1.f, false);
+          const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i], 1.f, true);
+          h[i >> 1][2 * (i & 1)] = __builtin_bit_cast(int, lo);
+          h[i >> 1][2 * (i & 1) + 1] = __builtin_bit_cast(int, hi);
+        }
+        *(i32x4*)dst = h[0];
+        *(i32x4*)(dst + 16) = h[1];
+        return;
+      }
+    }
+    *(i32x4*)dst = v;
+  };
 
   // ---- register state
   f32x16 o[kDvW / 32];  // O^T: dims 256dv + 32mt + 8(i/4) + 4h2 + i%4, head h0 + c32
@@ -460,31 +484,40 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   f32x4 sp[2][2];                      // partial logits of the stage being multiplied
   f32x4 prev[2][2];                    // partial logits of the stage in softmax
   const int qrow = tile_row(c16);
-  using KRaw = typename std::conditional<FP8, i32x2, bf16x8>::type;
-  constexpr int kEB = FP8 ? 1 : 2;     // bytes per cached element
+  using KRaw = typename std::conditional<FP8, i32x4, bf16x8>::type;
 
   // K fragment f = 2ks + kt of the stage at ring offset so: lane (m = c16, g4): row pi(m),
-  // dims 8g4 .. + 7 of the wave's fragment ks
+  // dims 8g4 .. + 7 of the wave's fragment ks (value dims: 16 bytes of 16-bit values; e4m3
+  // RoPE dims: 8 codes, in the low half)
   auto kread = [&](int so, int f) -> KRaw {
     const int ks = f >> 1, kt = f & 1;
     const char* tb = ring + so + kt * F::kWBytes;
-    const char* pa = ks < kNQ2 - 1
-                         ? tb + qrow * F::kAStride + kEB * (256 * dv + 32 * ks + 8 * g4)
-                         : tb + F::kABytes + qrow * F::kRStride + kEB * (32 * dv + 8 * g4);
-    return *(const KRaw*)pa;
-  };
-  auto widen = [&](KRaw cur) -> bf16x8 {
+    if (ks < kNQ2 - 1) return *(const KRaw*)(tb + qrow * F::kAStride + 2 * (256 * dv + 32 * ks + 8 * g4));
+    const char* pb = tb + F::kABytes + qrow * F::kRStride;
     if constexpr (FP8) {
-      const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, false);
-      const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[0], 1.f, true);
-      const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, false);
-      const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur[1], 1.f, true);
+      const i32x2 c = *(const i32x2*)(pb + 32 * dv + 8 * g4);
+      return i32x4{c[0], c[1], 0, 0};
+    } else {
+      return *(const KRaw*)(pb + 2 * (32 * dv + 8 * g4));
+    }
+  };
+  auto widen = [&](KRaw cur, int ks) -> QOp {
+    if constexpr (FP8) {
+      if (ks < kNQ2 - 1) return __builtin_bit_cast(f16x8, cur);
+      const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur[0], 1.f, false);
+      const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur[0], 1.f, true);
+      const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur[1], 1.f, false);
+      const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur[1], 1.f, true);
       return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
                                      __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4,
                                      5, 6, 7);
     } else {
       return cur;
     }
+  };
+  auto qkmma = [&](QOp a, QOp b, f32x4 c) -> f32x4 {
+    if constexpr (FP8) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   };
   // partial QK^T of the stage at ring offset so into sp
   auto qk = [&](int so) {
@@ -501,11 +534,11 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     for (int f = 0; f < kNF; ++f) {
       const KRaw cur = kr[f % kPre];
       if (f + kPre < kNF) kr[f % kPre] = kread(so, f + kPre);
-      const bf16x8 a = widen(cur);
+      const QOp a = widen(cur, f >> 1);
       const int ks = f >> 1, kt = f & 1;
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
-        sp[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], sp[kt][ht], 0, 0, 0);
+        sp[kt][ht] = qkmma(a, qf[ht][ks], sp[kt][ht]);
     }
   };
 
@@ -597,7 +630,9 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sn[i] = sc[i] * inv_smax;
-        rs[i] = sc[i] > 0.f ? smax / sc[i] : 0.f;
+        // (the normaliser's weight smax/scale through the hardware reciprocal: within 1 ulp,
+        // far below the fp16 rounding of P it multiplies)
+        rs[i] = sc[i] > 0.f ? smax * __builtin_amdgcn_rcpf(sc[i]) : 0.f;
       }
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
@@ -699,11 +734,11 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     for (int f = 0; f < kNF; ++f) {
       const KRaw cur = kr[f % kKPre];
       if (f + kKPre < kNF) kr[f % kKPre] = kread(so, f + kKPre);
-      const bf16x8 a = widen(cur);
+      const QOp a = widen(cur, f >> 1);
       const int ks = f >> 1, kt = f & 1;
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht)
-        sp[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], sp[kt][ht], 0, 0, 0);
+        sp[kt][ht] = qkmma(a, qf[ht][ks], sp[kt][ht]);
       __builtin_amdgcn_sched_barrier(0);
       slice(f);
       __builtin_amdgcn_sched_barrier(0);
@@ -719,24 +754,19 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     const int G = g4;
     const int d0 = 256 * dv + 32 * mi + 16 * (G & 1);
     const char* sb = ring + so + kt * F::kWBytes;
-    if constexpr (FP8) {
-      // lane k of the 16-row group: key j = k / 2 (row pi(8h + j)), bytes d0 + 8 (k % 2)
-      const int kr = 8 * (G >> 1) + 2 * ((c16 >> 1) & 3) + (c16 >> 3);
-      const i32x2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          LDS_PTR(i32x2, sb + kr * F::kAStride + d0 + 8 * (c16 & 1)));
-      const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, false);
-      const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[0], 1.f, true);
-      const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, false);
-      const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c8[1], 1.f, true);
-      return __builtin_shufflevector(__builtin_shufflevector(a0, a1, 0, 1, 2, 3),
-                                     __builtin_shufflevector(a2, a3, 0, 1, 2, 3), 0, 1, 2, 3,
-                                     4, 5, 6, 7);
+    // lane k of the 16-row group: keys j = k / 4 (row pi(8h + j) = 8h + 2j) and j + 4 (the
+    // next row), dims d0 + 4 (k % 4).  Whole-vector moves only: element-wise assembly of this
+    // operand from the two 64-bit halves was mistranslated by the compiler.
+    const int kr = 8 * (G >> 1) + 2 * (c16 >> 2);
+    const char* base = sb + kr * F::kAStride + 2 * (d0 + 4 * (c16 & 3));
+    if constexpr (FP8) {  // (16-bit values in LDS for both caches; fp16 for an e4m3 one)
+      typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+      const f16x4 lo = __builtin_bit_cast(
+          f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(LDS_PTR(h4, base)));
+      const f16x4 hi = __builtin_bit_cast(
+          f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(LDS_PTR(h4, base + F::kAStride)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     } else {
-      // lane k of the 16-row group: keys j = k / 4 (row pi(8h + j) = 8h + 2j) and j + 4
-      // (the next row), dims d0 + 4 (k % 4).  Whole-vector moves only: element-wise assembly
-      // of this operand from the two 64-bit halves was mistranslated by the compiler.
-      const int kr = 8 * (G >> 1) + 2 * (c16 >> 2);
-      const char* base = sb + kr * F::kAStride + 2 * (d0 + 4 * (c16 & 3));
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base));
       const bf16x4 hi =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + F::kAStride));
@@ -814,9 +844,9 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     pv_mul(
         so_pv,
         [&](int mi) {  // the queued rows of stage st + 1 into their ring slot
-          if (mi < kNL) *(i32x4*)(ring + so_wr + gofs(mi)) = qq[mi < kNL ? mi : 0];
+          if (mi < kNL) put(so_wr, mi < kNL ? mi : 0, qq[mi < kNL ? mi : 0]);
           if (mi == kDvW / 32 - 1 && kNL > kDvW / 32)  // (bf16: the ninth load)
-            *(i32x4*)(ring + so_wr + gofs(kNL - 1)) = qq[kNL - 1];
+            put(so_wr, kNL - 1, qq[kNL - 1]);
         },
         [&](int mi) {  // the gathers of stage st + 2 into the queue
           if (mi < kNL) qq[mi < kNL ? mi : 0] = gload(g2, mi < kNL ? mi : 0);
@@ -841,15 +871,26 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 #pragma unroll
       for (int k = 0; k < kNL; ++k) qq[k] = gload(g1, k);
 #pragma unroll
-      for (int k = 0; k < kNL; ++k) *(i32x4*)(ring + gofs(k)) = q0[k];
+      for (int k = 0; k < kNL; ++k) put(0, k, q0[k]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     {
 #pragma unroll
-      for (int k = 0; k < kNL; ++k) *(i32x4*)(ring + kSlot + gofs(k)) = qq[k];
+      for (int k = 0; k < kNL; ++k) put(kSlot, k, qq[k]);
       const Gath g2 = gath_rows(min(2, nst - 1));
 #pragma unroll
       for (int k = 0; k < kNL; ++k) qq[k] = gload(g2, k);
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int ks = 0; ks < kNQ2; ++ks) {
+          if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qf[ht][ks][i] = (_Float16)(float)qb[ht][ks][i];
+          } else {
+            qf[ht][ks] = qb[ht][ks];
+          }
+        }
       qk(0);
       write_xs(0);
       copy_prev();
