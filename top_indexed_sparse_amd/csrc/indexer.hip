@@ -424,6 +424,142 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   }
 }
 
+// Prefill scoring with shared key pages: four consecutive tokens per 4-wave workgroup (one per
+// wave) over one 1024-key chunk (16 pages).  The tokens of one request read the same pages:
+// the four waves split each page's eight 1 KB loads (wave w: loads 2w, 2w + 1), write them
+// once into a double-buffered LDS page (one barrier per page, the next page written while the
+// current one is scored), and every wave scores its own token from it, so a page crosses the
+// memory path and the LDS transpose once per workgroup instead of once per token.  A ring of
+// four pieces keeps three pages in flight per wave.  Tokens of the group that belong to
+// different requests are scored in one pass per request (every wave loads and waits in every
+// pass; a wave stores only in its own request's pass, through a buffer resource whose record
+// count is zero otherwise).  A wave without a token (the batch's last group) only loads.
+template <bool BQ>
+__global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t_begin,
+    int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
+    const float* kscale, float* __restrict__ scores, int64_t ld) {
+  constexpr int kChunk = 1024;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tl = blockIdx.x * 4 + wave;
+  const bool has = tl < t_count;
+  const int tc = min(tl, t_count - 1);  // (a wave without a token reads a valid query)
+  const int t = t_begin + tc;
+  const int k0 = blockIdx.y * kChunk;
+  const LocLoads lw = locate_issue(bt);
+  asm volatile("" ::: "memory");
+  QRaw qr;
+  a0_load(q_idx + (int64_t)t * kIH * kID, w + (int64_t)t * kIH, lane, qr);
+  const TokLoc loc = locate_finish(bt, t, lw);
+  __shared__ int req_sh[4], n_sh[4];
+  __shared__ __attribute__((aligned(16))) uint8_t pg_sh[2][kStage];
+  if (lane == 0) {
+    req_sh[wave] = has ? loc.b : -1;
+    n_sh[wave] = has ? loc.n : 0;
+  }
+  QOps<BQ> A;
+  float wp[4][4];
+  if constexpr (BQ) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A.a[m][i] = qr.r[m][i];
+        wp[m][i] = qr.w[m][i];
+      }
+  } else {
+    a0_prologue(qr, lane, A.a, wp);
+  }
+  __syncthreads();
+  int rq[4], nn[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rq[i] = __builtin_amdgcn_readfirstlane(req_sh[i]);
+    nn[i] = __builtin_amdgcn_readfirstlane(n_sh[i]);
+  }
+  float* out = scores + (int64_t)tc * ld;
+  const int my_k1 = has ? min(k0 + kChunk, loc.n) : 0;  // the token's keys below this bound
+  struct Piece {
+    i32x4 r[2];
+    float ks;
+    bool ok;
+  };
+#pragma unroll 1
+  for (int r = 0; r < 4; ++r) {
+    const int b = rq[r];
+    bool first = b >= 0;
+#pragma unroll
+    for (int r2 = 0; r2 < 4; ++r2)
+      if (r2 < r && rq[r2] == b) first = false;
+    if (!first) continue;  // (uniform: each request once)
+    int nmax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (rq[i] == b) nmax = max(nmax, nn[i]);
+    const int k1 = min(k0 + kChunk, nmax);
+    const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;
+    if (npg == 0) continue;  // (uniform)
+    // stores at byte offset 4*s of the token's row, kept for s < my_k1 in its own request's pass
+    const bool mine = has && loc.b == b;
+    const __amdgpu_buffer_rsrc_t orsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out, 0, mine ? my_k1 * 4 : 0, kBufDword3);
+    const int pcol = min((k0 >> 6) + lane, bt.pt_stride - 1);
+    const int my_page = bt.page_table[(int64_t)b * bt.pt_stride + pcol];
+    // (fetches past the last page re-read it: no branch around a load)
+    auto fetch = [&](int g, Piece& pc) {
+      const int page = __builtin_amdgcn_readlane(my_page, min(g, npg - 1));
+      pc.ok = page >= 0 && page < bt.n_pages;
+      const int64_t pg = pc.ok ? page : 0;
+      const uint8_t* base = kpool + pg * kPage * kID;
+      pc.r[0] = __builtin_nontemporal_load((const i32x4*)(base + 1024 * (2 * wave) + 16 * lane));
+      pc.r[1] = __builtin_nontemporal_load((const i32x4*)(base + 1024 * (2 * wave + 1) + 16 * lane));
+      pc.ks = kscale[pg * kPage + lane];
+    };
+    // the wave's two loads of a page into its rows of LDS page buffer u
+    auto put = [&](int u, const Piece& pc) {
+      uint8_t* st = pg_sh[u];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *(i32x4*)(st + (8 * (2 * wave + i) + (lane >> 3)) * kPitch + 16 * (lane & 7)) = pc.r[i];
+    };
+    Piece ring[4];
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      fetch(g, ring[g]);
+      asm volatile("" ::: "memory");
+    }
+    __syncthreads();  // (the previous pass's readers are done with the buffers)
+    put(0, ring[0]);
+    __syncthreads();
+    // page g from buffer g & 1 (ring slot g & 3): fetch page g + 3, write page g + 1 into the
+    // other buffer, score page g, wait for every wave
+#pragma unroll 1
+    for (int g0 = 0; g0 < npg; g0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = g0 + u;
+        if (g >= npg) break;  // (uniform; no load or store follows the exit)
+        fetch(g + 3, ring[(u + 3) & 3]);
+        asm volatile("" ::: "memory");
+        put((g + 1) & 1, ring[(u + 1) & 3]);
+        const uint8_t* st = pg_sh[g & 1];
+        const int n = lane & 15, gg = lane >> 4;
+        KTile4 kt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint8_t* row = st + (16 * j + n) * kPitch;
+          kt.lo[j] = *(const i32x4*)(row + 16 * gg);
+          kt.hi[j] = *(const i32x4*)(row + 64 + 16 * gg);
+        }
+        float sc = score_group<BQ>(A, wp, kt) * ring[u].ks;
+        if (!ring[u].ok) sc = -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
+                                              (k0 + 64 * g + lane) * 4, 0, 0);
+        __syncthreads();
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, int max_n,
                                   const float* q, const float* w, const float* kpool, int H,
@@ -444,12 +580,15 @@ hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, 
   dim3 grid(group ? (t_count + 3) / 4 : t_count, (max_n + chunk - 1) / chunk);
   // decode: one 8-wave workgroup per 4096-key chunk of a token (512 keys per wave); prefill:
   // four tokens per 4-wave workgroup sharing a 1024-key chunk
-  auto* fn = group ? (bf16_query ? idx_score_fp8_kernel<true, true>
-                                 : idx_score_fp8_kernel<true, false>)
-                   : (bf16_query ? idx_score_fp8_kernel<false, true>
-                                 : idx_score_fp8_kernel<false, false>);
-  hipLaunchKernelGGL(fn, grid, dim3(group ? 256 : 512), 0, st, bt, t_begin, t_count, q_idx, w,
-                     kpool, kscale, scores, ld, chunk);
+  if (group) {
+    auto* gfn = bf16_query ? idx_score_group_kernel<true> : idx_score_group_kernel<false>;
+    hipLaunchKernelGGL(gfn, grid, dim3(256), 0, st, bt, t_begin, t_count, q_idx, w, kpool, kscale,
+                       scores, ld);
+    return hipGetLastError();
+  }
+  auto* fn = bf16_query ? idx_score_fp8_kernel<false, true> : idx_score_fp8_kernel<false, false>;
+  hipLaunchKernelGGL(fn, grid, dim3(512), 0, st, bt, t_begin, t_count, q_idx, w, kpool, kscale,
+                     scores, ld, chunk);
   return hipGetLastError();
 }
 
