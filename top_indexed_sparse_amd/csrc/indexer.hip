@@ -242,33 +242,30 @@ __device__ __forceinline__ float score_group(const QOps<BQ>& A, const float (&wp
   return pair16_sum(k0, k1);
 }
 
-// GROUP == false (decode): one token per workgroup (blockIdx.x) and key chunk blockIdx.y of
-//   64 pages; the pages are dealt round-robin to the eight waves (wave w scores pages
-//   w, w+8, ... of the chunk), so that at each step the workgroup reads 64 KB of consecutive
-//   pages when the request's pages are consecutive.
-// GROUP == true (prefill): four consecutive tokens per workgroup, one per wave, each over
-//   all pages of the same chunk.
-template <bool GROUP, bool BQ>
-__global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBatch bt,
-    int t_begin, int t_count, const uint16_t* q_idx, const float* w,
-    const uint8_t* kpool, const float* kscale,
-    float* __restrict__ scores, int64_t ld, int chunk) {
+// Decode scoring: one token per workgroup (blockIdx.x) and key chunk blockIdx.y of 64 pages;
+// the pages are dealt round-robin to the eight waves (wave w scores pages w, w+8, ... of the
+// chunk), so that at each step the workgroup reads 64 KB of consecutive pages when the
+// request's pages are consecutive.
+template <bool BQ>
+__global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_begin,
+    int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
+    const float* kscale, float* __restrict__ scores, int64_t ld, int chunk) {
   // (the wave index through readfirstlane, so that the ranges derived from it are scalars)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  constexpr int kStep = GROUP ? 1 : 8;  // page stride of a wave within the chunk
-  const int tl = GROUP ? blockIdx.x * 4 + wave : blockIdx.x;
-  const int poff = GROUP ? 0 : wave;    // the wave's first page within the chunk
+  constexpr int kStep = 8;  // page stride of a wave within the chunk
+  const int tl = blockIdx.x;
+  const int poff = wave;    // the wave's first page within the chunk
   const int k0 = blockIdx.y * chunk;
-  if (tl >= t_count) return;  // (decode: the same for every wave of the workgroup)
+  if (tl >= t_count) return;  // (the same for every wave of the workgroup)
   const int t = t_begin + tl;
   // Page ids of the chunk, one per lane, fetched once (a scalar page-table load per page
   // would stall every prefetch on a scalar round trip).  Everything waits on them, so they
   // are requested first, together with the token's request lookup, for request min(t, B - 1)
   // (the request of token t when every request has one token), and again if that was not it.
   // The query goes out behind them (loads complete in issue order, so the first pages need
-  // not wait for it).  Decode: the eight waves share the token, so waves 0..3 each quantise
-  // one 16-head tile and hand it over through LDS (every wave loads tile wave & 3: a load
-  // under a branch would make the compiler wait for the query before the first pages).
+  // not wait for it).  The eight waves share the token, so waves 0..3 each quantise one
+  // 16-head tile and hand it over through LDS (every wave loads tile wave & 3: a load under a
+  // branch would make the compiler wait for the query before the first pages).
   const int pg0 = k0 >> 6;
   const int pcol = min(pg0 + lane, bt.pt_stride - 1);
   const int bguess = min(t, bt.B - 1);
@@ -277,16 +274,17 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   asm volatile("" ::: "memory");  // (the query loads stay behind these)
   const uint16_t* qrow = q_idx + (int64_t)t * kIH * kID;
   const float* wrow = w + (int64_t)t * kIH;
-  QRaw qr;
-  if (GROUP) a0_load(qrow, wrow, lane, qr);
-  else a0_load_tile(qrow, wrow, lane, wave & 3, qr.r[0], qr.w[0]);
+  i32x4 qr[4];
+  float qw[4];
+  a0_load_tile(qrow, wrow, lane, wave & 3, qr, qw);
   const TokLoc loc = locate_finish(bt, t, lw);
   const int k1 = min(k0 + chunk, loc.n);                 // the chunk's keys in range
   const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;  // its pages in range (<= 64)
   const bool active = npg > poff;  // the wave has a page in range
   // A wave with no keys leaves now, unless it quantises a query tile for the others (it
-  // then reads one page of its request and scores nothing).
-  if (!active && (GROUP || wave >= 4)) return;
+  // then reads one page of its request and scores nothing).  (An ended wave no longer takes
+  // part in the workgroup's barriers.)
+  if (!active && wave >= 4) return;
   if (loc.b != bguess) my_page = bt.page_table[(int64_t)loc.b * bt.pt_stride + pcol];
   float* out = scores + (int64_t)tl * ld;
 
@@ -297,34 +295,29 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
   // wave's last page re-reads that page, a page past it is not scored, and scores go out
   // through a buffer resource that ends at the chunk's last key in range, so the hardware
   // drops stores past it.
-  constexpr int kPages = GROUP ? 16 : 8;
+  constexpr int kPages = 8;
   auto page_id = [&](int g) {
     return __builtin_amdgcn_readlane(my_page, npg > 0 ? min(poff + g * kStep, npg - 1) : 0);
   };
   struct Slot {
     KPage kp;
-    float ks;
     bool ok;
   };
-  // decode: the key scales of all eight pages go out first (one short stream of small reads,
-  // ahead of the pages, so that waiting for a scale never waits for a page); prefill: each
-  // page's scales go out with the page
-  float ks[GROUP ? 1 : kPages];
+  // the key scales of all eight pages go out first (one short stream of small reads, ahead of
+  // the pages, so that waiting for a scale never waits for a page)
+  float ks[kPages];
   auto fetch = [&](int g, Slot& sl) {
     const int page = page_id(g);
     sl.ok = page >= 0 && page < bt.n_pages;
     const int64_t pg = sl.ok ? page : 0;
     load_kpage(kpool + pg * kPage * kID, lane, sl.kp);
-    if (GROUP) sl.ks = kscale[pg * kPage + lane];
   };
-  if (!GROUP) {
 #pragma unroll
-    for (int g = 0; g < kPages; ++g) {
-      const int page = page_id(g);
-      ks[GROUP ? 0 : g] = kscale[(int64_t)(page >= 0 && page < bt.n_pages ? page : 0) * kPage + lane];
-    }
-    asm volatile("" ::: "memory");
+  for (int g = 0; g < kPages; ++g) {
+    const int page = page_id(g);
+    ks[g] = kscale[(int64_t)(page >= 0 && page < bt.n_pages ? page : 0) * kPage + lane];
   }
+  asm volatile("" ::: "memory");
   // (kept in this order by the empty asm statements, which the key loads cannot cross as the
   // key pointers are not marked restrict: each wait in the loop counts the loads issued after
   // the page it waits for, and one moved behind later pages would make it wait for those too)
@@ -334,23 +327,11 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
     fetch(g, sl[g]);
     asm volatile("" ::: "memory");
   }
-  __shared__ __attribute__((aligned(16))) uint8_t stage_sh[(GROUP ? 4 : 8) * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_sh[8 * kStage];
   uint8_t* stage = stage_sh + wave * kStage;
   QOps<BQ> A;
   float wp[4][4];
-  if (GROUP) {
-    if constexpr (BQ) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          A.a[m][i] = qr.r[m][i];
-          wp[m][i] = qr.w[m][i];
-        }
-    } else {
-      a0_prologue(qr, lane, A.a, wp);
-    }
-  } else {
+  {
     // (e4m3: one 32-byte operand per lane and tile; bf16: the 64 loaded bytes as they are)
     __shared__ i32x4 a_sh[4][BQ ? 4 : 2][64];
     __shared__ f32x4 w_sh[4][64];
@@ -359,12 +340,12 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
       if constexpr (BQ) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          a_sh[wave][i][lane] = qr.r[0][i];
-          wt[i] = qr.w[0][i];
+          a_sh[wave][i][lane] = qr[i];
+          wt[i] = qw[i];
         }
       } else {
         i32x8 at;
-        a0_tile(qr.r[0], qr.w[0], lane, at, wt);
+        a0_tile(qr, qw, lane, at, wt);
         a_sh[wave][0][lane] = i32x4{at[0], at[1], at[2], at[3]};
         a_sh[wave][1][lane] = i32x4{at[4], at[5], at[6], at[7]};
       }
@@ -391,36 +372,24 @@ __global__ __launch_bounds__(GROUP ? 256 : 512) void idx_score_fp8_kernel(DevBat
       __builtin_amdgcn_make_buffer_rsrc(out, 0, k1 * 4, kBufDword3);
   // page g from ring slot u: fetch page g + 3 into the slot freed last (if there is more to
   // fetch), then score page g
-  auto step = [&](int g, int u, bool more, bool score, float scale) {
+  auto step = [&](int g, int u, bool more, float scale) {
     if (more) {
       fetch(g + 3, sl[(u + 3) & 3]);
       asm volatile("" ::: "memory");  // (the loads go out before this page is scored)
     }
     const Slot& c = sl[u];
-    float sc = 0.f;
-    if (score) {
-      KTile4 kt;
-      stage_ktile4(stage, lane, c.kp, kt);
-      sc = score_group<BQ>(A, wp, kt) * (GROUP ? c.ks : scale);
-      if (!c.ok) sc = -INFINITY;
-    }
+    KTile4 kt;
+    stage_ktile4(stage, lane, c.kp, kt);
+    float sc = score_group<BQ>(A, wp, kt) * scale;
+    if (!c.ok) sc = -INFINITY;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
                                           (k0 + 64 * (poff + g * kStep) + lane) * 4, 0, 0);
   };
-  if (GROUP) {
-    // sixteen pages four at a time, the exit test only at the top of each four (an exit
-    // between them would again make the compiler wait for every outstanding load)
-    for (int g = 0; g < kPages && g < npg; g += 4) {
+  // eight pages, unrolled in full: straight-line code, whose only exit ends the kernel
 #pragma unroll
-      for (int u = 0; u < 4; ++u) step(g + u, u, true, g + u < npg, 0.f);
-    }
-  } else {
-    // eight pages, unrolled in full: straight-line code, whose only exit ends the kernel
-#pragma unroll
-    for (int g = 0; g < kPages; ++g) {
-      if (poff + g * kStep >= npg) return;
-      step(g, g & 3, g + 3 < kPages, true, ks[GROUP ? 0 : g]);  // (g is a constant here)
-    }
+  for (int g = 0; g < kPages; ++g) {
+    if (poff + g * kStep >= npg) return;
+    step(g, g & 3, g + 3 < kPages, ks[g]);  // (g is a constant here)
   }
 }
 
@@ -586,7 +555,7 @@ hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, 
                        scores, ld);
     return hipGetLastError();
   }
-  auto* fn = bf16_query ? idx_score_fp8_kernel<false, true> : idx_score_fp8_kernel<false, false>;
+  auto* fn = bf16_query ? idx_score_fp8_kernel<true> : idx_score_fp8_kernel<false>;
   hipLaunchKernelGGL(fn, grid, dim3(512), 0, st, bt, t_begin, t_count, q_idx, w, kpool, kscale,
                      scores, ld, chunk);
   return hipGetLastError();
