@@ -43,7 +43,8 @@ def decode_rows(pool, scale, pt_row, positions, fmt: str) -> np.ndarray:
     """Logical positions of one request -> fp64 rows, through its page table.
 
     Physical slot of position s: page_table[s // 64] * 64 + s % 64.  ``fmt`` is 'f32',
-    'bf16' (uint16 bits) or 'e4m3' (uint8 codes times the slot's fp32 scale, exact in fp64)."""
+    'bf16' (uint16 bits), 'e4m3' (uint8 codes times the slot's fp32 scale, exact in fp64) or
+    'mxfp8' (uint8 codes, scale bytes [n_pages][64][D/32]: mx_decode)."""
     positions = np.asarray(positions, dtype=np.int64)
     D = pool.shape[-1]
     flat = pool.reshape(-1, D)
@@ -55,6 +56,8 @@ def decode_rows(pool, scale, pt_row, positions, fmt: str) -> np.ndarray:
         return bf16_decode(raw)
     if fmt == "e4m3":
         return e4m3_decode(raw) * scale.reshape(-1)[slot].astype(np.float64)[:, None]
+    if fmt == "mxfp8":
+        return mx_decode(raw, scale.reshape(-1, D // MX_GROUP)[slot])
     raise ValueError(fmt)
 
 
@@ -79,6 +82,59 @@ def quantize_row_e4m3(x) -> tuple[np.ndarray, np.float32]:
     return e4m3_encode(np.clip(y, -448.0, 448.0)), np.float32(scale)
 
 
+# ----------------------------------------------------------------------------- N2 (MXFP8)
+MX_GROUP = 32          # elements that share one scale ("Day 0 Support for New LLM
+                       # Architectures", Key Optimization 2: the indexer's Q and K, group 32)
+MX_E4M3_EMAX = 8       # exponent of e4m3's largest binade: 448 = 1.75 * 2^8
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """Shared exponent X of one MXFP8 group, the microscaling format named by Key Optimization 2
+    of "Day 0 Support for New LLM Architectures" (8-bit elements, one power-of-two scale per
+    32 of them).  The pages give only the name and the group size; the reading here is the
+    usual microscaling rule: X = floor(log2 amax) - 8 (8 = the element format's largest
+    exponent), so the largest magnitude of the group lands in e4m3's top binade [256, 512)
+    after division by 2^X.  X is clamped to the scale byte's range [-127, 127]; an all-zero
+    group (amax = 0) takes X = -127."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, E = np.frexp(amax)                   # amax = m * 2^E, m in [0.5, 1): floor(log2) = E - 1
+    X = np.where(amax > 0, E - 1 - MX_E4M3_EMAX, -127)
+    return np.clip(X, -127, 127).astype(np.int64)
+
+
+def mx_quantize(x, group: int = MX_GROUP) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise rows [..., D] to MXFP8: for each run of ``group`` consecutive elements, the
+    shared exponent X of mx_scale_exponent, the scale byte X + 127 (an E8M0 power of two), and
+    each element's e4m3 code by round-to-nearest-even of x / 2^X clamped to +-448 (the
+    division by a power of two is exact; values in (448, 512) saturate).  The sign of zero is
+    kept.  Returns (codes uint8 [..., D], scale bytes uint8 [..., D/group])."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    if D % group:
+        raise ValueError("row width must be a multiple of the group size")
+    xg = x.reshape(x.shape[:-1] + (D // group, group))
+    X = mx_scale_exponent(np.abs(xg).max(axis=-1))
+    v = np.ldexp(xg, -X[..., None])
+    codes = e4m3_encode(np.clip(v, -448.0, 448.0))
+    return codes.reshape(x.shape), (X + 127).astype(np.uint8)
+
+
+def mx_decode(codes, sbytes, group: int = MX_GROUP) -> np.ndarray:
+    """MXFP8 rows -> fp64: each code's e4m3 value times 2^(byte - 127) of its group (exact)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    sb = np.asarray(sbytes, dtype=np.uint8).astype(np.int64)
+    D = codes.shape[-1]
+    v = e4m3_decode(codes).reshape(codes.shape[:-1] + (D // group, group))
+    return np.ldexp(v, (sb - 127)[..., None]).reshape(codes.shape)
+
+
+def mx_quantize_query(q) -> np.ndarray:
+    """The indexer query as the MXFP8 scorer uses it: q_I [..., H, D] quantised per (token,
+    head, 32 consecutive dims) and decoded again (fp64)."""
+    codes, sb = mx_quantize(q)
+    return mx_decode(codes, sb)
+
+
 def cache_append(pool, scale, pt_row, positions, rows, fmt: str):
     """Append new rows of one request to a paged cache ("Day-0 Support for Large Model
     Inference", Core Operator Optimization 1: the selection index is kept on the device and
@@ -87,14 +143,17 @@ def cache_append(pool, scale, pt_row, positions, rows, fmt: str):
 
     Row i goes to logical position positions[i], i.e. physical slot
     page_table[p // 64] * 64 + p % 64, and is stored in the cache's format: 'e4m3' codes with
-    the slot's fp32 scale (quantize_row_e4m3), or 'bf16' (round to nearest even, scale
-    untouched).  A position whose page-table entry lies outside the pool is not written.
-    Returns updated copies (pool, scale); the arguments are not modified."""
+    the slot's fp32 scale (quantize_row_e4m3), 'mxfp8' codes with the slot's D/32 scale bytes
+    (mx_quantize of the fp32 row; scale is then uint8 [n_pages][64][D/32]), or 'bf16' (round
+    to nearest even, scale untouched).  A position whose page-table entry lies outside the
+    pool is not written.  Returns updated copies (pool, scale); the arguments are not
+    modified."""
     pool = np.array(pool, copy=True)
     scale = None if scale is None else np.array(scale, copy=True)
     D = pool.shape[-1]
     flat = pool.reshape(-1, D)
-    sflat = None if scale is None else scale.reshape(-1)
+    sflat = None if scale is None else (
+        scale.reshape(-1, D // MX_GROUP) if fmt == "mxfp8" else scale.reshape(-1))
     n_slots = flat.shape[0]
     rows = np.asarray(rows, dtype=np.float32)
     for i, p in enumerate(np.asarray(positions, dtype=np.int64)):
@@ -104,6 +163,8 @@ def cache_append(pool, scale, pt_row, positions, rows, fmt: str):
             continue
         if fmt == "e4m3":
             flat[slot], sflat[slot] = quantize_row_e4m3(rows[i])
+        elif fmt == "mxfp8":
+            flat[slot], sflat[slot] = mx_quantize(rows[i])
         elif fmt == "bf16":
             flat[slot] = bf16_round(rows[i])
         else:
@@ -158,14 +219,18 @@ class Oracle:
     """The oracle over one batch of raw inputs.
 
     ``inp`` carries the boundary's raw arrays: seq_lens, cu_q, positions, req, page_table,
-    q_idx, w, k_pool, k_scale, q, kv_pool, kv_scale, and ``wl.shape`` (H_I, D_I, K, H, D_qk,
-    D_v, fp32, kv_fp8, softmax_scale).  ``qmode`` is 'fp8' (A0 applied to q_I, as the e4m3
-    scorer does) or 'none' (q_I used as stored)."""
+    q_idx, w, k_pool, k_scale, q, kv_pool, kv_scale, ``wl.shape`` (H_I, D_I, K, H, D_qk,
+    D_v, fp32, kv_fp8, softmax_scale) and ``k_fmt``, the indexer key cache's format ('f32',
+    'e4m3' with one fp32 scale per token, or 'mxfp8' with one scale byte per 32 dims).
+    ``qmode`` is 'fp8' (A0 applied to q_I, as the e4m3 scorer does), 'mxfp8' (q_I quantised
+    per 32 dims, as the MXFP8 scorer does) or 'none' (q_I used as stored); the default
+    follows the key format."""
 
     def __init__(self, inp, qmode: str | None = None):
         self.inp = inp
         self.sh = inp.wl.shape
-        self.qmode = qmode or ("none" if self.sh.fp32 else "fp8")
+        self.k_fmt = getattr(inp, "k_fmt", None) or ("f32" if self.sh.fp32 else "e4m3")
+        self.qmode = qmode or {"f32": "none", "e4m3": "fp8", "mxfp8": "mxfp8"}[self.k_fmt]
         self._kcache = (None, None)
 
     # -- indexer keys of one request, decoded once
@@ -173,9 +238,9 @@ class Oracle:
         cb, rows = self._kcache
         if cb != b or rows.shape[0] < n:
             inp = self.inp
-            fmt = "f32" if self.sh.fp32 else "e4m3"
             L = int(inp.seq_lens[b])
-            rows = decode_rows(inp.k_pool, inp.k_scale, inp.page_table[b], np.arange(L), fmt)
+            rows = decode_rows(inp.k_pool, inp.k_scale, inp.page_table[b], np.arange(L),
+                               self.k_fmt)
             self._kcache = (b, rows)
         return rows[:n]
 
@@ -184,6 +249,8 @@ class Oracle:
         qi = qi.astype(np.float64) if self.sh.fp32 else bf16_decode(qi)
         if self.qmode == "fp8":
             qi, _ = a0_quantize(qi)
+        elif self.qmode == "mxfp8":
+            qi = mx_quantize_query(qi)
         return qi
 
     def scores(self, t: int) -> np.ndarray:

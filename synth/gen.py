@@ -10,13 +10,17 @@ Recipe (the same bytes go to the GPU path and to the oracle):
   * bf16 storage: fp32 -> bf16 with torch's round-to-nearest-even cast;
   * e4m3 storage with one fp32 scale per cached token: scale = amax/448, codes = torch's
     float8_e4m3fn cast of clamp(x/scale, +-448);
+  * MXFP8 indexer keys (``k_fmt='mxfp8'``): per 32 consecutive dims a scale byte 127 + X with
+    X = floor(log2 amax) - 8 (clamped to [-127, 127]), codes = torch's float8_e4m3fn cast of
+    clamp(x / 2^X, +-448);
   * structure: 'heavy' scales a seeded 1% of positions x8 in both caches before quantisation;
     'planted' adds sqrt(D_I)*u_b to a block of 4096 k_I rows at a seeded offset, u_b the unit
     vector along sum_h w[h] q_I[h] of the request's query token; 'ragged' uses a seeded random
     page table over a pool with 25% slack;
   * every cache slot that holds no token (slack pages, the tail of a request's last page, the
     spare page that unused page-table entries point at) holds poison: code 0x7E (448) with
-    scale 1e4, bf16 0x7F00, or fp32 1e30, so a read of a wrong slot shows in the results.
+    scale 1e4 (MXFP8: scale byte 147, i.e. 2^20), bf16 0x7F00, or fp32 1e30, so a read of a
+    wrong slot shows in the results.
 
 Nothing here computes a score, a selection or an attention output.
 """
@@ -36,6 +40,8 @@ POISON_E4M3 = 0x7E
 POISON_SCALE = 1.0e4
 POISON_BF16 = 0x7F00
 POISON_F32 = 1.0e30
+POISON_MX_BYTE = 147
+MX_GROUP = 32
 
 
 def _rng(seed: int, tensor: int, b: int, block: int) -> np.random.Generator:
@@ -68,6 +74,20 @@ def to_e4m3_per_token(rows: np.ndarray):
     return codes, scale
 
 
+def to_mxfp8(rows: np.ndarray):
+    """Per 32-dim group: scale byte 127 + X, X = floor(log2 amax) - 8 clamped to [-127, 127]
+    (-127 for an all-zero group), and e4m3fn codes of clamp(x / 2^X, +-448) (torch cast)."""
+    rows = np.ascontiguousarray(rows, dtype=np.float32)
+    n, D = rows.shape
+    g = rows.astype(np.float64).reshape(n, D // MX_GROUP, MX_GROUP)
+    amax = np.abs(g).max(axis=2)
+    _, E = np.frexp(amax)
+    X = np.clip(np.where(amax > 0, E - 9, -127), -127, 127)
+    y = np.clip(np.ldexp(g, -X[..., None]), -448.0, 448.0).reshape(n, D)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, (X + 127).astype(np.uint8)
+
+
 def ints_to_e4m3(rows: np.ndarray) -> np.ndarray:
     """Exact e4m3 codes of small integers (|x| <= 3 are all representable)."""
     t = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.float32))
@@ -89,11 +109,12 @@ class Inputs:
     q_idx: np.ndarray         # [T,H_I,D_I] f32 (tiny) or uint16 bf16 bits
     w: np.ndarray             # [T,H_I] f32
     k_pool: np.ndarray        # [P,64,D_I] f32 (tiny) or uint8 e4m3 codes
-    k_scale: np.ndarray | None  # [P,64] f32 or None (tiny)
+    k_scale: np.ndarray | None  # [P,64] f32, [P,64,D_I/32] uint8 (MXFP8) or None (tiny)
     q: np.ndarray             # [T,H,D_qk] f32 (tiny) or uint16 bf16 bits
     kv_pool: np.ndarray       # [P,64,D_qk] f32 / uint16 bf16 / uint8 e4m3
     kv_scale: np.ndarray | None  # [P,64] f32 or None
     info: dict = field(default_factory=dict)
+    k_fmt: str = "e4m3"       # indexer key cache: 'f32' | 'e4m3' | 'mxfp8'
 
     @property
     def T(self) -> int:
@@ -126,10 +147,15 @@ def _page_table(wl: Workload, seed: int, random_pages: bool):
 
 
 def make(wl: Workload, mode: str = "continuous", seed: int | None = None,
-         random_pages: bool | None = None) -> Inputs:
-    """Generate every input of workload ``wl`` in ``mode`` ('continuous' | 'exact')."""
+         random_pages: bool | None = None, k_fmt: str | None = None) -> Inputs:
+    """Generate every input of workload ``wl`` in ``mode`` ('continuous' | 'exact').  ``k_fmt``
+    is the indexer key cache's format: 'e4m3' (one fp32 scale per token, the default) or
+    'mxfp8' (one scale byte per 32 dims); fp32 workloads keep fp32 keys."""
     assert mode in ("continuous", "exact")
     sh = wl.shape
+    k_fmt = "f32" if sh.fp32 else (k_fmt or "e4m3")
+    assert k_fmt in (("f32",) if sh.fp32 else ("e4m3", "mxfp8"))
+    mx = k_fmt == "mxfp8"
     seed = seed_of(wl.cfg, mode) if seed is None else int(seed)
     rp = wl.paged_random if random_pages is None else bool(random_pages)
     exact = mode == "exact"
@@ -150,7 +176,8 @@ def make(wl: Workload, mode: str = "continuous", seed: int | None = None,
     w = np.empty((T, sh.H_I), dtype=np.float32)
     q = np.empty((T, sh.H, sh.D_qk), dtype=np.float32 if f32 else np.uint16)
     k_pool = np.empty((P, PAGE, sh.D_I), dtype=np.float32 if f32 else np.uint8)
-    k_scale = None if f32 else np.empty((P, PAGE), dtype=np.float32)
+    k_scale = None if f32 else (np.empty((P, PAGE, sh.D_I // MX_GROUP), dtype=np.uint8) if mx
+                                else np.empty((P, PAGE), dtype=np.float32))
     kv_dt = np.float32 if f32 else (np.uint8 if sh.kv_fp8 else np.uint16)
     kv_pool = np.empty((P, PAGE, sh.D_qk), dtype=kv_dt)
     kv_scale = np.empty((P, PAGE), dtype=np.float32) if (sh.kv_fp8 and not f32) else None
@@ -231,12 +258,14 @@ def make(wl: Workload, mode: str = "continuous", seed: int | None = None,
             kc, ks = np.where(valid[:, None], kr, np.float32(POISON_F32)), None
             cc, cs = np.where(valid[:, None], cr, np.float32(POISON_F32)), None
         else:
-            if exact:
+            if mx:
+                kc, ks = to_mxfp8(kr)
+            elif exact:
                 kc, ks = ints_to_e4m3(kr), np.ones(n, dtype=np.float32)
             else:
                 kc, ks = to_e4m3_per_token(kr)
             kc[~valid] = POISON_E4M3
-            ks[~valid] = POISON_SCALE
+            ks[~valid] = POISON_MX_BYTE if mx else POISON_SCALE
             if sh.kv_fp8:
                 cc, cs = to_e4m3_per_token(cr)
                 cc[~valid] = POISON_E4M3
@@ -269,7 +298,7 @@ def make(wl: Workload, mode: str = "continuous", seed: int | None = None,
         kv_pool[unused] = POISON_F32
     else:
         k_pool[unused] = POISON_E4M3
-        k_scale[unused] = POISON_SCALE
+        k_scale[unused] = POISON_MX_BYTE if mx else POISON_SCALE
         if sh.kv_fp8:
             kv_pool[unused] = POISON_E4M3
             kv_scale[unused] = POISON_SCALE
@@ -279,4 +308,4 @@ def make(wl: Workload, mode: str = "continuous", seed: int | None = None,
     return Inputs(wl=wl, mode=mode, seed=seed, seq_lens=seq_lens, q_lens=q_lens, cu_q=cu_q,
                   positions=positions, req=req, page_table=pt, n_pages=P, q_idx=q_idx, w=w,
                   k_pool=k_pool, k_scale=k_scale, q=q, kv_pool=kv_pool, kv_scale=kv_scale,
-                  info=info)
+                  info=info, k_fmt=k_fmt)
