@@ -9,7 +9,8 @@ cache cannot serve a step from the previous one.  Prints one JSON line.
 
 --workload tiny|prefill64k|decode1m|ragged measures another workload the same way (one
 input replica: their inputs dwarf the last-level cache) and prints its own line; the default
-line is decode32k.  Step times are the median of --repeats timed loops of --steps steps.  The
+line is decode32k.  --k-fmt mxfp8 runs the indexer on MXFP8 keys and queries (one scale byte
+per 32 dims) instead of e4m3 keys with one fp32 scale per token, and labels its line so.  Step times are the median of --repeats timed loops of --steps steps.  The
 oracle baseline times the fp64 CPU oracle on every query token of batches of at most
 --cpu-tokens tokens, and on a bounded sample of that many tokens otherwise.
 """
@@ -190,6 +191,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="decode32k",
                     choices=["tiny", "decode32k", "prefill64k", "decode1m", "ragged"])
+    ap.add_argument("--k-fmt", default="e4m3", choices=["e4m3", "mxfp8"],
+                    help="indexer key format: e4m3 + fp32 scale per token, or MXFP8")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (8 times) and exit: the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -217,13 +220,14 @@ def main():
     from synth.device import to_device
 
     torch.cuda.set_device(0)
-    main_line = args.workload == "decode32k"
+    mx = args.k_fmt == "mxfp8"
+    main_line = args.workload == "decode32k" and not mx
     wl = synth.workload(synth.NAMES.index(args.workload))
     sh = wl.shape
-    if not main_line:
+    if args.workload != "decode32k":
         args.replicas = 1
     t0 = time.perf_counter()
-    inp = synth.make(wl, "continuous")
+    inp = synth.make(wl, "continuous", k_fmt=None if sh.fp32 else args.k_fmt)
     log(f"generated {wl.name} in {time.perf_counter() - t0:.1f}s")
     base = to_device(inp)
     reps = [base] + [type(base)(**{k: (v.clone() if v is not None else None)
@@ -302,7 +306,9 @@ def main():
     calls = {
         "index_score": dict(ms=timed(score, args.steps), bytes=a["idx_kernel_bytes"],
                             flops=a["idx_flops"], peak=FP8_PEAK,
-                            kernels=["idx_score_f32_kernel" if sh.fp32 else "idx_score_fp8_kernel"]),
+                            kernels=["idx_score_f32_kernel" if sh.fp32 else
+                                     "idx_score_group_kernel" if inp.T >= 4 * inp.B else
+                                     "idx_score_fp8_kernel"]),
         "topk_select": dict(ms=timed(select, args.steps), bytes=a["topk_kernel_bytes"],
                             flops=0, peak=FP8_PEAK, kernels=["topk_select_kernel"]),
         "sparse_mla_attn": dict(ms=timed(attend, args.steps), bytes=a["attn_bytes"],
@@ -334,7 +340,8 @@ def main():
                     "bytes_per_launch": dom["bytes"]}
     res = {
         "metric": ("sparse-attn decode queries/s @32K ctx (index+topk+attn)" if main_line else
-                   f"{wl.name} {'queries' if decode else 'tokens'}/s (index+topk+attn)"),
+                   f"{wl.name} {'queries' if decode else 'tokens'}/s (index+topk+attn)"
+                   + (", MXFP8 indexer" if mx else "")),
         "value": T * 1000.0 / step_ms,
         "unit": "queries/s" if decode else "tokens/s",
         "n_gpus": 1,
@@ -347,7 +354,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("fp32" if sh.fp32 else
-                  f"fp8 indexer / bf16 attention over a {kv} cache, fp32 accumulate"),
+                  f"{'mxfp8' if mx else 'fp8'} indexer / bf16 attention over a {kv} cache, "
+                  "fp32 accumulate"),
         "data": "synthetic",
         "config": ({"workload": "decode32k", "batch": T, "context": int(inp.seq_lens[0]),
                     "new_tokens_per_request": 1, "indexer_heads": sh.H_I, "indexer_dim": sh.D_I,
@@ -355,6 +363,8 @@ def main():
                     "kv_cache": "bf16", "index_keys": "e4m3+fp32 scale/token",
                     "input_replicas": len(reps)} if main_line else
                    {"workload": wl.name, "requests": inp.B, "query_tokens": T,
+                    "index_keys": ("fp32" if sh.fp32 else "mxfp8 (e8m0 byte/32 dims)" if mx
+                                   else "e4m3+fp32 scale/token"),
                     "max_context": int(inp.seq_lens.max()),
                     "cached_tokens": int(inp.seq_lens.sum()), "indexer_heads": sh.H_I,
                     "indexer_dim": sh.D_I, "topk": K, "heads": sh.H, "qk_dim": sh.D_qk,

@@ -23,8 +23,9 @@
  *    the last failing call on the calling thread is returned by tis_last_error().
  *  - Calls are reentrant; calls that share a workspace on overlapping streams race.
  *  - Layouts are row-major and contiguous.  Caches are paged with 64 tokens per page:
- *    pool[n_pages][64][D] (+ one fp32 scale per token slot, scale[n_pages][64]).  The
- *    logical position s of request b lives in slot s % 64 of page page_table[b][s / 64].
+ *    pool[n_pages][64][D] (+ per-slot scales: one fp32 per token slot for e4m3,
+ *    scale[n_pages][64], or D/32 bytes for MXFP8, scale[n_pages][64][D/32]).  The logical
+ *    position s of request b lives in slot s % 64 of page page_table[b][s / 64].
  *  - Request b holds seq_lens[b] positions.  Its query tokens are its LAST
  *    q_len_b = cu_q[b+1] - cu_q[b] positions (the caller has already appended them to both
  *    caches); flattened token t of request b sits at position p_t = seq_lens[b] - q_len_b +
@@ -32,8 +33,8 @@
  *    cache_append writes those rows.
  *  - Page-table entries read by the library (logical pages below ceil(seq_lens[b]/64)) must
  *    lie in [0, n_pages); a position whose page is out of range is never read: it scores
- *    -inf and is skipped by attention.  Scales must be positive and finite; caches hold no
- *    NaN/Inf codes.
+ *    -inf and is skipped by attention.  Scales must be positive and finite (MXFP8 scale
+ *    bytes below 255); caches hold no NaN/Inf codes.
  */
 #ifndef TOPIDX_H
 #define TOPIDX_H
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define TIS_ABI_VERSION 3
+#define TIS_ABI_VERSION 4
 #define TIS_PAGE_SIZE 64
 
 typedef enum {
@@ -55,18 +56,32 @@ typedef enum {
   TIS_ERR_HIP = 3           /* a HIP launch failed; see tis_last_error() */
 } tis_status_t;
 
-typedef enum { TIS_F32 = 0, TIS_BF16 = 1, TIS_E4M3 = 2 /* OCP E4M3FN */ } tis_dtype_t;
+/* Storage formats.  TIS_E4M3 caches carry one fp32 scale per token slot.  TIS_MXFP8 ("Day 0
+ * Support for New LLM Architectures", Key Optimization 2: the indexer fully quantised as MXFP8,
+ * every 32 consecutive elements sharing one scale) is E4M3FN codes with one scale byte per 32
+ * consecutive elements of a row: byte b stands for 2^(b - 127) (b = 255 is not allowed), the
+ * element's value is code * 2^(b - 127); scale bytes are laid out [n_pages][64][D / 32]. */
+typedef enum {
+  TIS_F32 = 0,
+  TIS_BF16 = 1,
+  TIS_E4M3 = 2,  /* OCP E4M3FN */
+  TIS_MXFP8 = 3  /* E4M3FN codes + one power-of-two scale byte per 32 elements */
+} tis_dtype_t;
 
 /* Indexer query handling ("Day 0 Support for New LLM Architectures", Key Optimization 1: a
  * BF16 and a quantised implementation are kept side by side; Key Optimization 2: the indexer
- * query is quantised dynamically to FP8):
- *   TIS_QMODE_FP8  - quantise each (token, head) row of q_I to e4m3 with the smallest
- *                    power-of-two scale s that keeps max|q_I|/s <= 448 (round to nearest
- *                    even), fold s into the head weight, and score on FP8 matrix cores;
- *   TIS_QMODE_BF16 - use q_I as stored: bf16 queries are multiplied on bf16 matrix cores with
- *                    the e4m3 keys widened to bf16 (exactly: every e4m3 value is a bf16
- *                    value); fp32 queries with fp32 keys use the fp32 kernel. */
-typedef enum { TIS_QMODE_FP8 = 0, TIS_QMODE_BF16 = 1 } tis_qmode_t;
+ * query is quantised dynamically, as MXFP8 with group 32):
+ *   TIS_QMODE_FP8   - quantise each (token, head) row of q_I to e4m3 with the smallest
+ *                     power-of-two scale s that keeps max|q_I|/s <= 448 (round to nearest
+ *                     even), fold s into the head weight, and score on FP8 matrix cores;
+ *   TIS_QMODE_BF16  - use q_I as stored: bf16 queries are multiplied on bf16 matrix cores with
+ *                     the e4m3 keys widened to bf16 (exactly: every e4m3 value is a bf16
+ *                     value); fp32 queries with fp32 keys use the fp32 kernel;
+ *   TIS_QMODE_MXFP8 - with TIS_MXFP8 keys: quantise q_I per (token, head, 32 consecutive
+ *                     dims) with the shared exponent X = floor(log2 amax) - 8 (clamped to
+ *                     [-127, 127]; -127 for an all-zero group) and codes RNE(q / 2^X) clamped
+ *                     to +-448; both sides' scales enter the FP8 matrix products exactly. */
+typedef enum { TIS_QMODE_FP8 = 0, TIS_QMODE_BF16 = 1, TIS_QMODE_MXFP8 = 2 } tis_qmode_t;
 
 /* A ragged, paged batch ("Achieving Day-0 Readiness ... Million-Token Context", section 2.2:
  * the cache is cut into fixed-size blocks located through a block index table; "Day-0
@@ -90,20 +105,22 @@ typedef struct {
  * Architectures", Step 1: the light indexer scores each earlier position; Key Optimization 1:
  * relevance scores and head weights computed reading the paged K cache directly).
  *   score[t][s] = sum_h w[t][h] * max(0, q_I[t][h] . k_I[s]) for s in [0, p_t], where
- *   k_I[s] = k_code[s] * k_scale[s] (e4m3 keys) or the fp32 key.  With TIS_QMODE_FP8 the
- *   query is first quantised as described at tis_qmode_t.  Accumulation is fp32.
- * q_idx   [T][H_I][D_I]  q_dt = TIS_BF16 (with k_dt = TIS_E4M3, qmode FP8 or BF16;
- *                        H_I = 64, D_I = 128) or TIS_F32 (with k_dt = TIS_F32, qmode BF16;
- *                        H_I * D_I <= 8192)
+ *   k_I[s] = k_code[s] * k_scale[s] (e4m3 keys), the MXFP8 row's values (see tis_dtype_t) or
+ *   the fp32 key.  With TIS_QMODE_FP8 or TIS_QMODE_MXFP8 the query is first quantised as
+ *   described at tis_qmode_t.  Accumulation is fp32.
+ * q_idx   [T][H_I][D_I]  q_dt = TIS_BF16 (with k_dt = TIS_E4M3 and qmode FP8 or BF16, or with
+ *                        k_dt = TIS_MXFP8 and qmode MXFP8; H_I = 64, D_I = 128) or TIS_F32
+ *                        (with k_dt = TIS_F32, qmode BF16; H_I * D_I <= 8192)
  * w       [T][H_I] fp32 head weights
- * k_pool  [n_pages][64][D_I]; k_scale [n_pages][64] fp32 (e4m3 keys) or NULL (fp32 keys)
+ * k_pool  [n_pages][64][D_I]; k_scale: [n_pages][64] fp32 (e4m3 keys), [n_pages][64][D_I/32]
+ *         scale bytes (MXFP8 keys; 16-byte aligned) or NULL (fp32 keys)
  * scores  [T][ld_scores] fp32, ld_scores >= max p_t + 1 and a multiple of 4; entries
  *         s > p_t are not written.
  * ws      unused by this call (pass NULL, 0).
  */
 tis_status_t index_score(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
                          const float* w, const void* k_pool, tis_dtype_t k_dt,
-                         const float* k_scale, int32_t H_I, int32_t D_I, tis_qmode_t qmode,
+                         const void* k_scale, int32_t H_I, int32_t D_I, tis_qmode_t qmode,
                          float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
                          void* stream);
 
@@ -131,7 +148,7 @@ tis_status_t topk_select(const tis_batch_t* batch, const float* scores, int64_t 
  * topk_select over that chunk). */
 tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
                               const float* w, const void* k_pool, tis_dtype_t k_dt,
-                              const float* k_scale, int32_t H_I, int32_t D_I,
+                              const void* k_scale, int32_t H_I, int32_t D_I,
                               tis_qmode_t qmode, int32_t K, int32_t* topk_idx,
                               float* topk_val, void* ws, size_t ws_bytes, void* stream);
 
@@ -146,7 +163,7 @@ tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx, tis_d
  * or threads) race; calls ordered on one stream do not. */
 tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const void* q_idx,
                                       tis_dtype_t q_dt, const float* w, const void* k_pool,
-                                      tis_dtype_t k_dt, const float* k_scale, int32_t H_I,
+                                      tis_dtype_t k_dt, const void* k_scale, int32_t H_I,
                                       int32_t D_I, tis_qmode_t qmode, int32_t K,
                                       int32_t* topk_idx, float* topk_val, void* stream);
 
@@ -180,26 +197,31 @@ tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_
 /* cache_append - write the rows of the batch's query tokens into their slots of one paged
  * cache, the step before the path ("Day-0 Support for Large Model Inference", Core Operator
  * Optimization item 1: the index stays on the device and is updated incrementally; "Day 0
- * Support for New LLM Architectures", Key Optimization 2: an FP8 cache whose scale factors
- * are computed online, here one fp32 scale per token over the whole row).
+ * Support for New LLM Architectures", Key Optimization 2: FP8 caches whose scale factors are
+ * computed online: one fp32 scale per token over the whole row, or MXFP8 with one scale per
+ * 32 elements for the indexer keys).
  *   Row t of `rows` goes to position p_t of its request (see the conventions above), i.e.
  *   slot page_table[b][p_t / 64] * 64 + p_t % 64, and is stored as
  *     TIS_E4M3: pool_scale[slot] = amax / 448 rounded to fp32 (amax = the largest |x| of the
  *               row; a scale of 0 is replaced by 1), and each code is the e4m3 round-to-
  *               nearest-even of the fp32 quotient x / pool_scale[slot], clamped to +-448
  *               (the sign of zero is kept);
+ *     TIS_MXFP8: per 32 consecutive elements, pool_scale byte [slot][g] = X + 127 and each
+ *               code the e4m3 round-to-nearest-even of x / 2^X clamped to +-448, with X as at
+ *               TIS_QMODE_MXFP8 (D must be a multiple of 32);
  *     TIS_BF16: x rounded to bf16, to nearest even (pool_scale unused, must be NULL).
  *   A token whose page-table entry lies outside [0, n_pages) is not written.  Rows must be
  *   finite.  Call it once per cache (indexer keys: D = D_I; latent rows: D = D_qk).
  * rows        [T][D] TIS_F32 or TIS_BF16, 16-byte aligned
  * D           a multiple of 16, 16 <= D <= 2048
- * pool        [n_pages][64][D] of pool_dt (TIS_E4M3 or TIS_BF16), 16-byte aligned
- * pool_scale  [n_pages][64] fp32 (TIS_E4M3) or NULL (TIS_BF16)
+ * pool        [n_pages][64][D] of pool_dt (TIS_E4M3, TIS_MXFP8 or TIS_BF16), 16-byte aligned
+ * pool_scale  [n_pages][64] fp32 (TIS_E4M3), [n_pages][64][D/32] bytes (TIS_MXFP8) or NULL
+ *             (TIS_BF16)
  * Other slots of pool and pool_scale are left as they are.  Tokens of one call must not
  * share a slot (two writes of one slot race).
  */
 tis_status_t cache_append(const tis_batch_t* batch, const void* rows, tis_dtype_t rows_dt,
-                          int32_t D, void* pool, tis_dtype_t pool_dt, float* pool_scale,
+                          int32_t D, void* pool, tis_dtype_t pool_dt, void* pool_scale,
                           void* stream);
 
 /* Workspace sizes in bytes for the calls above, from the host fields of `batch` only (the

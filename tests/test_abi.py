@@ -3,6 +3,9 @@ and rejects bad arguments on the host before any launch (no GPU calls are made).
 import ctypes
 import os
 import re
+import struct
+import subprocess
+import tempfile
 
 import numpy as np
 import pytest
@@ -25,7 +28,59 @@ def test_exports_every_declared_symbol():
     lib = tis.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tis_abi_version() == 3
+    assert lib.tis_abi_version() == 4
+
+
+LLVM = "/opt/rocm/llvm/bin"
+
+
+def _device_kernel_names(lib_path):
+    """Kernel symbols of every gfx950 code object in the library's offload bundles (one bundle
+    per source file in the .hip_fatbin section)."""
+    with tempfile.TemporaryDirectory() as d:
+        fat = os.path.join(d, "fat.bin")
+        subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section",
+                        f".hip_fatbin={fat}", lib_path, os.path.join(d, "copy.so")], check=True)
+        data = open(fat, "rb").read()
+        names = set()
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        for i, m in enumerate(re.finditer(re.escape(magic), data)):
+            st = m.start()
+            n = struct.unpack_from("<Q", data, st + 24)[0]
+            p = st + 32
+            for _ in range(n):
+                off, size, tl = struct.unpack_from("<QQQ", data, p)
+                triple = data[p + 24:p + 24 + tl].decode()
+                p += 24 + tl
+                if triple.endswith("gfx950"):
+                    obj = os.path.join(d, f"dev{i}.o")
+                    open(obj, "wb").write(data[st + off:st + off + size])
+                    out = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--symbols",
+                                          "--wide", obj], capture_output=True, text=True,
+                                         check=True).stdout
+                    names |= set(re.findall(r"(_ZN3tis\S+)\.kd\b", out))
+        return names
+
+
+def _registered_kernel_names(lib_path):
+    """Mangled kernel names the host side registers (string literals in .rodata)."""
+    out = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "-p", ".rodata", lib_path],
+                         capture_output=True, text=True, check=True).stdout
+    return set(re.findall(r"\]\s+(_ZN3tis\S+)", out))
+
+
+def test_registered_kernels_exist_in_the_code_object():
+    """Every kernel the host registers by mangled name exists in the gfx950 code objects, and
+    the other way round.  A name that the host and device compilation passes mangle
+    differently (e.g. a kernel signature naming a type that depends on an unnamed enum) leaves
+    the launch without a kernel, and the runtime aborts the process at its first launch."""
+    tools = ("llvm-objcopy", "llvm-readelf")
+    if not all(os.path.exists(os.path.join(LLVM, t)) for t in tools):
+        pytest.skip("ROCm llvm tools not found")
+    host = _registered_kernel_names(L.LIB_PATH)
+    dev = _device_kernel_names(L.LIB_PATH)
+    assert len(host) >= 20
+    assert host == dev, (sorted(host - dev), sorted(dev - host))
 
 
 class FakeBatch:
@@ -157,11 +212,14 @@ def test_noalloc_rejects_rows_beyond_its_scratch():
 
 
 def test_query_modes():
-    """The two indexer query modes of the header: FP8 (dynamic e4m3 query) = 0 and BF16 (the
-    query as stored) = 1; combinations outside the supported ones are refused on the host."""
+    """The three indexer query modes of the header: FP8 (dynamic e4m3 query) = 0, BF16 (the
+    query as stored) = 1 and MXFP8 (group-32 scales, with MXFP8 keys) = 2; combinations
+    outside the supported ones are refused on the host."""
     src = open(os.path.join(ROOT, "include", "topidx.h")).read()
     assert re.search(r"TIS_QMODE_FP8\s*=\s*0", src) and re.search(r"TIS_QMODE_BF16\s*=\s*1", src)
-    assert (L.TIS_QMODE_FP8, L.TIS_QMODE_BF16) == (0, 1)
+    assert re.search(r"TIS_QMODE_MXFP8\s*=\s*2", src) and re.search(r"TIS_MXFP8\s*=\s*3", src)
+    assert (L.TIS_QMODE_FP8, L.TIS_QMODE_BF16, L.TIS_QMODE_MXFP8) == (0, 1, 2)
+    assert L.TIS_MXFP8 == 3
     b = FakeBatch([1000, 600], [0, 1, 3])
     # fp32 queries and keys: only "as stored"
     assert call_index(b, qdt=L.TIS_F32, kdt=L.TIS_F32, qm=L.TIS_QMODE_FP8, ks=None, H=4,
@@ -169,11 +227,20 @@ def test_query_modes():
     assert call_index(b, qm=7) == L.TIS_ERR_UNSUPPORTED
     assert call_index(b, qm=L.TIS_QMODE_BF16, H=32) == L.TIS_ERR_UNSUPPORTED
     assert call_index(b, qm=L.TIS_QMODE_BF16, ks=None) == L.TIS_ERR_INVALID
+    # MXFP8 queries go with MXFP8 keys only, and MXFP8 keys with MXFP8 queries only
+    assert call_index(b, qm=L.TIS_QMODE_MXFP8) == L.TIS_ERR_UNSUPPORTED          # e4m3 keys
+    assert call_index(b, kdt=L.TIS_MXFP8) == L.TIS_ERR_UNSUPPORTED               # FP8 query
+    assert call_index(b, kdt=L.TIS_MXFP8, qm=L.TIS_QMODE_BF16) == L.TIS_ERR_UNSUPPORTED
+    assert call_index(b, kdt=L.TIS_MXFP8, qm=L.TIS_QMODE_MXFP8, ks=None) == L.TIS_ERR_INVALID
+    assert call_index(b, kdt=L.TIS_MXFP8, qm=L.TIS_QMODE_MXFP8, ks=D + 4) == L.TIS_ERR_INVALID
+    assert call_index(b, kdt=L.TIS_MXFP8, qm=L.TIS_QMODE_MXFP8, H=32) == L.TIS_ERR_UNSUPPORTED
+    # the attention call takes no MXFP8 cache
+    assert call_attn(FakeBatch([1000], [0, 32]), kvdt=L.TIS_MXFP8, kvs=D) == L.TIS_ERR_UNSUPPORTED
 
 
 def test_cache_append_argument_validation():
     """cache_append: rows and pool set and aligned, D a multiple of 16 in [16, 2048], fp32 or
-    bf16 rows, an e4m3 cache with (a bf16 cache without) its scale array."""
+    bf16 rows, an e4m3 or MXFP8 cache with (a bf16 cache without) its scale array."""
     lib = tis.lib()
     b = FakeBatch([1000, 600], [0, 1, 3])
 
@@ -188,4 +255,8 @@ def test_cache_append_argument_validation():
     assert call(pdt=L.TIS_BF16) == L.TIS_ERR_INVALID          # bf16 cache takes no scale
     assert call(rdt=L.TIS_E4M3) == L.TIS_ERR_UNSUPPORTED
     assert call(pdt=L.TIS_F32, ps=None) == L.TIS_ERR_UNSUPPORTED
+    # MXFP8 caches: scale bytes required, D a multiple of 32
+    assert call(pdt=L.TIS_MXFP8, ps=None) == L.TIS_ERR_INVALID
+    assert call(pdt=L.TIS_MXFP8, Dd=80) == L.TIS_ERR_INVALID
+    assert "multiple of 32" in last_error()
     assert lib.cache_append(None, D, 0, 576, D, 2, D, None) == L.TIS_ERR_INVALID

@@ -1,5 +1,5 @@
 """GPU parity of cache_append (through the C ABI) against the oracle's cache append: every byte
-of the pool and every scale bit-exact, for e4m3 and bf16 caches, fp32 and bf16 rows, the
+of the pool and every scale bit-exact, for e4m3, MXFP8 and bf16 caches, fp32 and bf16 rows, the
 indexer-key and latent row widths; then one decode step over the appended caches (index,
 Top-K, attention) against the oracle."""
 import dataclasses
@@ -57,9 +57,10 @@ def _batch(rng, D):
 
 @pytest.mark.parametrize("D", [128, 576])
 @pytest.mark.parametrize("rows_dt", ["f32", "bf16"])
-@pytest.mark.parametrize("pool_dt", ["e4m3", "bf16"])
+@pytest.mark.parametrize("pool_dt", ["e4m3", "mxfp8", "bf16"])
 def test_append_bit_exact(D, rows_dt, pool_dt):
-    rng = np.random.default_rng(1000 * D + (rows_dt == "bf16") * 10 + (pool_dt == "bf16"))
+    rng = np.random.default_rng(1000 * D + (rows_dt == "bf16") * 10 +
+                                {"e4m3": 0, "bf16": 1, "mxfp8": 2}[pool_dt])
     seq_lens, q_lens, cu_q, pt, n_pages = _batch(rng, D)
     T = int(cu_q[-1])
     note(f"case cache_append D={D} rows={rows_dt} pool={pool_dt} T={T}")
@@ -72,6 +73,9 @@ def test_append_bit_exact(D, rows_dt, pool_dt):
     if pool_dt == "e4m3":
         pool = rng.integers(0, 0x7F, (n_pages, 64, D), dtype=np.uint8)
         scale = (rng.random((n_pages, 64)) + 0.5).astype(np.float32)
+    elif pool_dt == "mxfp8":
+        pool = rng.integers(0, 0x7F, (n_pages, 64, D), dtype=np.uint8)
+        scale = rng.integers(0, 255, (n_pages, 64, D // 32), dtype=np.uint8)
     else:
         pool = rng.integers(0, 1 << 14, (n_pages, 64, D), dtype=np.uint16)
         scale = None
@@ -84,7 +88,7 @@ def test_append_bit_exact(D, rows_dt, pool_dt):
             ref_pool, ref_scale = cache_append(ref_pool, ref_scale, pt[b], pos, rows[a:e],
                                                pool_dt)
     bt = tis.Batch(seq_lens, cu_q, pt, n_pages)
-    if pool_dt == "e4m3":
+    if pool_dt in ("e4m3", "mxfp8"):
         dpool = torch.from_numpy(pool).cuda()
         dscale = torch.from_numpy(scale).cuda()
     else:
@@ -95,6 +99,9 @@ def test_append_bit_exact(D, rows_dt, pool_dt):
     if pool_dt == "e4m3":
         got = dpool.cpu().numpy()
         assert np.array_equal(dscale.cpu().numpy().view(np.uint32), ref_scale.view(np.uint32))
+    elif pool_dt == "mxfp8":
+        got = dpool.cpu().numpy()
+        assert np.array_equal(dscale.cpu().numpy(), ref_scale)
     else:
         got = dpool.cpu().view(torch.int16).numpy().view(np.uint16)
     bad = np.argwhere(got != ref_pool)

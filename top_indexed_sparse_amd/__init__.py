@@ -8,9 +8,11 @@ from ._lib import (Batch, TisError, cache_append, index_score, index_score_topk,
                    index_score_topk_workspace_size,
                    lib, sparse_mla_attn, sparse_mla_attn_workspace_size, topk_select,
                    topk_select_workspace_size,
-                   TIS_F32, TIS_BF16, TIS_E4M3, TIS_QMODE_FP8, TIS_QMODE_BF16, LIB_PATH, EXPORTS)
+                   TIS_F32, TIS_BF16, TIS_E4M3, TIS_MXFP8, TIS_QMODE_FP8, TIS_QMODE_BF16,
+                   TIS_QMODE_MXFP8, LIB_PATH, EXPORTS)
 
 __all__ = ["Batch", "TisError", "cache_append", "index_score", "index_score_topk", "index_score_topk_noalloc",
            "index_score_topk_workspace_size", "lib", "sparse_mla_attn",
-           "sparse_mla_attn_workspace_size", "topk_select", "topk_select_workspace_size", "TIS_F32", "TIS_BF16", "TIS_E4M3",
-           "TIS_QMODE_FP8", "TIS_QMODE_BF16", "LIB_PATH", "EXPORTS"]
+           "sparse_mla_attn_workspace_size", "topk_select", "topk_select_workspace_size",
+           "TIS_F32", "TIS_BF16", "TIS_E4M3", "TIS_MXFP8", "TIS_QMODE_FP8", "TIS_QMODE_BF16",
+           "TIS_QMODE_MXFP8", "LIB_PATH", "EXPORTS"]

@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtopidx.so")
 
 TIS_OK, TIS_ERR_INVALID, TIS_ERR_UNSUPPORTED, TIS_ERR_HIP = 0, 1, 2, 3
-TIS_F32, TIS_BF16, TIS_E4M3 = 0, 1, 2
-TIS_QMODE_FP8, TIS_QMODE_BF16 = 0, 1
+TIS_F32, TIS_BF16, TIS_E4M3, TIS_MXFP8 = 0, 1, 2, 3
+TIS_QMODE_FP8, TIS_QMODE_BF16, TIS_QMODE_MXFP8 = 0, 1, 2
 PAGE_SIZE = 64
 
 EXPORTS = ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
@@ -78,7 +78,7 @@ def lib():
     for f in ("index_score_workspace_size", "topk_select_workspace_size",
               "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size"):
         getattr(L, f).restype = _SZ
-    if L.tis_abi_version() != 3:
+    if L.tis_abi_version() != 4:
         raise RuntimeError("libtopidx ABI version mismatch")
     _lib = L
     return L
@@ -101,6 +101,21 @@ def _dtype(t) -> int:
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return TIS_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _cache_dtype(pool, scale) -> int:
+    """A cache's format: uint8 codes with uint8 scale bytes are MXFP8, with fp32 scales e4m3."""
+    if pool.dtype == torch.uint8 and scale is not None and scale.dtype == torch.uint8:
+        return TIS_MXFP8
+    return _dtype(pool)
+
+
+def _qmode(q_idx, k_dt, qmode):
+    if qmode is not None:
+        return qmode
+    if q_idx.dtype == torch.float32:
+        return TIS_QMODE_BF16
+    return TIS_QMODE_MXFP8 if k_dt == TIS_MXFP8 else TIS_QMODE_FP8
 
 
 def _stream():
@@ -151,12 +166,13 @@ def _ws(nbytes: int, ws, device):
 
 
 def index_score(batch: Batch, q_idx, w, k_pool, k_scale, scores, qmode=None):
-    """scores[t, s] for s <= p_t (see index_score in topidx.h)."""
+    """scores[t, s] for s <= p_t (see index_score in topidx.h).  Keys are MXFP8 when k_scale
+    holds uint8 scale bytes; qmode defaults to the key format's quantised mode."""
     H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
-    if qmode is None:
-        qmode = TIS_QMODE_BF16 if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
+    kd = _cache_dtype(k_pool, k_scale)
+    qmode = _qmode(q_idx, kd, qmode)
     _check(lib().index_score(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_pool),
-                             _dtype(k_pool), _ptr(k_scale), H_I, D_I, qmode, _ptr(scores),
+                             kd, _ptr(k_scale), H_I, D_I, qmode, _ptr(scores),
                              int(scores.stride(0)), None, 0, _stream()))
     return scores
 
@@ -180,12 +196,12 @@ def index_score_topk_workspace_size(batch: Batch, H_I: int, D_I: int, K: int) ->
 def index_score_topk(batch: Batch, q_idx, w, k_pool, k_scale, K: int, topk_idx, topk_val=None,
                      ws=None, qmode=None):
     H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
-    if qmode is None:
-        qmode = TIS_QMODE_BF16 if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
+    kd = _cache_dtype(k_pool, k_scale)
+    qmode = _qmode(q_idx, kd, qmode)
     need = index_score_topk_workspace_size(batch, H_I, D_I, K)
     ws, nb = _ws(need, ws, q_idx.device)
     _check(lib().index_score_topk(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_pool),
-                                  _dtype(k_pool), _ptr(k_scale), H_I, D_I, qmode, int(K),
+                                  kd, _ptr(k_scale), H_I, D_I, qmode, int(K),
                                   _ptr(topk_idx), _ptr(topk_val), _ptr(ws), nb, _stream()))
     return topk_idx
 
@@ -194,10 +210,10 @@ def index_score_topk_noalloc(batch: Batch, q_idx, w, k_pool, k_scale, K: int, to
                              topk_val=None, qmode=None):
     """index_score_topk with the library's own per-device scratch (allocates nothing)."""
     H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
-    if qmode is None:
-        qmode = TIS_QMODE_BF16 if q_idx.dtype == torch.float32 else TIS_QMODE_FP8
+    kd = _cache_dtype(k_pool, k_scale)
+    qmode = _qmode(q_idx, kd, qmode)
     _check(lib().index_score_topk_noalloc(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w),
-                                          _ptr(k_pool), _dtype(k_pool), _ptr(k_scale), H_I, D_I,
+                                          _ptr(k_pool), kd, _ptr(k_scale), H_I, D_I,
                                           qmode, int(K), _ptr(topk_idx), _ptr(topk_val),
                                           _stream()))
     return topk_idx
@@ -225,9 +241,9 @@ def sparse_mla_attn(batch: Batch, q, kv_pool, kv_scale, topk_idx, softmax_scale:
 
 def cache_append(batch: Batch, rows, pool, pool_scale=None):
     """Write rows [T][D] (fp32 or bf16) of the batch's query tokens into their slots of a paged
-    cache pool [n_pages][64][D] (uint8 e4m3 codes with pool_scale [n_pages][64] fp32, or bf16
-    with pool_scale None)."""
+    cache pool [n_pages][64][D] (uint8 e4m3 codes with pool_scale [n_pages][64] fp32, uint8
+    MXFP8 codes with pool_scale [n_pages][64][D/32] uint8, or bf16 with pool_scale None)."""
     D = int(rows.shape[-1])
-    _check(lib().cache_append(batch.ref, _ptr(rows), _dtype(rows), D, _ptr(pool), _dtype(pool),
-                              _ptr(pool_scale), _stream()))
+    _check(lib().cache_append(batch.ref, _ptr(rows), _dtype(rows), D, _ptr(pool),
+                              _cache_dtype(pool, pool_scale), _ptr(pool_scale), _stream()))
     return pool

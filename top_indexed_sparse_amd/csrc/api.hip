@@ -93,10 +93,12 @@ tis::DevBatch dev_batch(const tis_batch_t* b) {
   return d;
 }
 
-enum class IdxPath { F32, FP8, BF16 };  // fp32 kernel; matrix-core scorer, e4m3 / bf16 query
+// fp32 kernel; matrix-core scorer with an e4m3 / bf16 query over per-token-scaled e4m3 keys,
+// or MXFP8 query and keys
+enum class IdxPath { F32, FP8, BF16, MX };
 
 tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* w,
-                              const void* k_pool, tis_dtype_t k_dt, const float* k_scale,
+                              const void* k_pool, tis_dtype_t k_dt, const void* k_scale,
                               int32_t H_I, int32_t D_I, tis_qmode_t qmode, IdxPath* path) {
   if (!q_idx || !w || !k_pool) return fail(TIS_ERR_INVALID, "q_idx, w and k_pool must be set");
   if (!aligned16(q_idx) || !aligned16(k_pool) || !aligned16(w))
@@ -118,13 +120,22 @@ tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* 
     *path = qmode == TIS_QMODE_FP8 ? IdxPath::FP8 : IdxPath::BF16;
     return TIS_OK;
   }
+  if (q_dt == TIS_BF16 && k_dt == TIS_MXFP8 && qmode == TIS_QMODE_MXFP8) {
+    if (!k_scale || !aligned16(k_scale))
+      return fail(TIS_ERR_INVALID, "MXFP8 keys need 16-byte aligned scale bytes");
+    if (H_I != 64 || D_I != 128)
+      return fail(TIS_ERR_UNSUPPORTED, "MXFP8 indexer supports H_I=64, D_I=128");
+    *path = IdxPath::MX;
+    return TIS_OK;
+  }
   return fail(TIS_ERR_UNSUPPORTED,
-              "indexer supports (f32, f32, BF16) and (bf16, e4m3, FP8 or BF16) for (q, k, qmode)");
+              "indexer supports (f32, f32, BF16), (bf16, e4m3, FP8 or BF16) and (bf16, MXFP8, "
+              "MXFP8) for (q, k, qmode)");
 }
 
 tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath path, int t0,
                        int tc, const void* q_idx, const float* w, const void* k_pool,
-                       const float* k_scale, int H_I, int D_I, float* scores, int64_t ld,
+                       const void* k_scale, int H_I, int D_I, float* scores, int64_t ld,
                        hipStream_t st) {
   const tis::DevBatch d = dev_batch(batch);
   hipError_t e;
@@ -133,8 +144,9 @@ tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath pat
                                     (const float*)k_pool, H_I, D_I, scores, ld, st);
   else
     e = tis::launch_index_score_fp8(d, t0, tc, hi.max_n, hi.prefill_like,
-                                    path == IdxPath::BF16, (const uint16_t*)q_idx, w,
-                                    (const uint8_t*)k_pool, k_scale, scores, ld, st);
+                                    path == IdxPath::BF16 ? 1 : path == IdxPath::MX ? 2 : 0,
+                                    (const uint16_t*)q_idx, w, (const uint8_t*)k_pool, k_scale,
+                                    scores, ld, st);
   return e == hipSuccess ? TIS_OK : hip_fail(e, "index_score launch");
 }
 
@@ -231,7 +243,7 @@ TIS_API size_t sparse_mla_attn_workspace_size(const tis_batch_t* batch, int32_t 
 
 TIS_API tis_status_t index_score(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
                                  const float* w, const void* k_pool, tis_dtype_t k_dt,
-                                 const float* k_scale, int32_t H_I, int32_t D_I,
+                                 const void* k_scale, int32_t H_I, int32_t D_I,
                                  tis_qmode_t qmode, float* scores, int64_t ld_scores, void* ws,
                                  size_t ws_bytes, void* stream) {
   (void)ws; (void)ws_bytes;
@@ -273,7 +285,7 @@ namespace {
 // selection's workspace); the arguments have been checked.
 tis_status_t fused_run(const tis_batch_t* batch, const HostInfo& hi, IdxPath path,
                        const void* q_idx, const float* w, const void* k_pool,
-                       const float* k_scale, int32_t H_I, int32_t D_I, int32_t K,
+                       const void* k_scale, int32_t H_I, int32_t D_I, int32_t K,
                        int32_t* topk_idx, float* topk_val, int rows, void* ws, hipStream_t s) {
   const int64_t ld = round4(hi.max_n);
   const size_t sbytes = fused_scores_bytes(rows, hi);
@@ -293,7 +305,7 @@ tis_status_t fused_run(const tis_batch_t* batch, const HostInfo& hi, IdxPath pat
 
 tis_status_t fused_checks(const tis_batch_t* batch, HostInfo* hi, const void* q_idx,
                           tis_dtype_t q_dt, const float* w, const void* k_pool,
-                          tis_dtype_t k_dt, const float* k_scale, int32_t H_I, int32_t D_I,
+                          tis_dtype_t k_dt, const void* k_scale, int32_t H_I, int32_t D_I,
                           tis_qmode_t qmode, int32_t K, const int32_t* topk_idx,
                           IdxPath* path) {
   tis_status_t st = check_batch(batch, hi);
@@ -338,7 +350,7 @@ tis_status_t scratch_address(void** out) {
 
 TIS_API tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_idx,
                                       tis_dtype_t q_dt, const float* w, const void* k_pool,
-                                      tis_dtype_t k_dt, const float* k_scale, int32_t H_I,
+                                      tis_dtype_t k_dt, const void* k_scale, int32_t H_I,
                                       int32_t D_I, tis_qmode_t qmode, int32_t K,
                                       int32_t* topk_idx, float* topk_val, void* ws,
                                       size_t ws_bytes, void* stream) {
@@ -358,7 +370,7 @@ TIS_API tis_status_t index_score_topk(const tis_batch_t* batch, const void* q_id
 TIS_API tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const void* q_idx,
                                               tis_dtype_t q_dt, const float* w,
                                               const void* k_pool, tis_dtype_t k_dt,
-                                              const float* k_scale, int32_t H_I, int32_t D_I,
+                                              const void* k_scale, int32_t H_I, int32_t D_I,
                                               tis_qmode_t qmode, int32_t K, int32_t* topk_idx,
                                               float* topk_val, void* stream) {
   HostInfo hi;
@@ -387,7 +399,7 @@ TIS_API tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const vo
 
 TIS_API tis_status_t cache_append(const tis_batch_t* batch, const void* rows,
                                   tis_dtype_t rows_dt, int32_t D, void* pool, tis_dtype_t pool_dt,
-                                  float* pool_scale, void* stream) {
+                                  void* pool_scale, void* stream) {
   tis_status_t st = check_batch(batch, nullptr);
   if (st != TIS_OK) return st;
   if (!rows || !pool) return fail(TIS_ERR_INVALID, "rows and pool must be set");
@@ -397,16 +409,23 @@ TIS_API tis_status_t cache_append(const tis_batch_t* batch, const void* rows,
     return fail(TIS_ERR_INVALID, "D must be a multiple of 16 in [16, 2048] (got %d)", D);
   if (rows_dt != TIS_F32 && rows_dt != TIS_BF16)
     return fail(TIS_ERR_UNSUPPORTED, "cache_append takes fp32 or bf16 rows");
+  int fmt;
   if (pool_dt == TIS_E4M3) {
     if (!pool_scale || ((uintptr_t)pool_scale & 3))
       return fail(TIS_ERR_INVALID, "an e4m3 cache needs a 4-byte aligned pool_scale");
+    fmt = 1;
+  } else if (pool_dt == TIS_MXFP8) {
+    if (!pool_scale) return fail(TIS_ERR_INVALID, "an MXFP8 cache needs pool_scale");
+    if (D % 32) return fail(TIS_ERR_INVALID, "an MXFP8 cache needs D a multiple of 32 (got %d)", D);
+    fmt = 2;
   } else if (pool_dt == TIS_BF16) {
     if (pool_scale) return fail(TIS_ERR_INVALID, "a bf16 cache takes no pool_scale");
+    fmt = 0;
   } else {
-    return fail(TIS_ERR_UNSUPPORTED, "cache_append writes e4m3 or bf16 caches");
+    return fail(TIS_ERR_UNSUPPORTED, "cache_append writes e4m3, MXFP8 or bf16 caches");
   }
   hipError_t e = tis::launch_cache_append(dev_batch(batch), rows, rows_dt == TIS_BF16, D, pool,
-                                          pool_dt == TIS_E4M3, pool_scale, (hipStream_t)stream);
+                                          fmt, pool_scale, (hipStream_t)stream);
   return e == hipSuccess ? TIS_OK : hip_fail(e, "cache_append launch");
 }
 

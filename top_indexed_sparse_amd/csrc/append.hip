@@ -1,5 +1,7 @@
 // Cache append: the rows of a batch's new tokens written into their slots of a paged cache, as
-// e4m3 codes with one fp32 scale per token, or as bf16.
+// e4m3 codes with one fp32 scale per token, as MXFP8 (e4m3 codes with one power-of-two scale
+// byte per 32 elements, the indexer keys' format of Key Optimization 2 of the same page), or as
+// bf16.
 //
 // Method: "Day 0 Support for New LLM Architectures", Key Optimization 2 (the FP8 cache whose
 // scale factors are computed online; here one scale per token over the whole row, amax/448,
@@ -42,9 +44,11 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <bool IN_BF16, bool OUT_E4M3>
+enum AppendFmt : int { kOutBf16 = 0, kOutE4m3 = 1, kOutMx = 2 };
+
+template <bool IN_BF16, int OUT>
 __global__ __launch_bounds__(256) void cache_append_kernel(DevBatch bt, const void* __restrict__ rows,
-    int D, uint8_t* __restrict__ pool, float* __restrict__ pool_scale) {
+    int D, uint8_t* __restrict__ pool, void* __restrict__ pool_scale) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= bt.T) return;  // (uniform over the wave)
@@ -77,7 +81,30 @@ __global__ __launch_bounds__(256) void cache_append_kernel(DevBatch bt, const vo
     v[j] = f;
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
   }
-  if (OUT_E4M3) {
+  if constexpr (OUT == kOutMx) {
+    // group i / 8 of piece i = lane + 64j: the eight lanes 8k..8k+7 of step j hold one group
+    // (D is a multiple of 32, so a group is wholly inside or wholly past the row)
+    uint32_t* out = (uint32_t*)(pool + slot * D);
+    uint8_t* sb = (uint8_t*)pool_scale + slot * (D / 32);
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) {
+      if (64 * j >= npc) break;  // (uniform)
+      const int i = lane + 64 * j;
+      float gm = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+#pragma unroll
+      for (int o = 4; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+      const int X = mx_exponent(gm);
+      if (i < npc) {
+        const float y[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t w = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w |= e4m3_code(fminf(fmaxf(ldexpf(y[e], -X), -448.f), 448.f)) << (8 * e);
+        out[i] = w;
+        if ((lane & 7) == 0) sb[i >> 3] = (uint8_t)(X + 127);
+      }
+    }
+  } else if constexpr (OUT == kOutE4m3) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     float scale = __fdiv_rn(amax, 448.f);
@@ -98,7 +125,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(DevBatch bt, const vo
         out[i] = w;
       }
     }
-    if (lane == 0) pool_scale[slot] = scale;
+    if (lane == 0) ((float*)pool_scale)[slot] = scale;
   } else {
     uint2* out = (uint2*)((uint16_t*)pool + slot * D);
 #pragma unroll
@@ -113,13 +140,18 @@ __global__ __launch_bounds__(256) void cache_append_kernel(DevBatch bt, const vo
 }
 
 hipError_t launch_cache_append(const DevBatch& bt, const void* rows, bool rows_bf16, int D,
-                               void* pool, bool pool_e4m3, float* pool_scale, hipStream_t st) {
+                               void* pool, int pool_fmt, void* pool_scale, hipStream_t st) {
   if (bt.T < 1) return hipSuccess;
   if (D < 16 || D % 16 || D > 2048) return hipErrorInvalidValue;
-  auto* fn = rows_bf16 ? (pool_e4m3 ? cache_append_kernel<true, true>
-                                    : cache_append_kernel<true, false>)
-                       : (pool_e4m3 ? cache_append_kernel<false, true>
-                                    : cache_append_kernel<false, false>);
+  if (pool_fmt == kOutMx && D % 32) return hipErrorInvalidValue;
+  using Fn = void (*)(DevBatch, const void*, int, uint8_t*, void*);
+  static const Fn fns[2][3] = {
+      {cache_append_kernel<false, kOutBf16>, cache_append_kernel<false, kOutE4m3>,
+       cache_append_kernel<false, kOutMx>},
+      {cache_append_kernel<true, kOutBf16>, cache_append_kernel<true, kOutE4m3>,
+       cache_append_kernel<true, kOutMx>}};
+  if (pool_fmt < 0 || pool_fmt > 2) return hipErrorInvalidValue;
+  const Fn fn = fns[rows_bf16 ? 1 : 0][pool_fmt];
   hipLaunchKernelGGL(fn, dim3((bt.T + 3) / 4), dim3(256), 0, st, bt, rows, D, (uint8_t*)pool,
                      pool_scale);
   return hipGetLastError();

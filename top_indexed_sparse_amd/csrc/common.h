@@ -116,6 +116,16 @@ __device__ __forceinline__ int64_t slot_of(const DevBatch& bt, int b, int s) {
   return (int64_t)page * kPage + (s & (kPage - 1));
 }
 
+// Shared exponent of an MXFP8 group (one power-of-two scale 2^X per 32 elements, stored as the
+// byte X + 127): X = floor(log2 amax) - 8, so that amax / 2^X lies in e4m3's top binade
+// [256, 512); at least -127 (-127 for an all-zero group; a finite fp32 amax keeps X <= 119).
+// frexp: amax = m 2^E with m in [0.5, 1), so floor(log2 amax) = E - 1.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  int E;
+  (void)frexpf(amax, &E);
+  return amax > 0.f ? max(E - 9, -127) : -127;
+}
+
 // Lane-pair sums across wave halves / 16-lane rows using the gfx950 permlane swaps:
 // permlane32_swap(a, b) -> {[a_lo32, b_lo32], [a_hi32, b_hi32]}; permlane16_swap does the
 // same with the 16-lane halves of each 32-lane half.

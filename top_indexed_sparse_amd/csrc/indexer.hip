@@ -17,12 +17,23 @@
 //   head weights are applied in-lane, and two permlane swaps finish the head sum while
 //   transposing four 16-key tiles so that lane l ends with the score of key base + l.
 //
+// MXFP8 mode (Key Optimization 2 of the same page: the indexer fully quantised as MXFP8, every
+// 32 consecutive elements of Q and K sharing one power-of-two scale): keys carry one scale
+// byte 127 + X per 32 dims, and the query is quantised in the prologue per (head, 32 dims)
+// with X = floor(log2 amax) - 8 (clamped to [-127, 127]) and codes RNE(q / 2^X) clamped to
+// +-448.  Both scales go to the matrix instruction's block-scale operands, which apply to
+// K blocks [32b, 32b+32): the lane layout above puts K index 16g+i (i < 16) in the first half
+// of lane (n, g)'s operand and 64+16g+i in the second, i.e. the dims in their own order, so
+// block b is dim group b and the scale byte of lane (n, g) is that of head/key n, group g.
+//
 // bf16 query mode (the quantisation-free implementation kept beside the quantised one, as in
 // Key Optimization 1): the same kernel with q_I used as stored on v_mfma_f32_16x16x32_bf16.
 // The 32 query dims a lane holds are already the four 8-dim k-steps of that instruction's A
 // layout (dims 16g.., 16g+8.., 64+16g.., 64+16g+8..), and each staged 16-byte run of key
 // bytes widens exactly (every e4m3 value is a bf16 value) into two B operands of the same
 // dims; the weights are used as given.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -138,6 +149,47 @@ __device__ __forceinline__ void a0_prologue(const QRaw& qr, int lane, i32x8 (&A)
   for (int m = 0; m < 4; ++m) a0_tile(qr.r[m], qr.w[m], lane, A[m], wp[m]);
 }
 
+// Quantise head tile m to MXFP8 in the MFMA A layout.  Lane (n, g) holds dims [16g, 16g+16)
+// (half of group g >> 1) and [64+16g, 64+16g+16) (half of group 2 + (g >> 1)); the other half
+// of each group sits in lane (n, g ^ 1).  sa = the scale byte of head n, group g, which lane
+// (n, g & 1 ? 2 : 0) computed for its first (g < 2) or second (g >= 2) half.  The weights are
+// used as given.
+__device__ __forceinline__ void mx_tile(const i32x4 (&r)[4], const float (&wr)[4], int lane,
+                                        i32x8& A, int& sa, float (&wp)[4]) {
+  const int n = lane & 15, g = lane >> 4;
+  uint32_t wd[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) wd[j] = (uint32_t)r[j >> 2][j & 3];
+  float v[32];
+  float am[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    v[2 * j] = __uint_as_float(wd[j] << 16);
+    v[2 * j + 1] = __uint_as_float(wd[j] & 0xffff0000u);
+    am[j >> 3] = fmaxf(am[j >> 3], fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+  }
+  int X[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) X[h] = mx_exponent(fmaxf(am[h], __shfl_xor(am[h], 16)));
+  // q / 2^X by exponent adjustment (exact), saturated to the largest finite e4m3 magnitude
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = -X[j >> 2];
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = fminf(fmaxf(ldexpf(v[4 * j + i], e), -448.f), 448.f);
+    int word = 0;
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], word, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+    A[j] = word;
+  }
+  const int src = n + 32 * (g & 1);
+  const int lo = __shfl(X[0], src), hi = __shfl(X[1], src);
+  sa = (g < 2 ? lo : hi) + 127;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wp[i] = wr[i];
+}
+
 struct KTile4 {
   i32x4 lo[4], hi[4];
 };
@@ -176,16 +228,51 @@ __device__ __forceinline__ void stage_ktile4(uint8_t* stage, int lane, const KPa
   }
 }
 
-// The query's A operands for the four 16-head tiles: e4m3 (one 16x16x128 step per tile) or
-// bf16 as stored (four 16x16x32 steps per tile, each the i32x4 of 8 dims the lane loaded).
-template <bool BQ>
+// Query modes of the matrix-core scorer: e4m3 with one power-of-two scale per head folded
+// into the weights, bf16 as stored, or MXFP8 (e4m3 with one scale byte per 32 dims).
+enum QMode : int { kQFp8 = 0, kQBf16 = 1, kQMx = 2 };
+
+// The query's A operands for the four 16-head tiles: e4m3 (one 16x16x128 step per tile, MXFP8
+// with the lane's block-scale byte) or bf16 as stored (four 16x16x32 steps per tile, each the
+// i32x4 of 8 dims the lane loaded).
+template <int QM>
 struct QOps {
   i32x8 a[4];
 };
 template <>
-struct QOps<true> {
+struct QOps<kQBf16> {
   i32x4 a[4][4];
 };
+template <>
+struct QOps<kQMx> {
+  i32x8 a[4];
+  int sa[4];
+};
+
+// The key scale word a lane loads for key `lane` of a page: the fp32 per-token scale, or
+// (MXFP8) the key's four scale bytes, group g in bits [8g, 8g+8).
+template <int QM>
+using KScale = typename std::conditional<QM == kQMx, uint32_t, float>::type;
+
+// All four head tiles in the mode's A layout.
+template <int QM>
+__device__ __forceinline__ void q_prologue(const QRaw& qr, int lane, QOps<QM>& A,
+                                           float (&wp)[4][4]) {
+  if constexpr (QM == kQBf16) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A.a[m][i] = qr.r[m][i];
+        wp[m][i] = qr.w[m][i];
+      }
+  } else if constexpr (QM == kQMx) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) mx_tile(qr.r[m], qr.w[m], lane, A.a[m], A.sa[m], wp[m]);
+  } else {
+    a0_prologue(qr, lane, A.a, wp);
+  }
+}
 
 // 8 e4m3 codes (two dwords) widened to bf16, exactly (scale 1)
 __device__ __forceinline__ bf16x8 widen8_bf16(int lo, int hi) {
@@ -198,15 +285,17 @@ __device__ __forceinline__ bf16x8 widen8_bf16(int lo, int hi) {
                                  6, 7);
 }
 
-// Scores of the 64 keys of one page-aligned group; lane l returns key base + l (unscaled).
-template <bool BQ>
-__device__ __forceinline__ float score_group(const QOps<BQ>& A, const float (&wp)[4][4],
-                                             const KTile4& kt) {
+// Scores of the 64 keys of one page-aligned group; lane l returns key base + l, times the
+// key's scale word ks (the key's fp32 scale; MXFP8: its scale bytes enter the products).
+template <int QM>
+__device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp)[4][4],
+                                             const KTile4& kt, KScale<QM> ks) {
+  const int lane = threadIdx.x & 63;
   float v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float acc = 0.f;
-    if constexpr (BQ) {
+    if constexpr (QM == kQBf16) {
       bf16x8 B[4];
       B[0] = widen8_bf16(kt.lo[j][0], kt.lo[j][1]);
       B[1] = widen8_bf16(kt.lo[j][2], kt.lo[j][3]);
@@ -226,10 +315,19 @@ __device__ __forceinline__ float score_group(const QOps<BQ>& A, const float (&wp
       i32x8 B;
       B[0] = kt.lo[j][0]; B[1] = kt.lo[j][1]; B[2] = kt.lo[j][2]; B[3] = kt.lo[j][3];
       B[4] = kt.hi[j][0]; B[5] = kt.hi[j][1]; B[6] = kt.hi[j][2]; B[7] = kt.hi[j][3];
+      // MXFP8: the B block-scale byte of lane (n, g) is group g of key 16j + n
+      int sb = 0;
+      if constexpr (QM == kQMx)
+        sb = __builtin_amdgcn_ubfe(
+            (uint32_t)__shfl((int)ks, 16 * j + (lane & 15)), 8 * (lane >> 4), 8);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c, 0, 0, 0, 0, 0, 0);
+        if constexpr (QM == kQMx)
+          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c, 0, 0, 0, A.sa[m],
+                                                               0, sb);
+        else
+          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c, 0, 0, 0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], fmaxf(c[i], 0.f), acc);
       }
@@ -239,17 +337,22 @@ __device__ __forceinline__ float score_group(const QOps<BQ>& A, const float (&wp
   // head sum over g and 4x4 transpose: lane l ends with tile (l >> 4), key (l & 15)
   float k0 = pair32_sum(v[0], v[2]);
   float k1 = pair32_sum(v[1], v[3]);
-  return pair16_sum(k0, k1);
+  const float r = pair16_sum(k0, k1);
+  if constexpr (QM == kQMx) return r;
+  else return r * ks;
 }
 
 // Decode scoring: one token per workgroup (blockIdx.x) and key chunk blockIdx.y of 64 pages;
 // the pages are dealt round-robin to the eight waves (wave w scores pages w, w+8, ... of the
 // chunk), so that at each step the workgroup reads 64 KB of consecutive pages when the
 // request's pages are consecutive.
-template <bool BQ>
+// (kernel signatures name no type that depends on the mode: the key scales come in untyped)
+template <int QM>
 __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
-    const float* kscale, float* __restrict__ scores, int64_t ld, int chunk) {
+    const void* kscale_raw, float* __restrict__ scores, int64_t ld, int chunk) {
+  constexpr bool BQ = QM == kQBf16;
+  const KScale<QM>* kscale = (const KScale<QM>*)kscale_raw;
   // (the wave index through readfirstlane, so that the ranges derived from it are scalars)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   constexpr int kStep = 8;  // page stride of a wave within the chunk
@@ -305,7 +408,7 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
   };
   // the key scales of all eight pages go out first (one short stream of small reads, ahead of
   // the pages, so that waiting for a scale never waits for a page)
-  float ks[kPages];
+  KScale<QM> ks[kPages];
   auto fetch = [&](int g, Slot& sl) {
     const int page = page_id(g);
     sl.ok = page >= 0 && page < bt.n_pages;
@@ -329,12 +432,14 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
   }
   __shared__ __attribute__((aligned(16))) uint8_t stage_sh[8 * kStage];
   uint8_t* stage = stage_sh + wave * kStage;
-  QOps<BQ> A;
+  QOps<QM> A;
   float wp[4][4];
   {
-    // (e4m3: one 32-byte operand per lane and tile; bf16: the 64 loaded bytes as they are)
+    // (e4m3: one 32-byte operand per lane and tile, plus the MXFP8 scale byte; bf16: the 64
+    // loaded bytes as they are)
     __shared__ i32x4 a_sh[4][BQ ? 4 : 2][64];
     __shared__ f32x4 w_sh[4][64];
+    __shared__ int s_sh[4][QM == kQMx ? 64 : 1];
     if (wave < 4) {
       float wt[4];
       if constexpr (BQ) {
@@ -345,7 +450,13 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
         }
       } else {
         i32x8 at;
-        a0_tile(qr, qw, lane, at, wt);
+        if constexpr (QM == kQMx) {
+          int sa;
+          mx_tile(qr, qw, lane, at, sa, wt);
+          s_sh[wave][lane] = sa;
+        } else {
+          a0_tile(qr, qw, lane, at, wt);
+        }
         a_sh[wave][0][lane] = i32x4{at[0], at[1], at[2], at[3]};
         a_sh[wave][1][lane] = i32x4{at[4], at[5], at[6], at[7]};
       }
@@ -361,6 +472,7 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
       } else {
         const i32x4 lo = a_sh[m][0][lane], hi = a_sh[m][1][lane];
         A.a[m] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (QM == kQMx) A.sa[m] = s_sh[m][lane];
       }
       const f32x4 wv = w_sh[m][lane];
 #pragma unroll
@@ -372,7 +484,7 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
       __builtin_amdgcn_make_buffer_rsrc(out, 0, k1 * 4, kBufDword3);
   // page g from ring slot u: fetch page g + 3 into the slot freed last (if there is more to
   // fetch), then score page g
-  auto step = [&](int g, int u, bool more, float scale) {
+  auto step = [&](int g, int u, bool more, KScale<QM> scale) {
     if (more) {
       fetch(g + 3, sl[(u + 3) & 3]);
       asm volatile("" ::: "memory");  // (the loads go out before this page is scored)
@@ -380,7 +492,7 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
     const Slot& c = sl[u];
     KTile4 kt;
     stage_ktile4(stage, lane, c.kp, kt);
-    float sc = score_group<BQ>(A, wp, kt) * scale;
+    float sc = score_group<QM>(A, wp, kt, scale);
     if (!c.ok) sc = -INFINITY;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
                                           (k0 + 64 * (poff + g * kStep) + lane) * 4, 0, 0);
@@ -403,11 +515,12 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
 // different requests are scored in one pass per request (every wave loads and waits in every
 // pass; a wave stores only in its own request's pass, through a buffer resource whose record
 // count is zero otherwise).  A wave without a token (the batch's last group) only loads.
-template <bool BQ>
+template <int QM>
 __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
-    const float* kscale, float* __restrict__ scores, int64_t ld) {
+    const void* kscale_raw, float* __restrict__ scores, int64_t ld) {
   constexpr int kChunk = 1024;
+  const KScale<QM>* kscale = (const KScale<QM>*)kscale_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int tl = blockIdx.x * 4 + wave;
   const bool has = tl < t_count;
@@ -425,19 +538,9 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
     req_sh[wave] = has ? loc.b : -1;
     n_sh[wave] = has ? loc.n : 0;
   }
-  QOps<BQ> A;
+  QOps<QM> A;
   float wp[4][4];
-  if constexpr (BQ) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        A.a[m][i] = qr.r[m][i];
-        wp[m][i] = qr.w[m][i];
-      }
-  } else {
-    a0_prologue(qr, lane, A.a, wp);
-  }
+  q_prologue<QM>(qr, lane, A, wp);
   __syncthreads();
   int rq[4], nn[4];
 #pragma unroll
@@ -449,7 +552,7 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
   const int my_k1 = has ? min(k0 + kChunk, loc.n) : 0;  // the token's keys below this bound
   struct Piece {
     i32x4 r[2];
-    float ks;
+    KScale<QM> ks;
     bool ok;
   };
 #pragma unroll 1
@@ -519,7 +622,7 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
           kt.lo[j] = *(const i32x4*)(row + 16 * gg);
           kt.hi[j] = *(const i32x4*)(row + 64 + 16 * gg);
         }
-        float sc = score_group<BQ>(A, wp, kt) * ring[u].ks;
+        float sc = score_group<QM>(A, wp, kt, ring[u].ks);
         if (!ring[u].ok) sc = -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
                                               (k0 + 64 * g + lane) * 4, 0, 0);
@@ -540,25 +643,41 @@ hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, 
   return hipGetLastError();
 }
 
-hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, bool bf16_query, const uint16_t* q_idx,
-                                  const float* w, const uint8_t* kpool, const float* kscale,
-                                  float* scores, int64_t ld, hipStream_t st) {
-  const int group = prefill_like ? 1 : 0;
+template <int QM>
+static hipError_t launch_mma(const DevBatch& bt, int t_begin, int t_count, int max_n,
+                             bool prefill_like, const uint16_t* q_idx, const float* w,
+                             const uint8_t* kpool, const void* kscale, float* scores, int64_t ld,
+                             hipStream_t st) {
   const int chunk = prefill_like ? 1024 : 4096;
-  dim3 grid(group ? (t_count + 3) / 4 : t_count, (max_n + chunk - 1) / chunk);
   // decode: one 8-wave workgroup per 4096-key chunk of a token (512 keys per wave); prefill:
   // four tokens per 4-wave workgroup sharing a 1024-key chunk
-  if (group) {
-    auto* gfn = bf16_query ? idx_score_group_kernel<true> : idx_score_group_kernel<false>;
-    hipLaunchKernelGGL(gfn, grid, dim3(256), 0, st, bt, t_begin, t_count, q_idx, w, kpool, kscale,
-                       scores, ld);
+  if (prefill_like) {
+    dim3 grid((t_count + 3) / 4, (max_n + chunk - 1) / chunk);
+    hipLaunchKernelGGL(idx_score_group_kernel<QM>, grid, dim3(256), 0, st, bt, t_begin, t_count,
+                       q_idx, w, kpool, kscale, scores, ld);
     return hipGetLastError();
   }
-  auto* fn = bf16_query ? idx_score_fp8_kernel<true> : idx_score_fp8_kernel<false>;
-  hipLaunchKernelGGL(fn, grid, dim3(512), 0, st, bt, t_begin, t_count, q_idx, w, kpool, kscale,
-                     scores, ld, chunk);
+  dim3 grid(t_count, (max_n + chunk - 1) / chunk);
+  hipLaunchKernelGGL(idx_score_fp8_kernel<QM>, grid, dim3(512), 0, st, bt, t_begin, t_count,
+                     q_idx, w, kpool, kscale, scores, ld, chunk);
   return hipGetLastError();
+}
+
+hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
+                                  bool prefill_like, int qmode, const uint16_t* q_idx,
+                                  const float* w, const uint8_t* kpool, const void* kscale,
+                                  float* scores, int64_t ld, hipStream_t st) {
+  switch (qmode) {
+    case kQBf16:
+      return launch_mma<kQBf16>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
+                                kscale, scores, ld, st);
+    case kQMx:
+      return launch_mma<kQMx>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
+                              kscale, scores, ld, st);
+    default:
+      return launch_mma<kQFp8>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
+                               kscale, scores, ld, st);
+  }
 }
 
 }  // namespace tis

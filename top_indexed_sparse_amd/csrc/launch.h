@@ -11,9 +11,11 @@ namespace tis {
 hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, int max_n,
                                   const float* q, const float* w, const float* kpool, int H,
                                   int D, float* scores, int64_t ld, hipStream_t st);
+// qmode: 0 = e4m3 query with per-head scales (per-token fp32 key scales), 1 = bf16 query
+// (per-token fp32 key scales), 2 = MXFP8 query and keys (kscale: four scale bytes per key)
 hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, bool bf16_query, const uint16_t* q_idx,
-                                  const float* w, const uint8_t* kpool, const float* kscale,
+                                  bool prefill_like, int qmode, const uint16_t* q_idx,
+                                  const float* w, const uint8_t* kpool, const void* kscale,
                                   float* scores, int64_t ld, hipStream_t st);
 hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
                        const float* scores, int64_t ld, int K, int32_t* idx, float* val,
@@ -32,7 +34,9 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
 int attn_split_count(int t_count, int K);
 int attn_keys_per_split(int K, int nsplit);
 size_t attn_smem_bytes(bool fp8, int kps);
+// pool_fmt: 0 = bf16, 1 = e4m3 with one fp32 scale per token, 2 = MXFP8 (one scale byte per
+// 32 elements)
 hipError_t launch_cache_append(const DevBatch& bt, const void* rows, bool rows_bf16, int D,
-                               void* pool, bool pool_e4m3, float* pool_scale, hipStream_t st);
+                               void* pool, int pool_fmt, void* pool_scale, hipStream_t st);
 
 }  // namespace tis
