@@ -18,6 +18,9 @@ What it computes (each function cites the passage it follows; the pages are the 
   * cache append  new rows written into their page slots: e4m3 with a per-token fp32 scale
             amax/448 (codes: RNE of the fp32 quotient, clamped to +-448), MXFP8 (below), or
             bf16 RNE.
+  * blocks  block-granular selection: a 64-position page scores the largest token score among
+            its causal positions; the K/64 best pages are kept (score desc, page asc) and
+            expanded to their causal positions.
   * MXFP8   the indexer's Q and K quantised per 32 consecutive elements with a shared
             power-of-two scale 2^X, X = floor(log2 amax) - 8, codes RNE(x / 2^X) clamped to
             +-448; scores then use the decoded values.
@@ -29,17 +32,20 @@ invariants; attention against a loop implementation of dense causal attention (K
 the K = 1 and equal-row special cases and the equal-logit lse closed form; the per-token
 quantiser against torch's float8 cast, hand-worked rows and its error bound; the MXFP8
 quantiser against a brute-force exponent search, torch's float8 cast, hand-worked groups, its
-error bound, and integer inputs that it must represent exactly.
+error bound, and integer inputs that it must represent exactly; block selection against a
+brute-force page scan, hand-worked rows and its equivalence with walking the token ranking
+until K/64 distinct pages are met.
 """
 from .codecs import (E4M3_TABLE, e4m3_decode, e4m3_round, e4m3_encode, bf16_decode,
                      bf16_round)
 from .method import (a0_scale, a0_quantize, token_scores, topk_token, sparse_mla_token,
                      decode_rows, quantize_row_e4m3, cache_append, mx_scale_exponent,
-                     mx_quantize, mx_decode, mx_quantize_query, MX_GROUP, Oracle)
+                     mx_quantize, mx_decode, mx_quantize_query, MX_GROUP, block_scores,
+                     topk_blocks, expand_blocks, Oracle)
 from . import brute
 
 __all__ = ["E4M3_TABLE", "e4m3_decode", "e4m3_round", "e4m3_encode", "bf16_decode",
            "bf16_round", "a0_scale", "a0_quantize", "token_scores", "topk_token",
            "sparse_mla_token", "decode_rows", "quantize_row_e4m3", "cache_append",
            "mx_scale_exponent", "mx_quantize", "mx_decode", "mx_quantize_query", "MX_GROUP",
-           "Oracle", "brute"]
+           "block_scores", "topk_blocks", "expand_blocks", "Oracle", "brute"]

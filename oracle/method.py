@@ -264,6 +264,14 @@ class Oracle:
         idx, kth = topk_token(S, self.sh.K if K is None else K)
         return idx, S, kth
 
+    def block_topk(self, t: int, K_blocks: int):
+        """Block-granular selection of token t: (block ids, block scores, kb-th block score,
+        expanded positions)."""
+        S = self.scores(t)
+        bs = block_scores(S)
+        blk, kth = topk_blocks(bs, K_blocks)
+        return blk, bs, kth, expand_blocks(blk, S.shape[0])
+
     def attention(self, t: int, idx):
         """Attention of token t over the positions in ``idx`` (entries <0 or >=L_b skipped)."""
         inp, sh = self.inp, self.sh
@@ -275,3 +283,37 @@ class Oracle:
         rows = decode_rows(inp.kv_pool, inp.kv_scale, inp.page_table[b], idx, fmt)
         q = inp.q[t].astype(np.float64) if sh.fp32 else bf16_decode(inp.q[t])
         return sparse_mla_token(q, rows, sh.softmax_scale, sh.D_v)
+
+
+# ----------------------------------------------------------------------------- N4
+def block_scores(S, page: int = PAGE) -> np.ndarray:
+    """Block (page) scores of one query for block-granular selection ("Day-0 Adaptation for
+    Trillion-Parameter Models": the index selection returns blocks of the cache layout, fetched
+    whole; "Achieving Day-0 Readiness ... Million-Token Context", section 2.2: fixed-size
+    blocks located through a block index table).  The pages do not say how a block is scored;
+    the reading here: a block's score is the largest token score among its causal positions,
+    so a block is kept whenever it holds a token the token-level selection would rank high.
+
+    S: the n = p_t + 1 token scores of positions 0..p_t.  Returns ceil(n / page) block scores,
+    block j covering positions [page*j, min(page*(j+1), n))."""
+    S = np.asarray(S, dtype=np.float64)
+    n = S.shape[0]
+    nb = -(-n // page)
+    return np.array([S[page * j:min(page * (j + 1), n)].max() for j in range(nb)],
+                    dtype=np.float64)
+
+
+def topk_blocks(bs, K_blocks: int):
+    """Top blocks of one query: the kb = min(K_blocks, nb) largest block scores under (score
+    desc, block asc), as topk_token orders positions.  Returns (block ids [K_blocks] int32
+    ascending, -1 padded; the kb-th largest block score, or None if kb = 0)."""
+    return topk_token(bs, K_blocks)
+
+
+def expand_blocks(blocks, n: int, page: int = PAGE) -> np.ndarray:
+    """Positions attended for selected blocks: entry page*i + r is page*blocks[i] + r when that
+    position is causal (< n) and the block is not padding, else -1 ([len(blocks) * page])."""
+    blocks = np.asarray(blocks, dtype=np.int64)
+    pos = blocks[:, None] * page + np.arange(page)[None, :]
+    ok = (blocks[:, None] >= 0) & (pos < n)
+    return np.where(ok, pos, -1).reshape(-1).astype(np.int32)
