@@ -10,7 +10,10 @@ cache cannot serve a step from the previous one.  Prints one JSON line.
 --workload tiny|prefill64k|decode1m|ragged measures another workload the same way (one
 input replica: their inputs dwarf the last-level cache) and prints its own line; the default
 line is decode32k.  --k-fmt mxfp8 runs the indexer on MXFP8 keys and queries (one scale byte
-per 32 dims) instead of e4m3 keys with one fp32 scale per token, and labels its line so.  Step times are the median of --repeats timed loops of --steps steps.  The
+per 32 dims) instead of e4m3 keys with one fp32 scale per token, and labels its line so.
+--select block runs block-granular selection instead: the scorer keeps one score per 64-key
+page (its largest), the K/64 best pages are kept and expanded to their causal positions, and
+the attention reads those K positions.  Step times are the median of --repeats timed loops of --steps steps.  The
 oracle baseline times the fp64 CPU oracle on every query token of batches of at most
 --cpu-tokens tokens, and on a bounded sample of that many tokens otherwise.
 """
@@ -35,9 +38,12 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic(inp):
+def algorithmic(inp, block=False):
     """Compulsory bytes / flops per step, stage by stage (inputs read once, outputs written
-    once, only the selected rows gathered), and per launch of each entry point."""
+    once, only the selected rows gathered), and per launch of each entry point.  block: the
+    scorer writes one score per 64-key page, the selection reads those and writes K/64 pages
+    plus K expanded positions, and the attention reads the causal rows of the kept pages
+    (at most K: counted as min(K, n))."""
     import numpy as np
     sh = inp.wl.shape
     n = inp.positions.astype(np.int64) + 1
@@ -52,6 +58,13 @@ def algorithmic(inp):
     # selected rows + indices + q + O (bf16) + lse
     attn_bytes = int((k * row).sum()) + inp.T * (4 * sh.K + sh.H * (sh.D_qk * 2 + sh.D_v * 2 + 4))
     attn_flops = int((2 * sh.H * k * (sh.D_qk + sh.D_v)).sum())
+    if block:
+        nb = (n + 63) // 64
+        topk_bytes = 4 * (sh.K // 64) * inp.T + 4 * sh.K * inp.T
+        return dict(idx_bytes=idx_bytes, idx_flops=idx_flops, topk_bytes=topk_bytes,
+                    attn_bytes=attn_bytes, attn_flops=attn_flops,
+                    idx_kernel_bytes=idx_bytes + int(4 * nb.sum()),
+                    topk_kernel_bytes=int(4 * nb.sum()) + topk_bytes)
     return dict(idx_bytes=idx_bytes, idx_flops=idx_flops, topk_bytes=topk_bytes,
                 attn_bytes=attn_bytes, attn_flops=attn_flops,
                 # unfused entry points: the scorer also writes one fp32 score per candidate,
@@ -136,7 +149,7 @@ def baseline_tokens(inp, n_sample: int):
     return sorted(pick)
 
 
-def cpu_baseline(inp, r_idx, r_out, out_bf16, tokens, unit):
+def cpu_baseline(inp, r_idx, r_out, out_bf16, tokens, unit, block=False):
     """The fp64 oracle timed on this host on a bounded sample of the same inputs; also a
     parity gate against the GPU results for those tokens (recall, and attention on the GPU's
     own selection within the gate: 1e-2 bf16 cache / 2e-2 e4m3 cache, plus half a bf16 ulp
@@ -148,7 +161,10 @@ def cpu_baseline(inp, r_idx, r_out, out_bf16, tokens, unit):
     t0 = time.perf_counter()
     chosen = []
     for t in tokens:                       # the oracle's own chain, timed
-        idx, S, kth = orc.topk(t)
+        if block:
+            idx = orc.block_topk(t, inp.wl.shape.K // 64)[3]
+        else:
+            idx, S, kth = orc.topk(t)
         orc.attention(t, idx)
         chosen.append(idx)
     dt = time.perf_counter() - t0
@@ -169,8 +185,8 @@ def cpu_baseline(inp, r_idx, r_out, out_bf16, tokens, unit):
     whole = len(tokens) == inp.T
     sample = (f"{len(tokens)} of {inp.T} query tokens" + ("" if whole else
               " (first/last, positions 2046-2049, request edges, seeded random fill)")
-              + ": the full per-token chain (e4m3/bf16 decode, fp64 scores, full-sort Top-K, "
-              "fp64 attention)")
+              + ": the full per-token chain (e4m3/bf16 decode, fp64 scores, full-sort "
+              + ("block selection" if block else "Top-K") + ", fp64 attention)")
     rec = dict(value=len(tokens) / dt, unit=unit, cores=cores, kind="oracle", sample=sample,
                cpu_model=model, blas=blas)
     if not whole:
@@ -193,6 +209,8 @@ def main():
                     choices=["tiny", "decode32k", "prefill64k", "decode1m", "ragged"])
     ap.add_argument("--k-fmt", default="e4m3", choices=["e4m3", "mxfp8"],
                     help="indexer key format: e4m3 + fp32 scale per token, or MXFP8")
+    ap.add_argument("--select", default="token", choices=["token", "block"],
+                    help="Top-K positions, or the K/64 best 64-position pages")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (8 times) and exit: the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -221,7 +239,8 @@ def main():
 
     torch.cuda.set_device(0)
     mx = args.k_fmt == "mxfp8"
-    main_line = args.workload == "decode32k" and not mx
+    block = args.select == "block"
+    main_line = args.workload == "decode32k" and not mx and not block
     wl = synth.workload(synth.NAMES.index(args.workload))
     sh = wl.shape
     if args.workload != "decode32k":
@@ -239,8 +258,12 @@ def main():
     out_dt = torch.float32 if sh.fp32 else torch.bfloat16
     out = [torch.empty((T, sh.H, sh.D_v), dtype=out_dt, device="cuda") for _ in reps]
     lse = [torch.empty((T, sh.H), dtype=torch.float32, device="cuda") for _ in reps]
-    ws_i = torch.empty(tis.index_score_topk_workspace_size(bt, sh.H_I, sh.D_I, K),
+    Kb = K // 64
+    ws_i = torch.empty(max(1, (tis.index_score_topk_block_workspace_size(bt, sh.H_I, sh.D_I, Kb)
+                               if block else
+                               tis.index_score_topk_workspace_size(bt, sh.H_I, sh.D_I, K))),
                        dtype=torch.uint8, device="cuda")
+    bidx = [torch.empty((T, Kb), dtype=torch.int32, device="cuda") for _ in reps]
     kv_code = tis.TIS_F32 if sh.fp32 else (tis.TIS_E4M3 if sh.kv_fp8 else tis.TIS_BF16)
     ws_a_bytes = tis.sparse_mla_attn_workspace_size(bt, K, sh.H, sh.D_qk, sh.D_v, kv_code)
     ws_a = torch.empty(max(1, ws_a_bytes),
@@ -249,7 +272,11 @@ def main():
     def step(i):
         r = i % len(reps)
         d = reps[r]
-        tis.index_score_topk(bt, d.q_idx, d.w, d.k_pool, d.k_scale, K, idx[r], ws=ws_i)
+        if block:
+            tis.index_score_topk_block(bt, d.q_idx, d.w, d.k_pool, d.k_scale, Kb, bidx[r],
+                                       topk_idx=idx[r], ws=ws_i)
+        else:
+            tis.index_score_topk(bt, d.q_idx, d.w, d.k_pool, d.k_scale, K, idx[r], ws=ws_i)
         tis.sparse_mla_attn(bt, d.q, d.kv_pool, d.kv_scale, idx[r], sh.softmax_scale, out[r],
                             lse[r], ws=ws_a)
 
@@ -281,16 +308,22 @@ def main():
 
     # each entry point alone, over the same replicas: the scorer (unfused, writes scores),
     # the selection over those scores, the attention call
-    ld = (bt.max_n + 3) // 4 * 4
+    ld = ((tis.blocks_of(bt.max_n) if block else bt.max_n) + 3) // 4 * 4
     scores = [torch.empty((T, ld), dtype=torch.float32, device="cuda") for _ in reps]
 
     def score(i):
         d = reps[i % len(reps)]
-        tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores[i % len(reps)])
+        if block:
+            tis.index_score_block(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores[i % len(reps)])
+        else:
+            tis.index_score(bt, d.q_idx, d.w, d.k_pool, d.k_scale, scores[i % len(reps)])
 
     def select(i):
         r = i % len(reps)
-        tis.topk_select(bt, scores[r], K, idx[r])
+        if block:
+            tis.topk_block_select(bt, scores[r], Kb, bidx[r], topk_idx=idx[r])
+        else:
+            tis.topk_select(bt, scores[r], K, idx[r])
 
     def attend(i):
         r = i % len(reps)
@@ -301,16 +334,18 @@ def main():
     for fn in (score, select, attend):
         for i in range(max(args.warmup, len(reps))):
             fn(i)
-    a = algorithmic(inp)
+    a = algorithmic(inp, block)
     kv = "f32" if sh.fp32 else ("fp8" if sh.kv_fp8 else "bf16")
     calls = {
-        "index_score": dict(ms=timed(score, args.steps), bytes=a["idx_kernel_bytes"],
+        ("index_score_block" if block else "index_score"): dict(
+                            ms=timed(score, args.steps), bytes=a["idx_kernel_bytes"],
                             flops=a["idx_flops"], peak=FP8_PEAK,
                             kernels=["idx_score_f32_kernel" if sh.fp32 else
                                      "idx_score_group_kernel" if inp.T >= 4 * inp.B else
                                      "idx_score_fp8_kernel"]),
-        "topk_select": dict(ms=timed(select, args.steps), bytes=a["topk_kernel_bytes"],
-                            flops=0, peak=FP8_PEAK, kernels=["topk_select_kernel"]),
+        ("topk_block_select" if block else "topk_select"): dict(
+            ms=timed(select, args.steps), bytes=a["topk_kernel_bytes"], flops=0, peak=FP8_PEAK,
+            kernels=["topk_select_kernel"] + (["expand_blocks_kernel"] if block else [])),
         "sparse_mla_attn": dict(ms=timed(attend, args.steps), bytes=a["attn_bytes"],
                                 flops=a["attn_flops"], peak=BF16_PEAK,
                                 kernels=[f"mla_attn_{kv}_kernel"] + (
@@ -341,7 +376,8 @@ def main():
     res = {
         "metric": ("sparse-attn decode queries/s @32K ctx (index+topk+attn)" if main_line else
                    f"{wl.name} {'queries' if decode else 'tokens'}/s (index+topk+attn)"
-                   + (", MXFP8 indexer" if mx else "")),
+                   + (", MXFP8 indexer" if mx else "")
+                   + (", block-granular selection" if block else "")),
         "value": T * 1000.0 / step_ms,
         "unit": "queries/s" if decode else "tokens/s",
         "n_gpus": 1,
@@ -365,6 +401,8 @@ def main():
                    {"workload": wl.name, "requests": inp.B, "query_tokens": T,
                     "index_keys": ("fp32" if sh.fp32 else "mxfp8 (e8m0 byte/32 dims)" if mx
                                    else "e4m3+fp32 scale/token"),
+                    "selection": ("K/64 pages of 64 positions (max score per page)" if block
+                                  else "K positions"),
                     "max_context": int(inp.seq_lens.max()),
                     "cached_tokens": int(inp.seq_lens.sum()), "indexer_heads": sh.H_I,
                     "indexer_dim": sh.D_I, "topk": K, "heads": sh.H, "qk_dim": sh.D_qk,
@@ -384,7 +422,7 @@ def main():
         ri = dict(zip(toks, idx[0].index_select(0, ix).cpu().numpy()))
         ro = dict(zip(toks, out[0].index_select(0, ix).float().cpu().numpy().astype(np.float64)))
         cb, secs, rec, excess = cpu_baseline(inp, ri, ro, out_dt == torch.bfloat16, toks,
-                                             res["unit"])
+                                             res["unit"], block)
         log(f"cpu oracle: {secs:.1f}s for {len(toks)} tokens on {cb['cores']} cores "
             f"({cb['cpu_model']}, {cb['blas']}); GPU recall {rec:.5f}, attention error "
             f"{excess:+.2e} relative to its gate")

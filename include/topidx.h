@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define TIS_ABI_VERSION 4
+#define TIS_ABI_VERSION 5
 #define TIS_PAGE_SIZE 64
 
 typedef enum {
@@ -224,6 +224,49 @@ tis_status_t cache_append(const tis_batch_t* batch, const void* rows, tis_dtype_
                           int32_t D, void* pool, tis_dtype_t pool_dt, void* pool_scale,
                           void* stream);
 
+/* Block-granular selection ("Day-0 Adaptation for Trillion-Parameter Models": the index
+ * selection returns blocks of the cache layout, which the attention fetches whole; "Achieving
+ * Day-0 Readiness ... Million-Token Context", section 2.2: fixed-size blocks located through a
+ * block index table).  A block is one 64-position page of the request; block j of token t
+ * covers positions [64j, min(64j + 64, n_t)), nb_t = ceil(n_t / 64) blocks in all.
+ *
+ * index_score_block - block scores: bscore[t][j] = the largest index_score of token t over the
+ *   causal positions of block j (the same fp32 values index_score would write), -inf for a block
+ *   whose page-table entry is out of range.  Arguments as index_score (matrix-core paths only:
+ *   bf16 queries; fp32 queries return TIS_ERR_UNSUPPORTED).
+ * block_scores [T][ld_blocks] fp32, ld_blocks >= max nb_t and a multiple of 4, 16-byte aligned;
+ *              entries j >= nb_t are not written. */
+tis_status_t index_score_block(const tis_batch_t* batch, const void* q_idx, tis_dtype_t q_dt,
+                               const float* w, const void* k_pool, tis_dtype_t k_dt,
+                               const void* k_scale, int32_t H_I, int32_t D_I, tis_qmode_t qmode,
+                               float* block_scores, int64_t ld_blocks, void* stream);
+
+/* topk_block_select - per token, the kb_t = min(K_blocks, nb_t) blocks with the largest block
+ *   scores under (score descending, block ascending), as topk_select orders positions.
+ * block_idx [T][K_blocks] int32: the kept blocks ascending, then -1 up to K_blocks.
+ * block_val [T][K_blocks] fp32 or NULL: their block scores (0 where block_idx = -1).
+ * topk_idx  [T][64 * K_blocks] int32 or NULL (16-byte aligned): the positions the attention
+ *           reads: entry 64i + r is 64 * block_idx[t][i] + r when that position is causal
+ *           (<= p_t), else -1 (also for padding blocks); it can be passed to sparse_mla_attn
+ *           with K = 64 * K_blocks.
+ * ws        topk_block_select_workspace_size() bytes (nonzero only for rows above 32768
+ *           blocks, i.e. contexts above 2M positions, with K_blocks <= 4096), 16-byte aligned.
+ * K_blocks  >= 1, K_blocks * 64 <= 2^24. */
+tis_status_t topk_block_select(const tis_batch_t* batch, const float* block_scores,
+                               int64_t ld_blocks, int32_t K_blocks, int32_t* block_idx,
+                               float* block_val, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* index_score_topk_block - index_score_block followed by topk_block_select with the block
+ * scores in the workspace (index_score_topk_block_workspace_size() bytes, 16-byte aligned);
+ * identical results to the two calls. */
+tis_status_t index_score_topk_block(const tis_batch_t* batch, const void* q_idx,
+                                    tis_dtype_t q_dt, const float* w, const void* k_pool,
+                                    tis_dtype_t k_dt, const void* k_scale, int32_t H_I,
+                                    int32_t D_I, tis_qmode_t qmode, int32_t K_blocks,
+                                    int32_t* block_idx, float* block_val, int32_t* topk_idx,
+                                    void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace sizes in bytes for the calls above, from the host fields of `batch` only (the
  * caller owns every buffer).  index_score needs none and returns 0.  topk_select: nonzero only
  * for the several-workgroups-per-row selection (see topk_select).  index_score_topk: one chunk
@@ -235,6 +278,9 @@ size_t index_score_topk_workspace_size(const tis_batch_t* batch, int32_t H_I, in
                                        int32_t K);
 size_t sparse_mla_attn_workspace_size(const tis_batch_t* batch, int32_t K, int32_t H,
                                       int32_t D_qk, int32_t D_v, tis_dtype_t kv_dt);
+size_t topk_block_select_workspace_size(const tis_batch_t* batch, int32_t K_blocks);
+size_t index_score_topk_block_workspace_size(const tis_batch_t* batch, int32_t H_I, int32_t D_I,
+                                             int32_t K_blocks);
 
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* tis_last_error(void);

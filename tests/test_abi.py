@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     lib = tis.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tis_abi_version() == 4
+    assert lib.tis_abi_version() == 5
 
 
 LLVM = "/opt/rocm/llvm/bin"
@@ -260,3 +260,43 @@ def test_cache_append_argument_validation():
     assert call(pdt=L.TIS_MXFP8, Dd=80) == L.TIS_ERR_INVALID
     assert "multiple of 32" in last_error()
     assert lib.cache_append(None, D, 0, 576, D, 2, D, None) == L.TIS_ERR_INVALID
+
+
+def test_block_selection_argument_validation():
+    """Block-granular calls: K_blocks >= 1, block_idx set, an aligned expansion buffer, block
+    rows of at least ceil(n / 64) entries, matrix-core scorer only; the workspace queries
+    follow the block row length."""
+    lib = tis.lib()
+    b = FakeBatch([1000, 600], [0, 1, 3])          # 16 blocks at most
+
+    def sel(ld=16, K=4, bi=D, bv=None, ti=D, ws=None, wsb=0):
+        return lib.topk_block_select(b.ref, D, ld, K, bi, bv, ti, ws, wsb, None)
+
+    assert sel(K=0) == L.TIS_ERR_INVALID
+    assert sel(bi=None) == L.TIS_ERR_INVALID
+    assert sel(ti=D + 4) == L.TIS_ERR_INVALID
+    assert sel(ld=12) == L.TIS_ERR_INVALID         # < 16 blocks
+    assert sel(ld=18) == L.TIS_ERR_INVALID         # not a multiple of 4
+    assert sel(K=(1 << 18) + 1) == L.TIS_ERR_INVALID
+    assert lib.topk_block_select_workspace_size(b.ref, 4) == 0
+    # a 3M-position row: 46,875 blocks, above the one-workgroup limit -> multi-workgroup rows
+    big = FakeBatch([3_000_000], [0, 1])
+    assert lib.topk_block_select_workspace_size(big.ref, 32) > 0
+
+    def blk(**kw):
+        a = dict(q=D, qdt=L.TIS_BF16, w=D, k=D, kdt=L.TIS_E4M3, ks=D, H=64, Dd=128,
+                 qm=L.TIS_QMODE_FP8, sc=D, ld=16)
+        a.update(kw)
+        return lib.index_score_block(b.ref, a["q"], a["qdt"], a["w"], a["k"], a["kdt"], a["ks"],
+                                     a["H"], a["Dd"], a["qm"], a["sc"], a["ld"], None)
+
+    assert blk(ld=8) == L.TIS_ERR_INVALID
+    assert blk(sc=D + 4) == L.TIS_ERR_INVALID
+    assert blk(qdt=L.TIS_F32, kdt=L.TIS_F32, qm=L.TIS_QMODE_BF16, ks=None, H=4,
+               Dd=32) == L.TIS_ERR_UNSUPPORTED
+    need = lib.index_score_topk_block_workspace_size(b.ref, 64, 128, 4)
+    assert need == 3 * 16 * 4 + (256 - 3 * 16 * 4 % 256) % 256   # T=3 rows of 16 block scores
+    assert lib.index_score_topk_block(b.ref, D, L.TIS_BF16, D, D, L.TIS_E4M3, D, 64, 128,
+                                      L.TIS_QMODE_FP8, 4, D, None, D, D, need - 1,
+                                      None) == L.TIS_ERR_INVALID
+    assert "workspace" in last_error()

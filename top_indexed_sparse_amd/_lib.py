@@ -19,8 +19,10 @@ PAGE_SIZE = 64
 
 EXPORTS = ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
            "sparse_mla_attn", "cache_append",
+           "index_score_block", "topk_block_select", "index_score_topk_block",
            "index_score_workspace_size", "topk_select_workspace_size",
            "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size",
+           "topk_block_select_workspace_size", "index_score_topk_block_workspace_size",
            "tis_last_error", "tis_abi_version")
 
 
@@ -68,17 +70,26 @@ def lib():
     L.sparse_mla_attn.argtypes = [_BP, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F,
                                   _P, _I32, _P, _P, _SZ, _P]
     L.cache_append.argtypes = [_BP, _P, _I32, _I32, _P, _I32, _P, _P]
+    L.index_score_block.argtypes = [_BP, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32, _P, _I64,
+                                    _P]
+    L.topk_block_select.argtypes = [_BP, _P, _I64, _I32, _P, _P, _P, _P, _SZ, _P]
+    L.index_score_topk_block.argtypes = [_BP, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32,
+                                         _I32, _P, _P, _P, _P, _SZ, _P]
     for f in ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
-              "sparse_mla_attn", "cache_append"):
+              "sparse_mla_attn", "cache_append", "index_score_block", "topk_block_select",
+              "index_score_topk_block"):
         getattr(L, f).restype = _I32
     L.index_score_workspace_size.argtypes = [_BP, _I32, _I32]
     L.topk_select_workspace_size.argtypes = [_BP, _I32]
     L.index_score_topk_workspace_size.argtypes = [_BP, _I32, _I32, _I32]
     L.sparse_mla_attn_workspace_size.argtypes = [_BP, _I32, _I32, _I32, _I32, _I32]
+    L.topk_block_select_workspace_size.argtypes = [_BP, _I32]
+    L.index_score_topk_block_workspace_size.argtypes = [_BP, _I32, _I32, _I32]
     for f in ("index_score_workspace_size", "topk_select_workspace_size",
-              "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size"):
+              "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size",
+              "topk_block_select_workspace_size", "index_score_topk_block_workspace_size"):
         getattr(L, f).restype = _SZ
-    if L.tis_abi_version() != 4:
+    if L.tis_abi_version() != 5:
         raise RuntimeError("libtopidx ABI version mismatch")
     _lib = L
     return L
@@ -247,3 +258,55 @@ def cache_append(batch: Batch, rows, pool, pool_scale=None):
     _check(lib().cache_append(batch.ref, _ptr(rows), _dtype(rows), D, _ptr(pool),
                               _cache_dtype(pool, pool_scale), _ptr(pool_scale), _stream()))
     return pool
+
+
+def blocks_of(n: int) -> int:
+    """Blocks (64-position pages) of a causal range of n positions."""
+    return -(-int(n) // PAGE_SIZE)
+
+
+def index_score_block(batch: Batch, q_idx, w, k_pool, k_scale, block_scores, qmode=None):
+    """block_scores[t, j]: the largest score of token t over the causal positions of page j
+    (see index_score_block in topidx.h)."""
+    H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    kd = _cache_dtype(k_pool, k_scale)
+    qmode = _qmode(q_idx, kd, qmode)
+    _check(lib().index_score_block(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_pool),
+                                   kd, _ptr(k_scale), H_I, D_I, qmode, _ptr(block_scores),
+                                   int(block_scores.stride(0)), _stream()))
+    return block_scores
+
+
+def topk_block_select_workspace_size(batch: Batch, K_blocks: int) -> int:
+    return int(lib().topk_block_select_workspace_size(batch.ref, int(K_blocks)))
+
+
+def topk_block_select(batch: Batch, block_scores, K_blocks: int, block_idx, block_val=None,
+                      topk_idx=None, ws=None):
+    """The K_blocks best pages per token (block_idx), optionally expanded to the positions
+    the attention reads (topk_idx [T][64 * K_blocks])."""
+    need = topk_block_select_workspace_size(batch, K_blocks)
+    ws, nb = _ws(need, ws, block_scores.device)
+    _check(lib().topk_block_select(batch.ref, _ptr(block_scores), int(block_scores.stride(0)),
+                                   int(K_blocks), _ptr(block_idx), _ptr(block_val),
+                                   _ptr(topk_idx), _ptr(ws), nb, _stream()))
+    return block_idx
+
+
+def index_score_topk_block_workspace_size(batch: Batch, H_I: int, D_I: int, K_blocks: int) -> int:
+    return int(lib().index_score_topk_block_workspace_size(batch.ref, H_I, D_I, int(K_blocks)))
+
+
+def index_score_topk_block(batch: Batch, q_idx, w, k_pool, k_scale, K_blocks: int, block_idx,
+                           block_val=None, topk_idx=None, ws=None, qmode=None):
+    """index_score_block + topk_block_select in one call (block scores in the workspace)."""
+    H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    kd = _cache_dtype(k_pool, k_scale)
+    qmode = _qmode(q_idx, kd, qmode)
+    need = index_score_topk_block_workspace_size(batch, H_I, D_I, K_blocks)
+    ws, nb = _ws(need, ws, q_idx.device)
+    _check(lib().index_score_topk_block(batch.ref, _ptr(q_idx), _dtype(q_idx), _ptr(w),
+                                        _ptr(k_pool), kd, _ptr(k_scale), H_I, D_I, qmode,
+                                        int(K_blocks), _ptr(block_idx), _ptr(block_val),
+                                        _ptr(topk_idx), _ptr(ws), nb, _stream()))
+    return block_idx

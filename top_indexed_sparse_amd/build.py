@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtopidx.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip", "blocks.hip"]
 ARCH = "gfx950"
 
 

@@ -90,6 +90,7 @@ tis::DevBatch dev_batch(const tis_batch_t* b) {
   d.T = b->T;
   d.pt_stride = b->pt_stride;
   d.n_pages = b->n_pages;
+  d.row_shift = 0;
   return d;
 }
 
@@ -133,10 +134,12 @@ tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* 
               "MXFP8) for (q, k, qmode)");
 }
 
+// block: one score per 64-key page (rows of ld entries) instead of one per key; the fp32
+// scorer has no block form (callers check)
 tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath path, int t0,
                        int tc, const void* q_idx, const float* w, const void* k_pool,
                        const void* k_scale, int H_I, int D_I, float* scores, int64_t ld,
-                       hipStream_t st) {
+                       hipStream_t st, bool block = false) {
   const tis::DevBatch d = dev_batch(batch);
   hipError_t e;
   if (path == IdxPath::F32)
@@ -145,8 +148,8 @@ tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath pat
   else
     e = tis::launch_index_score_fp8(d, t0, tc, hi.max_n, hi.prefill_like,
                                     path == IdxPath::BF16 ? 1 : path == IdxPath::MX ? 2 : 0,
-                                    (const uint16_t*)q_idx, w, (const uint8_t*)k_pool, k_scale,
-                                    scores, ld, st);
+                                    block, (const uint16_t*)q_idx, w, (const uint8_t*)k_pool,
+                                    k_scale, scores, ld, st);
   return e == hipSuccess ? TIS_OK : hip_fail(e, "index_score launch");
 }
 
@@ -395,6 +398,152 @@ TIS_API tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const vo
   if (st != TIS_OK) return st;
   return fused_run(batch, hi, path, q_idx, w, k_pool, k_scale, H_I, D_I, K, topk_idx, topk_val,
                    rows, ptr, (hipStream_t)stream);
+}
+
+// ============================================================================ block selection
+namespace {
+
+constexpr int kBlockShift = 6;  // one block = one 64-position page
+
+int blocks_of(int n) { return (n + (1 << kBlockShift) - 1) >> kBlockShift; }
+
+tis::DevBatch block_batch(const tis_batch_t* b) {
+  tis::DevBatch d = dev_batch(b);
+  d.row_shift = kBlockShift;
+  return d;
+}
+
+size_t block_rows_bytes(int rows, const HostInfo& hi) {
+  return ((size_t)rows * (size_t)round4(blocks_of(hi.max_n)) * sizeof(float) + 255) &
+         ~(size_t)255;
+}
+
+// selection over block rows, then the optional expansion to positions
+tis_status_t run_block_select(const tis_batch_t* batch, const HostInfo& hi, int t0, int tc,
+                              const float* bs, int64_t ld, int32_t K_blocks, int32_t* block_idx,
+                              float* block_val, int32_t* topk_idx, void* ws, hipStream_t s) {
+  hipError_t e = tis::launch_topk(block_batch(batch), t0, tc, blocks_of(hi.max_n), bs, ld,
+                                  K_blocks, block_idx, block_val, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "block selection launch");
+  if (topk_idx) {
+    e = tis::launch_expand_blocks(dev_batch(batch), t0, tc, block_idx, K_blocks, topk_idx, s);
+    if (e != hipSuccess) return hip_fail(e, "block expansion launch");
+  }
+  return TIS_OK;
+}
+
+tis_status_t check_block_outputs(int32_t K_blocks, const int32_t* block_idx,
+                                 const int32_t* topk_idx) {
+  if (K_blocks < 1) return fail(TIS_ERR_INVALID, "K_blocks must be >= 1");
+  if ((int64_t)K_blocks * TIS_PAGE_SIZE > (int64_t)1 << 24)
+    return fail(TIS_ERR_INVALID, "K_blocks * 64 must be <= 2^24");
+  if (!block_idx) return fail(TIS_ERR_INVALID, "block_idx must be set");
+  if (topk_idx && !aligned16(topk_idx))
+    return fail(TIS_ERR_INVALID, "topk_idx must be 16-byte aligned");
+  return TIS_OK;
+}
+
+}  // namespace
+
+TIS_API tis_status_t index_score_block(const tis_batch_t* batch, const void* q_idx,
+                                       tis_dtype_t q_dt, const float* w, const void* k_pool,
+                                       tis_dtype_t k_dt, const void* k_scale, int32_t H_I,
+                                       int32_t D_I, tis_qmode_t qmode, float* block_scores,
+                                       int64_t ld_blocks, void* stream) {
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  IdxPath path;
+  st = check_index_args(q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I, qmode, &path);
+  if (st != TIS_OK) return st;
+  if (path == IdxPath::F32)
+    return fail(TIS_ERR_UNSUPPORTED, "block scores need the matrix-core scorer (bf16 queries)");
+  if (!block_scores || !aligned16(block_scores))
+    return fail(TIS_ERR_INVALID, "block_scores must be 16-byte aligned");
+  if (ld_blocks < blocks_of(hi.max_n) || (ld_blocks & 3))
+    return fail(TIS_ERR_INVALID, "ld_blocks must be >= %d and a multiple of 4",
+                blocks_of(hi.max_n));
+  return run_index(batch, hi, path, 0, batch->T, q_idx, w, k_pool, k_scale, H_I, D_I,
+                   block_scores, ld_blocks, (hipStream_t)stream, true);
+}
+
+TIS_API size_t topk_block_select_workspace_size(const tis_batch_t* batch, int32_t K_blocks) {
+  HostInfo hi;
+  if (check_batch(batch, &hi) != TIS_OK || K_blocks < 1) return 0;
+  return tis::topk_ws_bytes(batch->T, blocks_of(hi.max_n), K_blocks);
+}
+
+TIS_API tis_status_t topk_block_select(const tis_batch_t* batch, const float* block_scores,
+                                       int64_t ld_blocks, int32_t K_blocks, int32_t* block_idx,
+                                       float* block_val, int32_t* topk_idx, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  st = check_block_outputs(K_blocks, block_idx, topk_idx);
+  if (st != TIS_OK) return st;
+  if (!block_scores || !aligned16(block_scores))
+    return fail(TIS_ERR_INVALID, "block_scores must be 16-byte aligned");
+  if (ld_blocks < blocks_of(hi.max_n) || (ld_blocks & 3))
+    return fail(TIS_ERR_INVALID, "ld_blocks must be >= %d and a multiple of 4",
+                blocks_of(hi.max_n));
+  const size_t need = tis::topk_ws_bytes(batch->T, blocks_of(hi.max_n), K_blocks);
+  if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
+    return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
+  return run_block_select(batch, hi, 0, batch->T, block_scores, ld_blocks, K_blocks, block_idx,
+                          block_val, topk_idx, ws, (hipStream_t)stream);
+}
+
+TIS_API size_t index_score_topk_block_workspace_size(const tis_batch_t* batch, int32_t H_I,
+                                                     int32_t D_I, int32_t K_blocks) {
+  (void)H_I; (void)D_I;
+  HostInfo hi;
+  if (check_batch(batch, &hi) != TIS_OK || K_blocks < 1) return 0;
+  const int rows = std::max(1, std::min<int>(batch->T, (int)(kScoreScratchBudget /
+                                                        (round4(blocks_of(hi.max_n)) * 4))));
+  return block_rows_bytes(rows, hi) + tis::topk_ws_bytes(rows, blocks_of(hi.max_n), K_blocks);
+}
+
+TIS_API tis_status_t index_score_topk_block(const tis_batch_t* batch, const void* q_idx,
+                                            tis_dtype_t q_dt, const float* w,
+                                            const void* k_pool, tis_dtype_t k_dt,
+                                            const void* k_scale, int32_t H_I, int32_t D_I,
+                                            tis_qmode_t qmode, int32_t K_blocks,
+                                            int32_t* block_idx, float* block_val,
+                                            int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  IdxPath path;
+  st = check_index_args(q_idx, q_dt, w, k_pool, k_dt, k_scale, H_I, D_I, qmode, &path);
+  if (st != TIS_OK) return st;
+  if (path == IdxPath::F32)
+    return fail(TIS_ERR_UNSUPPORTED, "block scores need the matrix-core scorer (bf16 queries)");
+  st = check_block_outputs(K_blocks, block_idx, topk_idx);
+  if (st != TIS_OK) return st;
+  const int nb = blocks_of(hi.max_n);
+  const int rows = std::max(1, std::min<int>(batch->T, (int)(kScoreScratchBudget /
+                                                        (round4(nb) * 4))));
+  const size_t sbytes = block_rows_bytes(rows, hi);
+  const size_t need = sbytes + tis::topk_ws_bytes(rows, nb, K_blocks);
+  if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
+    return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
+  hipStream_t s = (hipStream_t)stream;
+  float* bs = (float*)ws;
+  void* tws = (char*)ws + sbytes;
+  const int64_t ld = round4(nb);
+  for (int t0 = 0; t0 < batch->T; t0 += rows) {
+    const int tc = std::min(rows, batch->T - t0);
+    st = run_index(batch, hi, path, t0, tc, q_idx, w, k_pool, k_scale, H_I, D_I, bs, ld, s,
+                   true);
+    if (st != TIS_OK) return st;
+    // (the chunk's rows start at bs: the selection indexes its rows from t0)
+    st = run_block_select(batch, hi, t0, tc, bs, ld, K_blocks, block_idx, block_val, topk_idx,
+                          tws, s);
+    if (st != TIS_OK) return st;
+  }
+  return TIS_OK;
 }
 
 TIS_API tis_status_t cache_append(const tis_batch_t* batch, const void* rows,

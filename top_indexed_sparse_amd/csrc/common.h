@@ -30,12 +30,15 @@ constexpr int kBufDword3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Device view of a ragged paged batch (launches take a token range on top of it).
+// Device view of a ragged paged batch (launches take a token range on top of it).  row_shift:
+// the selection kernels' rows hold one entry per 2^row_shift positions (0: token scores;
+// 6: one score per 64-position page); no other kernel reads it.
 struct DevBatch {
   const int32_t* seq_lens;
   const int32_t* cu_q;
   const int32_t* page_table;
   int32_t B, T, pt_stride, n_pages;
+  int32_t row_shift;
 };
 
 // Where flattened token t sits: its request b (the largest b with cu_q[b] <= t, so empty
@@ -136,6 +139,13 @@ __device__ __forceinline__ float xor32_sum(float x) {
 __device__ __forceinline__ float xor32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Largest value over the 64 lanes of the wave (every lane gets it).
+__device__ __forceinline__ float wave_max(float x) {
+  x = xor32_max(x);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
 }
 // Pairwise sums across the halves: lanes [0,32) get a[l] + a[l+32], lanes [32,64) get
 // b[l-32] + b[l].  pair16_sum does the same within each 32-lane half, on 16-lane halves.

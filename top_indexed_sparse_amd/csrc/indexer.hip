@@ -347,7 +347,10 @@ __device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp
 // chunk), so that at each step the workgroup reads 64 KB of consecutive pages when the
 // request's pages are consecutive.
 // (kernel signatures name no type that depends on the mode: the key scales come in untyped)
-template <int QM>
+// BLK: block-granular scoring: instead of one score per key, one per 64-key page, the largest
+// score among the page's causal keys (-inf for a page whose table entry is out of range),
+// written to scores[tl][page]; the wave reduces the page's 64 scores and stores once.
+template <int QM, bool BLK>
 __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
     const void* kscale_raw, float* __restrict__ scores, int64_t ld, int chunk) {
@@ -479,9 +482,9 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
       for (int i = 0; i < 4; ++i) wp[m][i] = wv[i];
     }
   }
-  // stores at byte offset 4*s of the row, kept for s < k1
-  const __amdgpu_buffer_rsrc_t orsrc =
-      __builtin_amdgcn_make_buffer_rsrc(out, 0, k1 * 4, kBufDword3);
+  // stores at byte offset 4*s of the row, kept for s < k1 (BLK: 4*page, for pages below k1)
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      out, 0, BLK ? ((k1 + 63) >> 6) * 4 : k1 * 4, kBufDword3);
   // page g from ring slot u: fetch page g + 3 into the slot freed last (if there is more to
   // fetch), then score page g
   auto step = [&](int g, int u, bool more, KScale<QM> scale) {
@@ -494,8 +497,16 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
     stage_ktile4(stage, lane, c.kp, kt);
     float sc = score_group<QM>(A, wp, kt, scale);
     if (!c.ok) sc = -INFINITY;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
-                                          (k0 + 64 * (poff + g * kStep) + lane) * 4, 0, 0);
+    const int pos = k0 + 64 * (poff + g * kStep) + lane;
+    if constexpr (BLK) {
+      // the page's largest causal score, stored by lane 0 (the other lanes' offsets lie past
+      // the resource's end, so the hardware drops their stores)
+      const float m = wave_max(pos < k1 ? sc : -INFINITY);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc,
+                                            lane == 0 ? (pos >> 6) * 4 : 0x40000000, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc, pos * 4, 0, 0);
+    }
   };
   // eight pages, unrolled in full: straight-line code, whose only exit ends the kernel
 #pragma unroll
@@ -515,7 +526,7 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
 // different requests are scored in one pass per request (every wave loads and waits in every
 // pass; a wave stores only in its own request's pass, through a buffer resource whose record
 // count is zero otherwise).  A wave without a token (the batch's last group) only loads.
-template <int QM>
+template <int QM, bool BLK>
 __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
     const void* kscale_raw, float* __restrict__ scores, int64_t ld) {
@@ -571,9 +582,11 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
     const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;
     if (npg == 0) continue;  // (uniform)
     // stores at byte offset 4*s of the token's row, kept for s < my_k1 in its own request's pass
+    // (BLK: 4*page, for pages below my_k1)
     const bool mine = has && loc.b == b;
+    const int rec = BLK ? ((my_k1 + 63) >> 6) * 4 : my_k1 * 4;
     const __amdgpu_buffer_rsrc_t orsrc =
-        __builtin_amdgcn_make_buffer_rsrc(out, 0, mine ? my_k1 * 4 : 0, kBufDword3);
+        __builtin_amdgcn_make_buffer_rsrc(out, 0, mine ? rec : 0, kBufDword3);
     const int pcol = min((k0 >> 6) + lane, bt.pt_stride - 1);
     const int my_page = bt.page_table[(int64_t)b * bt.pt_stride + pcol];
     // (fetches past the last page re-read it: no branch around a load)
@@ -624,8 +637,14 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
         }
         float sc = score_group<QM>(A, wp, kt, ring[u].ks);
         if (!ring[u].ok) sc = -INFINITY;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc,
-                                              (k0 + 64 * g + lane) * 4, 0, 0);
+        const int pos = k0 + 64 * g + lane;
+        if constexpr (BLK) {
+          const float m = wave_max(pos < my_k1 ? sc : -INFINITY);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), orsrc,
+                                                lane == 0 ? (pos >> 6) * 4 : 0x40000000, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc, pos * 4, 0, 0);
+        }
         __syncthreads();
       }
     }
@@ -643,7 +662,7 @@ hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, 
   return hipGetLastError();
 }
 
-template <int QM>
+template <int QM, bool BLK>
 static hipError_t launch_mma(const DevBatch& bt, int t_begin, int t_count, int max_n,
                              bool prefill_like, const uint16_t* q_idx, const float* w,
                              const uint8_t* kpool, const void* kscale, float* scores, int64_t ld,
@@ -653,31 +672,44 @@ static hipError_t launch_mma(const DevBatch& bt, int t_begin, int t_count, int m
   // four tokens per 4-wave workgroup sharing a 1024-key chunk
   if (prefill_like) {
     dim3 grid((t_count + 3) / 4, (max_n + chunk - 1) / chunk);
-    hipLaunchKernelGGL(idx_score_group_kernel<QM>, grid, dim3(256), 0, st, bt, t_begin, t_count,
+    auto* gfn = idx_score_group_kernel<QM, BLK>;
+    hipLaunchKernelGGL(gfn, grid, dim3(256), 0, st, bt, t_begin, t_count,
                        q_idx, w, kpool, kscale, scores, ld);
     return hipGetLastError();
   }
   dim3 grid(t_count, (max_n + chunk - 1) / chunk);
-  hipLaunchKernelGGL(idx_score_fp8_kernel<QM>, grid, dim3(512), 0, st, bt, t_begin, t_count,
+  auto* fn = idx_score_fp8_kernel<QM, BLK>;
+  hipLaunchKernelGGL(fn, grid, dim3(512), 0, st, bt, t_begin, t_count,
                      q_idx, w, kpool, kscale, scores, ld, chunk);
   return hipGetLastError();
 }
 
-hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, int qmode, const uint16_t* q_idx,
-                                  const float* w, const uint8_t* kpool, const void* kscale,
-                                  float* scores, int64_t ld, hipStream_t st) {
+template <bool BLK>
+static hipError_t launch_mode(const DevBatch& bt, int t_begin, int t_count, int max_n,
+                              bool prefill_like, int qmode, const uint16_t* q_idx,
+                              const float* w, const uint8_t* kpool, const void* kscale,
+                              float* scores, int64_t ld, hipStream_t st) {
   switch (qmode) {
     case kQBf16:
-      return launch_mma<kQBf16>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
-                                kscale, scores, ld, st);
+      return launch_mma<kQBf16, BLK>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w,
+                                     kpool, kscale, scores, ld, st);
     case kQMx:
-      return launch_mma<kQMx>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
-                              kscale, scores, ld, st);
+      return launch_mma<kQMx, BLK>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
+                                   kscale, scores, ld, st);
     default:
-      return launch_mma<kQFp8>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
-                               kscale, scores, ld, st);
+      return launch_mma<kQFp8, BLK>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w,
+                                    kpool, kscale, scores, ld, st);
   }
+}
+
+hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
+                                  bool prefill_like, int qmode, bool block, const uint16_t* q_idx,
+                                  const float* w, const uint8_t* kpool, const void* kscale,
+                                  float* scores, int64_t ld, hipStream_t st) {
+  return block ? launch_mode<true>(bt, t_begin, t_count, max_n, prefill_like, qmode, q_idx, w,
+                                   kpool, kscale, scores, ld, st)
+               : launch_mode<false>(bt, t_begin, t_count, max_n, prefill_like, qmode, q_idx, w,
+                                    kpool, kscale, scores, ld, st);
 }
 
 }  // namespace tis

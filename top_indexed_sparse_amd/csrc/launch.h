@@ -12,9 +12,10 @@ hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, 
                                   const float* q, const float* w, const float* kpool, int H,
                                   int D, float* scores, int64_t ld, hipStream_t st);
 // qmode: 0 = e4m3 query with per-head scales (per-token fp32 key scales), 1 = bf16 query
-// (per-token fp32 key scales), 2 = MXFP8 query and keys (kscale: four scale bytes per key)
+// (per-token fp32 key scales), 2 = MXFP8 query and keys (kscale: four scale bytes per key).
+// block: one score per 64-key page (the largest causal key score) instead of one per key.
 hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, int qmode, const uint16_t* q_idx,
+                                  bool prefill_like, int qmode, bool block, const uint16_t* q_idx,
                                   const float* w, const uint8_t* kpool, const void* kscale,
                                   float* scores, int64_t ld, hipStream_t st);
 hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
@@ -31,6 +32,10 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
                            const int32_t* idx, int K, float softmax_scale, int nsplit,
                            void* out, bool out_f32, float* lse, float* part_o, float* part_ml,
                            hipStream_t st);
+// topk_idx[t][64*i + r] = 64*block_idx[t][i] + r for causal positions of kept pages, else -1
+hipError_t launch_expand_blocks(const DevBatch& bt, int t_begin, int t_count,
+                                const int32_t* block_idx, int K_blocks, int32_t* topk_idx,
+                                hipStream_t st);
 int attn_split_count(int t_count, int K);
 int attn_keys_per_split(int K, int nsplit);
 size_t attn_smem_bytes(bool fp8, int kps);

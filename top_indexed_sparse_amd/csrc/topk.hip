@@ -22,6 +22,14 @@
 
 namespace tis {
 
+// Entries of token t's selection row: its n causal positions, or ceil(n / 64) page scores for
+// block-granular selection (row_shift 6).
+__device__ __forceinline__ int row_len(const DevBatch& bt, int t) {
+  const int n = locate(bt, t).n;
+  return (n + (1 << bt.row_shift) - 1) >> bt.row_shift;
+}
+
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   u = u == 0x80000000u ? 0u : u;  // -0.0 ties with +0.0
@@ -258,6 +266,7 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
   const LocLoads lw = locate_issue(bt);
   load_first((int)min<int64_t>(ld, (int64_t)CH));
   n = locate_finish(bt, t, lw).n;
+  n = (n + (1 << bt.row_shift) - 1) >> bt.row_shift;  // (block rows: pages, not positions)
   int32_t* oi = out_idx + (int64_t)t * K;
   float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
 
@@ -534,7 +543,7 @@ __global__ __launch_bounds__(256) void topk_long_hist_kernel(DevBatch bt, int t_
   __shared__ uint32_t h[2048];
   const int tid = threadIdx.x, tl = blockIdx.y;
   for (int i = tid; i < 2048; i += 256) h[i] = 0u;
-  const int n = locate(bt, t_begin + tl).n;
+  const int n = row_len(bt, t_begin + tl);
   const float* row = scores + (int64_t)tl * ld;
   const int p0 = blockIdx.x * slice, p1 = min(n, p0 + slice);
   __syncthreads();
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(1024) void topk_long_pick_kernel(DevBatch bt, int t
   __shared__ uint32_t sh[48];
   __shared__ uint32_t pick[3];
   const int tid = threadIdx.x, tl = blockIdx.x;
-  const int n = locate(bt, t_begin + tl).n;
+  const int n = row_len(bt, t_begin + tl);
   uint32_t* st = state + 4 * tl;
   if (n <= K) {  // (uniform over the workgroup)
     if (tid == 0) st[0] = kLongAll;
@@ -625,7 +634,7 @@ __global__ __launch_bounds__(256) void topk_long_count_kernel(DevBatch bt, int t
   const uint32_t* st = state + 4 * tl;
   if (st[0] != kLongCand) return;
   const uint32_t thr = st[1] << 21;  // the candidates: keys in bins >= the picked one
-  const int n = locate(bt, t_begin + tl).n;
+  const int n = row_len(bt, t_begin + tl);
   const float* row = scores + (int64_t)tl * ld;
   const int p0 = blockIdx.x * slice, p1 = min(n, p0 + slice);
   if (tid == 0) c_sh = 0u;
@@ -650,7 +659,7 @@ __global__ __launch_bounds__(1024) void topk_long_write_kernel(DevBatch bt, int 
   const uint32_t* st = state + 4 * tl;
   if (st[0] != kLongCand) return;  // (uniform over the workgroup)
   const uint32_t thr = st[1] << 21;
-  const int n = locate(bt, t_begin + tl).n;
+  const int n = row_len(bt, t_begin + tl);
   const float* row = scores + (int64_t)tl * ld;
   uint64_t* out = cand + (int64_t)tl * kLongCap;
   const int p0 = s * slice, p1 = min(n, p0 + slice);
@@ -699,7 +708,7 @@ __global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int 
   int32_t* oi = out_idx + (int64_t)t * K;
   float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
   if (mode == kLongAll) {
-    const int n = locate(bt, t).n;
+    const int n = row_len(bt, t);
     for (int i = tid; i < K; i += 1024) {
       oi[i] = i < n ? i : -1;
       if (ov) ov[i] = i < n ? row[i] : 0.f;
