@@ -24,18 +24,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtopidx)")
 
 
-def command(out: str) -> list[str]:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+# Per-file code-generation options.  The scorer's matrix products write ordinary vector
+# registers (its epilogue reads every result at once; results in accumulator registers would
+# each be copied out first); the attention kernel keeps its accumulators where the compiler
+# puts them.
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def _common() -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-fvisibility=hidden",
             # packed fp32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def compile_command(src: str, obj: str) -> list[str]:
+    """One source file to an object holding its host code and gfx950 code object."""
+    return _common() + FILE_FLAGS.get(src, []) + ["-c", "-o", obj, os.path.join(CSRC, src)]
+
+
+def link_command(objs: list[str], out: str) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out] + objs
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,7 +58,19 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one hipcc per file) and link libtopidx.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="topidx_build_") as d:
+        objs = [os.path.join(d, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+            list(ex.map(lambda a: _run(compile_command(*a), verbose), zip(SOURCES, objs)))
+        tmp = LIB + ".tmp"
+        _run(link_command(objs, tmp), verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 

@@ -285,6 +285,9 @@ __device__ __forceinline__ bf16x8 widen8_bf16(int lo, int hi) {
                                  6, 7);
 }
 
+// max(0, x) in one instruction (median of x, 0 and the largest float; scores are finite)
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
+
 // Scores of the 64 keys of one page-aligned group; lane l returns key base + l, times the
 // key's scale word ks (the key's fp32 scale; MXFP8: its scale bytes enter the products).
 template <int QM>
@@ -309,7 +312,7 @@ __device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A.a[m][st]),
                                                       B[st], c, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], fmaxf(c[i], 0.f), acc);
+        for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], relu(c[i]), acc);
       }
     } else {
       i32x8 B;
@@ -320,17 +323,24 @@ __device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp
       if constexpr (QM == kQMx)
         sb = __builtin_amdgcn_ubfe(
             (uint32_t)__shfl((int)ks, 16 * j + (lane & 15)), 8 * (lane >> 4), 8);
+      // the four head tiles' products are independent: all four go out before the first is
+      // read (one accumulator reused would make each wait for the previous one's result)
+      f32x4 c[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        c[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (QM == kQMx)
-          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c, 0, 0, 0, A.sa[m],
-                                                               0, sb);
+          c[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c[m], 0, 0, 0,
+                                                                  A.sa[m], 0, sb);
         else
-          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], fmaxf(c[i], 0.f), acc);
+          c[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c[m], 0, 0, 0, 0,
+                                                                  0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], relu(c[m][i]), acc);
     }
     v[j] = acc;
   }
