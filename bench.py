@@ -194,6 +194,74 @@ def cpu_baseline(inp, r_idx, r_out, out_bf16, tokens, unit, block=False):
     return rec, dt, recall_hits / max(1, recall_tot), worst
 
 
+def dense_ab(args):
+    """Gather form (sparse_mla_attn) against dense-masked form (sparse_mla_attn_dense) of the
+    attention over the same selections, on the prefill workload's shapes (e4m3 latent cache,
+    K = 2048): one batch per band of causal lengths (lo, hi], i.e. the query tokens at
+    positions lo .. hi-1 of a hi-token sequence.  The dense form reads and multiplies every
+    causal row; the gather form only the K selected ones."""
+    import numpy as np
+    import torch
+    import synth
+    import top_indexed_sparse_amd as tis
+    from synth.device import to_device
+    base = synth.workload(synth.PREFILL64K)
+    sh = base.shape
+    bands = [(0, 2048), (2048, 4096), (4096, 8192), (8192, 16384)]
+    rows = []
+    stream = torch.cuda.current_stream()
+    for lo, hi in bands:
+        wl = synth.reduced(base, [hi], [hi - lo], name=f"prefill-band-{lo}-{hi}")
+        inp = synth.make(wl, "continuous")
+        d = to_device(inp)
+        bt = tis.Batch(inp.seq_lens, inp.cu_q, inp.page_table, inp.n_pages)
+        T, K = inp.T, sh.K
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        tis.index_score_topk(bt, d.q_idx, d.w, d.k_pool, d.k_scale, K, idx)
+        out = torch.empty((T, sh.H, sh.D_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((T, sh.H), dtype=torch.float32, device="cuda")
+        kvd = tis.TIS_E4M3
+        wsg = torch.empty(max(1, tis.sparse_mla_attn_workspace_size(bt, K, sh.H, sh.D_qk, sh.D_v,
+                                                                    kvd)),
+                          dtype=torch.uint8, device="cuda")
+        wsd = torch.empty(max(1, tis.sparse_mla_attn_dense_workspace_size(bt, K, sh.H, sh.D_qk,
+                                                                          sh.D_v, kvd)),
+                          dtype=torch.uint8, device="cuda")
+        res = {}
+        for form, fn, ws in (("gather", tis.sparse_mla_attn, wsg),
+                             ("dense", tis.sparse_mla_attn_dense, wsd)):
+            for _ in range(2):
+                fn(bt, d.q, d.kv_pool, d.kv_scale, idx, sh.softmax_scale, out, lse, ws=ws)
+            runs = []
+            for _ in range(max(1, args.repeats)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(args.steps):
+                    fn(bt, d.q, d.kv_pool, d.kv_scale, idx, sh.softmax_scale, out, lse, ws=ws)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                runs.append(e0.elapsed_time(e1) / args.steps)
+            res[form] = float(np.median(runs))
+        n = inp.positions.astype(np.int64) + 1
+        row = {"band": [lo, hi], "tokens": T, "mean_causal": float(n.mean()),
+               "selected_fraction": float((np.minimum(K, n) / n).mean()),
+               "gather_ms": round(res["gather"], 3), "dense_ms": round(res["dense"], 3),
+               "dense_over_gather": round(res["dense"] / res["gather"], 3)}
+        log(f"band ({lo}, {hi}]: {T} tokens, selected {row['selected_fraction']:.2f} of the "
+            f"causal rows; gather {res['gather']:.2f} ms, dense {res['dense']:.2f} ms")
+        rows.append(row)
+        del d, idx, out, lse, wsg, wsd
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "prefill attention: dense-masked form / gather form time",
+                      "unit": "ratio", "higher_is_better": False, "n_gpus": 1,
+                      "steps": args.steps, "repeats": args.repeats, "data": "synthetic",
+                      "config": {"workload": "prefill64k bands", "topk": base.shape.K,
+                                 "heads": sh.H, "qk_dim": sh.D_qk, "v_dim": sh.D_v,
+                                 "kv_cache": "fp8"},
+                      "bands": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +279,10 @@ def main():
                     help="indexer key format: e4m3 + fp32 scale per token, or MXFP8")
     ap.add_argument("--select", default="token", choices=["token", "block"],
                     help="Top-K positions, or the K/64 best 64-position pages")
+    ap.add_argument("--dense-ab", action="store_true",
+                    help="only run the A/B of the attention's gather form against its "
+                         "dense-masked form on bands of causal length of the prefill "
+                         "workload's shapes, and print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (8 times) and exit: the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -238,6 +310,9 @@ def main():
     from synth.device import to_device
 
     torch.cuda.set_device(0)
+    if args.dense_ab:
+        dense_ab(args)
+        return
     mx = args.k_fmt == "mxfp8"
     block = args.select == "block"
     main_line = args.workload == "decode32k" and not mx and not block

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define TIS_ABI_VERSION 5
+#define TIS_ABI_VERSION 6
 #define TIS_PAGE_SIZE 64
 
 typedef enum {
@@ -194,6 +194,22 @@ tis_status_t sparse_mla_attn(const tis_batch_t* batch, const void* q, tis_dtype_
                              int32_t D_v, float softmax_scale, void* out, tis_dtype_t out_dt,
                              float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* sparse_mla_attn_dense - the same attention as sparse_mla_attn, computed the dense-masked way
+ * ("Achieving Day-0 Readiness ... Million-Token Context", section 2.3: the prefill path treats
+ * sparse attention as a dense matrix product over the full key range with a row-wise sparse
+ * mask): every causal position 0..p_t of the token is read and multiplied, and the selection
+ * topk_idx[t] (K entries) only decides which positions keep their softmax weight.  Results
+ * equal sparse_mla_attn's up to rounding for selections without repeated positions (here a
+ * position listed twice counts once).  Arguments as sparse_mla_attn; matrix-core shapes only
+ * (H = 128, D_qk = 576, D_v = 512, bf16 q, bf16 or e4m3 cache), else TIS_ERR_UNSUPPORTED.
+ * ws: sparse_mla_attn_dense_workspace_size() bytes (split partials of one chunk of tokens). */
+tis_status_t sparse_mla_attn_dense(const tis_batch_t* batch, const void* q, tis_dtype_t q_dt,
+                                   const void* kv_pool, tis_dtype_t kv_dt,
+                                   const float* kv_scale, const int32_t* topk_idx, int32_t K,
+                                   int32_t H, int32_t D_qk, int32_t D_v, float softmax_scale,
+                                   void* out, tis_dtype_t out_dt, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* cache_append - write the rows of the batch's query tokens into their slots of one paged
  * cache, the step before the path ("Day-0 Support for Large Model Inference", Core Operator
  * Optimization item 1: the index stays on the device and is updated incrementally; "Day 0
@@ -278,6 +294,8 @@ size_t index_score_topk_workspace_size(const tis_batch_t* batch, int32_t H_I, in
                                        int32_t K);
 size_t sparse_mla_attn_workspace_size(const tis_batch_t* batch, int32_t K, int32_t H,
                                       int32_t D_qk, int32_t D_v, tis_dtype_t kv_dt);
+size_t sparse_mla_attn_dense_workspace_size(const tis_batch_t* batch, int32_t K, int32_t H,
+                                            int32_t D_qk, int32_t D_v, tis_dtype_t kv_dt);
 size_t topk_block_select_workspace_size(const tis_batch_t* batch, int32_t K_blocks);
 size_t index_score_topk_block_workspace_size(const tis_batch_t* batch, int32_t H_I, int32_t D_I,
                                              int32_t K_blocks);

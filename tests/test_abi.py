@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     lib = tis.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.tis_abi_version() == 5
+    assert lib.tis_abi_version() == 6
 
 
 LLVM = "/opt/rocm/llvm/bin"
@@ -300,3 +300,28 @@ def test_block_selection_argument_validation():
                                       L.TIS_QMODE_FP8, 4, D, None, D, D, need - 1,
                                       None) == L.TIS_ERR_INVALID
     assert "workspace" in last_error()
+
+
+def test_dense_attention_argument_validation():
+    """sparse_mla_attn_dense: the attention call's argument checks, matrix-core shapes only, and
+    a workspace for the split partials of long causal ranges."""
+    lib = tis.lib()
+    b = FakeBatch([9000], [0, 300])
+
+    def call(**kw):
+        a = dict(q=D, qdt=L.TIS_BF16, kv=D, kvdt=L.TIS_BF16, kvs=None, idx=D, K=64, H=128,
+                 Dqk=576, Dv=512, scale=0.1, out=D, odt=L.TIS_BF16, ws=None, wsb=0)
+        a.update(kw)
+        return lib.sparse_mla_attn_dense(b.ref, a["q"], a["qdt"], a["kv"], a["kvdt"], a["kvs"],
+                                         a["idx"], a["K"], a["H"], a["Dqk"], a["Dv"], a["scale"],
+                                         a["out"], a["odt"], None, a["ws"], a["wsb"], None)
+
+    assert call(Dv=600) == L.TIS_ERR_INVALID
+    assert call(qdt=L.TIS_F32, kvdt=L.TIS_F32, odt=L.TIS_F32, H=8, Dqk=80,
+                Dv=64) == L.TIS_ERR_UNSUPPORTED
+    need = lib.sparse_mla_attn_dense_workspace_size(b.ref, 64, 128, 576, 512, L.TIS_BF16)
+    assert need == 256 * 5 * 128 * 516 * 4          # chunks of 256 tokens, five 1,824-position splits
+    assert call() == L.TIS_ERR_INVALID and "workspace" in last_error()
+    short = FakeBatch([2000], [0, 300])
+    assert lib.sparse_mla_attn_dense_workspace_size(short.ref, 64, 128, 576, 512,
+                                                    L.TIS_BF16) == 0

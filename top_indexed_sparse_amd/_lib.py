@@ -20,6 +20,7 @@ PAGE_SIZE = 64
 EXPORTS = ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
            "sparse_mla_attn", "cache_append",
            "index_score_block", "topk_block_select", "index_score_topk_block",
+           "sparse_mla_attn_dense", "sparse_mla_attn_dense_workspace_size",
            "index_score_workspace_size", "topk_select_workspace_size",
            "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size",
            "topk_block_select_workspace_size", "index_score_topk_block_workspace_size",
@@ -70,6 +71,10 @@ def lib():
     L.sparse_mla_attn.argtypes = [_BP, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _F,
                                   _P, _I32, _P, _P, _SZ, _P]
     L.cache_append.argtypes = [_BP, _P, _I32, _I32, _P, _I32, _P, _P]
+    L.sparse_mla_attn_dense.argtypes = [_BP, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                        _I32, _F, _P, _I32, _P, _P, _SZ, _P]
+    L.sparse_mla_attn_dense_workspace_size.argtypes = [_BP, _I32, _I32, _I32, _I32, _I32]
+    L.sparse_mla_attn_dense_workspace_size.restype = _SZ
     L.index_score_block.argtypes = [_BP, _P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32, _P, _I64,
                                     _P]
     L.topk_block_select.argtypes = [_BP, _P, _I64, _I32, _P, _P, _P, _P, _SZ, _P]
@@ -77,7 +82,7 @@ def lib():
                                          _I32, _P, _P, _P, _P, _SZ, _P]
     for f in ("index_score", "topk_select", "index_score_topk", "index_score_topk_noalloc",
               "sparse_mla_attn", "cache_append", "index_score_block", "topk_block_select",
-              "index_score_topk_block"):
+              "index_score_topk_block", "sparse_mla_attn_dense"):
         getattr(L, f).restype = _I32
     L.index_score_workspace_size.argtypes = [_BP, _I32, _I32]
     L.topk_select_workspace_size.argtypes = [_BP, _I32]
@@ -89,7 +94,7 @@ def lib():
               "index_score_topk_workspace_size", "sparse_mla_attn_workspace_size",
               "topk_block_select_workspace_size", "index_score_topk_block_workspace_size"):
         getattr(L, f).restype = _SZ
-    if L.tis_abi_version() != 5:
+    if L.tis_abi_version() != 6:
         raise RuntimeError("libtopidx ABI version mismatch")
     _lib = L
     return L
@@ -310,3 +315,26 @@ def index_score_topk_block(batch: Batch, q_idx, w, k_pool, k_scale, K_blocks: in
                                         int(K_blocks), _ptr(block_idx), _ptr(block_val),
                                         _ptr(topk_idx), _ptr(ws), nb, _stream()))
     return block_idx
+
+
+def sparse_mla_attn_dense_workspace_size(batch: Batch, K: int, H: int, D_qk: int, D_v: int,
+                                         kv_dtype: int) -> int:
+    return int(lib().sparse_mla_attn_dense_workspace_size(batch.ref, int(K), H, D_qk, D_v,
+                                                          kv_dtype))
+
+
+def sparse_mla_attn_dense(batch: Batch, q, kv_pool, kv_scale, topk_idx, softmax_scale: float,
+                          out, lse=None, ws=None):
+    """sparse_mla_attn computed the dense-masked way (every causal row read and multiplied,
+    the selection as a mask)."""
+    H, D_qk = int(q.shape[1]), int(q.shape[2])
+    D_v = int(out.shape[2])
+    K = int(topk_idx.shape[1])
+    kvd = _dtype(kv_pool)
+    need = sparse_mla_attn_dense_workspace_size(batch, K, H, D_qk, D_v, kvd)
+    ws, nb = _ws(need, ws, q.device)
+    _check(lib().sparse_mla_attn_dense(batch.ref, _ptr(q), _dtype(q), _ptr(kv_pool), kvd,
+                                       _ptr(kv_scale), _ptr(topk_idx), K, H, D_qk, D_v,
+                                       float(softmax_scale), _ptr(out), _dtype(out), _ptr(lse),
+                                       _ptr(ws), nb, _stream()))
+    return out

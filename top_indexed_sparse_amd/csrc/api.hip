@@ -546,6 +546,75 @@ TIS_API tis_status_t index_score_topk_block(const tis_batch_t* batch, const void
   return TIS_OK;
 }
 
+// ============================================================================ dense-masked form
+namespace {
+
+constexpr size_t kDenseScratchBudget = size_t(1) << 30;
+
+// Token chunk and split count of the dense form: every chunk uses the same split count (that
+// of a full chunk), so the partials of one chunk fit the workspace.
+void dense_plan(const tis_batch_t* b, const HostInfo& hi, int* chunk, int* nsplit) {
+  int c = std::min(b->T, 256);
+  int ns = tis::attn_split_count(c, std::max(hi.max_n, 1));
+  const size_t per_tok = (size_t)ns * 128 * (512 + 4) * sizeof(float);
+  if (ns > 1) c = (int)std::max<size_t>(1, std::min<size_t>(c, kDenseScratchBudget / per_tok));
+  *chunk = c;
+  *nsplit = ns;
+}
+
+size_t dense_ws_bytes(const tis_batch_t* b, const HostInfo& hi) {
+  int c, ns;
+  dense_plan(b, hi, &c, &ns);
+  return ns > 1 ? (size_t)c * ns * 128 * (512 + 4) * sizeof(float) : 0;
+}
+
+}  // namespace
+
+TIS_API size_t sparse_mla_attn_dense_workspace_size(const tis_batch_t* batch, int32_t K,
+                                                    int32_t H, int32_t D_qk, int32_t D_v,
+                                                    tis_dtype_t kv_dt) {
+  (void)K; (void)H; (void)D_qk; (void)D_v; (void)kv_dt;
+  HostInfo hi;
+  if (check_batch(batch, &hi) != TIS_OK) return 0;
+  return dense_ws_bytes(batch, hi);
+}
+
+TIS_API tis_status_t sparse_mla_attn_dense(const tis_batch_t* batch, const void* q,
+                                           tis_dtype_t q_dt, const void* kv_pool,
+                                           tis_dtype_t kv_dt, const float* kv_scale,
+                                           const int32_t* topk_idx, int32_t K, int32_t H,
+                                           int32_t D_qk, int32_t D_v, float softmax_scale,
+                                           void* out, tis_dtype_t out_dt, float* lse, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  HostInfo hi;
+  tis_status_t st = check_batch(batch, &hi);
+  if (st != TIS_OK) return st;
+  AttnPath path;
+  st = check_attn_args(q, q_dt, kv_pool, kv_dt, kv_scale, topk_idx, K, H, D_qk, D_v,
+                       softmax_scale, out, out_dt, &path);
+  if (st != TIS_OK) return st;
+  if (path != AttnPath::MFMA)
+    return fail(TIS_ERR_UNSUPPORTED, "the dense-masked form runs on the matrix-core kernel only");
+  const size_t need = dense_ws_bytes(batch, hi);
+  if (ws_bytes < need || (need && (!ws || !aligned16(ws))))
+    return fail(TIS_ERR_INVALID, "workspace needs %zu bytes, 16-byte aligned", need);
+  int chunk, ns;
+  dense_plan(batch, hi, &chunk, &ns);
+  hipStream_t s = (hipStream_t)stream;
+  const tis::DevBatch d = dev_batch(batch);
+  float* part_o = ns > 1 ? (float*)ws : nullptr;
+  float* part_ml = ns > 1 ? part_o + (size_t)chunk * ns * 128 * 512 : nullptr;
+  for (int t0 = 0; t0 < batch->T; t0 += chunk) {
+    const int tc = std::min(chunk, batch->T - t0);
+    hipError_t e = tis::launch_mla_attn(d, t0, tc, kv_dt == TIS_E4M3, (const uint16_t*)q,
+                                        (const uint8_t*)kv_pool, kv_scale, topk_idx, K,
+                                        softmax_scale, ns, out, out_dt == TIS_F32, lse, part_o,
+                                        part_ml, s, std::max(hi.max_n, 1));
+    if (e != hipSuccess) return hip_fail(e, "sparse_mla_attn_dense launch");
+  }
+  return TIS_OK;
+}
+
 TIS_API tis_status_t cache_append(const tis_batch_t* batch, const void* rows,
                                   tis_dtype_t rows_dt, int32_t D, void* pool, tis_dtype_t pool_dt,
                                   void* pool_scale, void* stream) {

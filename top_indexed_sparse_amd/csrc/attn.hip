@@ -257,7 +257,13 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // logits and P relative to the split's largest scale; P is fp16 and the normaliser sums the same
 // rounded values.  Each wave writes its own heads' dims of O (or, with several splits, the
 // partials that mla_combine_kernel merges), transposed through LDS into whole lines.
-template <bool FP8, bool OUT_F32>
+// DENSE: the same attention computed the dense-masked way ("Achieving Day-0 Readiness ...
+// Million-Token Context", section 2.3: the prefill path multiplies over the full key range with
+// a row-wise sparse mask): split j covers the token's causal positions [j*kps, (j+1)*kps), every
+// one of them is gathered and multiplied, and the selection (the K entries of idx, built into an
+// LDS bitmask of the split's positions) only decides which rows' P is kept; the rest are masked
+// exactly as unselected rows (P = 0).  A position listed twice counts once.
+template <bool FP8, bool OUT_F32, bool DENSE = false>
 __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_count,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
     const float* __restrict__ kvscale, const int32_t* __restrict__ idx, int K, float c2,
@@ -294,9 +300,6 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   const int h0 = hg * kHW + hh * kHB;  // this wave's first head
 
   const int kbeg = split * kps;
-  const int nk = max(0, min(kps, K - kbeg));
-  const int nstage = (nk + kSR - 1) / kSR;
-  const int nrows = nstage * kSR;
 
   // ---- positions -> physical slots (and e4m3 row scales); masked keys read slot 0.  Each
   // thread translates up to kPer rows with its loads batched per step: the positions (they
@@ -304,13 +307,40 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // then the scales, so the chain costs three memory latencies however many rows there are.
   constexpr int kPer = kMaxKps / 256;
   int pos[kPer];
+  bool sel[kPer];  // (dense: the row is selected)
+  int nk;
+  TokLoc loc;
+  if constexpr (DENSE) {
+    uint32_t* bits = (uint32_t*)xs;  // (the logit exchange area is free until the loop)
+    if (tid < kMaxKps / 32) bits[tid] = 0u;
+    const LocLoads lw = locate_issue(bt);
+    loc = locate_finish(bt, t, lw);
+    nk = max(0, min(kps, loc.n - kbeg));  // the token's causal positions in this split
+    __syncthreads();
+    for (int i = tid; i < K; i += 256) {
+      const int e = idx[(int64_t)t * K + i] - kbeg;
+      if (e >= 0 && e < nk) atomicOr(&bits[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = tid + 256 * j;
-    pos[j] = i < nk ? idx[(int64_t)t * K + kbeg + i] : -1;
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + 256 * j;
+      pos[j] = i < nk ? kbeg + i : -1;
+      sel[j] = i < nk && ((bits[i >> 5] >> (i & 31)) & 1u) != 0u;
+    }
+  } else {
+    nk = max(0, min(kps, K - kbeg));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + 256 * j;
+      pos[j] = i < nk ? idx[(int64_t)t * K + kbeg + i] : -1;
+      sel[j] = true;
+    }
+    const LocLoads lw = locate_issue(bt);
+    loc = locate_finish(bt, t, lw);
   }
-  const LocLoads lw = locate_issue(bt);
-  const TokLoc loc = locate_finish(bt, t, lw);
+  const int nstage = (nk + kSR - 1) / kSR;
+  const int nrows = nstage * kSR;
   const int b = loc.b;
   const int Lb = loc.L;
   const int32_t* ptb = bt.page_table + (int64_t)b * bt.pt_stride;
@@ -355,7 +385,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       if (FP8) {  // scales in consumption order: entry 16*tile + m is row pi(m) of the tile
         const int r = i & (kWT - 1);
         scl[(i & ~(kWT - 1)) + ((r & 8) | ((r & 1) << 2) | ((r >> 1) & 3))] = scv[j];
-        smax = fmaxf(smax, scv[j]);
+        smax = fmaxf(smax, sel[j] ? scv[j] : 0.f);
       }
     }
   }
@@ -375,7 +405,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // tile q's mask (row r of a tile is consumed as m = (r & 8) | (r & 1) << 2 | (r >> 1) & 3)
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const uint64_t bj = __ballot(slot[j] >= 0);
+    const uint64_t bj = __ballot(slot[j] >= 0 && sel[j]);
     if (lane < 4) {
       const uint32_t nat = (uint32_t)(bj >> (16 * lane)) & 0xffffu;
       uint32_t m = 0u;
@@ -990,6 +1020,19 @@ __global__ __launch_bounds__(256, 1) void mla_attn_fp8_kernel(MLA_ATTN_ARGS) {
 __global__ __launch_bounds__(256, 1) void mla_attn_fp8_o32_kernel(MLA_ATTN_ARGS) {
   mla_attn_body<true, true>(MLA_ATTN_PASS);
 }
+// the dense-masked form (kps: the causal positions per split; K: the selection's width)
+__global__ __launch_bounds__(256, 1) void mla_attn_bf16_dense_kernel(MLA_ATTN_ARGS) {
+  mla_attn_body<false, false, true>(MLA_ATTN_PASS);
+}
+__global__ __launch_bounds__(256, 1) void mla_attn_bf16_o32_dense_kernel(MLA_ATTN_ARGS) {
+  mla_attn_body<false, true, true>(MLA_ATTN_PASS);
+}
+__global__ __launch_bounds__(256, 1) void mla_attn_fp8_dense_kernel(MLA_ATTN_ARGS) {
+  mla_attn_body<true, false, true>(MLA_ATTN_PASS);
+}
+__global__ __launch_bounds__(256, 1) void mla_attn_fp8_o32_dense_kernel(MLA_ATTN_ARGS) {
+  mla_attn_body<true, true, true>(MLA_ATTN_PASS);
+}
 
 // Merge split partials (m in log2 units; l = the normaliser of O, le = unrounded sum of P):
 // O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j,  lse = M + log2 sum_j 2^(m_j - M) le_j.
@@ -1121,12 +1164,17 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
                            const uint16_t* q, const uint8_t* kv, const float* kvscale,
                            const int32_t* idx, int K, float softmax_scale, int nsplit,
                            void* out, bool out_f32, float* lse, float* part_o, float* part_ml,
-                           hipStream_t st) {
-  const int kps = attn_keys_per_split(K, nsplit);
+                           hipStream_t st, int dense_n) {
+  // dense_n > 0: the dense-masked form over causal ranges of at most dense_n positions
+  const bool dense = dense_n > 0;
+  const int kps = attn_keys_per_split(dense ? dense_n : K, nsplit);
   const float c2 = softmax_scale * kLog2e;
   const size_t shm = attn_smem_bytes(fp8, kps);
-  auto* fn = fp8 ? (out_f32 ? mla_attn_fp8_o32_kernel : mla_attn_fp8_kernel)
-                 : (out_f32 ? mla_attn_bf16_o32_kernel : mla_attn_bf16_kernel);
+  auto* fn = dense ? (fp8 ? (out_f32 ? mla_attn_fp8_o32_dense_kernel : mla_attn_fp8_dense_kernel)
+                          : (out_f32 ? mla_attn_bf16_o32_dense_kernel
+                                     : mla_attn_bf16_dense_kernel))
+                   : (fp8 ? (out_f32 ? mla_attn_fp8_o32_kernel : mla_attn_fp8_kernel)
+                          : (out_f32 ? mla_attn_bf16_o32_kernel : mla_attn_bf16_kernel));
   // above 64 KB the kernel's dynamic LDS limit has to be raised before the launch (a
   // host-side attribute; set on every such launch so it holds on whichever device is current)
   if (shm > 65536) {

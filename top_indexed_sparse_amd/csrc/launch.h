@@ -31,7 +31,7 @@ hipError_t launch_mla_attn(const DevBatch& bt, int t_begin, int t_count, bool fp
                            const uint16_t* q, const uint8_t* kv, const float* kvscale,
                            const int32_t* idx, int K, float softmax_scale, int nsplit,
                            void* out, bool out_f32, float* lse, float* part_o, float* part_ml,
-                           hipStream_t st);
+                           hipStream_t st, int dense_n = 0);
 // topk_idx[t][64*i + r] = 64*block_idx[t][i] + r for causal positions of kept pages, else -1
 hipError_t launch_expand_blocks(const DevBatch& bt, int t_begin, int t_count,
                                 const int32_t* block_idx, int K_blocks, int32_t* topk_idx,
