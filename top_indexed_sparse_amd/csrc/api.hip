@@ -8,6 +8,7 @@
 #include <cmath>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "launch.h"
 #include "topidx.h"
@@ -134,23 +135,96 @@ tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* 
               "MXFP8) for (q, k, qmode)");
 }
 
+// The matrix-core scorer's work list ("Day 0 Support for New LLM Architectures", Key
+// Optimization 3: balance the causal work of long inputs; "Day-0 Support for Large Model
+// Inference", Core Operator Optimization 2: requests of different lengths share the device).
+// A launch covers a token range with a grid of (token group) x (key chunk) units sized by the
+// range's longest causal length; a unit past its tokens' range only looks its tokens up and
+// exits.  Batches that mix short and long requests therefore run as a few launches over runs of
+// consecutive requests, each sized by its own longest request: the cuts (at request boundaries)
+// minimise the units launched plus a per-launch cost, by dynamic programming over the cut points.
+struct Segment {
+  int t0, tc, max_n;
+};
+
+std::vector<Segment> plan_segments(const tis_batch_t* b, int t0, int tc, bool prefill_like) {
+  const int tok = prefill_like ? 4 : 1;         // tokens per unit
+  const int chunk = prefill_like ? 1024 : 4096;  // keys per unit
+  constexpr double kLaunchUnits = 3000.0;       // a launch's fixed cost, in units
+  // intervals between consecutive cut points lie within one request; each interval's longest
+  // causal length is that of its last token
+  std::vector<int> cut{t0};
+  std::vector<int> imax;
+  const int t1 = t0 + tc;
+  for (int r = 0; r < b->B; ++r) {
+    const int a = std::max(b->cu_q_host[r], t0), e = std::min(b->cu_q_host[r + 1], t1);
+    if (a >= e) continue;
+    if (a > cut.back()) {  // (tokens before this request in the range: none, cu_q is sorted)
+      cut.push_back(a);
+      imax.push_back(0);
+    }
+    const int n_last = b->seq_lens_host[r] - (b->cu_q_host[r + 1] - (e - 1)) + 1;
+    cut.push_back(e);
+    imax.push_back(n_last);
+  }
+  const int m = (int)cut.size() - 1;  // intervals
+  std::vector<Segment> segs;
+  if (m <= 0) return segs;
+  auto units = [&](int ntok, int maxn) {
+    return (double)((ntok + tok - 1) / tok) * (double)((maxn + chunk - 1) / chunk);
+  };
+  if (m == 1 || m > 256) {  // one launch (beyond 256 requests the plan is not worth its cost)
+    int mx = 0;
+    for (int v : imax) mx = std::max(mx, v);
+    segs.push_back({t0, tc, mx});
+    return segs;
+  }
+  std::vector<double> best(m + 1, 0.0);
+  std::vector<int> from(m + 1, 0);
+  for (int j = 1; j <= m; ++j) {
+    best[j] = 1e300;
+    int mx = 0;
+    for (int i = j - 1; i >= 0; --i) {
+      mx = std::max(mx, imax[i]);
+      const double c = best[i] + kLaunchUnits + units(cut[j] - cut[i], mx);
+      if (c < best[j]) {
+        best[j] = c;
+        from[j] = i;
+      }
+    }
+  }
+  for (int j = m; j > 0; j = from[j]) {
+    const int i = from[j];
+    int mx = 0;
+    for (int k = i; k < j; ++k) mx = std::max(mx, imax[k]);
+    segs.push_back({cut[i], cut[j] - cut[i], mx});
+  }
+  std::reverse(segs.begin(), segs.end());
+  return segs;
+}
+
 // block: one score per 64-key page (rows of ld entries) instead of one per key; the fp32
-// scorer has no block form (callers check)
+// scorer has no block form (callers check).  Rows of scores are those of tokens t0 .. t0+tc-1.
 tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath path, int t0,
                        int tc, const void* q_idx, const float* w, const void* k_pool,
                        const void* k_scale, int H_I, int D_I, float* scores, int64_t ld,
                        hipStream_t st, bool block = false) {
   const tis::DevBatch d = dev_batch(batch);
   hipError_t e;
-  if (path == IdxPath::F32)
+  if (path == IdxPath::F32) {
     e = tis::launch_index_score_f32(d, t0, tc, hi.max_n, (const float*)q_idx, w,
                                     (const float*)k_pool, H_I, D_I, scores, ld, st);
-  else
-    e = tis::launch_index_score_fp8(d, t0, tc, hi.max_n, hi.prefill_like,
+    return e == hipSuccess ? TIS_OK : hip_fail(e, "index_score launch");
+  }
+  for (const Segment& sg : plan_segments(batch, t0, tc, hi.prefill_like)) {
+    if (sg.max_n < 1) continue;
+    e = tis::launch_index_score_fp8(d, sg.t0, sg.tc, sg.max_n, hi.prefill_like,
                                     path == IdxPath::BF16 ? 1 : path == IdxPath::MX ? 2 : 0,
                                     block, (const uint16_t*)q_idx, w, (const uint8_t*)k_pool,
-                                    k_scale, scores, ld, st);
-  return e == hipSuccess ? TIS_OK : hip_fail(e, "index_score launch");
+                                    k_scale, scores + (int64_t)(sg.t0 - t0) * ld, ld, st);
+    if (e != hipSuccess) return hip_fail(e, "index_score launch");
+  }
+  return TIS_OK;
 }
 
 int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
