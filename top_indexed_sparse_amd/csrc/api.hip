@@ -140,9 +140,10 @@ tis_status_t check_index_args(const void* q_idx, tis_dtype_t q_dt, const float* 
 // Inference", Core Operator Optimization 2: requests of different lengths share the device).
 // A launch covers a token range with a grid of (token group) x (key chunk) units sized by the
 // range's longest causal length; a unit past its tokens' range only looks its tokens up and
-// exits.  Batches that mix short and long requests therefore run as a few launches over runs of
-// consecutive requests, each sized by its own longest request: the cuts (at request boundaries)
-// minimise the units launched plus a per-launch cost, by dynamic programming over the cut points.
+// exits.  Batches that mix short and long requests, and a long prefill's causal triangle,
+// therefore run as a few launches over runs of consecutive tokens, each sized by its own longest
+// causal length: the cuts (at request boundaries and every few thousand tokens within a
+// request) minimise the units launched plus a per-launch cost, by dynamic programming.
 struct Segment {
   int t0, tc, max_n;
 };
@@ -151,21 +152,25 @@ std::vector<Segment> plan_segments(const tis_batch_t* b, int t0, int tc, bool pr
   const int tok = prefill_like ? 4 : 1;         // tokens per unit
   const int chunk = prefill_like ? 1024 : 4096;  // keys per unit
   constexpr double kLaunchUnits = 3000.0;       // a launch's fixed cost, in units
+  if (tc < 1) return {};
   // intervals between consecutive cut points lie within one request; each interval's longest
   // causal length is that of its last token
+  // Within a request the causal length grows by one per token (a prefill's triangle), so a
+  // request's range is also cut every `step` tokens (a multiple of the group; enough to keep
+  // the plan at about 128 intervals besides the request boundaries).
   std::vector<int> cut{t0};
   std::vector<int> imax;
   const int t1 = t0 + tc;
+  const int step = std::max(2048, (tc / 128 + tok - 1) / tok * tok);
   for (int r = 0; r < b->B; ++r) {
     const int a = std::max(b->cu_q_host[r], t0), e = std::min(b->cu_q_host[r + 1], t1);
     if (a >= e) continue;
-    if (a > cut.back()) {  // (tokens before this request in the range: none, cu_q is sorted)
-      cut.push_back(a);
-      imax.push_back(0);
+    for (int c = a; c < e; c += step) {
+      const int ce = std::min(e, c + step);
+      const int n_last = b->seq_lens_host[r] - (b->cu_q_host[r + 1] - (ce - 1)) + 1;
+      cut.push_back(ce);
+      imax.push_back(n_last);
     }
-    const int n_last = b->seq_lens_host[r] - (b->cu_q_host[r + 1] - (e - 1)) + 1;
-    cut.push_back(e);
-    imax.push_back(n_last);
   }
   const int m = (int)cut.size() - 1;  // intervals
   std::vector<Segment> segs;
@@ -173,7 +178,7 @@ std::vector<Segment> plan_segments(const tis_batch_t* b, int t0, int tc, bool pr
   auto units = [&](int ntok, int maxn) {
     return (double)((ntok + tok - 1) / tok) * (double)((maxn + chunk - 1) / chunk);
   };
-  if (m == 1 || m > 256) {  // one launch (beyond 256 requests the plan is not worth its cost)
+  if (m == 1 || m > 512) {  // one launch (beyond 512 intervals the plan is not worth its cost)
     int mx = 0;
     for (int v : imax) mx = std::max(mx, v);
     segs.push_back({t0, tc, mx});
