@@ -152,7 +152,7 @@ constexpr int kKPre = 6, kVPre = 3;
 constexpr int kOStage = kDvW + 4;  // floats per head row when O is staged for the stores
 
 // Dynamic LDS: ring of three stages (two tiles each) | rows[kMaxKps] | masks[kMaxKps/16] |
-// scl[kMaxKps] (e4m3) | partial logits [2][4 waves][4 tiles][64 lanes] f32x4 | red/anyv.
+// scl[kMaxKps] (e4m3) | partial logits [2][4 waves][4 tiles][64 lanes] f32x4 | red/anyv/lastv.
 template <bool FP8>
 struct AttnSmem {
   static constexpr int rows = kRing * 2 * KvFmt<FP8>::kWBytes;
@@ -263,6 +263,17 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // one of them is gathered and multiplied, and the selection (the K entries of idx, built into an
 // LDS bitmask of the split's positions) only decides which rows' P is kept; the rest are masked
 // exactly as unselected rows (P = 0).  A position listed twice counts once.
+// Token order of a launch: v -> token, a bijection of [0, n): the first 16*S positions
+// (S = n / 16) are 16 segments of S, segment g taking the place of segment g/2 (g even) or
+// 15 - g/2 (g odd); the rest stay where they are.
+__device__ __forceinline__ int zigzag16(int v, int n) {
+  const int S = n >> 4;
+  if (S == 0 || v >= 16 * S) return v;
+  const int g = v / S, j = v - g * S;
+  const int seg = (g & 1) ? 15 - (g >> 1) : (g >> 1);
+  return seg * S + j;
+}
+
 template <bool FP8, bool OUT_F32, bool DENSE = false>
 __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_count,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -288,14 +299,18 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
 
   // workgroup -> (token, split, head group); the workgroups of one token sit on one XCD
   // (workgroups are dealt to the 8 XCDs round-robin), so its rows are fetched from HBM once
-  // and served to the other head group from that XCD's L2
+  // and served to the other head group from that XCD's L2.  Each XCD takes a contiguous range
+  // of virtual tokens, and the virtual tokens are the launch's tokens in zigzag order ("Day 0
+  // Support for New LLM Architectures", Key Optimization 3, applied to the XCDs): cut into 16
+  // segments, XCD x gets segments x and 15 - x, so that in a causal batch (work growing with
+  // the token's position) no XCD holds all of the longest tokens.
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7, slot8 = blockIdx.x >> 3;
   const int per = nblk >> 3, extra = nblk & 7;
   const int pidx = xcd * per + min(xcd, extra) + slot8;
   const int hg = pidx & 1;
   const int split = (pidx >> 1) % nsplit;
-  const int tl = (pidx >> 1) / nsplit;
+  const int tl = zigzag16((pidx >> 1) / nsplit, t_count);
   const int t = t_begin + tl;
   const int h0 = hg * kHW + hh * kHB;  // this wave's first head
 
@@ -393,12 +408,23 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
     for (int o = 32; o > 0; o >>= 1) smax = fmaxf(smax, __shfl_xor(smax, o));
     if (lane == 0) red[wave] = smax;
   }
-  {  // some selected row of the wave's rows (-1 if there is none): one ballot
+  int* lastv = anyv + 4;
+  {  // some selected row of the wave's rows (-1 if there is none): one ballot; and the last row
+     // that is read at all (the stages past it hold only padding and are skipped)
     int v = -1;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) v = max(v, slot[j]);
     const uint64_t bb = __ballot(v >= 0);
-    if (lane == 0) anyv[wave] = bb ? __builtin_amdgcn_readlane(v, __builtin_ctzll(bb)) : -1;
+    int last = -1;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint64_t bv = __ballot(slot[j] >= 0);
+      if (bv) last = 256 * j + 64 * wave + 63 - __builtin_clzll(bv);
+    }
+    if (lane == 0) {
+      anyv[wave] = bb ? __builtin_amdgcn_readlane(v, __builtin_ctzll(bb)) : -1;
+      lastv[wave] = last;
+    }
   }
   // per 16-row tile: bit m = row pi(m) selected (the order in which the keys are consumed),
   // from one ballot per row step: rows 256j + 64wave + l, four tiles, lane q < 4 writes
@@ -421,7 +447,9 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // whose P is zero: exactly nothing is added).  A split without any selected row skips
   // the loop, leaving O = 0 and l = 0.
   const int fill = __builtin_amdgcn_readfirstlane(max(max(anyv[0], anyv[1]), max(anyv[2], anyv[3])));
-  const int nst = fill >= 0 ? nstage : 0;
+  const int lastrow =
+      __builtin_amdgcn_readfirstlane(max(max(lastv[0], lastv[1]), max(lastv[2], lastv[3])));
+  const int nst = fill >= 0 ? min(nstage, lastrow / kSR + 1) : 0;
   const float inv_smax = smax > 0.f ? 1.f / smax : 0.f;
 
   // ---- gathers: wave w loads rows 8w .. 8w + 7 of each stage, i.e. rows 8(w & 1) .. of tile
