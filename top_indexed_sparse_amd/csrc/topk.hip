@@ -100,15 +100,13 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_
   mx = __builtin_amdgcn_readlane(wave_incl(lane < 16 ? sh[16 + lane] : 0u, 0u, fmax_), 15);
 }
 
-// LDS of the selection kernel: histogram, scan scratch, picks and the candidate list.
-constexpr int kCandMax = 8192;
-constexpr int kListMax = kCandMax / 2;  // candidate list: keys and positions
+// LDS of the streamed selection (rows longer than one chunk) and of the long-row final step:
+// two histograms, scan scratch and picks.
 struct SelSmem {
   uint32_t hist[2048];
   uint32_t hist2[2048];
   uint32_t sh[48];    // scan totals (0..15), row min/max (16..47)
   uint32_t pick[4];
-  uint32_t candk[kCandMax];
 };
 
 // Long-row selection state per row, words [mode, bin, candidates, keys above the bin]
@@ -120,13 +118,14 @@ constexpr int kLongSlices = 1024;   // slices per row at most
 // Radix select of the krem-th largest key among the keys produced by `each` (called with a
 // visitor), over r = key - base with digits of up to 11 bits from bit `hi` down.  Returns the
 // threshold key; krem is left as the number of keys equal to it that are taken.  The two
-// histograms alternate, the next one being cleared while the current one fills: three
-// barriers per digit.
+// 2048-bin histograms h0 and h1 alternate, the next one being cleared while the current one
+// fills: three barriers per digit.  sh: 16 words of scan scratch; pick: 2 words.
 template <typename Each>
 __device__ __forceinline__ uint32_t radix_select(uint32_t base, int hi, uint32_t& krem,
-                                                 SelSmem& S, Each each) {
+                                                 uint32_t* h0, uint32_t* h1, uint32_t* sh,
+                                                 uint32_t* pick, Each each) {
   const int tid = threadIdx.x;
-  uint32_t* hb[2] = {S.hist, S.hist2};
+  uint32_t* hb[2] = {h0, h1};
   int cur = 0;
   uint32_t prefix = 0u;
   hb[0][tid] = 0u;
@@ -147,73 +146,442 @@ __device__ __forceinline__ uint32_t radix_select(uint32_t base, int hi, uint32_t
     // bins in descending order: thread i owns bins 2047-2i and 2046-2i
     const uint32_t ch = h[2047 - 2 * tid], cl = h[2046 - 2 * tid];
     uint32_t tot;
-    const uint32_t above_h = block_excl_scan(ch + cl, S.sh, tot);
+    const uint32_t above_h = block_excl_scan(ch + cl, sh, tot);
     const uint32_t above_l = above_h + ch;
     if (ch && above_h < krem && krem <= above_h + ch) {
-      S.pick[0] = 2047 - 2 * tid;
-      S.pick[1] = above_h;
+      pick[0] = 2047 - 2 * tid;
+      pick[1] = above_h;
     }
     if (cl && above_l < krem && krem <= above_l + cl) {
-      S.pick[0] = 2046 - 2 * tid;
-      S.pick[1] = above_l;
+      pick[0] = 2046 - 2 * tid;
+      pick[1] = above_l;
     }
     __syncthreads();
-    prefix = (prefix << (hi - lo)) | S.pick[0];
-    krem -= S.pick[1];
+    prefix = (prefix << (hi - lo)) | pick[0];
+    krem -= pick[1];
     hi = lo;
     cur ^= 1;
   }
   return base + prefix;
 }
+template <typename Each>
+__device__ __forceinline__ uint32_t radix_select(uint32_t base, int hi, uint32_t& krem,
+                                                 SelSmem& S, Each each) {
+  return radix_select(base, hi, krem, S.hist, S.hist2, S.sh, S.pick, each);
+}
 
-// One 1024-thread workgroup per row; thread i owns NPT consecutive positions per chunk of
-// 1024*NPT (rows that fit one chunk keep their keys in registers, loaded before the token's
-// causal length is known and masked after).
-// Threshold search, rows held in registers: a sample (2 keys per thread, at a fixed stride)
-// is histogrammed over the row's key range; the bin where the sample count from the top
-// reaches 1.25x the expected share of K (plus 16) gives a lower bound T_lo.  The keys >= T_lo
-// (normally ~1.4 K of them) are histogrammed again over their own range, which puts the
-// k-th largest key in a bin of a few keys: those are ranked by one wave (or, for larger bins,
-// radix-selected).  When fewer than K keys reach T_lo, or the bin would overflow the list
-// (heavy ties, adversarial orders), the exact radix select runs over the whole row instead;
-// every path gives the same threshold.
+// Bin of the want-th largest count over 2048 bins, counted from the top (thread i owns bins
+// 2047-2i and 2046-2i).  The thread whose bins hold it writes [bin, count above it, its
+// count] to pick[0..2]; one barrier inside the scan, none after (the caller's follows).
+__device__ __forceinline__ void pick_bin(const uint32_t* h, uint32_t want, uint32_t* sh,
+                                         uint32_t* pick) {
+  const int tid = threadIdx.x;
+  const uint32_t ch = h[2047 - 2 * tid], cl = h[2046 - 2 * tid];
+  uint32_t tot;
+  const uint32_t above_h = block_excl_scan(ch + cl, sh, tot);
+  const uint32_t above_l = above_h + ch;
+  if (ch && above_h < want && want <= above_h + ch) {
+    pick[0] = 2047 - 2 * tid;
+    pick[1] = above_h;
+    pick[2] = ch;
+  }
+  if (cl && above_l < want && want <= above_l + cl) {
+    pick[0] = 2046 - 2 * tid;
+    pick[1] = above_l;
+    pick[2] = cl;
+  }
+}
+
+// ---------------------------------------------------------------- rows held on chip
+// A row of at most 1024*NPT entries stays on the CU.  Thread (wave w, lane l) keeps the
+// 16-byte pieces it loaded, piece i = scores of positions 64*NPT*w + 256*i + 4*l .. + 3
+// (coalesced loads, no transposition), and the row is also written to LDS in position
+// order.  Entries past the row are NaN (scores are never NaN), so no comparison selects them.
+//  1. Sample: two scores per thread, lane l taking the first score of pieces l mod (NPT/8)
+//     and l mod (NPT/8) + NPT/8 (positions at a stride of NPT/2 over the row), histogrammed
+//     over the sample's key range; the bin where the count from the top reaches 1.25x the
+//     expected share of K (+16) gives a lower bound tlo of the K-th largest key.
+//  2. One pass over the registers: each score is compared with tlo's value and the result
+//     shifted into a per-thread bit mask; the row maximum comes along.
+//  3. Each wave reserves room in an LDS list with one atomic and writes its candidates'
+//     positions (the set bits of the masks), in no particular order.
+//  4. The candidates' keys (read from the LDS row) are histogrammed over [tlo, max]; a scan
+//     finds the bin of the K-th largest.  Keys above the bin are taken.  A bin taken whole
+//     ends the search; a bin of at most 64 keys is ranked by one wave; a larger one is
+//     histogrammed again over its own range, down to single key values.  The result is the
+//     threshold key T and the number of keys equal to T that are taken.
+//  5. Taken positions are set in an LDS bitmap, the ties at T in a second one.  Thread i
+//     emits the set bits of word i at its offset from one scan of (taken, tie) counts, with
+//     ties in position order up to their quota: the output is in ascending position order.
+// When fewer than K, or more than the list holds, reach tlo (heavy ties, adversarial orders),
+// an exact radix select over the registers gives T, and the bitmaps come from the registers.
+constexpr int kResListMax = 3904;  // candidate positions of a row held on chip
+constexpr int kResRankMax = 64;    // keys of a bin ranked by one wave
+
 template <int NPT>
-__global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ only,
-    int32_t* __restrict__ out_idx,
-    float* __restrict__ out_val) {
-  extern __shared__ __attribute__((aligned(16))) char smraw[];
+struct ResLds {  // byte offsets in the dynamic LDS
+  static constexpr int CH = 1024 * NPT;
+  static constexpr size_t row = 0;                        // float[CH], position order
+  static constexpr size_t hA = row + 4 * (size_t)CH;      // u32[2048]: sample histogram, bitmaps
+  static constexpr size_t hB = hA + 8192;                 // u32[2048]: candidate histogram
+  static constexpr size_t list = hB + 8192;               // u32[kResListMax]: positions
+  static constexpr size_t rank = list + 4 * kResListMax;  // u32[2][kResRankMax]: (key, position)
+  static constexpr size_t sh = rank + 8 * kResRankMax;    // u32[48]: scan scratch, min/max
+  static constexpr size_t misc = sh + 192;                // u32[8]: picks, counters
+  static constexpr size_t bytes = misc + 32;
+};
+static_assert(ResLds<32>::bytes <= 160 * 1024, "a row held on chip fits the CU's LDS");
+
+template <int NPT>
+__device__ __forceinline__ void select_resident(const uint4 (&v)[NPT / 4], int n, int k,
+                                                char* smraw, int32_t* __restrict__ oi,
+                                                float* __restrict__ ov) {
+  using L = ResLds<NPT>;
+  constexpr int Q = NPT / 4, CH = L::CH, NW = CH / 32;  // pieces per thread, bitmap words
+  const int tid = threadIdx.x, lane = tid & 63;
+  float* rowf = (float*)(smraw + L::row);
+  uint32_t* hA = (uint32_t*)(smraw + L::hA);
+  uint32_t* hB = (uint32_t*)(smraw + L::hB);
+  uint32_t* list = (uint32_t*)(smraw + L::list);
+  uint32_t* rk = (uint32_t*)(smraw + L::rank);
+  uint32_t* sh = (uint32_t*)(smraw + L::sh);
+  uint32_t* pick = (uint32_t*)(smraw + L::misc);  // [bin, above, count, tie quota]
+  uint32_t* cnt = pick + 4;                       // [list length, max key, rank fill]
+  const int pl = (tid >> 6) * 64 * NPT + 4 * lane;  // position of piece 0's first score
+
+  float x[NPT];  // x[4i + e]: position pl + 256i + e
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    x[4 * i] = __uint_as_float(v[i].x);
+    x[4 * i + 1] = __uint_as_float(v[i].y);
+    x[4 * i + 2] = __uint_as_float(v[i].z);
+    x[4 * i + 3] = __uint_as_float(v[i].w);
+  }
+  if (!__all(pl - 4 * lane + 64 * NPT <= n)) {  // (the wave's span crosses the row's end)
+#pragma unroll
+    for (int j = 0; j < NPT; ++j)
+      if (pl + 256 * (j >> 2) + (j & 3) >= n) x[j] = __uint_as_float(0x7fc00000u);
+  }
+#pragma unroll
+  for (int i = 0; i < Q; ++i)
+    *(float4*)(rowf + pl + 256 * i) = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  hA[tid] = 0u;
+  hA[tid + 1024] = 0u;
+  hB[tid] = 0u;
+  hB[tid + 1024] = 0u;
+  if (tid < 8) pick[tid] = 0u;  // (picks and counters)
+
+  // ---- 1. sampled lower bound (the sample's min/max barrier also orders the clears above)
+  float sa, sb;
+  if constexpr (Q == 1) {
+    sa = x[0];
+    sb = x[2];
+  } else {
+    constexpr int H = Q / 2;
+    const int r = lane & (H - 1);
+    sa = x[0];
+    sb = x[4 * H];
+#pragma unroll
+    for (int i = 1; i < H; ++i)
+      if (r == i) {
+        sa = x[4 * i];
+        sb = x[4 * (i + H)];
+      }
+  }
+  const uint32_t ka = sa == sa ? order_key(sa) : 0u, kb = sb == sb ? order_key(sb) : 0u;
+  uint32_t smin1 = min(ka - 1u, kb - 1u), smax = max(ka, kb);  // (invalid key 0 -> ~0u)
+  block_minmax(smin1, smax, sh + 16);
+  const uint32_t smin = smin1 + 1u;
+  const uint32_t sspan = smax - smin;
+  const int shift = max(0, (sspan ? 32 - __clz(sspan) : 0) - 11);
+  if (ka) atomicAdd(&hA[(ka - smin) >> shift], 1u);
+  if (kb) atomicAdd(&hA[(kb - smin) >> shift], 1u);
+  __syncthreads();
+  {
+    const uint32_t ch = hA[2047 - 2 * tid], cl = hA[2046 - 2 * tid];
+    uint32_t tot;  // valid samples
+    const uint32_t above_h = block_excl_scan(ch + cl, sh, tot);
+    const uint32_t want =
+        min(tot, (uint32_t)(((uint64_t)k * tot * 5u) / (4ull * (uint64_t)n)) + 16u);
+    const uint32_t above_l = above_h + ch;
+    if (ch && above_h < want && want <= above_h + ch) pick[2] = 2047 - 2 * tid;
+    if (cl && above_l < want && want <= above_l + cl) pick[2] = 2046 - 2 * tid;
+    __syncthreads();
+  }
+  const uint32_t tlo = smin + (pick[2] << shift);
+
+  // ---- 2. candidate masks (bit NPT-1-j: score j reaches tlo) and the row maximum
+  const float tf = key_value(tlo);  // (x >= tf exactly when order_key(x) >= tlo)
+  uint32_t m = 0u;
+  float rmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    // m = 2m + (x >= tf): the compare's lane mask is the carry-in of one add (with the two
+    // wait states a carry read needs after the compare writes it)
+    asm("v_cmp_le_f32_e32 vcc, %2, %1\n\ts_nop 1\n\tv_addc_co_u32_e32 %0, vcc, %3, %3, vcc"
+        : "=v"(m) : "v"(x[j]), "s"(tf), "v"(m) : "vcc");
+    rmax = fmaxf(rmax, x[j]);  // (NaN entries are skipped)
+  }
+  // ---- 3. the wave's candidates into the list
+  {
+    const uint32_t c = __popc(m);
+    const uint32_t inc = wave_incl_scan(c);
+    uint32_t base = 0u;
+    if (lane == 63) base = atomicAdd(&cnt[0], inc);
+    uint32_t o = __builtin_amdgcn_readlane(base, 63) + inc - c;
+    for (uint32_t mm = m; mm; mm &= mm - 1u, ++o) {
+      const int j = NPT - 1 - __builtin_ctz(mm);
+      if (o < (uint32_t)kResListMax) list[o] = (uint32_t)(pl + 256 * (j >> 2) + (j & 3));
+    }
+    auto fmax_ = [](uint32_t a, uint32_t b) { return max(a, b); };
+    const uint32_t wm = wave_incl(order_key(rmax), 0u, fmax_);
+    if (lane == 63) atomicMax(&cnt[1], wm);
+  }
+  __syncthreads();
+  const uint32_t C = cnt[0];
+  uint32_t* taken;
+  uint32_t* ties;
+  uint32_t quota;  // keys equal to the threshold that are taken (first in position order)
+
+  if (C >= (uint32_t)k && C <= (uint32_t)kResListMax) {
+    // ---- 4. histogram of the candidates over [tlo, max]
+    const uint32_t kmax = cnt[1];
+    const uint32_t cspan = kmax - tlo;
+    const int shift2 = max(0, (cspan ? 32 - __clz(cspan) : 0) - 11);
+    constexpr int E = (kResListMax + 1023) / 1024;
+    uint32_t lk[E], lp[E];  // entry tid + 1024e: key (0 past the list) and position
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t i = (uint32_t)tid + 1024u * e;
+      lp[e] = i < C ? list[i] : 0u;
+      lk[e] = i < C ? order_key(rowf[lp[e]]) : 0u;
+      if (i < C) atomicAdd(&hB[(lk[e] - tlo) >> shift2], 1u);
+    }
+    hA[tid] = 0u;  // (the bitmaps; the sample histogram was last read before tlo's barrier)
+    hA[tid + 1024] = 0u;
+    __syncthreads();
+    pick_bin(hB, (uint32_t)k, sh, pick);
+    __syncthreads();
+    uint32_t lo = tlo + (pick[0] << shift2);  // the bin: keys lo .. lo + 2^s - 1
+    int s = shift2;
+    uint32_t cb = pick[2];
+    uint32_t krem = (uint32_t)k - pick[1];    // keys of the bin that are taken
+    taken = hA;
+    ties = hA + NW;
+    auto mark = [&](uint32_t* w, uint32_t p) { atomicOr(&w[p >> 5], 1u << (p & 31)); };
+    auto top_of = [](uint32_t l, int sb) {
+      return (uint32_t)min<uint64_t>((uint64_t)l + ((1ull << sb) - 1ull), 0xffffffffull);
+    };
+    if (cb != krem && cb <= (uint32_t)kResRankMax && s > 0) {
+      // a few keys in the bin: keys above it are taken now, the bin's keys are collected
+      // and ranked by one wave, which takes them or marks the ties
+      const uint32_t hi = top_of(lo, s);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (lk[e] > hi) mark(taken, lp[e]);
+        else if (lk[e] >= lo) {
+          const uint32_t sl = atomicAdd(&cnt[2], 1u);  // (< cb <= kResRankMax)
+          rk[2 * sl] = lk[e];
+          rk[2 * sl + 1] = lp[e];
+        }
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const bool has = (uint32_t)tid < cb;
+        const uint32_t mine = has ? rk[2 * tid] : 0u, mp = has ? rk[2 * tid + 1] : 0u;
+        uint32_t gt = 0u, ge = 0u;
+        for (uint32_t j = 0; j < cb; ++j) {  // (lane j holds key j)
+          const uint32_t ot = __builtin_amdgcn_readlane(mine, j);
+          gt += ot > mine ? 1u : 0u;
+          ge += ot >= mine ? 1u : 0u;
+        }
+        if (has && ge <= krem) mark(taken, mp);  // (every key >= this one fits)
+        else if (has && gt < krem) {             // this key is the threshold: a tie
+          mark(ties, mp);
+          pick[3] = krem - gt;                   // (the same value from every tie)
+        }
+      }
+      __syncthreads();
+      quota = pick[3];
+    } else {
+      // threshold (T, quota): the bin taken whole, a bin of one key value, or narrower bins
+      // (histograms alternating between hB and hA) down to a rank by one wave
+      uint32_t T;
+      uint32_t* hc = hA;
+      uint32_t* hn = hB;
+      bool used_a = false;
+      while (true) {
+        if (cb == krem) {  // the whole bin: every key >= lo, no ties
+          T = lo - 1u;
+          quota = 0u;
+          break;
+        }
+        if (s == 0) {  // every key of the bin equals lo
+          T = lo;
+          quota = krem;
+          break;
+        }
+        const uint32_t hi = top_of(lo, s);
+        if (cb <= (uint32_t)kResRankMax) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (lk[e] >= lo && lk[e] <= hi) {
+              const uint32_t sl = atomicAdd(&cnt[2], 1u);
+              rk[2 * sl] = lk[e];
+            }
+          __syncthreads();
+          if (tid < 64) {
+            const bool has = (uint32_t)tid < cb;
+            const uint32_t mine = has ? rk[2 * tid] : 0u;
+            uint32_t gt = 0u, ge = 0u;
+            for (uint32_t j = 0; j < cb; ++j) {
+              const uint32_t ot = __builtin_amdgcn_readlane(mine, j);
+              gt += ot > mine ? 1u : 0u;
+              ge += ot >= mine ? 1u : 0u;
+            }
+            if (has && gt < krem && krem <= ge) {  // the krem-th largest of the bin
+              pick[0] = mine;
+              pick[1] = krem - gt;
+            }
+          }
+          __syncthreads();
+          T = pick[0];
+          quota = pick[1];
+          break;
+        }
+        const int s2 = max(0, s - 11);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (lk[e] >= lo && lk[e] <= hi) atomicAdd(&hc[(lk[e] - lo) >> s2], 1u);
+        hn[tid] = 0u;
+        hn[tid + 1024] = 0u;
+        used_a = true;
+        __syncthreads();
+        pick_bin(hc, krem, sh, pick);
+        __syncthreads();
+        lo += pick[0] << s2;
+        krem -= pick[1];
+        cb = pick[2];
+        s = s2;
+        uint32_t* t0 = hc;
+        hc = hn;
+        hn = t0;
+      }
+      if (used_a) {  // (the bitmaps held a histogram)
+        __syncthreads();
+        hA[tid] = 0u;
+        hA[tid + 1024] = 0u;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (lk[e] > T) mark(taken, lp[e]);
+        else if (lk[e] == T && lk[e] != 0u) mark(ties, lp[e]);
+      }
+      __syncthreads();
+    }
+  } else {
+    // ---- exact radix select over the registers (keys; 0 for entries past the row)
+    uint32_t kk[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) kk[j] = x[j] == x[j] ? order_key(x[j]) : 0u;
+    uint32_t kmin = ~0u, kmx = 0u;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      kmin = min(kmin, kk[j] - 1u);
+      kmx = max(kmx, kk[j]);
+    }
+    block_minmax(kmin, kmx, sh + 16);
+    kmin += 1u;
+    taken = list;  // (the list is not used on this path)
+    ties = list + NW;
+    for (int i = tid; i < 2 * NW; i += 1024) list[i] = 0u;
+    const uint32_t span = kmx - kmin;
+    quota = (uint32_t)k;
+    const uint32_t T = radix_select(kmin, span ? 32 - __clz(span) : 0, quota, hA, hB, sh, pick,
+                                    [&](auto&& f) {
+#pragma unroll
+                                      for (int j = 0; j < NPT; ++j)
+                                        if (kk[j] != 0u) f(kk[j]);
+                                    });
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      uint32_t g = 0u, q = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kx = kk[4 * i + e];
+        g |= (kx > T ? 1u : 0u) << e;
+        q |= (kx == T && kx != 0u ? 1u : 0u) << e;
+      }
+      const int p = pl + 256 * i;  // (the piece's four positions share a bitmap word)
+      if (g) atomicOr(&taken[p >> 5], g << (p & 31));
+      if (q) atomicOr(&ties[p >> 5], q << (p & 31));
+    }
+    __syncthreads();
+  }
+
+  // ---- 5. emission: thread i owns bitmap word i (positions 32i .. 32i + 31)
+  uint32_t tw = 0u, ew = 0u;
+  if (tid < NW) {
+    tw = taken[tid];
+    ew = ties[tid];
+  }
+  uint32_t tot;
+  const uint32_t before = block_excl_scan(__popc(tw) | ((uint32_t)__popc(ew) << 16), sh, tot);
+  const uint32_t eb = before >> 16;  // ties before this thread's
+  uint32_t o = (before & 0xffffu) + min(eb, quota);
+  for (uint32_t a = quota > eb ? quota - eb : 0u; a && ew; --a) {
+    tw |= ew & (0u - ew);  // the lowest remaining tie
+    ew &= ew - 1u;
+  }
+  while (tw) {  // four positions at a time, their values read together
+    int pp[4];
+    float vv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pp[e] = tw ? 32 * tid + __builtin_ctz(tw) : -1;
+      tw &= tw - 1u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = pp[e] >= 0 ? rowf[pp[e]] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (pp[e] >= 0 && o < (uint32_t)k) {  // (exactly k are set; the bound keeps every
+        oi[o] = pp[e];                      //  store in the row)
+        if (ov) ov[o] = vv[e] + 0.f;        // (+ 0: -0.0 comes out as +0.0, as from a key)
+        ++o;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- rows longer than a chunk
+// (1024*32 positions): each pass streams the row through registers, thread i holding 32
+// consecutive positions of each chunk.  The key range is measured, then a radix select
+// over the whole row gives T; the compaction keeps keys > T and the first krem keys == T
+// chunk by chunk, one block scan per chunk.
+__device__ __forceinline__ void select_streamed(const float* __restrict__ row, int n, int k,
+                                                int K, char* smraw, int32_t* __restrict__ oi,
+                                                float* __restrict__ ov) {
+  constexpr int NPT = 32, CH = 1024 * NPT;
   SelSmem& S = *(SelSmem*)smraw;
   const int tid = threadIdx.x;
-  const int tl = blockIdx.x;
-  const int t = t_begin + tl;
-  const float* row = scores + (int64_t)tl * ld;
-  // (after the long-row selection: only the rows it left over)
-  if (only && only[4 * tl] != kLongOver) return;
-  constexpr int CH = 1024 * NPT;
-  uint32_t key[NPT];  // the raw score bits until to_keys, then the order keys
-
-  // scores of chunk c0 at positions < lim (positions past it read nothing)
-  auto load_raw = [&](int c0, int lim) {
+  uint32_t key[NPT];
+  auto load_chunk = [&](int c0) {
     const int p0 = c0 + tid * NPT;
 #pragma unroll
     for (int j = 0; j < NPT; j += 4) {
       const int p = p0 + j;
-      if (p + 3 < lim) {
+      if (p + 3 < n) {
         const uint4 f = *(const uint4*)(row + p);
         key[j] = f.x; key[j + 1] = f.y; key[j + 2] = f.z; key[j + 3] = f.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[j + e] = (p + e < lim) ? __float_as_uint(row[p + e]) : 0u;
+        for (int e = 0; e < 4; ++e) key[j + e] = (p + e < n) ? __float_as_uint(row[p + e]) : 0u;
       }
     }
-  };
-  // Positions past the row hold key 0, which no score maps to (the smallest key, of -inf,
-  // is 0x007fffff): validity is key != 0, and every threshold below is above 0.
-  int n = 0;
-  auto to_keys = [&](int c0) {
-    const int p0 = c0 + tid * NPT;
-    if (__all(p0 + NPT <= n)) {  // (the wave is inside the row: no position test)
+    // positions past the row hold key 0, which no score maps to (the smallest key, of -inf,
+    // is 0x007fffff)
+    if (__all(p0 + NPT <= n)) {
 #pragma unroll
       for (int j = 0; j < NPT; ++j) key[j] = order_key(__uint_as_float(key[j]));
     } else {
@@ -222,266 +590,26 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
         key[j] = p0 + j < n ? order_key(__uint_as_float(key[j])) : 0u;
     }
   };
-  auto load_chunk = [&](int c0) {
-    load_raw(c0, n);
-    to_keys(c0);
-  };
-  // The first chunk arrives through LDS: each wave reads its 256*NPT bytes with coalesced
-  // 1 KB loads (16-byte piece P = 64i + lane of the wave's span belongs to thread P / Q of the
-  // wave, Q = NPT/4 pieces per thread), stores them swizzled (piece q of thread u at slot
-  // u*Q + (q ^ ((u >> sw) & (Q-1))), which keeps both the stores and the reads below on 16
-  // distinct 4-bank groups per 16 lanes) and reads its own Q pieces back.  Read directly, each
-  // load instruction would touch 64 lines for 16 bytes of each.  The buffer overlaps S.
-  auto load_first = [&](int lim) {
-    if constexpr (NPT == 4) {
-      load_raw(0, lim);  // (one piece per thread: already coalesced)
-    } else {
-      constexpr int Q = NPT / 4;
-      constexpr int sw = Q == 8 ? 1 : Q == 4 ? 2 : 3;  // log2(16 / Q)
-      const int lane = tid & 63;
-      const int wb = (tid >> 6) * 64 * NPT;  // the wave's first position
-      uint4 v[Q];
-#pragma unroll
-      for (int i = 0; i < Q; ++i) {
-        const int p = wb + 256 * i + 4 * lane;  // (lim and p are multiples of 4)
-        v[i] = *(const uint4*)(row + min(p, lim - 4));
-        if (p >= lim) v[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      char* wbuf = smraw + (tid >> 6) * 64 * NPT * 4;
-#pragma unroll
-      for (int i = 0; i < Q; ++i) {
-        const int u = (64 * i + lane) / Q, q = lane % Q;
-        *(uint4*)(wbuf + 16 * (u * Q + (q ^ ((u >> sw) & (Q - 1))))) = v[i];
-      }
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const uint4 x = *(const uint4*)(wbuf + 16 * (lane * Q + (q ^ ((lane >> sw) & (Q - 1)))));
-        key[4 * q] = x.x; key[4 * q + 1] = x.y; key[4 * q + 2] = x.z; key[4 * q + 3] = x.w;
-      }
-    }
-  };
-
-  // the first chunk goes out before the token lookup (up to the row stride, which bounds
-  // every causal length), so the two memory latencies overlap
-  const LocLoads lw = locate_issue(bt);
-  load_first((int)min<int64_t>(ld, (int64_t)CH));
-  n = locate_finish(bt, t, lw).n;
-  n = (n + (1 << bt.row_shift) - 1) >> bt.row_shift;  // (block rows: pages, not positions)
-  int32_t* oi = out_idx + (int64_t)t * K;
-  float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
-
-  if (n <= K) {  // everything is selected
-    for (int i = tid; i < K; i += 1024) {
-      oi[i] = i < n ? i : -1;
-      if (ov) ov[i] = i < n ? row[i] : 0.f;
-    }
-    return;
-  }
-  const int k = K;
-  const bool cached = n <= CH;
-  // visits every valid key of the row (from registers when cached)
   auto each_row = [&](auto&& f) {
     for (int c0 = 0; c0 < n; c0 += CH) {
-      if (!cached) load_chunk(c0);
+      load_chunk(c0);
 #pragma unroll
       for (int j = 0; j < NPT; ++j)
         if (key[j] != 0u) f(key[j]);
     }
   };
-
-  __syncthreads();  // (every wave has read its first chunk back before S is written)
-  to_keys(0);
-  S.hist[tid] = 0u;
-  S.hist[tid + 1024] = 0u;
-  S.hist2[tid] = 0u;
-  S.hist2[tid + 1024] = 0u;
-  if (tid == 0) S.pick[3] = 0u;
-
+  uint32_t kmin = ~0u, kmax = 0u;
+  each_row([&](uint32_t kk) { kmin = min(kmin, kk); kmax = max(kmax, kk); });
+  block_minmax(kmin, kmax, S.sh + 16);
+  const uint32_t span = kmax - kmin;
   uint32_t krem = (uint32_t)k;
-  uint32_t T = 0u;
-  if (cached) {
-    // ---- sampled lower bound of the threshold, over the key range of the sample (keys above
-    // it are all candidates anyway); its barrier also orders the clears above
-    uint32_t smin1 = min(key[0] - 1u, key[NPT / 2] - 1u);  // (invalid key 0 -> 0xffffffff)
-    uint32_t smax = max(key[0], key[NPT / 2]);
-    block_minmax(smin1, smax, S.sh + 16);
-    const uint32_t smin = smin1 + 1u;
-    const uint32_t sspan = smax - smin;
-    const int shift = max(0, (sspan ? 32 - __clz(sspan) : 0) - 11);
-    if (key[0] != 0u) atomicAdd(&S.hist[(key[0] - smin) >> shift], 1u);
-    if (key[NPT / 2] != 0u) atomicAdd(&S.hist[(key[NPT / 2] - smin) >> shift], 1u);
-    __syncthreads();
-    const uint32_t nsamp = (uint32_t)((n + NPT - 1) / NPT + (n + NPT / 2 - 1) / NPT);
-    const uint32_t want = min(nsamp, (uint32_t)(((uint64_t)k * nsamp * 5) / (4ull * n)) + 16u);
-    {
-      const uint32_t ch = S.hist[2047 - 2 * tid], cl = S.hist[2046 - 2 * tid];
-      uint32_t tot;
-      const uint32_t above_h = block_excl_scan(ch + cl, S.sh, tot);
-      const uint32_t above_l = above_h + ch;
-      if (ch && above_h < want && want <= above_h + ch) S.pick[2] = 2047 - 2 * tid;
-      if (cl && above_l < want && want <= above_l + cl) S.pick[2] = 2046 - 2 * tid;
-      __syncthreads();
-    }
-    const uint32_t tlo = smin + (S.pick[2] << shift);
-    // ---- list the keys >= tlo with their positions, in position order (~1.4 K of them)
-    uint32_t c = 0u, kmax = 0u;
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-      c += key[j] >= tlo ? 1u : 0u;
-      kmax = max(kmax, key[j]);
-    }
-    uint32_t C;
-    uint32_t o = block_excl_scan_max(c, kmax, S.sh, C);
-    if (C >= (uint32_t)k && C <= (uint32_t)kListMax) {
-      uint32_t* lk = S.candk;              // keys
-      uint32_t* lp = S.candk + kListMax;   // positions
-      {
-        const uint32_t p0 = (uint32_t)(tid * NPT);
-#pragma unroll
-        for (int j = 0; j < NPT; ++j)
-          if (key[j] >= tlo) {
-            lk[o] = key[j];
-            lp[o] = p0 + j;
-            ++o;
-          }
-      }
-      __syncthreads();
-      // ---- histogram of the list over [tlo, kmax]: the k-th largest lies in one bin
-      const uint32_t cspan = kmax - tlo;
-      const int shift2 = max(0, (cspan ? 32 - __clz(cspan) : 0) - 11);
-      for (uint32_t i = tid; i < C; i += 1024) atomicAdd(&S.hist2[(lk[i] - tlo) >> shift2], 1u);
-      __syncthreads();
-      {
-        const uint32_t ch = S.hist2[2047 - 2 * tid], cl = S.hist2[2046 - 2 * tid];
-        uint32_t tot;
-        const uint32_t above_h = block_excl_scan(ch + cl, S.sh, tot);
-        const uint32_t above_l = above_h + ch;
-        if (ch && above_h < (uint32_t)k && (uint32_t)k <= above_h + ch) {
-          S.pick[0] = 2047 - 2 * tid;
-          S.pick[1] = above_h;
-        }
-        if (cl && above_l < (uint32_t)k && (uint32_t)k <= above_l + cl) {
-          S.pick[0] = 2046 - 2 * tid;
-          S.pick[1] = above_l;
-        }
-        __syncthreads();
-      }
-      const uint32_t b2 = S.pick[0];
-      const uint32_t tb = tlo + (b2 << shift2);  // the bin holds keys tb .. tb + 2^shift2 - 1
-      const uint32_t cb = S.hist2[b2];
-      krem = (uint32_t)k - S.pick[1];            // keys of the bin that are taken
-      if (cb == krem) {  // the whole bin: every key >= tb, none equal to the threshold
-        T = tb - 1u;
-        krem = 0u;
-      } else if (cb <= 64u) {
-        // one wave ranks the bin: the key with (# greater) < krem <= (# greater or equal)
-        const uint32_t bhi =
-            (uint32_t)min<uint64_t>((uint64_t)tb + ((1u << shift2) - 1u), 0xffffffffull);
-        uint32_t* bl = S.hist;  // (free since the sample)
-        for (uint32_t i = tid; i < C; i += 1024)
-          if (lk[i] >= tb && lk[i] <= bhi) bl[atomicAdd(&S.pick[3], 1u)] = lk[i];
-        __syncthreads();
-        if (tid < 64) {
-          const uint32_t mine = tid < (int)cb ? bl[tid] : 0u;
-          uint32_t gt = 0u, ge = 0u;
-          for (uint32_t j = 0; j < cb; ++j) {
-            const uint32_t ot = bl[j];
-            gt += ot > mine ? 1u : 0u;
-            ge += ot >= mine ? 1u : 0u;
-          }
-          const uint64_t hit = __ballot(tid < (int)cb && gt < krem && krem <= ge);
-          const int src = (int)__builtin_ctzll(hit);  // (never empty: ranks cover 1..cb)
-          if (tid == 0) {
-            S.pick[0] = __builtin_amdgcn_readlane(mine, src);
-            S.pick[1] = krem - __builtin_amdgcn_readlane(gt, src);
-          }
-        }
-        __syncthreads();
-        T = S.pick[0];
-        krem = S.pick[1];
-      } else {
-        // a larger bin: radix select within it (list keys outside the bin fall outside the
-        // digit prefix and are not counted)
-        T = radix_select(tb, shift2, krem, S, [&](auto&& f) {
-          for (uint32_t i = tid; i < C; i += 1024) f(lk[i]);
-        });
-      }
-      // ---- compaction over the list (position order): an entry is taken if its key is > T,
-      // or == T with fewer than krem earlier entries == T.  Thread i owns entries E*i ..
-      const uint32_t E = (C + 1023u) / 1024u;
-      uint32_t cgt = 0u, ceq = 0u;
-      for (uint32_t e = 0; e < E; ++e) {
-        const uint32_t i = (uint32_t)tid * E + e;
-        if (i < C) {
-          cgt += lk[i] > T ? 1u : 0u;
-          ceq += lk[i] == T ? 1u : 0u;
-        }
-      }
-      uint32_t tot;
-      const uint32_t before = block_excl_scan(cgt | (ceq << 16), S.sh, tot);
-      uint32_t eqb = before >> 16;
-      uint32_t oo = (before & 0xffffu) + min(eqb, krem);
-      for (uint32_t e = 0; e < E; ++e) {
-        const uint32_t i = (uint32_t)tid * E + e;
-        if (i < C) {
-          const uint32_t kk = lk[i];
-          const bool eq = kk == T;
-          if (kk > T || (eq && eqb < krem)) {
-            oi[oo] = (int32_t)lp[i];
-            if (ov) ov[oo] = key_value(kk);
-            ++oo;
-          }
-          eqb += eq ? 1u : 0u;
-        }
-      }
-      return;
-    }
-  }
-  {  // whole-row radix select (streamed rows, or a short list that failed)
-    uint32_t kmin = ~0u, kmax = 0u;
-    each_row([&](uint32_t kk) { kmin = min(kmin, kk); kmax = max(kmax, kk); });
-    __syncthreads();  // (the list path may still be reading sh)
-    block_minmax(kmin, kmax, S.sh + 16);
-    const uint32_t span = kmax - kmin;
-    krem = (uint32_t)k;
-    T = radix_select(kmin, span ? 32 - __clz(span) : 0, krem, S, each_row);
-  }
-  // T is the threshold key; krem elements equal to T are taken (in position order)
-
-  // ---- order-preserving compaction: one scan of the per-thread counts of keys > T (low 16
-  // bits) and == T (high 16 bits; both totals stay below 2^16 per chunk).  Rows held in
-  // registers stage the k positions and keys in LDS and write them out coalesced.
-  if (cached && k <= kCandMax) {
-    uint32_t cgt = 0u, ceq = 0u;
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-      cgt += key[j] > T ? 1u : 0u;
-      ceq += key[j] == T ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t before = block_excl_scan(cgt | (ceq << 16), S.sh, tot);
-    uint32_t e = before >> 16;  // ties before this thread
-    uint32_t o = (before & 0xffffu) + min(e, krem);
-    uint32_t sel = 0u;  // bit j: position p0 + j is taken
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-      const bool eq = key[j] == T;
-      sel |= (key[j] > T || (eq && e < krem)) ? (1u << j) : 0u;
-      e += eq ? 1u : 0u;
-    }
-    const uint32_t p0 = (uint32_t)(tid * NPT);
-    for (; sel; sel &= sel - 1u) S.candk[o++] = p0 + (uint32_t)__builtin_ctz(sel);
-    __syncthreads();
-    for (int i = tid; i < k; i += 1024) {
-      const int32_t p = (int32_t)S.candk[i];
-      oi[i] = p;
-      if (ov) ov[i] = row[p] + 0.f;  // (+ 0: -0.0 comes out as +0.0, as from a key)
-    }
-    return;
-  }
+  const uint32_t T = radix_select(kmin, span ? 32 - __clz(span) : 0, krem, S, each_row);
+  // T is the threshold key; krem elements equal to T are taken (in position order).
+  // Order-preserving compaction: one scan of the per-thread counts of keys > T (low 16 bits)
+  // and == T (high 16 bits; both totals stay below 2^16 per chunk).
   uint32_t run_gt = 0u, run_eq = 0u;
   for (int c0 = 0; c0 < n; c0 += CH) {
-    if (!cached) load_chunk(c0);
+    load_chunk(c0);
     uint32_t cgt = 0u, ceq = 0u;
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
@@ -505,11 +633,82 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
       }
       e += eq ? 1u : 0u;
     }
+    __syncthreads();  // (the next chunk's scan writes sh)
   }
   for (int i = k + tid; i < K; i += 1024) {
     oi[i] = -1;
     if (ov) ov[i] = 0.f;
   }
+}
+
+// One 1024-thread workgroup per row of at most 1024*NPT entries (longer rows are left to
+// topk_stream_kernel).  The first 1024*NPT entries are requested as coalesced 16-byte pieces
+// before the token's causal length is known (up to the row stride, which bounds every causal
+// length), so the two memory latencies overlap.
+template <int NPT>
+__global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ only,
+    int32_t* __restrict__ out_idx,
+    float* __restrict__ out_val) {
+  extern __shared__ __attribute__((aligned(16))) char smraw[];
+  const int tid = threadIdx.x;
+  const int tl = blockIdx.x;
+  const int t = t_begin + tl;
+  const float* row = scores + (int64_t)tl * ld;
+  // (after the long-row selection: only the rows it left over)
+  if (only && only[4 * tl] != kLongOver) return;
+  constexpr int CH = 1024 * NPT, Q = NPT / 4;
+
+  const LocLoads lw = locate_issue(bt);
+  uint4 v[Q];
+  {
+    const int lim = (int)min<int64_t>(ld, (int64_t)CH);  // (ld is a multiple of 4)
+    const int pl = (tid >> 6) * 64 * NPT + 4 * (tid & 63);
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int p = pl + 256 * i;
+      v[i] = *(const uint4*)(row + min(p, lim - 4));
+      if (p >= lim) v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  int n = locate_finish(bt, t, lw).n;
+  n = (n + (1 << bt.row_shift) - 1) >> bt.row_shift;  // (block rows: pages, not positions)
+  int32_t* oi = out_idx + (int64_t)t * K;
+  float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
+
+  if (n > CH) return;
+  if (n <= K) {  // everything is selected
+    for (int i = tid; i < K; i += 1024) {
+      oi[i] = i < n ? i : -1;
+      if (ov) ov[i] = i < n ? row[i] : 0.f;
+    }
+    return;
+  }
+  select_resident<NPT>(v, n, K, smraw, oi, ov);
+}
+
+// One 1024-thread workgroup per row longer than 1024*32 entries (the others return at once).
+__global__ __launch_bounds__(1024) void topk_stream_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ only,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_val) {
+  extern __shared__ __attribute__((aligned(16))) char smraw[];
+  const int tid = threadIdx.x;
+  const int tl = blockIdx.x;
+  const int t = t_begin + tl;
+  if (only && only[4 * tl] != kLongOver) return;
+  const int n = row_len(bt, t);  // (each wave looks it up)
+  if (n <= 1024 * 32) return;
+  const float* row = scores + (int64_t)tl * ld;
+  int32_t* oi = out_idx + (int64_t)t * K;
+  float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
+  if (n <= K) {  // everything is selected
+    for (int i = tid; i < K; i += 1024) {
+      oi[i] = i < n ? i : -1;
+      if (ov) ov[i] = i < n ? row[i] : 0.f;
+    }
+    return;
+  }
+  select_streamed(row, n, K, K, smraw, oi, ov);
 }
 
 
@@ -805,13 +1004,25 @@ hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
   auto* fn = npt == 4 ? topk_select_kernel<4>
              : npt == 8 ? topk_select_kernel<8>
              : npt == 16 ? topk_select_kernel<16> : topk_select_kernel<32>;
-  // dynamic LDS: the selection's, or the first chunk's transposition if larger
-  const size_t shm = std::max(sizeof(SelSmem), (size_t)4096 * (size_t)npt);
+  // dynamic LDS: a row held on chip (row, histograms, list, bitmaps), or the streamed
+  // selection's histograms if larger
+  const size_t res = npt == 4 ? ResLds<4>::bytes
+                     : npt == 8 ? ResLds<8>::bytes
+                     : npt == 16 ? ResLds<16>::bytes : ResLds<32>::bytes;
+  const size_t shm = std::max(sizeof(SelSmem), res);
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(t_count), dim3(1024), shm, st, bt, t_begin, scores, ld, K, only,
                      idx, val);
+  if (max_n > 1024 * 32) {  // rows longer than one chunk
+    const size_t sshm = sizeof(SelSmem);
+    e = hipFuncSetAttribute((const void*)topk_stream_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_stream_kernel, dim3(t_count), dim3(1024), sshm, st, bt, t_begin,
+                       scores, ld, K, only, idx, val);
+  }
   return hipGetLastError();
 }
 
