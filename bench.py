@@ -13,7 +13,10 @@ line is decode32k.  --k-fmt mxfp8 runs the indexer on MXFP8 keys and queries (on
 per 32 dims) instead of e4m3 keys with one fp32 scale per token, and labels its line so.
 --select block runs block-granular selection instead: the scorer keeps one score per 64-key
 page (its largest), the K/64 best pages are kept and expanded to their causal positions, and
-the attention reads those K positions.  Step times are the median of --repeats timed loops of --steps steps.  The
+the attention reads those K positions.  Step times are the median of --repeats timed loops of
+--steps steps.  By default the untimed warmup runs steps until at least 100 ms of device time
+have passed (at least 5 steps; the count is reported): the GPU's clock takes ~15 ms of steady
+work to settle, and a serving loop runs at the settled clock.  --warmup W runs exactly W.  The
 oracle baseline times the fp64 CPU oracle on every query token of batches of at most
 --cpu-tokens tokens, and on a bounded sample of that many tokens otherwise.
 """
@@ -266,7 +269,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed warmup steps (default: until 100 ms of device time, >= 5)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed loops of --steps steps each; the median is reported")
@@ -376,8 +380,23 @@ def main():
             runs.append(timed_once(fn, n))
         return float(np.median(runs))
 
-    for i in range(args.warmup):
-        step(i)
+    def warm(fn, w):
+        """Untimed calls of fn: exactly w, or (w < 0) until 100 ms of device time have passed
+        and at least 5 calls; returns the count."""
+        if w >= 0:
+            for i in range(w):
+                fn(i)
+            torch.cuda.synchronize()
+            return w
+        n, t0 = 0, time.perf_counter()
+        while n < 5 or time.perf_counter() - t0 < 0.1:
+            for _ in range(5):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        return n
+
+    n_warm = warm(step, args.warmup)
     step_runs = []
     step_ms = timed(step, args.steps, step_runs)
 
@@ -407,8 +426,7 @@ def main():
                             lse[r], ws=ws_a)
 
     for fn in (score, select, attend):
-        for i in range(max(args.warmup, len(reps))):
-            fn(i)
+        warm(fn, max(args.warmup, len(reps)) if args.warmup >= 0 else -1)
     a = algorithmic(inp, block)
     kv = "f32" if sh.fp32 else ("fp8" if sh.kv_fp8 else "bf16")
     calls = {
@@ -457,7 +475,7 @@ def main():
         "unit": "queries/s" if decode else "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": step_ms,
         "repeats": len(step_runs),
         "ms_per_step_runs": [round(x, 5) for x in step_runs],

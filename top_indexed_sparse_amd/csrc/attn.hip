@@ -428,20 +428,24 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   }
   // per 16-row tile: bit m = row pi(m) selected (the order in which the keys are consumed),
   // from one ballot per row step: rows 256j + 64wave + l, four tiles, lane q < 4 writes
-  // tile q's mask (row r of a tile is consumed as m = (r & 8) | (r & 1) << 2 | (r >> 1) & 3)
+  // tile q's mask.  Row r of a tile is consumed as m = (r & 8) | (r & 1) << 2 | (r >> 1) & 3:
+  // within each byte the even rows' bits go to the low nibble and the odd rows' to the high
+  // one, an unzip of each byte in three mask-and-shift steps per half.
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const uint64_t bj = __ballot(slot[j] >= 0 && sel[j]);
     if (lane < 4) {
       const uint32_t nat = (uint32_t)(bj >> (16 * lane)) & 0xffffu;
-      uint32_t m = 0u;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        m |= ((nat >> r) & 1u) << ((r & 8) | ((r & 1) << 2) | ((r >> 1) & 3));
-      masks[(256 * j + 64 * wave) / kWT + lane] = (uint16_t)m;
+      uint32_t e = nat & 0x5555u, o = (nat >> 1) & 0x5555u;
+      e = (e | (e >> 1)) & 0x3333u;
+      o = (o | (o >> 1)) & 0x3333u;
+      e = (e | (e >> 2)) & 0x0f0fu;
+      o = (o | (o >> 2)) & 0x0f0fu;
+      masks[(256 * j + 64 * wave) / kWT + lane] = (uint16_t)(e | (o << 4));
     }
   }
-  __syncthreads();
+  // (LDS only: the wave's Q loads stay in flight across the barrier, under the first gathers)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (FP8) smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   // Rows that are not selected are gathered from a selected row of the split (finite data,
   // whose P is zero: exactly nothing is added).  A split without any selected row skips

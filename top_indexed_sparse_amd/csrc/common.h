@@ -89,13 +89,13 @@ __device__ __forceinline__ LocLoads locate_issue(const DevBatch& bt) {
 __device__ __forceinline__ TokLoc locate_finish(const DevBatch& bt, int t, LocLoads w0) {
   const int lane = threadIdx.x & 63;
   const int c = __popcll(__ballot(lane + 1 <= bt.B - 1 && w0.cq <= t));
-  if (c < 64) {
-    TokLoc r;
-    r.b = c;
-    r.L = __builtin_amdgcn_readlane(w0.sl, c);
-    r.n = r.L - (__builtin_amdgcn_readlane(w0.cq, c) - t) + 1;
-    return r;
-  }
+  // (both values are read out before the branch: a load whose value is used only inside it
+  // is sunk into it by the compiler, which costs a second memory round trip)
+  TokLoc r;
+  r.b = c;
+  r.L = __builtin_amdgcn_readlane(w0.sl, min(c, 63));
+  r.n = r.L - (__builtin_amdgcn_readlane(w0.cq, min(c, 63)) - t) + 1;
+  if (c < 64) return r;
   for (int base = 64;; base += 64) {  // more than 64 requests: the remaining windows
     const int i = base + lane;
     const int cq = i + 1 <= bt.B ? bt.cu_q[i + 1] : 0;
