@@ -26,8 +26,9 @@
 //   * the stages are software pipelined (QK^T of stage st beside the softmax of stage
 //     st - 1, then PV of st - 1 beside the ring writes and gathers), with the order of
 //     matrix and vector work pinned by scheduling fences;
-//   * the running max is raised lazily (only when a stage exceeds it by 2^8), so rescaling
-//     the accumulators is rare;
+//   * the running max is raised lazily, only when a stage's P would exceed 2^15 (fp16 P of an
+//     e4m3 cache: below the format's largest value) or 2^30 (bf16 P), so rescaling the
+//     accumulators is rare even where the logits grow along the selected positions;
 //   * e4m3: per-token scales go into the logits in fp32 and into P relative to the split's
 //     largest scale; P then is fp16 (11-bit significand) so that heavy rows stay accurate,
 //     and the normaliser is accumulated from the same rounded P values;
@@ -251,9 +252,10 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // The stages are software pipelined.  In the iteration of stage st a wave computes its partial
 // QK^T of stage st while it finishes the softmax of stage st - 1 (whose logits its partner
 // completed before the barrier), then runs PV of stage st - 1 while it writes the gathered rows
-// of stage st + 1 into the LDS ring (three stages) and issues the gathers of stage st + 3 (two
-// stages of rows in flight in registers).  The running max is raised lazily (only when a tile
-// exceeds it by 2^8), by recomputing the stage's softmax.  e4m3: per-row scales enter the fp32
+// of stage st + 1 into the LDS ring (three stages) and issues the gathers of stage st + 2 (one
+// stage of rows in flight in registers).  The running max is raised lazily (only when a
+// stage's P would exceed 2^15 with fp16 P, 2^30 with bf16 P), by recomputing the stage's
+// softmax.  e4m3: per-row scales enter the fp32
 // logits and P relative to the split's largest scale; P is fp16 and the normaliser sums the same
 // rounded values.  Each wave writes its own heads' dims of O (or, with several splits, the
 // partials that mla_combine_kernel merges), transposed through LDS into whole lines.
@@ -608,7 +610,11 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
   // t = z - m_run with z = s * zsc (zsc = softmax scale * log2 e, times the row scale for e4m3),
   // p = 2^t.  Masked keys get t = -inf, hence p = 0; m_run starts at a finite floor so this
   // holds before the first live key too.  Returns whether the running max must be raised
-  // (some t of the stage above 8: a lane-local test, uniform through __any).
+  // (some t of the stage above kRaiseAt: a lane-local test, uniform through __any).  P = 2^t is
+  // then at most 2^15 as fp16 (largest finite value 65504) or 2^30 as bf16, summed in fp32; the
+  // formats' relative precision does not depend on the magnitude.  A threshold of 8 raised the
+  // max in 26 of 63 stages of prefill rows whose logits grow along the positions.
+  constexpr float kRaiseAt = FP8 ? 15.f : 30.f;
   float pv[2][2][4];
   uint32_t mk[2];
   f32x4 zsc[2];
@@ -642,7 +648,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
           tmax = fmaxf(tmax, tzv);
           pv[kt][ht][i] = __builtin_amdgcn_exp2f(tzv);
         }
-    return tmax > 8.f;
+    return tmax > kRaiseAt;
   };
   // raise the running max of each head to the stage's, rescale l, le and O, recompute p
   auto raise = [&](int xo) {
@@ -806,7 +812,7 @@ __device__ __forceinline__ void mla_attn_body(DevBatch bt, int t_begin, int t_co
       __builtin_amdgcn_sched_barrier(0);
     }
     pack_tile(1);
-    return tmax > 8.f;
+    return tmax > kRaiseAt;
   };
 
   // ---- O^T[32 dims][32 heads] += V^T[32 dims][16 keys] . P^T over the wave's 8 dim tiles of
