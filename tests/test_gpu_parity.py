@@ -316,6 +316,55 @@ def test_topk_crafted_long_rows():
             assert np.all(val[b, k:] == 0.0), (b, K)
 
 
+def test_topk_streamed_rows():
+    """Top-K over more than 64 rows longer than 32768 positions (one workgroup per row, the row
+    streamed): the one-pass candidate list over a uniform sample's bound, with ties at the
+    threshold (scores rounded to 1/8), sparse rows, signed zeros and -inf, a rising ramp, and
+    rows whose candidates overflow the list (a constant row, four distinct values), which the
+    exact streamed radix select finishes.  Every row equals the oracle's Top-K, values
+    included, for K = 1, 100, 2048 and 4096."""
+    import top_indexed_sparse_amd as tis
+    from oracle.method import topk_token
+    rng = np.random.default_rng(20261204)
+    B = 66
+    lens = rng.integers(32769, 90001, B)
+    lens[:4] = [32769, 65536, 90000, 40001]
+    ld = 90000
+    S = np.zeros((B, ld), np.float32)
+    for b in range(B):
+        kind = b % 7
+        x = rng.standard_normal(ld).astype(np.float32)
+        if kind == 1:
+            x = np.round(x * 8.0) / 8.0
+        elif kind == 2:
+            x = (rng.exponential(size=ld) * (rng.random(ld) < 0.2)).astype(np.float32)
+        elif kind == 3:
+            x[::7] = -0.0
+            x[::11] = 0.0
+            x[::13] = -np.inf
+        elif kind == 4:
+            x = rng.integers(0, 4, ld).astype(np.float32)
+        elif kind == 5:
+            x += np.linspace(0.0, 6.0, ld, dtype=np.float32)
+        elif kind == 6 and b == 6:
+            x[:] = 2.5
+        S[b] = x
+    bt = tis.Batch(np.array(lens, np.int32), np.arange(B + 1, dtype=np.int32),
+                   np.zeros((B, -(-ld // 64)), np.int32), 1)
+    scores = torch.from_numpy(S).cuda()
+    for K in (1, 100, 2048, 4096):
+        note(f"case Top-K on streamed rows, K={K}")
+        idx = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+        val = torch.full((B, K), 7.0, dtype=torch.float32, device="cuda")
+        tis.topk_select(bt, scores, K, idx, val)
+        idx, val = idx.cpu().numpy(), val.cpu().numpy()
+        for b in range(B):
+            ref = topk_token(S[b, :lens[b]].astype(np.float64), K)[0]
+            assert np.array_equal(idx[b], ref), (b, K)
+            k = int((ref >= 0).sum())
+            assert np.array_equal(val[b, :k], S[b, ref[:k]] + np.float32(0.0)), (b, K)
+
+
 def test_fused_call_crafted_scores():
     """index_score_topk on crafted score rows made by the scorer itself: every key page holds
     the same codes, so a token's score at position s is the key scale of s times one per-token

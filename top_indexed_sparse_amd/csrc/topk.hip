@@ -555,7 +555,226 @@ __device__ __forceinline__ void select_resident(const uint4 (&v)[NPT / 4], int n
 }
 
 // ---------------------------------------------------------------- rows longer than a chunk
-// (1024*32 positions): each pass streams the row through registers, thread i holding 32
+// Rows longer than 1024*32 entries, first attempt: the threshold search of rows held on chip,
+// with the row read once.
+//  1. A uniform sample of 2048 scores (positions floor(s n / 2048)) gives tlo as above.
+//  2. One pass over the row in 32K-entry chunks of coalesced pieces (thread (w, l), piece i:
+//     positions c0 + 2048w + 256i + 4l .. + 3) lists the positions of the scores >= tlo in
+//     position order: per piece a wave scan of the lanes' counts, per chunk a scan of the
+//     waves' totals.
+//  3. The candidates' keys are read back by position (thread i owns list entries 8i .. 8i + 7);
+//     the threshold key T and the quota of ties at T come from the candidate histogram, bins
+//     narrowed down to a rank by one wave or to a single key value.
+//  4. A block scan of (> T, == T) counts compacts the list in position order.
+// Returns false, having written nothing, when fewer than K or more than the list holds reach
+// tlo; the caller then runs the exact streamed radix select.
+constexpr int kStreamListMax = 8192;  // candidate positions of a streamed row
+struct StreamLds {
+  uint32_t hA[2048];
+  uint32_t hB[2048];
+  uint32_t list[kStreamListMax];
+  uint32_t rk[64];
+  uint32_t sh[48];   // scan totals (0..15), min/max (16..47)
+  uint32_t pick[4];  // [bin or T, above or quota, count, -]
+  uint32_t cnt[4];   // [rank fill]
+};
+
+__device__ __forceinline__ bool select_stream_list(const float* __restrict__ row, int n, int k,
+                                                   char* smraw, int32_t* __restrict__ oi,
+                                                   float* __restrict__ ov) {
+  constexpr int CH = 1024 * 32, E = kStreamListMax / 1024;
+  StreamLds& S = *(StreamLds*)smraw;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  S.hA[tid] = 0u;
+  S.hA[tid + 1024] = 0u;
+  S.hB[tid] = 0u;
+  S.hB[tid + 1024] = 0u;
+  if (tid < 4) S.pick[tid] = 0u;
+  else if (tid < 8) S.cnt[tid - 4] = 0u;
+
+  // ---- 1. sampled lower bound (the min/max barrier also orders the clears above)
+  const uint32_t ka = order_key(row[(int)(((int64_t)tid * n) >> 11)]);
+  const uint32_t kb = order_key(row[(int)(((int64_t)(tid + 1024) * n) >> 11)]);
+  uint32_t smin = min(ka, kb), smax = max(ka, kb);
+  block_minmax(smin, smax, S.sh + 16);
+  const uint32_t sspan = smax - smin;
+  const int shift = max(0, (sspan ? 32 - __clz(sspan) : 0) - 11);
+  atomicAdd(&S.hA[(ka - smin) >> shift], 1u);
+  atomicAdd(&S.hA[(kb - smin) >> shift], 1u);
+  __syncthreads();
+  {
+    const uint32_t want = min(2048u, (uint32_t)(((uint64_t)k * 2048u * 5u) / (4ull * n)) + 16u);
+    pick_bin(S.hA, want, S.sh, S.pick);
+    __syncthreads();
+  }
+  const uint32_t tlo = smin + (S.pick[0] << shift);
+  const float tf = key_value(tlo);  // (x >= tf exactly when order_key(x) >= tlo)
+
+  // ---- 2. the candidates' positions, in position order, and the row maximum
+  uint32_t run = 0u;  // entries listed so far
+  float rmax = -INFINITY;
+  const int pl = wave * 2048 + 4 * lane;
+  for (int c0 = 0; c0 < n; c0 += CH) {
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = c0 + pl + 256 * i;
+      if (p + 3 < n) {
+        const float4 f = *(const float4*)(row + p);
+        x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[4 * i + e] = p + e < n ? row[p + e] : __uint_as_float(0x7fc00000u);  // (NaN)
+      }
+    }
+    uint32_t bits[8], ex[8], wbase[8];
+    uint32_t wtot = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bits[i] = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bits[i] |= (x[4 * i + e] >= tf ? 1u : 0u) << e;
+        rmax = fmaxf(rmax, x[4 * i + e]);  // (NaN entries are skipped)
+      }
+      const uint32_t c = __popc(bits[i]);
+      const uint32_t inc = wave_incl_scan(c);
+      ex[i] = inc - c;
+      wbase[i] = wtot;
+      wtot += __builtin_amdgcn_readlane(inc, 63);
+    }
+    if (lane == 0) S.sh[wave] = wtot;
+    __syncthreads();
+    const uint32_t ws = wave_incl_scan(lane < 16 ? S.sh[lane] : 0u);
+    const uint32_t before = wave ? __builtin_amdgcn_readlane(ws, wave - 1) : 0u;
+    const uint32_t ctot = __builtin_amdgcn_readlane(ws, 15);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t o = run + before + wbase[i] + ex[i];
+      const uint32_t p = (uint32_t)(c0 + pl + 256 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((bits[i] >> e) & 1u) {
+          if (o < (uint32_t)kStreamListMax) S.list[o] = p + e;
+          ++o;
+        }
+    }
+    run += ctot;
+    __syncthreads();  // (the next chunk's scan writes sh)
+  }
+  const uint32_t C = run;  // (uniform)
+  uint32_t kmin_unused = ~0u, kmax = order_key(rmax);
+  block_minmax(kmin_unused, kmax, S.sh + 16);  // (its barrier also publishes the list)
+  if (C < (uint32_t)k || C > (uint32_t)kStreamListMax) return false;
+
+  // ---- 3. keys by position; histogram over [tlo, max]; the threshold
+  uint32_t lk[E], lp[E];  // entries E*tid .. : key (0 past the list) and position
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t i = (uint32_t)(E * tid + e);
+    lp[e] = i < C ? S.list[i] : 0u;
+    lk[e] = i < C ? order_key(row[lp[e]]) : 0u;
+  }
+  const uint32_t cspan = kmax - tlo;
+  const int shift2 = max(0, (cspan ? 32 - __clz(cspan) : 0) - 11);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (lk[e] != 0u) atomicAdd(&S.hB[(lk[e] - tlo) >> shift2], 1u);
+  S.hA[tid] = 0u;  // (the sample histogram was last read before tlo's barrier)
+  S.hA[tid + 1024] = 0u;
+  __syncthreads();
+  pick_bin(S.hB, (uint32_t)k, S.sh, S.pick);
+  __syncthreads();
+  uint32_t lo = tlo + (S.pick[0] << shift2);  // the bin: keys lo .. lo + 2^s - 1
+  int s = shift2;
+  uint32_t cb = S.pick[2];
+  uint32_t krem = (uint32_t)k - S.pick[1];
+  uint32_t T, quota;
+  uint32_t* hc = S.hA;
+  uint32_t* hn = S.hB;
+  while (true) {
+    if (cb == krem) {  // the whole bin: every key >= lo, no ties
+      T = lo - 1u;
+      quota = 0u;
+      break;
+    }
+    if (s == 0) {  // every key of the bin equals lo
+      T = lo;
+      quota = krem;
+      break;
+    }
+    const uint32_t hi =
+        (uint32_t)min<uint64_t>((uint64_t)lo + ((1ull << s) - 1ull), 0xffffffffull);
+    if (cb <= 64u) {  // one wave ranks the bin's keys (lane j holds key j)
+      __syncthreads();  // (the previous level's picks have been read)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (lk[e] >= lo && lk[e] <= hi) S.rk[atomicAdd(&S.cnt[0], 1u)] = lk[e];
+      __syncthreads();
+      if (tid < 64) {
+        const bool has = (uint32_t)tid < cb;
+        const uint32_t mine = has ? S.rk[tid] : 0u;
+        uint32_t gt = 0u, ge = 0u;
+        for (uint32_t j = 0; j < cb; ++j) {
+          const uint32_t ot = __builtin_amdgcn_readlane(mine, j);
+          gt += ot > mine ? 1u : 0u;
+          ge += ot >= mine ? 1u : 0u;
+        }
+        if (has && gt < krem && krem <= ge) {  // the krem-th largest of the bin
+          S.pick[0] = mine;
+          S.pick[1] = krem - gt;
+        }
+      }
+      __syncthreads();
+      T = S.pick[0];
+      quota = S.pick[1];
+      break;
+    }
+    const int s2 = max(0, s - 11);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (lk[e] >= lo && lk[e] <= hi) atomicAdd(&hc[(lk[e] - lo) >> s2], 1u);
+    hn[tid] = 0u;
+    hn[tid + 1024] = 0u;
+    __syncthreads();
+    pick_bin(hc, krem, S.sh, S.pick);
+    __syncthreads();
+    lo += S.pick[0] << s2;
+    krem -= S.pick[1];
+    cb = S.pick[2];
+    s = s2;
+    uint32_t* t0 = hc;
+    hc = hn;
+    hn = t0;
+  }
+
+  // ---- 4. compaction in list (= position) order
+  uint32_t cgt = 0u, ceq = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    cgt += lk[e] > T ? 1u : 0u;
+    ceq += lk[e] == T && lk[e] != 0u ? 1u : 0u;
+  }
+  uint32_t tot;
+  __syncthreads();  // (sh: the last pick's scan)
+  const uint32_t bsc = block_excl_scan(cgt | (ceq << 16), S.sh, tot);
+  uint32_t eb = bsc >> 16;  // ties before this thread's
+  uint32_t o = (bsc & 0xffffu) + min(eb, quota);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool eq = lk[e] == T && lk[e] != 0u;
+    if ((lk[e] > T || (eq && eb < quota)) && o < (uint32_t)k) {
+      oi[o] = (int32_t)lp[e];
+      if (ov) ov[o] = key_value(lk[e]);  // (the score; -0.0 comes out as +0.0)
+      ++o;
+    }
+    eb += eq ? 1u : 0u;
+  }
+  return true;
+}
+
+// Exact fallback: each pass streams the row through registers, thread i holding 32
 // consecutive positions of each chunk.  The key range is measured, then a radix select
 // over the whole row gives T; the compaction keeps keys > T and the first krem keys == T
 // chunk by chunk, one block scan per chunk.
@@ -708,7 +927,7 @@ __global__ __launch_bounds__(1024) void topk_stream_kernel(DevBatch bt, int t_be
     }
     return;
   }
-  select_streamed(row, n, K, K, smraw, oi, ov);
+  if (!select_stream_list(row, n, K, smraw, oi, ov)) select_streamed(row, n, K, K, smraw, oi, ov);
 }
 
 
@@ -1016,7 +1235,7 @@ hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
   hipLaunchKernelGGL(fn, dim3(t_count), dim3(1024), shm, st, bt, t_begin, scores, ld, K, only,
                      idx, val);
   if (max_n > 1024 * 32) {  // rows longer than one chunk
-    const size_t sshm = sizeof(SelSmem);
+    const size_t sshm = std::max(sizeof(SelSmem), sizeof(StreamLds));
     e = hipFuncSetAttribute((const void*)topk_stream_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
     if (e != hipSuccess) return e;
