@@ -172,7 +172,9 @@ def test_long_row_selection_workspace():
     lib = tis.lib()
     b = FakeBatch([40000, 1000], [0, 1, 2])
     need = lib.topk_select_workspace_size(b.ref, 2048)
-    assert need == 2 * (8192 * 8 + 2048 * 4 + 1024 * 4 + 16)
+    # per row: 8192 (key, position) candidates, state (16 bytes), (offset, count) of each
+    # 16384-position slice
+    assert need == 2 * (8 * 8192 + 16 + 8 * 3)
     assert lib.topk_select_workspace_size(b.ref, 5000) == 0           # K above 4096
     assert lib.topk_select_workspace_size(FakeBatch([30000], [0, 1]).ref, 2048) == 0
     assert lib.topk_select(b.ref, D, 40000, 2048, D, None, D, need - 1, None) == L.TIS_ERR_INVALID

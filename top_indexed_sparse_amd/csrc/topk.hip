@@ -109,11 +109,11 @@ struct SelSmem {
   uint32_t pick[4];
 };
 
-// Long-row selection state per row, words [mode, bin, candidates, keys above the bin]
-constexpr uint32_t kLongCand = 0u, kLongAll = 1u, kLongOver = 2u;
-constexpr int kLongCap = 8192;      // candidates per row (8 per thread of the last step)
+// Long-row selection state per row, words [mode, tlo, candidates reserved, -]
+constexpr uint32_t kLongCand = 0u, kLongAll = 1u;
+constexpr int kLongCap = 8192;      // candidate positions per row (8 per thread of the last step)
 constexpr int kLongRows = 64;       // at most this many rows per launch take the long-row path
-constexpr int kLongSlices = 1024;   // slices per row at most
+constexpr int kLongSlice = 16384;   // entries per slice
 
 // Radix select of the krem-th largest key among the keys produced by `each` (called with a
 // visitor), over r = key - base with digits of up to 11 bits from bit `hi` down.  Returns the
@@ -579,6 +579,116 @@ struct StreamLds {
   uint32_t cnt[4];   // [rank fill]
 };
 
+// Threshold and compaction over a position-ordered candidate list: thread i holds entries
+// E*i .. E*i + E - 1 (keys, 0 past the list, and positions); every listed key is >= tlo and kmax
+// is the largest.  The candidate histogram over [tlo, kmax] puts the K-th largest in one bin;
+// the bin taken whole ends the search, a bin of one key value fixes it, a bin of at most 64
+// keys is ranked by one wave (lane j holds key j, the others read with readlane), a larger bin
+// is histogrammed again over its own range.  Then one block scan of (> T, == T) counts writes
+// the keys > T and the first `quota` keys == T in list order.  S.hB and S.cnt[0] must be zero,
+// and visible to every thread, on entry.
+template <int E>
+__device__ __forceinline__ void select_listed(const uint32_t (&lk)[E], const uint32_t (&lp)[E],
+                                              uint32_t tlo, uint32_t kmax, int k, StreamLds& S,
+                                              int32_t* __restrict__ oi, float* __restrict__ ov) {
+  const int tid = threadIdx.x;
+  const uint32_t cspan = kmax - tlo;
+  const int shift2 = max(0, (cspan ? 32 - __clz(cspan) : 0) - 11);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (lk[e] != 0u) atomicAdd(&S.hB[(lk[e] - tlo) >> shift2], 1u);
+  S.hA[tid] = 0u;  // (hA's earlier contents were last read before the caller's last barrier)
+  S.hA[tid + 1024] = 0u;
+  __syncthreads();
+  pick_bin(S.hB, (uint32_t)k, S.sh, S.pick);
+  __syncthreads();
+  uint32_t lo = tlo + (S.pick[0] << shift2);  // the bin: keys lo .. lo + 2^s - 1
+  int s = shift2;
+  uint32_t cb = S.pick[2];
+  uint32_t krem = (uint32_t)k - S.pick[1];
+  uint32_t T, quota;
+  uint32_t* hc = S.hA;
+  uint32_t* hn = S.hB;
+  while (true) {
+    if (cb == krem) {  // the whole bin: every key >= lo, no ties
+      T = lo - 1u;
+      quota = 0u;
+      break;
+    }
+    if (s == 0) {  // every key of the bin equals lo
+      T = lo;
+      quota = krem;
+      break;
+    }
+    const uint32_t hi =
+        (uint32_t)min<uint64_t>((uint64_t)lo + ((1ull << s) - 1ull), 0xffffffffull);
+    if (cb <= 64u) {  // one wave ranks the bin's keys (lane j holds key j)
+      __syncthreads();  // (the previous level's picks have been read)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (lk[e] >= lo && lk[e] <= hi) S.rk[atomicAdd(&S.cnt[0], 1u)] = lk[e];
+      __syncthreads();
+      if (tid < 64) {
+        const bool has = (uint32_t)tid < cb;
+        const uint32_t mine = has ? S.rk[tid] : 0u;
+        uint32_t gt = 0u, ge = 0u;
+        for (uint32_t j = 0; j < cb; ++j) {
+          const uint32_t ot = __builtin_amdgcn_readlane(mine, j);
+          gt += ot > mine ? 1u : 0u;
+          ge += ot >= mine ? 1u : 0u;
+        }
+        if (has && gt < krem && krem <= ge) {  // the krem-th largest of the bin
+          S.pick[0] = mine;
+          S.pick[1] = krem - gt;
+        }
+      }
+      __syncthreads();
+      T = S.pick[0];
+      quota = S.pick[1];
+      break;
+    }
+    const int s2 = max(0, s - 11);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (lk[e] >= lo && lk[e] <= hi) atomicAdd(&hc[(lk[e] - lo) >> s2], 1u);
+    hn[tid] = 0u;
+    hn[tid + 1024] = 0u;
+    __syncthreads();
+    pick_bin(hc, krem, S.sh, S.pick);
+    __syncthreads();
+    lo += S.pick[0] << s2;
+    krem -= S.pick[1];
+    cb = S.pick[2];
+    s = s2;
+    uint32_t* t0 = hc;
+    hc = hn;
+    hn = t0;
+  }
+
+  // ---- 4. compaction in list (= position) order
+  uint32_t cgt = 0u, ceq = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    cgt += lk[e] > T ? 1u : 0u;
+    ceq += lk[e] == T && lk[e] != 0u ? 1u : 0u;
+  }
+  uint32_t tot;
+  __syncthreads();  // (sh: the last pick's scan)
+  const uint32_t bsc = block_excl_scan(cgt | (ceq << 16), S.sh, tot);
+  uint32_t eb = bsc >> 16;  // ties before this thread's
+  uint32_t o = (bsc & 0xffffu) + min(eb, quota);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool eq = lk[e] == T && lk[e] != 0u;
+    if ((lk[e] > T || (eq && eb < quota)) && o < (uint32_t)k) {
+      oi[o] = (int32_t)lp[e];
+      if (ov) ov[o] = key_value(lk[e]);  // (the score; -0.0 comes out as +0.0)
+      ++o;
+    }
+    eb += eq ? 1u : 0u;
+  }
+}
+
 __device__ __forceinline__ bool select_stream_list(const float* __restrict__ row, int n, int k,
                                                    char* smraw, int32_t* __restrict__ oi,
                                                    float* __restrict__ ov) {
@@ -676,101 +786,7 @@ __device__ __forceinline__ bool select_stream_list(const float* __restrict__ row
     lp[e] = i < C ? S.list[i] : 0u;
     lk[e] = i < C ? order_key(row[lp[e]]) : 0u;
   }
-  const uint32_t cspan = kmax - tlo;
-  const int shift2 = max(0, (cspan ? 32 - __clz(cspan) : 0) - 11);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (lk[e] != 0u) atomicAdd(&S.hB[(lk[e] - tlo) >> shift2], 1u);
-  S.hA[tid] = 0u;  // (the sample histogram was last read before tlo's barrier)
-  S.hA[tid + 1024] = 0u;
-  __syncthreads();
-  pick_bin(S.hB, (uint32_t)k, S.sh, S.pick);
-  __syncthreads();
-  uint32_t lo = tlo + (S.pick[0] << shift2);  // the bin: keys lo .. lo + 2^s - 1
-  int s = shift2;
-  uint32_t cb = S.pick[2];
-  uint32_t krem = (uint32_t)k - S.pick[1];
-  uint32_t T, quota;
-  uint32_t* hc = S.hA;
-  uint32_t* hn = S.hB;
-  while (true) {
-    if (cb == krem) {  // the whole bin: every key >= lo, no ties
-      T = lo - 1u;
-      quota = 0u;
-      break;
-    }
-    if (s == 0) {  // every key of the bin equals lo
-      T = lo;
-      quota = krem;
-      break;
-    }
-    const uint32_t hi =
-        (uint32_t)min<uint64_t>((uint64_t)lo + ((1ull << s) - 1ull), 0xffffffffull);
-    if (cb <= 64u) {  // one wave ranks the bin's keys (lane j holds key j)
-      __syncthreads();  // (the previous level's picks have been read)
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (lk[e] >= lo && lk[e] <= hi) S.rk[atomicAdd(&S.cnt[0], 1u)] = lk[e];
-      __syncthreads();
-      if (tid < 64) {
-        const bool has = (uint32_t)tid < cb;
-        const uint32_t mine = has ? S.rk[tid] : 0u;
-        uint32_t gt = 0u, ge = 0u;
-        for (uint32_t j = 0; j < cb; ++j) {
-          const uint32_t ot = __builtin_amdgcn_readlane(mine, j);
-          gt += ot > mine ? 1u : 0u;
-          ge += ot >= mine ? 1u : 0u;
-        }
-        if (has && gt < krem && krem <= ge) {  // the krem-th largest of the bin
-          S.pick[0] = mine;
-          S.pick[1] = krem - gt;
-        }
-      }
-      __syncthreads();
-      T = S.pick[0];
-      quota = S.pick[1];
-      break;
-    }
-    const int s2 = max(0, s - 11);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (lk[e] >= lo && lk[e] <= hi) atomicAdd(&hc[(lk[e] - lo) >> s2], 1u);
-    hn[tid] = 0u;
-    hn[tid + 1024] = 0u;
-    __syncthreads();
-    pick_bin(hc, krem, S.sh, S.pick);
-    __syncthreads();
-    lo += S.pick[0] << s2;
-    krem -= S.pick[1];
-    cb = S.pick[2];
-    s = s2;
-    uint32_t* t0 = hc;
-    hc = hn;
-    hn = t0;
-  }
-
-  // ---- 4. compaction in list (= position) order
-  uint32_t cgt = 0u, ceq = 0u;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    cgt += lk[e] > T ? 1u : 0u;
-    ceq += lk[e] == T && lk[e] != 0u ? 1u : 0u;
-  }
-  uint32_t tot;
-  __syncthreads();  // (sh: the last pick's scan)
-  const uint32_t bsc = block_excl_scan(cgt | (ceq << 16), S.sh, tot);
-  uint32_t eb = bsc >> 16;  // ties before this thread's
-  uint32_t o = (bsc & 0xffffu) + min(eb, quota);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool eq = lk[e] == T && lk[e] != 0u;
-    if ((lk[e] > T || (eq && eb < quota)) && o < (uint32_t)k) {
-      oi[o] = (int32_t)lp[e];
-      if (ov) ov[o] = key_value(lk[e]);  // (the score; -0.0 comes out as +0.0)
-      ++o;
-    }
-    eb += eq ? 1u : 0u;
-  }
+  select_listed<E>(lk, lp, tlo, kmax, k, S, oi, ov);
   return true;
 }
 
@@ -866,16 +882,13 @@ __device__ __forceinline__ void select_streamed(const float* __restrict__ row, i
 // length), so the two memory latencies overlap.
 template <int NPT>
 __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ only,
-    int32_t* __restrict__ out_idx,
+    const float* __restrict__ scores, int64_t ld, int K, int32_t* __restrict__ out_idx,
     float* __restrict__ out_val) {
   extern __shared__ __attribute__((aligned(16))) char smraw[];
   const int tid = threadIdx.x;
   const int tl = blockIdx.x;
   const int t = t_begin + tl;
   const float* row = scores + (int64_t)tl * ld;
-  // (after the long-row selection: only the rows it left over)
-  if (only && only[4 * tl] != kLongOver) return;
   constexpr int CH = 1024 * NPT, Q = NPT / 4;
 
   const LocLoads lw = locate_issue(bt);
@@ -908,13 +921,12 @@ __global__ __launch_bounds__(1024) void topk_select_kernel(DevBatch bt, int t_be
 
 // One 1024-thread workgroup per row longer than 1024*32 entries (the others return at once).
 __global__ __launch_bounds__(1024) void topk_stream_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ only,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_val) {
+    const float* __restrict__ scores, int64_t ld, int K, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_val) {
   extern __shared__ __attribute__((aligned(16))) char smraw[];
   const int tid = threadIdx.x;
   const int tl = blockIdx.x;
   const int t = t_begin + tl;
-  if (only && only[4 * tl] != kLongOver) return;
   const int n = row_len(bt, t);  // (each wave looks it up)
   if (n <= 1024 * 32) return;
   const float* row = scores + (int64_t)tl * ld;
@@ -932,289 +944,273 @@ __global__ __launch_bounds__(1024) void topk_stream_kernel(DevBatch bt, int t_be
 
 
 // ---------------------------------------------------------------- long rows, few of them
-// With few rows of many positions, one workgroup per row leaves most of the chip idle and
-// streams each row through one CU.  Then every row is cut into slices:
-//   0. the row's histogram and state words are cleared;
-//   1. each slice histograms the top 11 bits of its keys in LDS and adds the non-empty bins to
-//      the row's histogram;
-//   2. one workgroup per row finds the bin b holding the k-th largest key: the keys in bins
-//      >= b (at least k of them) are the candidates;
-//   3. each slice counts its candidates, then writes them (key, position) to the row's list
-//      at the offset of the slices before it, so the list is in position order;
-//   4. one workgroup per row holds the list in registers, radix-selects the threshold key T
-//      among the keys of the picked bin (the keys above it are all taken) and keeps the keys
-//      > T and the first ones == T, in list (= position) order.
-// Rows with n <= K take every position in step 4.  A row whose list would exceed kLongCap
-// (many equal or nearly equal scores) is marked in step 2 and selected afterwards by the
-// one-workgroup kernel, which skips every other row.  The result is the same selection.
+// With few rows of many positions (at most kLongRows per launch, rows over 32K entries,
+// K <= 4096), one workgroup per row would leave most of the chip idle and read each row through
+// one CU.  Three launches instead:
+//   1. one workgroup per row: 8192 scores in 512 runs of 16 at uniform sites give the lower
+//      bound tlo of the K-th largest key (as for streamed rows); the row's candidate count is
+//      reset;
+//   2. one workgroup per 16384-entry slice (coalesced 16-byte pieces): the slice's scores
+//      >= tlo are counted, room for them is reserved in the row's candidate list (at most
+//      kLongCap positions) with one atomic per slice (few slices per row: the atomics of one
+//      row serialise), and their (key, position) pairs are written there in position order,
+//      with the slice's (offset, count);
+//   3. one workgroup per row: thread i fetches list entries 8i .. 8i + 7 of the slices'
+//      candidates in slice (= position) order, and the threshold and compaction of streamed
+//      rows finish the row.  A row whose candidates overflow the list or fall short of K (many equal
+//      scores) is selected by the exact streamed select in the same workgroup.
+// Rows with n <= K take every position in step 3.
 
-__global__ __launch_bounds__(256) void topk_long_zero_kernel(uint32_t* __restrict__ hist,
-                                                             uint32_t* __restrict__ state) {
-  const int tl = blockIdx.x;
-  for (int i = threadIdx.x; i < 2048; i += 256) hist[(int64_t)tl * 2048 + i] = 0u;
-  if (threadIdx.x < 4) state[4 * tl + threadIdx.x] = 0u;
-}
-
-__global__ __launch_bounds__(256) void topk_long_hist_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int K, int slice,
-    uint32_t* __restrict__ hist) {
+__global__ __launch_bounds__(1024) void topk_long_sample_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int K, uint32_t* __restrict__ state) {
   __shared__ uint32_t h[2048];
-  const int tid = threadIdx.x, tl = blockIdx.y;
-  for (int i = tid; i < 2048; i += 256) h[i] = 0u;
-  const int n = row_len(bt, t_begin + tl);
-  const float* row = scores + (int64_t)tl * ld;
-  const int p0 = blockIdx.x * slice, p1 = min(n, p0 + slice);
-  __syncthreads();
-  if (n > K) {
-    for (int p = p0 + 4 * tid; p < p1; p += 1024) {
-      float v[4];
-      if (p + 3 < p1) {
-        const float4 f = *(const float4*)(row + p);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = p + e < p1 ? row[p + e] : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {  // (key 0 is never listed: it is not counted either)
-        const uint32_t k = order_key(v[e]);
-        if (p + e < p1 && k != 0u) atomicAdd(&h[k >> 21], 1u);
-      }
-    }
-  }
-  __syncthreads();
-  uint32_t* gh = hist + (int64_t)tl * 2048;
-  for (int i = tid; i < 2048; i += 256)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-__global__ __launch_bounds__(1024) void topk_long_pick_kernel(DevBatch bt, int t_begin, int K,
-    const uint32_t* __restrict__ hist, uint32_t* __restrict__ state) {
   __shared__ uint32_t sh[48];
-  __shared__ uint32_t pick[3];
+  __shared__ uint32_t pick[4];
   const int tid = threadIdx.x, tl = blockIdx.x;
-  const int n = row_len(bt, t_begin + tl);
-  uint32_t* st = state + 4 * tl;
-  if (n <= K) {  // (uniform over the workgroup)
-    if (tid == 0) st[0] = kLongAll;
+  const int n = row_len(bt, t_begin + tl);  // (each wave looks it up)
+  uint32_t* s = state + 4 * tl;
+  if (n <= K) {
+    if (tid == 0) {
+      s[0] = kLongAll;
+      s[2] = 0u;
+    }
     return;
   }
-  // bins in descending order: thread i owns bins 2047 - 2i and 2046 - 2i
-  const uint32_t* hr = hist + (int64_t)tl * 2048;
-  const uint32_t ch = hr[2047 - 2 * tid], cl = hr[2046 - 2 * tid];
-  if (tid == 0) {  // (no bin reaches K only when keys 0 were left out: overflow, as for ties)
-    pick[0] = 0u;
-    pick[1] = ~0u;
-    pick[2] = 0u;
+  const float* row = scores + (int64_t)tl * ld;
+  h[tid] = 0u;
+  h[tid + 1024] = 0u;
+  if (tid < 4) pick[tid] = 0u;
+  // 8192 scores: 512 runs of 16 consecutive positions at uniform sites (a run starts at
+  // floor(r (n - 16) / 511) rounded down to a multiple of 4, so each of a run's four threads
+  // reads one 16-byte piece, the last ending at n - 1 at most); two runs per group of four
+  // threads.  (Rows shorter than 16 read their positions clamped to the row.)
+  uint32_t kk[8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (tid >> 2) + 256 * j;
+    const int base = n >= 16 ? (int)(((int64_t)r * (n - 16)) / 511) & ~3 : 0;
+    const int p = base + 4 * (tid & 3);
+    float f[4];
+    if (p + 3 < n) {
+      const float4 v = *(const float4*)(row + p);
+      f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = row[min(p + e, n - 1)];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kk[4 * j + e] = order_key(f[e]);
   }
-  uint32_t tot;
-  const uint32_t above_h = block_excl_scan(ch + cl, sh, tot);
-  const uint32_t above_l = above_h + ch;
-  const uint32_t k = (uint32_t)K;
-  if (ch && above_h < k && k <= above_h + ch) {
-    pick[0] = 2047 - 2 * tid;
-    pick[1] = above_h + ch;
-    pick[2] = above_h;
+  uint32_t mn = ~0u, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mn = min(mn, kk[j]);
+    mx = max(mx, kk[j]);
   }
-  if (cl && above_l < k && k <= above_l + cl) {
-    pick[0] = 2046 - 2 * tid;
-    pick[1] = above_l + cl;
-    pick[2] = above_l;
-  }
+  block_minmax(mn, mx, sh + 16);  // (its barrier also orders the clears above)
+  const uint32_t span = mx - mn;
+  const int shift = max(0, (span ? 32 - __clz(span) : 0) - 11);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) atomicAdd(&h[(kk[j] - mn) >> shift], 1u);
+  __syncthreads();
+  const uint32_t want = min(8192u, (uint32_t)(((uint64_t)K * 8192u * 5u) / (4ull * n)) + 16u);
+  pick_bin(h, want, sh, pick);
   __syncthreads();
   if (tid == 0) {
-    st[0] = pick[1] > (uint32_t)kLongCap ? kLongOver : kLongCand;
-    st[1] = pick[0];
-    st[2] = pick[1];
-    st[3] = pick[2];
+    s[0] = kLongCand;
+    s[1] = mn + (pick[0] << shift);
+    s[2] = 0u;
   }
 }
 
-// keys of positions p .. p + 3 of a slice ending at p1 (key 0 past it)
-__device__ __forceinline__ void long_keys4(const float* row, int p, int p1, uint32_t key[4]) {
-  float v[4];
-  if (p + 3 < p1) {
-    const float4 f = *(const float4*)(row + p);
-    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = p + e < p1 ? row[p + e] : 0.f;
+__global__ __launch_bounds__(1024) void topk_long_list_kernel(DevBatch bt, int t_begin,
+    const float* __restrict__ scores, int64_t ld, int nsl, uint32_t* __restrict__ state,
+    uint32_t* __restrict__ slices, uint64_t* __restrict__ cand) {
+  __shared__ uint32_t wt[16];
+  __shared__ uint32_t base_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sl = blockIdx.x, tl = blockIdx.y;
+  uint32_t* s = state + 4 * tl;
+  if (s[0] != kLongCand) return;
+  const int n = row_len(bt, t_begin + tl);  // (each wave looks it up)
+  const int s0 = sl * kLongSlice;
+  uint32_t* so = slices + ((int64_t)tl * nsl + sl) * 2;
+  if (s0 >= n) {
+    if (tid == 0) {
+      so[0] = 0u;
+      so[1] = 0u;
+    }
+    return;
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) key[e] = p + e < p1 ? order_key(v[e]) : 0u;
-}
-
-__global__ __launch_bounds__(256) void topk_long_count_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int slice, const uint32_t* __restrict__ state,
-    uint32_t* __restrict__ counts) {
-  __shared__ uint32_t c_sh;
-  const int tid = threadIdx.x, tl = blockIdx.y;
-  const uint32_t* st = state + 4 * tl;
-  if (st[0] != kLongCand) return;
-  const uint32_t thr = st[1] << 21;  // the candidates: keys in bins >= the picked one
-  const int n = row_len(bt, t_begin + tl);
+  const float tf = key_value(s[1]);  // (x >= tf exactly when order_key(x) >= tlo)
   const float* row = scores + (int64_t)tl * ld;
-  const int p0 = blockIdx.x * slice, p1 = min(n, p0 + slice);
-  if (tid == 0) c_sh = 0u;
-  __syncthreads();
-  uint32_t c = 0u;
-  for (int p = p0 + 4 * tid; p < p1; p += 1024) {
-    uint32_t key[4];
-    long_keys4(row, p, p1, key);
+  const int pl = s0 + 1024 * wave + 4 * lane;  // piece i: positions pl + 256 i .. + 3
+  uint32_t bits[4], ex[4], wb[4];
+  float xk[4][4];
+  uint32_t wtot = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) c += key[e] >= thr && key[e] != 0u ? 1u : 0u;
-  }
-  if (c) atomicAdd(&c_sh, c);
-  __syncthreads();
-  if (tid == 0) counts[(int64_t)tl * kLongSlices + blockIdx.x] = c_sh;
-}
-
-__global__ __launch_bounds__(1024) void topk_long_write_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int slice, const uint32_t* __restrict__ state,
-    const uint32_t* __restrict__ counts, uint64_t* __restrict__ cand) {
-  __shared__ uint32_t sh[48];
-  const int tid = threadIdx.x, tl = blockIdx.y, s = blockIdx.x;
-  const uint32_t* st = state + 4 * tl;
-  if (st[0] != kLongCand) return;  // (uniform over the workgroup)
-  const uint32_t thr = st[1] << 21;
-  const int n = row_len(bt, t_begin + tl);
-  const float* row = scores + (int64_t)tl * ld;
-  uint64_t* out = cand + (int64_t)tl * kLongCap;
-  const int p0 = s * slice, p1 = min(n, p0 + slice);
-  // this slice's offset: the candidates of the slices before it (s < 1024 threads)
-  uint32_t base;
-  block_excl_scan(tid < s ? counts[(int64_t)tl * kLongSlices + tid] : 0u, sh, base);
-  const int iters = p1 > p0 ? (p1 - p0 + 4095) / 4096 : 0;
-  for (int it = 0; it < iters; ++it) {
-    const int p = p0 + 4096 * it + 4 * tid;
-    uint32_t key[4];
-    long_keys4(row, p, p1, key);
-    uint32_t c = 0u;
+  for (int i = 0; i < 4; ++i) {
+    const int p = pl + 256 * i;
+    float x[4];
+    if (p + 3 < n) {
+      const float4 f = *(const float4*)(row + p);
+      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) c += key[e] >= thr && key[e] != 0u ? 1u : 0u;
-    __syncthreads();  // (sh of the previous scan has been read)
-    uint32_t tot;
-    uint32_t o = base + block_excl_scan(c, sh, tot);
+      for (int e = 0; e < 4; ++e) x[e] = p + e < n ? row[p + e] : __uint_as_float(0x7fc00000u);
+    }
+    bits[i] = 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (key[e] >= thr && key[e] != 0u) {
-        if (o < (uint32_t)kLongCap) out[o] = ((uint64_t)key[e] << 32) | (uint32_t)(p + e);
+      bits[i] |= (x[e] >= tf ? 1u : 0u) << e;
+      xk[i][e] = x[e];
+    }
+    const uint32_t c = __popc(bits[i]);
+    const uint32_t inc = wave_incl_scan(c);
+    ex[i] = inc - c;
+    wb[i] = wtot;
+    wtot += __builtin_amdgcn_readlane(inc, 63);
+  }
+  if (lane == 0) wt[wave] = wtot;
+  __syncthreads();
+  const uint32_t ws = wave_incl_scan(lane < 16 ? wt[lane] : 0u);
+  const uint32_t before = wave ? __builtin_amdgcn_readlane(ws, wave - 1) : 0u;
+  const uint32_t total = __builtin_amdgcn_readlane(ws, 15);
+  if (tid == 0) base_sh = total ? atomicAdd(&s[2], total) : 0u;
+  __syncthreads();
+  const uint32_t base = base_sh;
+  if (tid == 0) {
+    so[0] = base;
+    so[1] = total;
+  }
+  uint64_t* cl = cand + (int64_t)tl * kLongCap;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t o = base + before + wb[i] + ex[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((bits[i] >> e) & 1u) {
+        if (o < (uint32_t)kLongCap)
+          cl[o] = ((uint64_t)order_key(xk[i][e]) << 32) | (uint32_t)(pl + 256 * i + e);
         ++o;
       }
-    }
-    base += tot;
   }
 }
 
 __global__ __launch_bounds__(1024) void topk_long_final_kernel(DevBatch bt, int t_begin,
-    const float* __restrict__ scores, int64_t ld, int K, const uint32_t* __restrict__ state,
+    const float* __restrict__ scores, int64_t ld, int K, int nsl,
+    const uint32_t* __restrict__ state, const uint32_t* __restrict__ slices,
     const uint64_t* __restrict__ cand, int32_t* __restrict__ out_idx,
     float* __restrict__ out_val) {
   extern __shared__ __attribute__((aligned(16))) char smraw[];
-  SelSmem& S = *(SelSmem*)smraw;
-  const int tid = threadIdx.x, tl = blockIdx.x;
+  constexpr int E = kLongCap / 1024;
+  StreamLds& S = *(StreamLds*)smraw;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tl = blockIdx.x;
   const int t = t_begin + tl;
-  const uint32_t* st = state + 4 * tl;
-  // the list, 8 consecutive entries per thread (position order), requested with the state
-  // (entries past the list's end are not used)
-  uint64_t cv[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) cv[j] = cand[(int64_t)tl * kLongCap + 8 * tid + j];
-  const uint32_t mode = st[0];
-  if (mode == kLongOver) return;
+  const int n = row_len(bt, t);
   const float* row = scores + (int64_t)tl * ld;
   int32_t* oi = out_idx + (int64_t)t * K;
   float* ov = out_val ? out_val + (int64_t)t * K : nullptr;
-  if (mode == kLongAll) {
-    const int n = row_len(bt, t);
+  const uint32_t* s = state + 4 * tl;
+  if (s[0] == kLongAll) {
     for (int i = tid; i < K; i += 1024) {
       oi[i] = i < n ? i : -1;
       if (ov) ov[i] = i < n ? row[i] : 0.f;
     }
     return;
   }
-  // key 0 past the list's end
-  const uint32_t cnt = min(st[2], (uint32_t)kLongCap);
-  uint32_t key[8], pos[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint64_t c = 8u * tid + j < cnt ? cv[j] : 0ull;
-    key[j] = (uint32_t)(c >> 32);
-    pos[j] = (uint32_t)c;
+  const uint32_t tlo = s[1], C = s[2];
+  if (C < (uint32_t)K || C > (uint32_t)kLongCap) {  // (many equal scores: the exact select)
+    select_streamed(row, n, K, K, smraw, oi, ov);
+    return;
   }
-  // the keys above the picked bin are all taken; the rest come from within it
-  uint32_t krem = (uint32_t)K - st[3];
-  const uint32_t T = radix_select(st[1] << 21, 21, krem, S, [&](auto&& f) {
+  // list entries E*tid .. E*tid + E - 1 of the slices' candidates in slice (= position)
+  // order, 1024 slices at a time: the slices' source offsets and destinations are staged in
+  // hA, and each entry of the group finds its slice by binary search over the destinations
+  // (all of a thread's loads in flight together)
+  uint32_t* src = S.hA;
+  uint32_t* dst = S.hA + 1024;
+  uint32_t lk[E], lp[E];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (key[j] != 0u) f(key[j]);
-  });
-  uint32_t gt = 0u, eq = 0u;
+  for (int e = 0; e < E; ++e) lk[e] = lp[e] = 0u;  // (key 0 past the list)
+  uint32_t run = 0u;
+  for (int g = 0; g < nsl; g += 1024) {
+    const int sl = g + tid;
+    const uint32_t* so = slices + ((int64_t)tl * nsl + sl) * 2;
+    const uint32_t c = sl < nsl ? so[1] : 0u;
+    const uint32_t o = sl < nsl ? so[0] : 0u;
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan(c, S.sh, tot);
+    src[tid] = o;
+    dst[tid] = run + pre;
+    __syncthreads();
+    const int ng = min(1024, nsl - g);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    gt += key[j] > T ? 1u : 0u;
-    eq += key[j] == T ? 1u : 0u;
-  }
-  uint32_t tot;
-  uint32_t er = block_excl_scan(eq, S.sh, tot);  // ties before this thread's
-  const uint32_t teq = er < krem ? min(eq, krem - er) : 0u;
-  __syncthreads();
-  uint32_t o = block_excl_scan(gt + teq, S.sh, tot);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bool sel = key[j] > T;
-    if (key[j] == T) {
-      sel = er < krem;
-      ++er;
+    for (int e = 0; e < E; ++e) {
+      const uint32_t d = (uint32_t)(E * tid + e);
+      if (d >= run && d < run + tot) {
+        int lo = 0, hi = ng - 1;  // the last slice whose destination is <= d
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (dst[mid] <= d) lo = mid;
+          else hi = mid - 1;
+        }
+        const uint32_t q = src[lo] + (d - dst[lo]);
+        if (q < (uint32_t)kLongCap) {
+          const uint64_t pr = cand[(int64_t)tl * kLongCap + q];
+          lk[e] = (uint32_t)(pr >> 32);
+          lp[e] = (uint32_t)pr;
+        }
+      }
     }
-    if (sel && o < (uint32_t)K) {  // (exactly K are selected; the bound keeps it in the row)
-      oi[o] = (int32_t)pos[j];
-      if (ov) ov[o] = key_value(key[j]);  // (the score; -0.0 comes out as +0.0)
-      ++o;
-    }
+    run += tot;
+    __syncthreads();  // (the staging and sh are reused)
   }
+  uint32_t kmn = ~0u, kmx = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) kmx = max(kmx, lk[e]);
+  S.hB[tid] = 0u;
+  S.hB[tid + 1024] = 0u;
+  if (tid < 4) S.cnt[tid] = 0u;
+  block_minmax(kmn, kmx, S.sh + 16);  // (its barrier also publishes the clears)
+  select_listed<E>(lk, lp, tlo, kmx, K, S, oi, ov);
 }
 
 bool topk_long_rows(int max_n, int K) { return max_n > 32768 && K <= kLongCap / 2; }
-constexpr size_t kLongRowBytes = (size_t)kLongCap * 8 + 2048 * 4 + kLongSlices * 4 + 16;
+// long-row workspace per row: the candidate list of (key, position) pairs, state, the slices'
+// (offset, count)
+size_t long_row_bytes(int max_n) {
+  const size_t nsl = ((size_t)max_n + kLongSlice - 1) / kLongSlice;
+  return 8 * (size_t)kLongCap + 16 + 8 * nsl;
+}
 
 // workspace of a launch over up to `rows` rows (any smaller launch fits in it too)
 size_t topk_ws_bytes(int rows, int max_n, int K) {
-  return topk_long_rows(max_n, K) ? (size_t)std::min(rows, kLongRows) * kLongRowBytes : 0;
+  return topk_long_rows(max_n, K) ? (size_t)std::min(rows, kLongRows) * long_row_bytes(max_n)
+                                  : 0;
 }
 
 hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
                        const float* scores, int64_t ld, int K, int32_t* idx, float* val,
                        void* ws, hipStream_t st) {
-  const uint32_t* only = nullptr;
   if (t_count <= kLongRows && topk_long_rows(max_n, K)) {
-    // ws: candidates [t_count][kLongCap] | histograms [t_count][2048] |
-    //     slice counts [t_count][kLongSlices] | state [t_count][4]
+    // ws: candidates [t_count][kLongCap] (key, position) | state [t_count][4] |
+    //     slices [t_count][nsl][2]
+    const int nsl = (max_n + kLongSlice - 1) / kLongSlice;
     uint64_t* cand = (uint64_t*)ws;
-    uint32_t* hist = (uint32_t*)(cand + (size_t)t_count * kLongCap);
-    uint32_t* counts = hist + (size_t)t_count * 2048;
-    uint32_t* state = counts + (size_t)t_count * kLongSlices;
-    // slices of a multiple of 4096 positions, about 1024 workgroups in all (at most
-    // kLongSlices per row)
-    const int S = std::min((max_n + 8191) / 8192, std::max(1, kLongSlices / t_count));
-    const int slice = ((max_n + S - 1) / S + 4095) / 4096 * 4096;
-    const int nsl = (max_n + slice - 1) / slice;
-    hipLaunchKernelGGL(topk_long_zero_kernel, dim3(t_count), dim3(256), 0, st, hist, state);
-    hipLaunchKernelGGL(topk_long_hist_kernel, dim3(nsl, t_count), dim3(256), 0, st, bt, t_begin,
-                       scores, ld, K, slice, hist);
-    hipLaunchKernelGGL(topk_long_pick_kernel, dim3(t_count), dim3(1024), 0, st, bt, t_begin, K,
-                       hist, state);
-    hipLaunchKernelGGL(topk_long_count_kernel, dim3(nsl, t_count), dim3(256), 0, st, bt,
-                       t_begin, scores, ld, slice, state, counts);
-    hipLaunchKernelGGL(topk_long_write_kernel, dim3(nsl, t_count), dim3(1024), 0, st, bt,
-                       t_begin, scores, ld, slice, state, counts, cand);
-    const size_t fshm = sizeof(SelSmem);
+    uint32_t* state = (uint32_t*)(cand + (size_t)t_count * kLongCap);
+    uint32_t* slices = state + 4 * (size_t)t_count;
+    hipLaunchKernelGGL(topk_long_sample_kernel, dim3(t_count), dim3(1024), 0, st, bt, t_begin,
+                       scores, ld, K, state);
+    hipLaunchKernelGGL(topk_long_list_kernel, dim3(nsl, t_count), dim3(1024), 0, st, bt,
+                       t_begin, scores, ld, nsl, state, slices, cand);
+    const size_t fshm = std::max(sizeof(SelSmem), sizeof(StreamLds));
     hipError_t e = hipFuncSetAttribute((const void*)topk_long_final_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)fshm);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_long_final_kernel, dim3(t_count), dim3(1024), fshm, st, bt, t_begin,
-                       scores, ld, K, state, cand, idx, val);
-    only = state;  // the one-workgroup kernel below finishes the rows marked as overflowing
+                       scores, ld, K, nsl, state, slices, cand, idx, val);
+    return hipGetLastError();  // (every row is finished by the final kernel)
   }
   // keys per thread: the smallest power of two (>= 4) that keeps the longest row in registers,
   // up to 32 (32768 positions); longer rows stream through 1024*32-key chunks per pass
@@ -1232,15 +1228,15 @@ hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(t_count), dim3(1024), shm, st, bt, t_begin, scores, ld, K, only,
-                     idx, val);
+  hipLaunchKernelGGL(fn, dim3(t_count), dim3(1024), shm, st, bt, t_begin, scores, ld, K, idx,
+                     val);
   if (max_n > 1024 * 32) {  // rows longer than one chunk
     const size_t sshm = std::max(sizeof(SelSmem), sizeof(StreamLds));
     e = hipFuncSetAttribute((const void*)topk_stream_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_stream_kernel, dim3(t_count), dim3(1024), sshm, st, bt, t_begin,
-                       scores, ld, K, only, idx, val);
+                       scores, ld, K, idx, val);
   }
   return hipGetLastError();
 }
