@@ -208,6 +208,37 @@ std::vector<Segment> plan_segments(const tis_batch_t* b, int t0, int tc, bool pr
   return segs;
 }
 
+// Pages per wave of the decode scorer over tokens t0 .. t0+tc-1 (a workgroup scores a chunk
+// of 512 * np keys of one token, one workgroup per compute unit at a time): of 8, 16 and 32,
+// the one with the fewest rounds of workgroups over the 256 units, each round costing its
+// chunk plus the workgroup's set-up (the request lookup, the query quantisation and the
+// filling of the page ring, about two pages per wave).  Few long rows thus take large chunks
+// and pay the set-up once per chunk instead of once per 4,096 keys, while batches whose
+// 4,096-key chunks already fill the chip keep them.  (The kernel takes up to 64; 32 already
+// brings the set-up below 6% of a workgroup's time.)
+int decode_pages_per_wave(const tis_batch_t* b, int t0, int tc) {
+  constexpr int kUnits = 256, kSetup = 2;
+  int best = 8;
+  int64_t best_cost = INT64_MAX;
+  for (int np = 8; np <= 32; np *= 2) {
+    const int64_t ck = 512 * (int64_t)np;
+    int64_t units = 0;
+    for (int r = 0; r < b->B; ++r) {
+      const int a = std::max(b->cu_q_host[r], t0), e = std::min(b->cu_q_host[r + 1], t0 + tc);
+      for (int t = a; t < e; ++t) {
+        const int64_t n = (int64_t)b->seq_lens_host[r] - (b->cu_q_host[r + 1] - t) + 1;
+        units += (n + ck - 1) / ck;
+      }
+    }
+    const int64_t cost = (units + kUnits - 1) / kUnits * (np + kSetup);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = np;
+    }
+  }
+  return best;
+}
+
 // block: one score per 64-key page (rows of ld entries) instead of one per key; the fp32
 // scorer has no block form (callers check).  Rows of scores are those of tokens t0 .. t0+tc-1.
 tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath path, int t0,
@@ -223,7 +254,8 @@ tis_status_t run_index(const tis_batch_t* batch, const HostInfo& hi, IdxPath pat
   }
   for (const Segment& sg : plan_segments(batch, t0, tc, hi.prefill_like)) {
     if (sg.max_n < 1) continue;
-    e = tis::launch_index_score_fp8(d, sg.t0, sg.tc, sg.max_n, hi.prefill_like,
+    const int np = hi.prefill_like ? 0 : decode_pages_per_wave(batch, sg.t0, sg.tc);
+    e = tis::launch_index_score_fp8(d, sg.t0, sg.tc, sg.max_n, hi.prefill_like, np,
                                     path == IdxPath::BF16 ? 1 : path == IdxPath::MX ? 2 : 0,
                                     block, (const uint16_t*)q_idx, w, (const uint8_t*)k_pool,
                                     k_scale, scores + (int64_t)(sg.t0 - t0) * ld, ld, st);

@@ -197,6 +197,8 @@ struct KTile4 {
 // One 8 KB page of keys (64 rows of 128 bytes) in eight non-temporal loads of 1 KB each:
 // load i, lane l gets bytes [1024i + 16l, +16), i.e. row 8i + (l >> 3), bytes 16(l & 7)...
 // (whole rows per instruction stream better than the MFMA layout's 64-byte half rows).
+// Cache-policy bits of a buffer load: the non-temporal bit, as __builtin_nontemporal_load sets it.
+constexpr int kAuxNT = 2;
 struct KPage {
   i32x4 r[8];
 };
@@ -204,6 +206,14 @@ __device__ __forceinline__ void load_kpage(const uint8_t* page_base, int lane, K
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     kp.r[i] = __builtin_nontemporal_load((const i32x4*)(page_base + 1024 * i + 16 * lane));
+}
+
+// The same eight loads through a buffer resource based at the page (offsets past its record
+// count read nothing and return zeros); non-temporal, as above.
+__device__ __forceinline__ void load_kpage_rsrc(__amdgpu_buffer_rsrc_t r, int lane, KPage& kp) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    kp.r[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 1024 * i + 16 * lane, 0, kAuxNT));
 }
 
 // Rows of the wave's LDS staging buffer are kPitch bytes apart, so that the sixteen rows read
@@ -352,10 +362,12 @@ __device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp
   else return r * ks;
 }
 
-// Decode scoring: one token per workgroup (blockIdx.x) and key chunk blockIdx.y of 64 pages;
-// the pages are dealt round-robin to the eight waves (wave w scores pages w, w+8, ... of the
-// chunk), so that at each step the workgroup reads 64 KB of consecutive pages when the
-// request's pages are consecutive.
+// Decode scoring: one token per workgroup (blockIdx.x) and key chunk blockIdx.y of 8 * np pages
+// (np pages per wave, np <= 64); the pages are dealt round-robin to the eight waves (wave w
+// scores pages w, w+8, ... of the chunk), so that at each step the workgroup reads 64 KB of
+// consecutive pages when the request's pages are consecutive.  The host picks np so that the
+// grid still covers the chip: long rows at few tokens take large chunks, which pays the
+// token's set-up (request lookup, query quantisation, filling the page ring) once per chunk.
 // (kernel signatures name no type that depends on the mode: the key scales come in untyped)
 // BLK: block-granular scoring: instead of one score per key, one per 64-key page, the largest
 // score among the page's causal keys (-inf for a page whose table entry is out of range),
@@ -363,7 +375,7 @@ __device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp
 template <int QM, bool BLK>
 __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
-    const void* kscale_raw, float* __restrict__ scores, int64_t ld, int chunk) {
+    const void* kscale_raw, float* __restrict__ scores, int64_t ld, int np) {
   constexpr bool BQ = QM == kQBf16;
   const KScale<QM>* kscale = (const KScale<QM>*)kscale_raw;
   // (the wave index through readfirstlane, so that the ranges derived from it are scalars)
@@ -371,19 +383,21 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
   constexpr int kStep = 8;  // page stride of a wave within the chunk
   const int tl = blockIdx.x;
   const int poff = wave;    // the wave's first page within the chunk
+  const int chunk = 64 * kStep * np;
   const int k0 = blockIdx.y * chunk;
   if (tl >= t_count) return;  // (the same for every wave of the workgroup)
   const int t = t_begin + tl;
-  // Page ids of the chunk, one per lane, fetched once (a scalar page-table load per page
-  // would stall every prefetch on a scalar round trip).  Everything waits on them, so they
-  // are requested first, together with the token's request lookup, for request min(t, B - 1)
-  // (the request of token t when every request has one token), and again if that was not it.
-  // The query goes out behind them (loads complete in issue order, so the first pages need
-  // not wait for it).  The eight waves share the token, so waves 0..3 each quantise one
-  // 16-head tile and hand it over through LDS (every wave loads tile wave & 3: a load under a
-  // branch would make the compiler wait for the query before the first pages).
+  // The wave's page ids, lane g holding that of its page g (chunk page poff + 8g), fetched
+  // once (a scalar page-table load per page would stall every prefetch on a scalar round
+  // trip).  Everything waits on them, so they are requested first, together with the token's
+  // request lookup, for request min(t, B - 1) (the request of token t when every request has
+  // one token), and again if that was not it.  The query goes out behind them (loads complete
+  // in issue order, so the first pages need not wait for it).  The eight waves share the
+  // token, so waves 0..3 each quantise one 16-head tile and hand it over through LDS (every
+  // wave loads tile wave & 3: a load under a branch would make the compiler wait for the
+  // query before the first pages).
   const int pg0 = k0 >> 6;
-  const int pcol = min(pg0 + lane, bt.pt_stride - 1);
+  const int pcol = min(pg0 + poff + kStep * min(lane, np - 1), bt.pt_stride - 1);
   const int bguess = min(t, bt.B - 1);
   int my_page = bt.page_table[(int64_t)bguess * bt.pt_stride + pcol];
   const LocLoads lw = locate_issue(bt);
@@ -395,48 +409,44 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
   a0_load_tile(qrow, wrow, lane, wave & 3, qr, qw);
   const TokLoc loc = locate_finish(bt, t, lw);
   const int k1 = min(k0 + chunk, loc.n);                 // the chunk's keys in range
-  const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;  // its pages in range (<= 64)
-  const bool active = npg > poff;  // the wave has a page in range
+  const int npg = k0 < k1 ? (k1 - 1 - k0) / 64 + 1 : 0;  // its pages in range (<= 8 np)
+  const int gn = npg > poff ? (npg - poff + kStep - 1) / kStep : 0;  // the wave's, in range
   // A wave with no keys leaves now, unless it quantises a query tile for the others (it
-  // then reads one page of its request and scores nothing).  (An ended wave no longer takes
+  // then scores nothing and its page fetches read nothing).  (An ended wave no longer takes
   // part in the workgroup's barriers.)
-  if (!active && wave >= 4) return;
+  if (gn == 0 && wave >= 4) return;
   if (loc.b != bguess) my_page = bt.page_table[(int64_t)loc.b * bt.pt_stride + pcol];
   float* out = scores + (int64_t)tl * ld;
 
-  // Page g of the wave is page poff + g * kStep of the chunk, g < kPages; it is in range while
-  // that is below npg.  A four-slot ring of pages keeps three in flight while one is scored.
-  // Nothing in the page loop branches around a load or a store (under a branch the compiler
-  // waits for every outstanding load, which would leave one page in flight): a fetch past the
-  // wave's last page re-reads that page, a page past it is not scored, and scores go out
-  // through a buffer resource that ends at the chunk's last key in range, so the hardware
-  // drops stores past it.
-  constexpr int kPages = 8;
-  auto page_id = [&](int g) {
-    return __builtin_amdgcn_readlane(my_page, npg > 0 ? min(poff + g * kStep, npg - 1) : 0);
-  };
+  // Page g of the wave is in range while g < gn.  A four-slot ring of pages keeps three in
+  // flight while one is scored.  Nothing in the page loop branches around a load or a store
+  // (under a branch the compiler waits for every outstanding load, which would leave one page
+  // in flight): a page and its key scales are fetched through buffer resources whose record
+  // count is zero past the wave's last page (or for a table entry out of range), so those
+  // fetches return zeros without reading memory, and scores go out through a buffer resource
+  // that ends at the chunk's last key in range, so the hardware drops stores past it.
   struct Slot {
     KPage kp;
+    KScale<QM> ks;
     bool ok;
   };
-  // the key scales of all eight pages go out first (one short stream of small reads, ahead of
-  // the pages, so that waiting for a scale never waits for a page)
-  KScale<QM> ks[kPages];
   auto fetch = [&](int g, Slot& sl) {
-    const int page = page_id(g);
+    const int page = __builtin_amdgcn_readlane(my_page, g & 63);
     sl.ok = page >= 0 && page < bt.n_pages;
-    const int64_t pg = sl.ok ? page : 0;
-    load_kpage(kpool + pg * kPage * kID, lane, sl.kp);
+    const bool on = sl.ok && g < gn;
+    const int64_t pg = on ? page : 0;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kpool + pg * kPage * kID), 0, on ? kPage * kID : 0, kBufDword3);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kscale + pg * kPage), 0, on ? kPage * (int)sizeof(KScale<QM>) : 0, kBufDword3);
+    // (the key scale first: one short read ahead of the page's eight, so that waiting for a
+    // scale never waits for a page)
+    sl.ks = __builtin_bit_cast(KScale<QM>, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * lane, 0, 0));
+    load_kpage_rsrc(kr, lane, sl.kp);
   };
-#pragma unroll
-  for (int g = 0; g < kPages; ++g) {
-    const int page = page_id(g);
-    ks[g] = kscale[(int64_t)(page >= 0 && page < bt.n_pages ? page : 0) * kPage + lane];
-  }
-  asm volatile("" ::: "memory");
-  // (kept in this order by the empty asm statements, which the key loads cannot cross as the
-  // key pointers are not marked restrict: each wait in the loop counts the loads issued after
-  // the page it waits for, and one moved behind later pages would make it wait for those too)
+  // (kept in this order by the empty asm statements: each wait in the loop counts the loads
+  // issued after the page it waits for, and one moved behind later pages would make it wait
+  // for those too)
   Slot sl[4];
 #pragma unroll
   for (int g = 0; g < 3; ++g) {
@@ -476,7 +486,7 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
       w_sh[wave][lane] = f32x4{wt[0], wt[1], wt[2], wt[3]};
     }
     __syncthreads();
-    if (!active) return;
+    if (gn == 0) return;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       if constexpr (BQ) {
@@ -495,17 +505,14 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
   // stores at byte offset 4*s of the row, kept for s < k1 (BLK: 4*page, for pages below k1)
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       out, 0, BLK ? ((k1 + 63) >> 6) * 4 : k1 * 4, kBufDword3);
-  // page g from ring slot u: fetch page g + 3 into the slot freed last (if there is more to
-  // fetch), then score page g
-  auto step = [&](int g, int u, bool more, KScale<QM> scale) {
-    if (more) {
-      fetch(g + 3, sl[(u + 3) & 3]);
-      asm volatile("" ::: "memory");  // (the loads go out before this page is scored)
-    }
+  // page g from ring slot u: fetch page g + 3 into the slot freed last, then score page g
+  auto step = [&](int g, int u) {
+    fetch(g + 3, sl[(u + 3) & 3]);
+    asm volatile("" ::: "memory");  // (the loads go out before this page is scored)
     const Slot& c = sl[u];
     KTile4 kt;
     stage_ktile4(stage, lane, c.kp, kt);
-    float sc = score_group<QM>(A, wp, kt, scale);
+    float sc = score_group<QM>(A, wp, kt, c.ks);
     if (!c.ok) sc = -INFINITY;
     const int pos = k0 + 64 * (poff + g * kStep) + lane;
     if constexpr (BLK) {
@@ -518,11 +525,13 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), orsrc, pos * 4, 0, 0);
     }
   };
-  // eight pages, unrolled in full: straight-line code, whose only exit ends the kernel
+  // four pages per iteration, so that every ring slot is a fixed register set.  The loop has
+  // one exit, at its end (an exit between its pages would make the compiler's wait insertion
+  // assume that path could loop as well, and wait for a page more); the pages of the last
+  // iteration past the wave's range read nothing and store nothing.
+  for (int g0 = 0; g0 < gn; g0 += 4) {
 #pragma unroll
-  for (int g = 0; g < kPages; ++g) {
-    if (poff + g * kStep >= npg) return;
-    step(g, g & 3, g + 3 < kPages, ks[g]);  // (g is a constant here)
+    for (int u = 0; u < 4; ++u) step(g0 + u, u);
   }
 }
 
@@ -674,51 +683,53 @@ hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, 
 
 template <int QM, bool BLK>
 static hipError_t launch_mma(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                             bool prefill_like, const uint16_t* q_idx, const float* w,
+                             bool prefill_like, int np, const uint16_t* q_idx, const float* w,
                              const uint8_t* kpool, const void* kscale, float* scores, int64_t ld,
                              hipStream_t st) {
-  const int chunk = prefill_like ? 1024 : 4096;
-  // decode: one 8-wave workgroup per 4096-key chunk of a token (512 keys per wave); prefill:
-  // four tokens per 4-wave workgroup sharing a 1024-key chunk
+  // decode: one 8-wave workgroup per chunk of 512 * np keys of a token (64 np keys per wave);
+  // prefill: four tokens per 4-wave workgroup sharing a 1024-key chunk
   if (prefill_like) {
+    const int chunk = 1024;
     dim3 grid((t_count + 3) / 4, (max_n + chunk - 1) / chunk);
     auto* gfn = idx_score_group_kernel<QM, BLK>;
     hipLaunchKernelGGL(gfn, grid, dim3(256), 0, st, bt, t_begin, t_count,
                        q_idx, w, kpool, kscale, scores, ld);
     return hipGetLastError();
   }
+  if (np < 1 || np > 64) return hipErrorInvalidValue;  // (lane g holds page g of a wave)
+  const int chunk = 512 * np;
   dim3 grid(t_count, (max_n + chunk - 1) / chunk);
   auto* fn = idx_score_fp8_kernel<QM, BLK>;
   hipLaunchKernelGGL(fn, grid, dim3(512), 0, st, bt, t_begin, t_count,
-                     q_idx, w, kpool, kscale, scores, ld, chunk);
+                     q_idx, w, kpool, kscale, scores, ld, np);
   return hipGetLastError();
 }
 
 template <bool BLK>
 static hipError_t launch_mode(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                              bool prefill_like, int qmode, const uint16_t* q_idx,
+                              bool prefill_like, int np, int qmode, const uint16_t* q_idx,
                               const float* w, const uint8_t* kpool, const void* kscale,
                               float* scores, int64_t ld, hipStream_t st) {
   switch (qmode) {
     case kQBf16:
-      return launch_mma<kQBf16, BLK>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w,
+      return launch_mma<kQBf16, BLK>(bt, t_begin, t_count, max_n, prefill_like, np, q_idx, w,
                                      kpool, kscale, scores, ld, st);
     case kQMx:
-      return launch_mma<kQMx, BLK>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w, kpool,
+      return launch_mma<kQMx, BLK>(bt, t_begin, t_count, max_n, prefill_like, np, q_idx, w, kpool,
                                    kscale, scores, ld, st);
     default:
-      return launch_mma<kQFp8, BLK>(bt, t_begin, t_count, max_n, prefill_like, q_idx, w,
+      return launch_mma<kQFp8, BLK>(bt, t_begin, t_count, max_n, prefill_like, np, q_idx, w,
                                     kpool, kscale, scores, ld, st);
   }
 }
 
 hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, int qmode, bool block, const uint16_t* q_idx,
+                                  bool prefill_like, int np, int qmode, bool block, const uint16_t* q_idx,
                                   const float* w, const uint8_t* kpool, const void* kscale,
                                   float* scores, int64_t ld, hipStream_t st) {
-  return block ? launch_mode<true>(bt, t_begin, t_count, max_n, prefill_like, qmode, q_idx, w,
+  return block ? launch_mode<true>(bt, t_begin, t_count, max_n, prefill_like, np, qmode, q_idx, w,
                                    kpool, kscale, scores, ld, st)
-               : launch_mode<false>(bt, t_begin, t_count, max_n, prefill_like, qmode, q_idx, w,
+               : launch_mode<false>(bt, t_begin, t_count, max_n, prefill_like, np, qmode, q_idx, w,
                                     kpool, kscale, scores, ld, st);
 }
 

@@ -14,8 +14,9 @@ hipError_t launch_index_score_f32(const DevBatch& bt, int t_begin, int t_count, 
 // qmode: 0 = e4m3 query with per-head scales (per-token fp32 key scales), 1 = bf16 query
 // (per-token fp32 key scales), 2 = MXFP8 query and keys (kscale: four scale bytes per key).
 // block: one score per 64-key page (the largest causal key score) instead of one per key.
+// np (decode only, 1..64): key pages per wave of a workgroup's chunk (512 * np keys).
 hipError_t launch_index_score_fp8(const DevBatch& bt, int t_begin, int t_count, int max_n,
-                                  bool prefill_like, int qmode, bool block, const uint16_t* q_idx,
+                                  bool prefill_like, int np, int qmode, bool block, const uint16_t* q_idx,
                                   const float* w, const uint8_t* kpool, const void* kscale,
                                   float* scores, int64_t ld, hipStream_t st);
 hipError_t launch_topk(const DevBatch& bt, int t_begin, int t_count, int max_n,
