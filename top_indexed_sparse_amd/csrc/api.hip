@@ -149,9 +149,10 @@ struct Segment {
 };
 
 std::vector<Segment> plan_segments(const tis_batch_t* b, int t0, int tc, bool prefill_like) {
-  const int tok = prefill_like ? 4 : 1;         // tokens per unit
-  const int chunk = prefill_like ? 1024 : 4096;  // keys per unit
-  constexpr double kLaunchUnits = 3000.0;       // a launch's fixed cost, in units
+  const int tok = prefill_like ? 4 : 1;  // tokens per unit
+  const int chunk = 4096;                // keys per unit
+  // a launch's fixed cost, in units (a prefill unit scores four tokens)
+  const double kLaunchUnits = prefill_like ? 750.0 : 3000.0;
   if (tc < 1) return {};
   // intervals between consecutive cut points lie within one request; each interval's longest
   // causal length is that of its last token

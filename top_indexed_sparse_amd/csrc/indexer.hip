@@ -216,26 +216,38 @@ __device__ __forceinline__ void load_kpage_rsrc(__amdgpu_buffer_rsrc_t r, int la
     kp.r[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 1024 * i + 16 * lane, 0, kAuxNT));
 }
 
-// Rows of the wave's LDS staging buffer are kPitch bytes apart, so that the sixteen rows read
-// by one MFMA-layout load fall on distinct banks.
-constexpr int kPitch = 144;
-constexpr int kStage = 64 * kPitch;  // bytes per wave
+// A key page in LDS: 64 rows of 128 bytes, the 16-byte column c of row r stored at column
+// c ^ ((r >> 1) & 7).  With 64 banks of 4 bytes, each 16-lane quarter of a 16-byte access
+// covers 256 bytes: a quarter of a row write (two rows, all eight columns) and of a
+// matrix-layout read (sixteen rows, one column each) then falls on 64 distinct banks.
+constexpr int kRowB = 128;
+constexpr int kStage = 64 * kRowB;  // bytes per page
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + 16 * (c ^ ((r >> 1) & 7)); }
 
-// Through the wave's own staging buffer into the MFMA B layout: lane (n = l & 15, g = l >> 4)
-// takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row 16j + n.  (LDS operations of one
-// wave complete in order, so the buffer can be rewritten by the next group without a wait.)
-__device__ __forceinline__ void stage_ktile4(uint8_t* stage, int lane, const KPage& kp,
-                                             KTile4& kt) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *(i32x4*)(stage + (8 * i + (lane >> 3)) * kPitch + 16 * (lane & 7)) = kp.r[i];
+// load i of a page (see load_kpage) into the page buffer: lane l holds row 8i + (l >> 3),
+// column l & 7
+__device__ __forceinline__ void put_load(uint8_t* st, int i, int lane, i32x4 v) {
+  *(i32x4*)(st + swz(8 * i + (lane >> 3), lane & 7)) = v;
+}
+
+// The four 16-key tiles of a page buffer in the MFMA B layout: lane (n = l & 15, g = l >> 4)
+// takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row 16j + n.
+__device__ __forceinline__ void read_ktile4(const uint8_t* st, int lane, KTile4& kt) {
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint8_t* row = stage + (16 * j + n) * kPitch;
-    kt.lo[j] = *(const i32x4*)(row + 16 * g);
-    kt.hi[j] = *(const i32x4*)(row + 64 + 16 * g);
+    kt.lo[j] = *(const i32x4*)(st + swz(16 * j + n, g));
+    kt.hi[j] = *(const i32x4*)(st + swz(16 * j + n, 4 + g));
   }
+}
+
+// Through the wave's own page buffer into the MFMA B layout.  (LDS operations of one wave
+// complete in order, so the buffer can be rewritten by the next page without a wait.)
+__device__ __forceinline__ void stage_ktile4(uint8_t* stage, int lane, const KPage& kp,
+                                             KTile4& kt) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) put_load(stage, i, lane, kp.r[i]);
+  read_ktile4(stage, lane, kt);
 }
 
 // Query modes of the matrix-core scorer: e4m3 with one power-of-two scale per head folded
@@ -536,7 +548,8 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
 }
 
 // Prefill scoring with shared key pages: four consecutive tokens per 4-wave workgroup (one per
-// wave) over one 1024-key chunk (16 pages).  The tokens of one request read the same pages:
+// wave) over one 4096-key chunk (64 pages, so that the query's load and quantisation are paid
+// once per 64 pages).  The tokens of one request read the same pages:
 // the four waves split each page's eight 1 KB loads (wave w: loads 2w, 2w + 1), write them
 // once into a double-buffered LDS page (one barrier per page, the next page written while the
 // current one is scored), and every wave scores its own token from it, so a page crosses the
@@ -549,7 +562,7 @@ template <int QM, bool BLK>
 __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
     const void* kscale_raw, float* __restrict__ scores, int64_t ld) {
-  constexpr int kChunk = 1024;
+  constexpr int kChunk = 4096;
   const KScale<QM>* kscale = (const KScale<QM>*)kscale_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int tl = blockIdx.x * 4 + wave;
@@ -608,22 +621,27 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
         __builtin_amdgcn_make_buffer_rsrc(out, 0, mine ? rec : 0, kBufDword3);
     const int pcol = min((k0 >> 6) + lane, bt.pt_stride - 1);
     const int my_page = bt.page_table[(int64_t)b * bt.pt_stride + pcol];
-    // (fetches past the last page re-read it: no branch around a load)
+    // (no branch around a load: a page past the range is fetched through buffer resources
+    // whose record count is zero, which return zeros without reading memory)
     auto fetch = [&](int g, Piece& pc) {
-      const int page = __builtin_amdgcn_readlane(my_page, min(g, npg - 1));
+      const int page = __builtin_amdgcn_readlane(my_page, g & 63);
       pc.ok = page >= 0 && page < bt.n_pages;
-      const int64_t pg = pc.ok ? page : 0;
-      const uint8_t* base = kpool + pg * kPage * kID;
-      pc.r[0] = __builtin_nontemporal_load((const i32x4*)(base + 1024 * (2 * wave) + 16 * lane));
-      pc.r[1] = __builtin_nontemporal_load((const i32x4*)(base + 1024 * (2 * wave + 1) + 16 * lane));
-      pc.ks = kscale[pg * kPage + lane];
+      const bool on = pc.ok && g < npg;
+      const int64_t pg = on ? page : 0;
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kpool + pg * kPage * kID), 0, on ? kPage * kID : 0, kBufDword3);
+      const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kscale + pg * kPage), 0, on ? kPage * (int)sizeof(KScale<QM>) : 0, kBufDword3);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        pc.r[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                kr, 1024 * (2 * wave + i) + 16 * lane, 0, kAuxNT));
+      pc.ks = __builtin_bit_cast(KScale<QM>, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * lane, 0, 0));
     };
     // the wave's two loads of a page into its rows of LDS page buffer u
     auto put = [&](int u, const Piece& pc) {
-      uint8_t* st = pg_sh[u];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        *(i32x4*)(st + (8 * (2 * wave + i) + (lane >> 3)) * kPitch + 16 * (lane & 7)) = pc.r[i];
+      for (int i = 0; i < 2; ++i) put_load(pg_sh[u], 2 * wave + i, lane, pc.r[i]);
     };
     Piece ring[4];
 #pragma unroll
@@ -635,25 +653,20 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
     put(0, ring[0]);
     __syncthreads();
     // page g from buffer g & 1 (ring slot g & 3): fetch page g + 3, write page g + 1 into the
-    // other buffer, score page g, wait for every wave
+    // other buffer, score page g, wait for every wave.  Four pages per iteration and one exit,
+    // at its end (an exit between pages would make the compiler's wait insertion assume that
+    // path could loop as well, and drain the ring at every iteration); the last iteration's
+    // pages past the range read nothing and store nothing.
 #pragma unroll 1
     for (int g0 = 0; g0 < npg; g0 += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int g = g0 + u;
-        if (g >= npg) break;  // (uniform; no load or store follows the exit)
         fetch(g + 3, ring[(u + 3) & 3]);
         asm volatile("" ::: "memory");
-        put((g + 1) & 1, ring[(u + 1) & 3]);
-        const uint8_t* st = pg_sh[g & 1];
-        const int n = lane & 15, gg = lane >> 4;
+        put((u + 1) & 1, ring[(u + 1) & 3]);
         KTile4 kt;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint8_t* row = st + (16 * j + n) * kPitch;
-          kt.lo[j] = *(const i32x4*)(row + 16 * gg);
-          kt.hi[j] = *(const i32x4*)(row + 64 + 16 * gg);
-        }
+        read_ktile4(pg_sh[u & 1], lane, kt);
         float sc = score_group<QM>(A, wp, kt, ring[u].ks);
         if (!ring[u].ok) sc = -INFINITY;
         const int pos = k0 + 64 * g + lane;
@@ -687,9 +700,9 @@ static hipError_t launch_mma(const DevBatch& bt, int t_begin, int t_count, int m
                              const uint8_t* kpool, const void* kscale, float* scores, int64_t ld,
                              hipStream_t st) {
   // decode: one 8-wave workgroup per chunk of 512 * np keys of a token (64 np keys per wave);
-  // prefill: four tokens per 4-wave workgroup sharing a 1024-key chunk
+  // prefill: four tokens per 4-wave workgroup sharing a 4096-key chunk
   if (prefill_like) {
-    const int chunk = 1024;
+    const int chunk = 4096;
     dim3 grid((t_count + 3) / 4, (max_n + chunk - 1) / chunk);
     auto* gfn = idx_score_group_kernel<QM, BLK>;
     hipLaunchKernelGGL(gfn, grid, dim3(256), 0, st, bt, t_begin, t_count,
