@@ -310,22 +310,65 @@ __device__ __forceinline__ bf16x8 widen8_bf16(int lo, int hi) {
 // max(0, x) in one instruction (median of x, 0 and the largest float; scores are finite)
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
 
+// The head-weighted ReLU sum of key tile j (16 keys) on the FP8 matrix instruction, from the
+// tile's two 16-byte halves in the MFMA B layout (lo: bytes [16g, 16g+16) of row 16j + n, hi:
+// bytes [64+16g, 64+16g+16)).  The four head tiles' products go out before the first is read
+// (one accumulator reused would make each wait for the previous one's result).  MXFP8: the B
+// block-scale byte of lane (n, g) is group g of key 16j + n.
+template <int QM>
+__device__ __forceinline__ float fp8_tile_sum(const QOps<QM>& A, const float (&wp)[4][4],
+                                              i32x4 lo, i32x4 hi, KScale<QM> ks, int j) {
+  const int lane = threadIdx.x & 63;
+  const i32x8 B = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  int sb = 0;
+  if constexpr (QM == kQMx)
+    sb = __builtin_amdgcn_ubfe((uint32_t)__shfl((int)ks, 16 * j + (lane & 15)), 8 * (lane >> 4),
+                               8);
+  f32x4 c[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    c[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (QM == kQMx)
+      c[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c[m], 0, 0, 0, A.sa[m],
+                                                              0, sb);
+    else
+      c[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c[m], 0, 0, 0, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float acc = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], relu(c[m][i]), acc);
+  return acc;
+}
+
+// Head sum over g and 4x4 transpose of the four tiles' partial sums: lane l ends with the score
+// of key 16 (l >> 4) + (l & 15), times the key's scale (MXFP8: its scales entered the products).
+template <int QM>
+__device__ __forceinline__ float group_finish(const float (&v)[4], KScale<QM> ks) {
+  float k0 = pair32_sum(v[0], v[2]);
+  float k1 = pair32_sum(v[1], v[3]);
+  const float r = pair16_sum(k0, k1);
+  if constexpr (QM == kQMx) return r;
+  else return r * ks;
+}
+
 // Scores of the 64 keys of one page-aligned group; lane l returns key base + l, times the
 // key's scale word ks (the key's fp32 scale; MXFP8: its scale bytes enter the products).
 template <int QM>
 __device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp)[4][4],
                                              const KTile4& kt, KScale<QM> ks) {
-  const int lane = threadIdx.x & 63;
   float v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float acc = 0.f;
     if constexpr (QM == kQBf16) {
       bf16x8 B[4];
       B[0] = widen8_bf16(kt.lo[j][0], kt.lo[j][1]);
       B[1] = widen8_bf16(kt.lo[j][2], kt.lo[j][3]);
       B[2] = widen8_bf16(kt.hi[j][0], kt.hi[j][1]);
       B[3] = widen8_bf16(kt.hi[j][2], kt.hi[j][3]);
+      float acc = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -336,42 +379,27 @@ __device__ __forceinline__ float score_group(const QOps<QM>& A, const float (&wp
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], relu(c[i]), acc);
       }
+      v[j] = acc;
     } else {
-      i32x8 B;
-      B[0] = kt.lo[j][0]; B[1] = kt.lo[j][1]; B[2] = kt.lo[j][2]; B[3] = kt.lo[j][3];
-      B[4] = kt.hi[j][0]; B[5] = kt.hi[j][1]; B[6] = kt.hi[j][2]; B[7] = kt.hi[j][3];
-      // MXFP8: the B block-scale byte of lane (n, g) is group g of key 16j + n
-      int sb = 0;
-      if constexpr (QM == kQMx)
-        sb = __builtin_amdgcn_ubfe(
-            (uint32_t)__shfl((int)ks, 16 * j + (lane & 15)), 8 * (lane >> 4), 8);
-      // the four head tiles' products are independent: all four go out before the first is
-      // read (one accumulator reused would make each wait for the previous one's result)
-      f32x4 c[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        c[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (QM == kQMx)
-          c[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c[m], 0, 0, 0,
-                                                                  A.sa[m], 0, sb);
-        else
-          c[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A.a[m], B, c[m], 0, 0, 0, 0,
-                                                                  0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(wp[m][i], relu(c[m][i]), acc);
+      v[j] = fp8_tile_sum<QM>(A, wp, kt.lo[j], kt.hi[j], ks, j);
     }
-    v[j] = acc;
   }
-  // head sum over g and 4x4 transpose: lane l ends with tile (l >> 4), key (l & 15)
-  float k0 = pair32_sum(v[0], v[2]);
-  float k1 = pair32_sum(v[1], v[3]);
-  const float r = pair16_sum(k0, k1);
-  if constexpr (QM == kQMx) return r;
-  else return r * ks;
+  return group_finish<QM>(v, ks);
+}
+
+// The same for an FP8 mode straight from a page buffer in LDS, each key tile read just before
+// its products (the four tiles held at once would cost 24 more registers per lane).
+template <int QM>
+__device__ __forceinline__ float score_group_lds(const QOps<QM>& A, const float (&wp)[4][4],
+                                                 const uint8_t* st, KScale<QM> ks) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    v[j] = fp8_tile_sum<QM>(A, wp, *(const i32x4*)(st + swz(16 * j + n, g)),
+                            *(const i32x4*)(st + swz(16 * j + n, 4 + g)), ks, j);
+  return group_finish<QM>(v, ks);
 }
 
 // Decode scoring: one token per workgroup (blockIdx.x) and key chunk blockIdx.y of 8 * np pages
@@ -558,8 +586,10 @@ __global__ __launch_bounds__(512) void idx_score_fp8_kernel(DevBatch bt, int t_b
 // different requests are scored in one pass per request (every wave loads and waits in every
 // pass; a wave stores only in its own request's pass, through a buffer resource whose record
 // count is zero otherwise).  A wave without a token (the batch's last group) only loads.
+// (FP8 modes: at most 128 registers, four waves per SIMD, so that one wave's vector epilogue
+// overlaps another's matrix products; the bf16 query mode needs more)
 template <int QM, bool BLK>
-__global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t_begin,
+__global__ __launch_bounds__(256, QM == kQBf16 ? 1 : 4) void idx_score_group_kernel(DevBatch bt, int t_begin,
     int t_count, const uint16_t* q_idx, const float* w, const uint8_t* kpool,
     const void* kscale_raw, float* __restrict__ scores, int64_t ld) {
   constexpr int kChunk = 4096;
@@ -665,9 +695,14 @@ __global__ __launch_bounds__(256) void idx_score_group_kernel(DevBatch bt, int t
         fetch(g + 3, ring[(u + 3) & 3]);
         asm volatile("" ::: "memory");
         put((u + 1) & 1, ring[(u + 1) & 3]);
-        KTile4 kt;
-        read_ktile4(pg_sh[u & 1], lane, kt);
-        float sc = score_group<QM>(A, wp, kt, ring[u].ks);
+        float sc;
+        if constexpr (QM == kQBf16) {
+          KTile4 kt;
+          read_ktile4(pg_sh[u & 1], lane, kt);
+          sc = score_group<QM>(A, wp, kt, ring[u].ks);
+        } else {
+          sc = score_group_lds<QM>(A, wp, pg_sh[u & 1], ring[u].ks);
+        }
         if (!ring[u].ok) sc = -INFINITY;
         const int pos = k0 + 64 * g + lane;
         if constexpr (BLK) {
