@@ -194,26 +194,23 @@ struct KTile4 {
   i32x4 lo[4], hi[4];
 };
 
-// One 8 KB page of keys (64 rows of 128 bytes) in eight non-temporal loads of 1 KB each:
-// load i, lane l gets bytes [1024i + 16l, +16), i.e. row 8i + (l >> 3), bytes 16(l & 7)...
-// (whole rows per instruction stream better than the MFMA layout's 64-byte half rows).
-// Cache-policy bits of a buffer load: the non-temporal bit, as __builtin_nontemporal_load sets it.
+// Cache-policy bits of a buffer load: the non-temporal bit (the one __builtin_nontemporal_load
+// sets).
 constexpr int kAuxNT = 2;
+
+// One 8 KB page of keys (64 rows of 128 bytes) in eight non-temporal loads of 1 KB each,
+// through a buffer resource based at the page (offsets past its record count read nothing and
+// return zeros): load i, lane l gets bytes [1024i + 16l, +16), i.e. row 8i + (l >> 3), bytes
+// 16(l & 7)... (whole rows per instruction stream better than the MFMA layout's 64-byte half
+// rows).
 struct KPage {
   i32x4 r[8];
 };
-__device__ __forceinline__ void load_kpage(const uint8_t* page_base, int lane, KPage& kp) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    kp.r[i] = __builtin_nontemporal_load((const i32x4*)(page_base + 1024 * i + 16 * lane));
-}
-
-// The same eight loads through a buffer resource based at the page (offsets past its record
-// count read nothing and return zeros); non-temporal, as above.
 __device__ __forceinline__ void load_kpage_rsrc(__amdgpu_buffer_rsrc_t r, int lane, KPage& kp) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    kp.r[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 1024 * i + 16 * lane, 0, kAuxNT));
+    kp.r[i] = __builtin_bit_cast(
+        i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 1024 * i + 16 * lane, 0, kAuxNT));
 }
 
 // A key page in LDS: 64 rows of 128 bytes, the 16-byte column c of row r stored at column
@@ -224,7 +221,7 @@ constexpr int kRowB = 128;
 constexpr int kStage = 64 * kRowB;  // bytes per page
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowB + 16 * (c ^ ((r >> 1) & 7)); }
 
-// load i of a page (see load_kpage) into the page buffer: lane l holds row 8i + (l >> 3),
+// load i of a page (see load_kpage_rsrc) into the page buffer: lane l holds row 8i + (l >> 3),
 // column l & 7
 __device__ __forceinline__ void put_load(uint8_t* st, int i, int lane, i32x4 v) {
   *(i32x4*)(st + swz(8 * i + (lane >> 3), lane & 7)) = v;
