@@ -56,6 +56,9 @@ LONG4 = [M - 1, M - 777, M - 5005, M - 25391]
     (LONG4, True, "e4m3", False),                       # 32 pages per wave
     (LONG4, True, "mxfp8", False),                      # MXFP8 keys and query
     (LONG4, False, "e4m3", True),                       # the bf16 query as stored
+    # long rows among short ones: the launches are planned per run of tokens, each with its
+    # own chunk size
+    ([M - 777] + [3000 + 97 * i for i in range(20)] + [M - 9000], True, "e4m3", False),
 ])
 def test_decode_scorer_long_chunks(lens, random_pages, k_fmt, bf16_query):
     inp = _inputs(lens, random_pages, k_fmt)
@@ -93,7 +96,8 @@ def test_decode_scorer_long_chunks(lens, random_pages, k_fmt, bf16_query):
         # pages at the chunk edges of every chunk size, the last ones and a seeded fill
         edge = [c // 64 + o for step in (4096, 8192, 16384) for c in range(step, n, step)
                 for o in (-1, 0)]
-        pages = np.unique(np.concatenate([edge, np.arange(max(0, nbt - 8), nbt),
+        pages = np.unique(np.concatenate([np.asarray(edge, dtype=np.int64),
+                                          np.arange(max(0, nbt - 8), nbt),
                                           rng.integers(0, nbt, size=200)]))
         for j in pages:
             pp = np.arange(64 * j, min(64 * j + 64, n))
