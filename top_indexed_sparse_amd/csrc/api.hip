@@ -219,12 +219,15 @@ std::vector<Segment> plan_segments(const tis_batch_t* b, int t0, int tc, bool pr
 // brings the set-up below 6% of a workgroup's time.)
 int decode_pages_per_wave(const tis_batch_t* b, int t0, int tc) {
   constexpr int kUnits = 256, kSetup = 2;
+  // the requests that hold tokens t0 .. t0+tc-1: from the last r with cu_q[r] <= t0
+  const int r0 = std::max(
+      0, (int)(std::upper_bound(b->cu_q_host, b->cu_q_host + b->B + 1, t0) - b->cu_q_host) - 1);
   int best = 8;
   int64_t best_cost = INT64_MAX;
   for (int np = 8; np <= 32; np *= 2) {
     const int64_t ck = 512 * (int64_t)np;
     int64_t units = 0;
-    for (int r = 0; r < b->B; ++r) {
+    for (int r = r0; r < b->B && b->cu_q_host[r] < t0 + tc; ++r) {
       const int a = std::max(b->cu_q_host[r], t0), e = std::min(b->cu_q_host[r + 1], t0 + tc);
       for (int t = a; t < e; ++t) {
         const int64_t n = (int64_t)b->seq_lens_host[r] - (b->cu_q_host[r + 1] - t) + 1;
