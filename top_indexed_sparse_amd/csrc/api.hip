@@ -44,6 +44,12 @@ constexpr int kMaxPages = 1 << 24;
 // Scores that do not stay on chip go to a workspace of at most this many bytes; longer
 // batches are processed in row chunks.
 constexpr size_t kScoreScratchBudget = size_t(1) << 30;
+// ... unless that holds fewer than kMinChunkRows rows (long rows): then up to kMinChunkRows
+// rows within kScoreScratchMax bytes, since each chunk's launches end in a partly idle tail
+// (ragged, rows up to 252K positions: 49 chunks of 1,065 rows took the fused call 26.4 ms, 13
+// of 4,096 rows 25.0 ms; prefill64k keeps its 4,096-row chunks, which larger ones slowed).
+constexpr size_t kScoreScratchMax = size_t(1) << 32;
+constexpr int64_t kMinChunkRows = 4096;
 
 struct HostInfo {
   int max_n = 0;   // longest causal range of any query token (= max seq_len with q_len > 0)
@@ -276,10 +282,13 @@ size_t fused_scores_bytes(int rows, const HostInfo& hi) {
 }
 
 // score rows per chunk under a byte budget for the score rows (0 if one row does not fit)
+// Rows of scores per chunk of the fused call: within `budget` bytes, or (long rows) up to
+// kMinChunkRows rows within `cap` bytes.
 int fused_rows_per_chunk(const tis_batch_t* b, const HostInfo& hi,
-                         size_t budget = kScoreScratchBudget) {
-  const int64_t row_bytes = round4(hi.max_n) * 4;
-  int64_t r = (int64_t)budget / std::max<int64_t>(row_bytes, 1);
+                         size_t budget = kScoreScratchBudget, size_t cap = kScoreScratchMax) {
+  const int64_t row_bytes = std::max<int64_t>(round4(hi.max_n) * 4, 1);
+  int64_t r = (int64_t)budget / row_bytes;
+  if (r < kMinChunkRows) r = std::max(r, std::min<int64_t>(kMinChunkRows, (int64_t)cap / row_bytes));
   return (int)std::min<int64_t>(r, b->T);
 }
 
@@ -498,7 +507,8 @@ TIS_API tis_status_t index_score_topk_noalloc(const tis_batch_t* batch, const vo
   if (st != TIS_OK) return st;
   // the selection's workspace is bounded by its 64-row limit; the rest holds score rows
   const size_t sel = tis::topk_ws_bytes(64, hi.max_n, K);
-  const int rows = fused_rows_per_chunk(batch, hi, kNoAllocScratch - sel - 256);
+  const int rows = fused_rows_per_chunk(batch, hi, kNoAllocScratch - sel - 256,
+                                        kNoAllocScratch - sel - 256);
   if (rows < 1)
     return fail(TIS_ERR_INVALID,
                 "index_score_topk_noalloc: a score row of %d positions does not fit its %zu-byte "
